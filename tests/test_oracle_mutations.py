@@ -1,0 +1,211 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches each.
+
+Every mutant replaces one oracle function (via monkeypatch, on the CPU) with a
+copy that has one realistic bug: a different operation order, rounding mode,
+range, granularity, index, sign, dropped term or transposed operand.  The
+test passes when at least one pin of ``test_oracle_pins`` fails under it.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle.tq_oracle as tqo
+import test_oracle_pins as pins
+
+_orig = {name: getattr(tqo, name) for name in (
+    "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
+    "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
+    "subspace_split")}
+
+
+def _q_reciprocal(a, bits=4):
+    a = np.asarray(a, dtype=np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    amax = np.max(np.abs(a), axis=1)
+    s = (amax / np.float32(qmax)).astype(np.float32)
+    c = np.zeros(a.shape, np.int16)
+    live = s > 0
+    mult = (np.float32(qmax) / amax[live]).astype(np.float32)
+    c[live] = np.clip(np.rint(a[live] * mult[:, None]), -(qmax + 1), qmax)
+    return c, s
+
+
+def _q_half_away(a, bits=4):
+    a = np.asarray(a, dtype=np.float32)
+    c, s = _orig["quantize_rows"](a, bits)
+    qmax = (1 << (bits - 1)) - 1
+    live = s > 0
+    q = (a[live] / s[live][:, None]).astype(np.float32)
+    c[live] = np.clip(np.sign(q) * np.floor(np.abs(q) + 0.5), -(qmax + 1), qmax)
+    return c, s
+
+
+def _q_qmax_pow2(a, bits=4):
+    return _q_scale_by(a, bits, 1 << (bits - 1))  # q_max taken as 2^(N-1)
+
+
+def _q_scale_by(a, bits, qmax_used):
+    a = np.asarray(a, dtype=np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    amax = np.max(np.abs(a), axis=1)
+    s = (amax / np.float32(qmax_used)).astype(np.float32)
+    c = np.zeros(a.shape, np.int16)
+    live = s > 0
+    c[live] = np.clip(np.rint((a[live] / s[live][:, None]).astype(np.float32)), -(qmax + 1), qmax)
+    return c, s
+
+
+def _q_per_tensor(a, bits=4):
+    a = np.asarray(a, dtype=np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    amax = np.float32(np.max(np.abs(a))) if a.size else np.float32(0)
+    s = np.full(a.shape[0], amax / np.float32(qmax), dtype=np.float32)
+    c = np.zeros(a.shape, np.int16)
+    if amax > 0:
+        c = np.clip(np.rint((a / s[:, None]).astype(np.float32)), -(qmax + 1), qmax).astype(np.int16)
+    return c, s
+
+
+def _q_no_clamp_low(a, bits=4):
+    a = np.asarray(a, dtype=np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    c, s = _orig["quantize_rows"](a, bits)
+    live = s > 0
+    c[live] = np.clip(np.rint((a[live] / s[live][:, None]).astype(np.float32)), -qmax, qmax)
+    return c, s
+
+
+def _w_per_input_channel(w, bits=4):
+    c, s = tqo.quantize_rows(np.asarray(w, np.float32), bits)  # rows of W instead of columns
+    return np.ascontiguousarray(c.T), s
+
+
+def _pack_swapped(codes):
+    c = np.asarray(codes)
+    u = (c.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[..., 1::2] | (u[..., 0::2] << 4)).astype(np.uint8)
+
+
+def _unpack_no_sign(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int16)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def _matmul_drop_last(cx, cw):
+    cx, cw = np.asarray(cx), np.asarray(cw)
+    return _orig["int_matmul"](cx[:, :-1], cw[:, :-1])  # last k term dropped
+
+
+def _matmul_int16_wrap(cx, cw):
+    return _orig["int_matmul"](cx, cw).astype(np.int16).astype(np.int64)
+
+
+def _lowrank_quantized_x(x, l1, l2):
+    c, s = tqo.quantize_rows(x, 4)
+    return _orig["lowrank_branch"](c * s[:, None].astype(np.float64), l1, l2)
+
+
+def _lowrank_sign(x, l1, l2):
+    t, y = _orig["lowrank_branch"](x, l1, l2)
+    return t, -y
+
+
+def _lowrank_drop(x, l1, l2):
+    t, y = _orig["lowrank_branch"](x, l1, l2)
+    return t, 0 * y
+
+
+def _linear_sx_only_first(x, r, l1=None, l2=None, rows=None, cols=None, bits=4):
+    out = _orig["tq_linear_ref"](x, r, l1, l2, rows, cols, bits)
+    # every row dequantised with the first token's scale
+    base = out["s_x"][0] * out["s_w"].astype(np.float64)[None, :] * out["acc"]
+    true = out["s_x"].astype(np.float64)[:, None] * out["s_w"].astype(np.float64)[None, :] * out["acc"]
+    out["Y"] = out["Y"] - true + base
+    return out
+
+
+def _mp_bits_swapped(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi=8):
+    return _orig["tq_linear_mp_ref"](xrot, wrot, d_hi, rows, cols, bits_hi, bits_lo)
+
+
+def _mp_shared_scale(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi=8):
+    out = _orig["tq_linear_mp_ref"](xrot, wrot, d_hi, rows, cols, bits_lo, bits_hi)
+    y = out["s_xl"][:, None].astype(np.float64) * out["s_wl"][None, :] * (out["acc_l"] + out["acc_h"])
+    out["Y"] = y
+    return out
+
+
+def _mp_hi_first(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi=8):
+    x = np.asarray(xrot, np.float32)
+    w = np.asarray(wrot, np.float32)
+    d = x.shape[1]
+    order = np.r_[d_hi:d, 0:d_hi]  # the FIRST d_hi coordinates used as the high subspace
+    return _orig["tq_linear_mp_ref"](x[:, order], w[order], d_hi, rows, cols, bits_lo, bits_hi)
+
+
+def _hadamard_bad(k):
+    h = np.array([[1]], dtype=np.int64)
+    while h.shape[0] < k:
+        h = np.vstack([np.hstack([h, h]), np.hstack([-h, h])])
+    return h
+
+
+def _rotation_no_norm(signs, block, perm=None):
+    return _orig["block_rotation"](signs, block, perm) * np.sqrt(1.0 + 1.0 / block)
+
+
+def _split_swapped(x, w, u, d_hi):
+    u = np.asarray(u, dtype=np.float64)
+    uh, ul = u[:, :d_hi], u[:, d_hi:]
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    return x @ ul, x @ uh, ul.T @ w, uh.T @ w
+
+
+MUTANTS = {
+    "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
+    "quantize_weight": [_w_per_input_channel],
+    "pack_int4": [_pack_swapped],
+    "unpack_int4": [_unpack_no_sign],
+    "int_matmul": [_matmul_drop_last, _matmul_int16_wrap],
+    "lowrank_branch": [_lowrank_quantized_x, _lowrank_sign, _lowrank_drop],
+    "tq_linear_ref": [_linear_sx_only_first],
+    "tq_linear_mp_ref": [_mp_bits_swapped, _mp_shared_scale, _mp_hi_first],
+    "hadamard": [_hadamard_bad],
+    "block_rotation": [_rotation_no_norm],
+    "subspace_split": [_split_swapped],
+}
+
+CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]
+
+
+def _run_all_pins():
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 -- any failure counts as "caught"
+            failed.append((pin.__name__, type(e).__name__))
+    # the slow brute force only for quantiser mutants that may slip past the rest
+    return failed
+
+
+@pytest.mark.parametrize("target,mutant", CASES, ids=[f"{n}:{f.__name__}" for n, f in CASES])
+def test_mutant_is_caught(monkeypatch, target, mutant):
+    monkeypatch.setattr(tqo, target, mutant)
+    failed = _run_all_pins()
+    if not failed and target == "quantize_rows":
+        try:
+            pins.pin_quantizer_bruteforce(amaxes=(3.0,))
+        except Exception as e:  # noqa: BLE001
+            failed.append(("pin_quantizer_bruteforce", type(e).__name__))
+    assert failed, f"mutant {mutant.__name__} of {target} passed every pin"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert _run_all_pins() == []

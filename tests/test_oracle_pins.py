@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+the pages' definitions, closed forms, exact rational arithmetic or brute force
+on tiny inputs.  They are run as tests here and again by
+``test_oracle_mutations.py`` against deliberately broken copies of the oracle,
+to show that a plausible mistake anywhere in it fails at least one pin.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+import os
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.tq_oracle as tqo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# helpers written from IEEE 754 / integer arithmetic, not from the oracle
+# ----------------------------------------------------------------------------
+
+def rn32(q: Fraction) -> Fraction:
+    """Round a rational to the nearest binary32 value, ties to even (IEEE 754)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)  # below the normal range the quantum stays 2^-149
+    quantum = Fraction(2) ** (e - 23)
+    m = round(a / quantum)  # Fraction rounding: nearest, ties to even
+    return sign * m * quantum
+
+
+def rne_int(v: Fraction) -> int:
+    return round(v)  # ties to even for Fraction
+
+
+def f32_hex(v) -> str:
+    return "0x%08x" % int(np.asarray(v, dtype=np.float32).view(np.uint32))
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+def bf16_all_finite() -> np.ndarray:
+    """Every finite bf16 value (both signs), as float32."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    pos = (bits << 16).view(np.float32)
+    return np.concatenate([pos, -pos[1:]])
+
+
+def lossless_codes(rng, rows, k, qmax):
+    """Integer codes in [-qmax, qmax] with one +-qmax in every row."""
+    c = rng.integers(-qmax, qmax + 1, size=(rows, k)).astype(np.int64)
+    j = rng.integers(0, k, size=rows)
+    c[np.arange(rows), j] = np.where(rng.integers(0, 2, size=rows) == 1, qmax, -qmax)
+    return c
+
+
+# ----------------------------------------------------------------------------
+# quantiser
+# ----------------------------------------------------------------------------
+
+def pin_quantizer_golden():
+    for name, bits, vals, s_hex, codes in read_golden("quantizer_examples.txt"):
+        row = np.array([[float(v) for v in vals.split()]], dtype=np.float32)
+        c, s = tqo.quantize_rows(row, int(bits))
+        assert f32_hex(s[0]) == s_hex.lower(), (name, f32_hex(s[0]), s_hex)
+        assert c[0].tolist() == [int(v) for v in codes.split()], (name, c[0].tolist(), codes)
+
+
+def pin_quantizer_bruteforce(amaxes=(3.0, 1.0, 0.69921875, 12.375, 1.5 * 2.0 ** -100), bits=4):
+    """Every finite bf16 x with |x| <= amax, against exact rational arithmetic."""
+    allv = bf16_all_finite()
+    qmax = (1 << (bits - 1)) - 1
+    for amax in amaxes:
+        xs = allv[np.abs(allv) <= np.float32(amax)]
+        rows = np.stack([np.full(xs.shape, amax, dtype=np.float32), xs], axis=1)
+        c, s = tqo.quantize_rows(rows, bits)
+        s_ref = rn32(Fraction(float(np.float32(amax))) / qmax)
+        assert Fraction(float(s[0])) == s_ref, (amax, float(s[0]), s_ref)
+        assert np.all(s == s[0])
+        got = c[:, 1].astype(np.int64)
+        exp = np.empty_like(got)
+        for i, x in enumerate(xs.tolist()):
+            v = rne_int(rn32(Fraction(x) / s_ref))
+            exp[i] = min(max(v, -(qmax + 1)), qmax)
+        bad = np.nonzero(got != exp)[0]
+        assert bad.size == 0, (amax, xs[bad[:5]].tolist(), got[bad[:5]].tolist(), exp[bad[:5]].tolist())
+        assert np.all(c[:, 0] == qmax)
+
+
+def pin_quantizer_invariants(seed=7):
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal((64, 96)) * np.exp(rng.uniform(-6, 6, size=(64, 1)))).astype(np.float32)
+    a[3, 17] *= 50  # an outlier
+    for bits in (4, 8):
+        qmax = (1 << (bits - 1)) - 1
+        c, s = tqo.quantize_rows(a, bits)
+        # absmax element maps to +-qmax; all codes within [-qmax, qmax]
+        j = np.argmax(np.abs(a), axis=1)
+        assert np.all(np.abs(c[np.arange(a.shape[0]), j]) == qmax)
+        assert np.all(np.sign(c[np.arange(a.shape[0]), j]) == np.sign(a[np.arange(a.shape[0]), j]))
+        assert np.abs(c).max() <= qmax
+        # dequantisation error <= s/2 (+ the fp32 rounding of x/s), in exact fp64
+        err = np.abs(a.astype(np.float64) - c.astype(np.float64) * s.astype(np.float64)[:, None])
+        assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 2.0 ** -21 * qmax))
+        # scale is fl32(max|row| / qmax)
+        amax = np.max(np.abs(a), axis=1)
+        assert np.array_equal(s, (amax / np.float32(qmax)).astype(np.float32))
+        # power-of-two scaling of a row leaves codes, scales by 2^k exactly
+        for k in (-5, 3):
+            c2, s2 = tqo.quantize_rows(a * np.float32(2.0 ** k), bits)
+            assert np.array_equal(c2, c)
+            assert np.array_equal(s2, (s * np.float32(2.0 ** k)).astype(np.float32))
+        # negation flips codes (round-half-even is symmetric)
+        c3, s3 = tqo.quantize_rows(-a, bits)
+        assert np.array_equal(c3, -c) and np.array_equal(s3, s)
+        # rows are independent: scaling one row does not touch the others
+        b = a.copy()
+        b[5] *= np.float32(1000.0)
+        c4, s4 = tqo.quantize_rows(b, bits)
+        keep = np.arange(a.shape[0]) != 5
+        assert np.array_equal(c4[keep], c[keep]) and np.array_equal(s4[keep], s[keep])
+
+
+def pin_weight_is_per_output_channel(seed=8):
+    rng = np.random.default_rng(seed)
+    d, m = 24, 10
+    cw = lossless_codes(rng, m, d, 7)  # output channel j = row j of C_w
+    sw = (2.0 ** rng.integers(-9, -3, size=m)).astype(np.float32)
+    w = (cw * sw[:, None]).T.astype(np.float32)  # d x m, column j = channel j
+    c, s = tqo.quantize_weight(w, 4)
+    assert c.shape == (m, d)
+    assert np.array_equal(c, cw)
+    assert np.array_equal(s, sw)
+
+
+# ----------------------------------------------------------------------------
+# packing
+# ----------------------------------------------------------------------------
+
+def pin_pack_golden():
+    g = dict((k, v) for k, v in read_golden("pack_example.txt"))
+    codes = np.array([[int(t) for t in r.split()] for r in g["codes"].split(";")])
+    expect = np.array([[int(t, 16) for t in r.split()] for r in g["bytes"].split(";")], dtype=np.uint8)
+    assert np.array_equal(tqo.pack_int4(codes), expect)
+    assert np.array_equal(tqo.unpack_int4(expect), codes)
+
+
+def pin_pack_roundtrip(seed=9):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(-8, 8, size=(7, 40))
+    p = tqo.pack_int4(c)
+    assert p.dtype == np.uint8 and p.shape == (7, 20)
+    assert np.array_equal(tqo.unpack_int4(p), c)
+    # every byte value decodes and re-encodes to itself
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    assert np.array_equal(tqo.pack_int4(tqo.unpack_int4(allb)), allb)
+    c8 = rng.integers(-128, 128, size=(3, 9))
+    assert np.array_equal(tqo.pack_codes(c8, 8).view(np.int8).astype(np.int64), c8)
+
+
+# ----------------------------------------------------------------------------
+# integer accumulation
+# ----------------------------------------------------------------------------
+
+def pin_accumulator_bruteforce(seed=10):
+    rng = random.Random(seed)
+    for (n, k, m, lo, hi) in ((3, 5, 4, -8, 7), (2, 33, 3, -128, 127), (1, 1, 1, -8, 7), (4, 64, 5, -7, 7)):
+        cx = [[rng.randint(lo, hi) for _ in range(k)] for _ in range(n)]
+        cw = [[rng.randint(lo, hi) for _ in range(k)] for _ in range(m)]
+        exp = [[sum(cx[i][t] * cw[j][t] for t in range(k)) for j in range(m)] for i in range(n)]
+        got = tqo.int_matmul(np.array(cx), np.array(cw))
+        assert got.tolist() == exp
+
+
+def pin_accumulator_invariants(seed=11):
+    rng = np.random.default_rng(seed)
+    cx = rng.integers(-7, 8, size=(6, 128))
+    cw1 = rng.integers(-7, 8, size=(5, 128))
+    cw2 = rng.integers(-7, 8, size=(5, 128))
+    base = tqo.int_matmul(cx, cw1)
+    perm = rng.permutation(128)
+    assert np.array_equal(tqo.int_matmul(cx[:, perm], cw1[:, perm]), base)
+    assert np.array_equal(tqo.int_matmul(cx, cw1 + cw2), base + tqo.int_matmul(cx, cw2))
+    # extreme magnitudes stay exact
+    big = tqo.int_matmul(np.full((1, 14336), -8), np.full((1, 14336), -8))
+    assert int(big[0, 0]) == 64 * 14336
+
+
+# ----------------------------------------------------------------------------
+# the layer
+# ----------------------------------------------------------------------------
+
+def pin_linear_golden():
+    g = dict((k, v) for k, v in read_golden("linear_example.txt"))
+
+    def mat(s):
+        return np.array([[float(t) for t in r.split()] for r in s.split(";")], dtype=np.float32)
+
+    out = tqo.tq_linear_ref(mat(g["X"]), mat(g["R"]), mat(g["L1"]), mat(g["L2"]))
+    assert int(out["acc"][0, 0]) == int(g["acc"])
+    num, den = (int(t) for t in g["Y_num_den"].split())
+    assert Fraction(float(out["Y"][0, 0])) == Fraction(num, den)
+
+
+def _lossless_case(rng, n, d, m):
+    cx = lossless_codes(rng, n, d, 7)
+    sx = (2.0 ** rng.integers(-6, 3, size=n)).astype(np.float32)
+    cw = lossless_codes(rng, m, d, 7)
+    sw = (2.0 ** rng.integers(-10, -4, size=m)).astype(np.float32)
+    x = (cx * sx[:, None]).astype(np.float32)
+    r = (cw * sw[:, None]).T.astype(np.float32)
+    return x, r, cx, sx, cw, sw
+
+
+def pin_linear_lossless(seed=12):
+    """Inputs that quantise without loss: Y(r=0) equals X R exactly."""
+    rng = np.random.default_rng(seed)
+    n, d, m = 5, 48, 7
+    x, r, cx, sx, cw, sw = _lossless_case(rng, n, d, m)
+    out = tqo.tq_linear_ref(x, r)
+    assert np.array_equal(out["codes_x"], cx) and np.array_equal(out["s_x"], sx)
+    assert np.array_equal(out["codes_w"], cw) and np.array_equal(out["s_w"], sw)
+    assert np.array_equal(out["acc"], cx @ cw.T)
+    assert np.array_equal(out["Y"], x.astype(np.float64) @ r.astype(np.float64))
+    # r = 0 (empty low-rank factors) reduces to the same pure W4A4 output
+    out0 = tqo.tq_linear_ref(x, r, np.zeros((d, 0), np.float32), np.zeros((0, m), np.float32))
+    assert np.array_equal(out0["Y"], out["Y"])
+
+
+def pin_linear_lowrank(seed=13):
+    rng = np.random.default_rng(seed)
+    n, d, m, rk = 6, 40, 9, 3
+    x, r, *_ = _lossless_case(rng, n, d, m)
+    l1 = rng.standard_normal((d, rk)).astype(np.float32)
+    l2 = rng.standard_normal((rk, m)).astype(np.float32)
+    x64, r64, l164, l264 = (a.astype(np.float64) for a in (x, r, l1, l2))
+    full = tqo.tq_linear_ref(x, r, l1, l2)["Y"]
+    ref = x64 @ r64 + x64 @ (l164 @ l264)
+    assert np.allclose(full, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # R = 0: scales 0, codes 0, output = X (L1 L2) by associativity, from the
+    # unquantised X (a generic X, whose quantisation is lossy)
+    xg = rng.standard_normal((n, d)).astype(np.float32)
+    z = tqo.tq_linear_ref(xg, np.zeros_like(r), l1, l2)
+    assert np.all(z["s_w"] == 0) and np.all(z["codes_w"] == 0)
+    lr = xg.astype(np.float64) @ (l164 @ l264)
+    assert np.allclose(z["Y"], lr, rtol=1e-12, atol=1e-12 * np.abs(lr).max())
+    # L2 = 0 gives the pure W4A4 output
+    assert np.array_equal(tqo.tq_linear_ref(x, r, l1, np.zeros_like(l2))["Y"], tqo.tq_linear_ref(x, r)["Y"])
+
+
+def pin_linear_sampling(seed=14):
+    """Sampled rows / columns equal the corresponding entries of the full output."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((9, 64)).astype(np.float32)
+    r = (rng.standard_normal((64, 11)) * 0.02).astype(np.float32)
+    l1 = rng.standard_normal((64, 4)).astype(np.float32)
+    l2 = rng.standard_normal((4, 11)).astype(np.float32)
+    full = tqo.tq_linear_ref(x, r, l1, l2)
+    rows, cols = np.array([8, 0, 3]), np.array([10, 2])
+    part = tqo.tq_linear_ref(x, r, l1, l2, rows=rows, cols=cols)
+    assert np.array_equal(part["Y"], full["Y"][np.ix_(rows, cols)])
+    assert np.array_equal(part["acc"], full["acc"][np.ix_(rows, cols)])
+
+
+# ----------------------------------------------------------------------------
+# rotation and the two-subspace form
+# ----------------------------------------------------------------------------
+
+def pin_hadamard():
+    for k in (1, 2, 8, 128):
+        h = tqo.hadamard(k)
+        assert np.array_equal(h @ h.T, k * np.eye(k, dtype=np.int64))
+        idx = np.arange(k)
+        pc = np.vectorize(lambda v: bin(int(v)).count("1"))(idx[:, None] & idx[None, :])
+        assert np.array_equal(h, np.where(pc % 2 == 0, 1, -1))  # Sylvester form
+
+
+def pin_rotation_identities(seed=15):
+    rng = np.random.default_rng(seed)
+    d, n, m, dh = 256, 5, 7, 32
+    signs = np.where(rng.integers(0, 2, size=d) == 1, 1.0, -1.0)
+    perm = rng.permutation(d)
+    u = tqo.block_rotation(signs, 128, perm)
+    assert np.allclose(u @ u.T, np.eye(d), atol=1e-13)
+    x = rng.standard_normal((n, d))
+    w = rng.standard_normal((d, m))
+    xu, uw = tqo.rotate(x, w, u)
+    assert np.allclose(xu @ uw, x @ w, rtol=1e-12, atol=1e-12)  # Eq. 3
+    ul, uh = u[:, : d - dh], u[:, d - dh:]
+    assert np.allclose(ul @ ul.T + uh @ uh.T, np.eye(d), atol=1e-13)  # Eq. 5
+    xl, xh, wl, wh = tqo.subspace_split(x, w, u, dh)
+    assert xl.shape == (n, d - dh) and xh.shape == (n, dh) and wl.shape == (d - dh, m) and wh.shape == (dh, m)
+    assert np.allclose(xl @ wl + xh @ wh, x @ w, rtol=1e-12, atol=1e-12)  # Eq. 8
+    # X_l, X_h are the column blocks of X U; W_l, W_h the row blocks of U^T W
+    assert np.allclose(np.hstack([xl, xh]), xu, rtol=0, atol=1e-13)
+    assert np.allclose(np.vstack([wl, wh]), uw, rtol=0, atol=1e-13)
+
+
+def pin_two_subspace_lossless(seed=16):
+    """Eq. 9 with inputs that quantise without loss is exactly X_l W_l + X_h W_h."""
+    rng = np.random.default_rng(seed)
+    n, dl, dh, m = 4, 64, 16, 6
+    cxl = lossless_codes(rng, n, dl, 7)
+    cxh = lossless_codes(rng, n, dh, 127)
+    cwl = lossless_codes(rng, m, dl, 7)
+    cwh = lossless_codes(rng, m, dh, 127)
+    sxl = 2.0 ** rng.integers(-4, 2, size=n)
+    sxh = 2.0 ** rng.integers(-9, -5, size=n)
+    swl = 2.0 ** rng.integers(-8, -3, size=m)
+    swh = 2.0 ** rng.integers(-12, -8, size=m)
+    xl, xh = cxl * sxl[:, None], cxh * sxh[:, None]
+    wl, wh = (cwl * swl[:, None]).T, (cwh * swh[:, None]).T
+    xrot = np.hstack([xl, xh]).astype(np.float32)
+    wrot = np.vstack([wl, wh]).astype(np.float32)
+    out = tqo.tq_linear_mp_ref(xrot, wrot, dh)
+    assert np.array_equal(out["codes_xl"], cxl) and np.array_equal(out["codes_xh"], cxh)
+    assert np.array_equal(out["codes_wl"], cwl) and np.array_equal(out["codes_wh"], cwh)
+    assert np.array_equal(out["acc_l"], cxl @ cwl.T) and np.array_equal(out["acc_h"], cxh @ cwh.T)
+    assert np.array_equal(out["Y"], xl @ wl + xh @ wh)
+    # d_hi = d is W8A8; d_hi = 0 is W4A4, both on the rotated data
+    x8 = (cxh * sxh[:, None]).astype(np.float32)
+    w8 = (cwh * swh[:, None]).T.astype(np.float32)
+    assert np.array_equal(tqo.tq_linear_mp_ref(x8, w8, dh)["Y"], x8.astype(np.float64) @ w8)
+    x4 = (cxl * sxl[:, None]).astype(np.float32)
+    w4 = (cwl * swl[:, None]).T.astype(np.float32)
+    assert np.array_equal(tqo.tq_linear_mp_ref(x4, w4, 0)["Y"], x4.astype(np.float64) @ w4)
+    assert np.array_equal(tqo.tq_linear_mp_ref(x4, w4, 0)["Y"], tqo.tq_linear_ref(x4, w4)["Y"])
+
+
+ALL_PINS = [
+    pin_quantizer_golden,
+    pin_quantizer_invariants,
+    pin_weight_is_per_output_channel,
+    pin_pack_golden,
+    pin_pack_roundtrip,
+    pin_accumulator_bruteforce,
+    pin_accumulator_invariants,
+    pin_linear_golden,
+    pin_linear_lossless,
+    pin_linear_lowrank,
+    pin_linear_sampling,
+    pin_hadamard,
+    pin_rotation_identities,
+    pin_two_subspace_lossless,
+]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+@pytest.mark.slow
+def test_pin_quantizer_bruteforce_int4():
+    pin_quantizer_bruteforce()
+
+
+@pytest.mark.slow
+def test_pin_quantizer_bruteforce_int8():
+    pin_quantizer_bruteforce(amaxes=(100.0, 0.375), bits=8)

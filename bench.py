@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the rank-augmented W4A4 linear layer on one MI355X.
+
+One step = one tq_linear call (per-token activation quantisation, first
+low-rank stage, integer GEMM and the shared epilogue) on the Llama-3-8B
+attention-projection workload (n = d = m = 4096, r = 32), inputs resident in
+HBM.  Prints ONE JSON line (stdout); progress goes to stderr.
+
+  value     effective int ops/s of the whole call, 2 n d m / t, in TOPS
+  roofline  the integer GEMM kernel: algorithmic 2 n d m per launch over its
+            average launch duration (HIP events on the launch stream),
+            against the MI355X dense int8 MFMA peak (5.0 POP/s)
+  cpu_baseline  the CPU oracle on the same workload (a bounded sample)
+  sweep     the other workloads (decode rows against the 8 TB/s HBM peak)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tq_linear effective TOPS + % int8-MFMA peak (prefill); GB/s + % HBM (decode)"
+PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_w4a4_attn_proj.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_augmented_quantized_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_hash or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def alg_bytes(n, d, m, r, x_bytes=2, y_bytes=2):
+    """Bytes the layer itself must move: X, weight codes + scales, L1, L2, Y."""
+    return n * d * x_bytes + d * m // 2 + 4 * m + 2 * d * r + 2 * r * m + y_bytes * n * m
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        fn(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def kernel_ms(fn, steps, torch, tq):
+    tq.tq_profile_reset()
+    tq.tq_profile_enable(True)
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    stats = tq.tq_profile_read()
+    tq.tq_profile_enable(False)
+    tq.tq_profile_reset()
+    return {k: v[1] / v[0] for k, v in stats.items()}
+
+
+class LinearCase:
+    """Device-resident inputs of one rank-augmented workload, with `copies`
+    independent weight sets cycled through so that repeated calls stream the
+    weights from HBM rather than from the last-level cache."""
+
+    def __init__(self, wl, n, copies, torch, tq, dev):
+        from workloads import draw_linear
+
+        c = draw_linear(wl, n=n)
+        self.n, self.d, self.m, self.r = n, wl.d, wl.m, wl.r
+        xdt = torch.bfloat16 if wl.x_dtype == "bf16" else torch.float32
+        self.x_bytes = 2 if wl.x_dtype == "bf16" else 4
+        self.X = torch.from_numpy(c["X"]).to(dev).to(xdt)
+        R = torch.from_numpy(c["R"]).to(dev)
+        L1 = torch.from_numpy(c["L1"]).to(dev).bfloat16()
+        L2 = torch.from_numpy(c["L2"]).to(dev).bfloat16()
+        self.w = []
+        for _ in range(copies):
+            wc, sw = tq.tq_pack_weight(R, 4)
+            lr = tq.tq_pack_lowrank(L1, L2) if self.r else None
+            self.w.append((wc, sw, lr))
+        del R
+        self.Y = torch.empty((n, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws = tq.linear_workspace(n, self.d, self.m, self.r, dev)
+        self.tq = tq
+
+    def __call__(self, i):
+        wc, sw, lr = self.w[i % len(self.w)]
+        self.tq.tq_linear(self.X, wc, sw, lr, self.m, self.r, Y=self.Y, ws=self.ws)
+
+
+class MpCase:
+    def __init__(self, wl, torch, tq, dev):
+        from workloads import draw_two_subspace
+
+        c = draw_two_subspace(wl)
+        self.n, self.d, self.m, self.dh = wl.n, wl.d, wl.m, wl.d_hi
+        dl = self.d - self.dh
+        self.X = torch.from_numpy(c["Xrot"]).to(dev).bfloat16()
+        W = torch.from_numpy(c["Wrot"])
+        self.wl = tq.tq_pack_weight(W[:dl].contiguous().to(dev), 4)
+        self.wh = tq.tq_pack_weight(W[dl:].contiguous().to(dev), 8)
+        del W, c
+        self.Y = torch.empty((self.n, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(tq.tq_linear_mp_workspace_bytes(self.n, self.d, self.dh), dtype=torch.uint8, device=dev)
+        self.tq = tq
+
+    def __call__(self, i):
+        self.tq.tq_linear_mp(self.X, self.dh, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m, Y=self.Y,
+                             ws=self.ws)
+
+
+def cpu_baseline(wl, rows):
+    """The oracle as it stands, timed on the host on the first `rows` tokens."""
+    import oracle.tq_oracle as tqo
+    from workloads import draw_linear
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    c = draw_linear(wl, n=rows)
+    t0 = time.perf_counter()
+    tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * wl.d * wl.m
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {wl.n} tokens, all {wl.m} output channels; numpy/fp64 oracle incl. "
+                      f"weight and activation quantisation, exact integer product, fp64 epilogue; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn_proj")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copies", type=int, default=16, help="weight copies cycled through (defeats the MALL)")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding is a "
+              "design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rank_augmented_quantized_amd as tq
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tq.load()
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    n, d, m, r = wl.n, wl.d, wl.m, wl.r
+
+    log(f"[bench] {wl.title}: building inputs")
+    case = LinearCase(wl, n, 2, torch, tq, dev)
+    ms = time_calls(case, args.steps, args.warmup, torch)
+    ops = 2.0 * n * d * m
+    value = ops / (ms * 1e-3) / 1e12
+    log(f"[bench] {wl.title}: {ms * 1e3:.1f} us/call, {value:.1f} TOPS")
+    kms = kernel_ms(case, args.steps, torch, tq)
+    gemm = kms.get("gemm_w4a4") or max(kms.values())
+    achieved = ops / (gemm * 1e-3) / 1e12
+    khash = kernel_source_hash()
+    traffic = read_traffic(khash)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic, "kernel": "gemm_w4a4",
+                "kernel_us": round(gemm * 1e3, 2),
+                "kernels_us": {k: round(v * 1e3, 2) for k, v in kms.items()}}
+    log(f"[bench] kernels: {roofline['kernels_us']}")
+    del case
+    torch.cuda.empty_cache()
+
+    sweep = []
+    if not args.no_sweep:
+        for name, ns in (("mlp_gate_up", (1, 16, 256, 4096)), ("mlp_down", (1, 8, 32)), ("small", (16,))):
+            w = WORKLOADS[name]
+            for nn in ns:
+                c = LinearCase(w, nn, args.copies if nn <= 256 else 2, torch, tq, dev)
+                t = time_calls(c, max(20, args.steps // 2), 10, torch)
+                km = kernel_ms(c, 20, torch, tq)
+                b = alg_bytes(nn, w.d, w.m, w.r, c.x_bytes)
+                o = 2.0 * nn * w.d * w.m
+                row = {"workload": w.title, "n": nn, "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
+                       "GBps": round(b / (t * 1e-3) / 1e9, 1), "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                       "pct_hbm": round(100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                       "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+                sweep.append(row)
+                log(f"[bench] sweep {row}")
+                del c
+                torch.cuda.empty_cache()
+        w = WORKLOADS["two_subspace"]
+        log(f"[bench] {w.title}: building inputs")
+        c = MpCase(w, torch, tq, dev)
+        t = time_calls(c, 20, 3, torch)
+        km = kernel_ms(c, 10, torch, tq)
+        o = 2.0 * w.n * w.d * w.m
+        b = w.n * w.d * 2 + (w.d - w.d_hi) * w.m // 2 + w.d_hi * w.m + 8 * w.m + 2 * w.n * w.m
+        row = {"workload": w.title, "n": w.n, "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
+               "GBps": round(b / (t * 1e-3) / 1e9, 1), "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+               "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+        sweep.append(row)
+        log(f"[bench] sweep {row}")
+        del c
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} tokens")
+        cpu = cpu_baseline(wl, args.cpu_rows)
+        log(f"[bench] cpu baseline {cpu}")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": wl.title, "n": n, "d": d, "m": m, "r": r, "x_dtype": wl.x_dtype, "y_dtype": "bf16",
+                   "pct_int8_mfma_peak": round(100 * value / PEAK_INT8_TOPS, 2)},
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "kernel_source_hash": khash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

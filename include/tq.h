@@ -1,0 +1,210 @@
+/*
+ * tq.h -- C ABI of the rank-augmented W4A4 linear layer for MI355X (gfx950).
+ *
+ * The layer computes, for activations X (n x d) and a weight split into a
+ * residual R (d x m) and low-rank factors L1 (d x r), L2 (r x m),
+ *
+ *     Y = s_x s_w^T (.) (Q4(X) Q4(R)) + (X L1) L2                           (1)
+ *
+ * the low-rank + residual form of the SVDQuant/TwinQuant line of work
+ * ("TwinQuant: Learnable Subspace Decomposition for W4A4 LLM Quantization",
+ * section 02.A; one shared epilogue as in section 04.C, Figure 4), and the
+ * two-subspace mixed-precision form
+ *
+ *     Y = Q_l(X_l) Q_l(W_l) + Q_h(X_h) Q_h(W_h)                             (2)
+ *
+ * of "CoQuant: Joint Weight-Activation Subspace Projection for
+ * Mixed-Precision LLMs", Eq. 9, on activations and weights already rotated by
+ * an orthogonal U (CoQuant Eq. 3, 6, 7).
+ *
+ * Quantiser (TwinQuant notes section 02, quantization formula; CoQuant Eq. 1
+ * with zero-point 0): per row of X (token) and per output channel of the
+ * weight, amax = max|v|, s = fl32(amax / q_max) with q_max = 2^(bits-1) - 1,
+ * code = clamp(rne(fl32(v / s)), -2^(bits-1), q_max); rne rounds half to
+ * even, fl32 is an IEEE fp32 division; a row whose s is 0 gets codes 0.
+ * Codes and their integer products are exact; the integer product of the
+ * residual is accumulated exactly in int32 (TwinQuant notes section 02 and
+ * Figure 4).
+ *
+ * Conventions for every entry point:
+ *  - Every pointer is a DEVICE pointer (memory of the current HIP device),
+ *    except where stated.  The caller owns all memory; the library never
+ *    allocates device memory and keeps no state between calls except the
+ *    optional profiling record (tq_profile_*).
+ *  - Every call is asynchronous on `stream` (0 = the null stream).  A status
+ *    other than TQ_OK from argument checking means nothing was enqueued.
+ *    TQ_ERR_HIP reports a launch failure (hipGetLastError after the launch);
+ *    faults during execution surface at the caller's next synchronisation.
+ *  - Matrices are row-major and densely packed.  Device pointers must be
+ *    16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *  - Codes: 4-bit codes are two's-complement nibbles, two per byte, the even
+ *    index of each pair in the low nibble; 8-bit codes are int8.  A code
+ *    matrix of `rows` x `k` therefore occupies rows * k * bits / 8 bytes, the
+ *    k dimension contiguous ("K-contiguous").
+ *  - Shapes: n == 0 is a valid no-op.  d must be a positive multiple of 32 and
+ *    m positive; any n and m are handled (no tile multiple needed).  r may be
+ *    0..256.  Non-finite inputs are outside the contract (codes unspecified).
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_NULL = -1,      /* a required pointer is NULL */
+  TQ_ERR_SHAPE = -2,     /* a size is out of range or breaks a multiple-of rule */
+  TQ_ERR_DTYPE = -3,     /* unsupported element type */
+  TQ_ERR_BITS = -4,      /* unsupported bit width */
+  TQ_ERR_ALIGN = -5,     /* a pointer is not 16-byte aligned */
+  TQ_ERR_WORKSPACE = -6, /* workspace smaller than the queried size */
+  TQ_ERR_HIP = -7        /* the HIP runtime reported an error */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* tq_status_string(tq_status s);
+
+/* ABI version of this header (major * 100 + minor). */
+int tq_version(void);
+
+/* Bytes of a code matrix: rows * k * bits / 8 (0 for invalid arguments). */
+size_t tq_codes_bytes(int64_t rows, int64_t k, int bits);
+
+/*
+ * tq_pack_weight -- offline per-output-channel symmetric quantisation.
+ *   W       d x m weight (Y = X W), element type w_dt (TQ_F32 or TQ_BF16).
+ *   bits    4 or 8.
+ *   w_codes out: m x (d*bits/8) bytes; row j holds output channel j (column j
+ *           of W) with k contiguous.
+ *   s_w     out: m fp32 scales.
+ * Per-channel symmetric weights follow CoQuant's experimental protocol (the
+ * ResQ setting: per-channel symmetric weight quantisation).
+ */
+tq_status tq_pack_weight(const void* W, tq_dtype w_dt, int64_t d, int64_t m, int bits,
+                         void* w_codes, float* s_w, hipStream_t stream);
+
+/* Bytes of the packed low-rank factors of tq_pack_lowrank. */
+size_t tq_lowrank_bytes(int64_t d, int64_t m, int64_t r);
+
+/*
+ * tq_pack_lowrank -- lays out the low-rank factors for tq_linear (offline).
+ *   L1      d x r, L2 r x m, element type dt (TQ_F32 values are rounded to
+ *           bf16, ties to even; TQ_BF16 values are copied).
+ *   lowrank out: tq_lowrank_bytes(d, m, r) bytes, an opaque bf16 layout
+ *           (L1 and L2 transposed, r padded with zeros to a multiple of 32).
+ * The factors U, V of TwinQuant notes section 02.A (L1 = U, L2 = V).
+ */
+tq_status tq_pack_lowrank(const void* L1, const void* L2, tq_dtype dt, int64_t d, int64_t m,
+                          int64_t r, void* lowrank, hipStream_t stream);
+
+/*
+ * tq_quantize_act -- per-token symmetric quantisation of activations.
+ *   X       n x d, element type x_dt.  bits 4 or 8.
+ *   x_codes out: n x (d*bits/8) bytes.   s_x out: n fp32 scales.
+ * "The residual GEMM quantizes activations concurrently" (TwinQuant notes
+ * section 04.C); per-token activation scales (CoQuant protocol).
+ */
+tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int bits,
+                          void* x_codes, float* s_x, hipStream_t stream);
+
+/* Workspace bytes tq_linear needs for these sizes. */
+size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
+
+/*
+ * tq_linear -- the rank-augmented quantised linear layer, equation (1).
+ *   X        n x d activations (x_dt), quantised per token at 4 bits inside
+ *            the call; the low-rank branch takes X itself (as bf16).
+ *   w_codes, s_w   the residual from tq_pack_weight(R, ..., bits = 4).
+ *   lowrank  from tq_pack_lowrank(L1, L2, ...), or NULL iff r == 0.
+ *   Y        out: n x m, element type y_dt (TQ_BF16 or TQ_F32), rounded to
+ *            nearest even from the fp32 epilogue.
+ *   ws       device workspace of at least tq_linear_workspace_bytes(n,d,m,r)
+ *            bytes.  Its first 256 bytes are completion counters of the
+ *            small-n path (n <= 32): they must be zero before the first call
+ *            that uses this workspace (e.g. hipMemset once after allocating
+ *            it), and every call leaves them zero.  The rest is scratch whose
+ *            contents on entry are ignored.
+ * For n <= 32 the call runs a memory-bound path (weight codes streamed once);
+ * otherwise a tiled MFMA path.  Both produce bit-identical integer
+ * accumulators.
+ */
+tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                    const void* w_codes, const float* s_w, const void* lowrank,
+                    void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tq_linear_workspace_offsets -- where tq_linear keeps its intermediate
+ * results inside the workspace, for inspection after a call:
+ *   off[0] s_x (n fp32), off[1] activation codes (n x d/2 bytes),
+ *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
+ *   >= 32; absent when r == 0).  Returns TQ_ERR_SHAPE for invalid sizes.
+ */
+tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[3]);
+
+/* Workspace bytes tq_linear_mp needs for these sizes. */
+size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
+
+/*
+ * tq_linear_mp -- the two-subspace mixed-precision layer, equation (2).
+ *   Xrot     n x d rotated activations (x_dt).  The first d - d_hi columns
+ *            are the low-precision subspace (4 bits), the last d_hi columns
+ *            the high-precision subspace (8 bits); each subspace has its own
+ *            per-token scale.  d - d_hi must be a multiple of 32 and d_hi a
+ *            multiple of 16 (either may be 0).
+ *   wl_codes, s_wl  tq_pack_weight of the first d - d_hi rows of the rotated
+ *            weight at bits = 4;  wh_codes, s_wh  of the last d_hi rows at
+ *            bits = 8 (NULL allowed when d_hi == 0).
+ *   Y, y_dt, ws, ws_bytes as in tq_linear (workspace from
+ *            tq_linear_mp_workspace_bytes).
+ * CoQuant Eq. 9 with 8-bit high-precision and 4-bit low-precision subspaces
+ * (CoQuant experimental protocol).
+ */
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                       const void* wl_codes, const float* s_wl, const void* wh_codes,
+                       const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * tq_debug_accumulate -- exact integer product of two code matrices, exported.
+ *   x_codes  n x k codes, w_codes m x k codes (both bits wide, K-contiguous).
+ *   acc      out: n x m int32, acc[i][j] = sum_t x[i][t] * w[j][t], exactly.
+ * Runs the same integer main loops as tq_linear / tq_linear_mp (the prefill
+ * loop for n > 32, the small-n loop otherwise) so the accumulators of the
+ * product path can be checked bit for bit.  k must be a multiple of 32
+ * (bits = 4) or 16 (bits = 8).
+ */
+tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k,
+                              int64_t m, int bits, int32_t* acc, hipStream_t stream);
+
+/*
+ * Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by a pair of HIP events recorded on the launch stream.
+ * tq_profile_read synchronises on the recorded events and returns, per kernel
+ * name, the number of launches and their summed duration in milliseconds
+ * (host arrays of `max` entries; returns the number of kernel names, or a
+ * negative tq_status).  tq_profile_reset drops the record.  Not thread-safe.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} tq_kernel_stat;
+
+tq_status tq_profile_enable(int on);
+int tq_profile_read(tq_kernel_stat* out, int max);
+tq_status tq_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,24 @@
+"""Rank-augmented W4A4 linear layer for MI355X (gfx950).
+
+The computation lives in the HIP library ``libtq.so`` (C ABI: include/tq.h);
+``rank_augmented_quantized_amd.tq`` is its Python binding.
+"""
+
+from .tq import (  # noqa: F401
+    TQError,
+    linear_workspace,
+    load,
+    tq_codes_bytes,
+    tq_debug_accumulate,
+    tq_linear,
+    tq_linear_mp,
+    tq_linear_mp_workspace_bytes,
+    tq_linear_workspace_bytes,
+    tq_linear_workspace_offsets,
+    tq_pack_lowrank,
+    tq_pack_weight,
+    tq_profile_enable,
+    tq_profile_read,
+    tq_profile_reset,
+    tq_quantize_act,
+)

@@ -1,0 +1,402 @@
+// C ABI of the rank-augmented W4A4 layer: argument checking, workspace
+// layout, kernel selection and optional per-kernel event timing.  Every
+// check runs before any HIP call, so a failing check enqueues nothing.
+
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_kernels.h"
+
+namespace {
+
+using tq::GemmArgs;
+
+constexpr int kSmallN = 32;       // n <= kSmallN takes the memory-bound small-n path
+constexpr int kDecodeChunk = 512;  // k per partial block of the small-n low-rank stage
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// r rounded up to the padded width of the packed low-rank factors.
+int64_t r_padded(int64_t r) {
+  if (r <= 0) return 0;
+  int64_t p = 32;
+  while (p < r) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// profiling
+// ---------------------------------------------------------------------------
+struct ProfRecord {
+  std::string name;
+  hipEvent_t e0, e1;
+};
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<ProfRecord> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+// Wraps one kernel launch; returns the launcher's error.
+template <typename F>
+hipError_t timed(const char* name, hipStream_t st, F&& launch) {
+  Profiler& p = prof();
+  if (!p.on) return launch();
+  hipEvent_t e0 = p.get(), e1 = p.get();
+  if (e0) hipEventRecord(e0, st);
+  hipError_t err = launch();
+  if (e1) hipEventRecord(e1, st);
+  if (e0 && e1)
+    p.recs.push_back({name, e0, e1});
+  return err;
+}
+
+#define TQ_RUN(name, st, expr)                                  \
+  do {                                                           \
+    hipError_t _e = timed(name, st, [&]() { return (expr); });  \
+    if (_e != hipSuccess) return TQ_ERR_HIP;                     \
+  } while (0)
+
+struct LinearWs {
+  size_t ctr, sx, xc, t, p, total;
+  int r_pad, nchunk;
+  bool small;
+};
+
+LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
+  (void)m;
+  LinearWs w{};
+  w.small = n <= kSmallN;
+  w.r_pad = (int)r_padded(r);
+  w.nchunk = (int)((d + kDecodeChunk - 1) / kDecodeChunk);
+  size_t o = 0;
+  w.ctr = o;
+  o += 256;
+  w.sx = o;
+  o = align256(o + (size_t)n * 4);
+  w.xc = o;
+  o = align256(o + (size_t)n * (size_t)d / 2);
+  w.t = o;
+  o = align256(o + (size_t)n * (size_t)w.r_pad * 2);
+  w.p = o;
+  if (w.small && w.r_pad > 0) o = align256(o + (size_t)w.nchunk * (size_t)n * (size_t)w.r_pad * 4);
+  w.total = o;
+  return w;
+}
+
+struct MpWs {
+  size_t sxl, sxh, xl, xh, total;
+};
+
+MpWs mp_ws(int64_t n, int64_t d, int64_t d_hi) {
+  MpWs w{};
+  const int64_t dl = d - d_hi;
+  size_t o = 0;
+  w.sxl = o;
+  o = align256(o + (size_t)n * 4);
+  w.sxh = o;
+  o = align256(o + (size_t)n * 4);
+  w.xl = o;
+  o = align256(o + (size_t)n * (size_t)dl / 2);
+  w.xh = o;
+  o = align256(o + (size_t)n * (size_t)d_hi);
+  w.total = o;
+  return w;
+}
+
+bool valid_dtype(tq_dtype t) { return t == TQ_F32 || t == TQ_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_NULL: return "TQ_ERR_NULL: a required pointer is NULL";
+    case TQ_ERR_SHAPE: return "TQ_ERR_SHAPE: a size is out of range";
+    case TQ_ERR_DTYPE: return "TQ_ERR_DTYPE: unsupported element type";
+    case TQ_ERR_BITS: return "TQ_ERR_BITS: unsupported bit width";
+    case TQ_ERR_ALIGN: return "TQ_ERR_ALIGN: pointer not 16-byte aligned";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE: workspace too small";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown tq_status";
+}
+
+int tq_version(void) { return 100; }
+
+size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
+  if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
+  return (size_t)rows * (size_t)k * (size_t)bits / 8;
+}
+
+tq_status tq_pack_weight(const void* W, tq_dtype w_dt, int64_t d, int64_t m, int bits, void* w_codes, float* s_w,
+                         hipStream_t stream) {
+  if (bits != 4 && bits != 8) return TQ_ERR_BITS;
+  if (!valid_dtype(w_dt)) return TQ_ERR_DTYPE;
+  if (d <= 0 || m <= 0 || d > kMaxDim || m > kMaxDim || d % (bits == 4 ? 32 : 16)) return TQ_ERR_SHAPE;
+  if (!W || !w_codes || !s_w) return TQ_ERR_NULL;
+  if (!aligned16(W) || !aligned16(w_codes) || !aligned16(s_w)) return TQ_ERR_ALIGN;
+  TQ_RUN("pack_weight", stream, tq::launch_pack_weight(W, w_dt == TQ_BF16, (int)d, (int)m, bits, w_codes, s_w, stream));
+  return TQ_OK;
+}
+
+size_t tq_lowrank_bytes(int64_t d, int64_t m, int64_t r) {
+  if (d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
+  const int64_t rp = r_padded(r);
+  return (size_t)(rp * d + m * rp) * 2;
+}
+
+tq_status tq_pack_lowrank(const void* L1, const void* L2, tq_dtype dt, int64_t d, int64_t m, int64_t r,
+                          void* lowrank, hipStream_t stream) {
+  if (!valid_dtype(dt)) return TQ_ERR_DTYPE;
+  if (d <= 0 || m <= 0 || d > kMaxDim || m > kMaxDim || d % 32 || r < 1 || r > 256) return TQ_ERR_SHAPE;
+  if (!L1 || !L2 || !lowrank) return TQ_ERR_NULL;
+  if (!aligned16(lowrank)) return TQ_ERR_ALIGN;
+  const int rp = (int)r_padded(r);
+  TQ_RUN("pack_lowrank", stream,
+         tq::launch_pack_lowrank(L1, L2, dt == TQ_BF16, (int)d, (int)m, (int)r, rp, lowrank, stream));
+  return TQ_OK;
+}
+
+tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int bits, void* x_codes, float* s_x,
+                          hipStream_t stream) {
+  if (bits != 4 && bits != 8) return TQ_ERR_BITS;
+  if (!valid_dtype(x_dt)) return TQ_ERR_DTYPE;
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxDim || d % (bits == 4 ? 32 : 16)) return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!X || !x_codes || !s_x) return TQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(x_codes) || !aligned16(s_x)) return TQ_ERR_ALIGN;
+  TQ_RUN("quant_rows", stream,
+         tq::launch_quant_rows(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, bits, bits, x_codes, s_x, nullptr, nullptr,
+                               stream));
+  return TQ_OK;
+}
+
+size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r) {
+  if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
+  return linear_ws(n, d, m, r).total;
+}
+
+tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                    const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxDim || m <= 0 || m > kMaxDim || d % 32 || r < 0 || r > 256)
+    return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!X || !w_codes || !s_w || !Y || !ws || (r > 0 && !lowrank)) return TQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(w_codes) || !aligned16(s_w) || !aligned16(Y) || !aligned16(ws) ||
+      (r > 0 && !aligned16(lowrank)))
+    return TQ_ERR_ALIGN;
+  const LinearWs L = linear_ws(n, d, m, r);
+  if (ws_bytes < L.total) return TQ_ERR_WORKSPACE;
+
+  uint8_t* base = (uint8_t*)ws;
+  unsigned* ctr = (unsigned*)(base + L.ctr);
+  float* sx = (float*)(base + L.sx);
+  uint8_t* xc = base + L.xc;
+  tq::bf16_t* T = (tq::bf16_t*)(base + L.t);
+  float* P = (float*)(base + L.p);
+  const tq::bf16_t* L1t = (const tq::bf16_t*)lowrank;
+  const tq::bf16_t* L2t = lowrank ? L1t + (size_t)L.r_pad * d : nullptr;
+  const bool xb = x_dt == TQ_BF16;
+
+  GemmArgs g{};
+  g.A = xc;
+  g.lda = d / 2;
+  g.B = (const uint8_t*)w_codes;
+  g.ldb = d / 2;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(d / 2);
+  g.sx = sx;
+  g.sw = s_w;
+  g.T = L.r_pad ? T : nullptr;
+  g.L2t = L2t;
+  g.r_pad = L.r_pad;
+  g.Y = Y;
+  g.ldy = m;
+  g.y_bf16 = y_dt == TQ_BF16;
+
+  if (L.small) {
+    TQ_RUN("prologue_small_n", stream,
+           tq::launch_prologue_decode(X, xb, (int)n, (int)d, L1t, L.r_pad, kDecodeChunk, L.nchunk, xc, sx, P, T, ctr,
+                                      stream));
+    TQ_RUN("gemm_small_n", stream, tq::launch_gemv(g, 4, tq::EPI_LINEAR, stream));
+  } else {
+    TQ_RUN("prologue_prefill", stream,
+           tq::launch_prologue_prefill(X, xb, (int)n, (int)d, L1t, L.r_pad, xc, sx, T, stream));
+    TQ_RUN("gemm_w4a4", stream, tq::launch_gemm(g, 4, tq::EPI_LINEAR, stream));
+  }
+  return TQ_OK;
+}
+
+tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[3]) {
+  if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256 || d % 32) return TQ_ERR_SHAPE;
+  if (!off) return TQ_ERR_NULL;
+  const LinearWs L = linear_ws(n, d, m, r);
+  off[0] = L.sx;
+  off[1] = L.xc;
+  off[2] = L.t;
+  return TQ_OK;
+}
+
+size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi) {
+  if (n < 0 || d <= 0 || d_hi < 0 || d_hi > d) return 0;
+  return mp_ws(n, d, d_hi).total;
+}
+
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                       const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
+                       tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
+  const int64_t dl = d - d_hi;
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxDim || m <= 0 || m > kMaxDim || d_hi < 0 || d_hi > d || dl % 32 ||
+      d_hi % 16)
+    return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!Xrot || !Y || !ws || (dl > 0 && (!wl_codes || !s_wl)) || (d_hi > 0 && (!wh_codes || !s_wh)))
+    return TQ_ERR_NULL;
+  if (!aligned16(Xrot) || !aligned16(Y) || !aligned16(ws) || (dl > 0 && (!aligned16(wl_codes) || !aligned16(s_wl))) ||
+      (d_hi > 0 && (!aligned16(wh_codes) || !aligned16(s_wh))))
+    return TQ_ERR_ALIGN;
+  const MpWs W = mp_ws(n, d, d_hi);
+  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  float* sxl = (float*)(base + W.sxl);
+  float* sxh = (float*)(base + W.sxh);
+  uint8_t* xl = base + W.xl;
+  uint8_t* xh = base + W.xh;
+  const bool xb = x_dt == TQ_BF16;
+  if (dl > 0 && d_hi > 0) {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)dl, 4, 8, xl, sxl, xh, sxh, stream));
+  } else if (dl > 0) {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)d, 4, 4, xl, sxl, nullptr, nullptr, stream));
+  } else {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
+  }
+  GemmArgs g{};
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Y = Y;
+  g.ldy = m;
+  g.y_bf16 = y_dt == TQ_BF16;
+  // low subspace is the main (4-bit) segment, the high subspace the second (8-bit) segment
+  g.A = xl;
+  g.lda = dl / 2;
+  g.B = (const uint8_t*)wl_codes;
+  g.ldb = dl / 2;
+  g.Kb = (int)(dl / 2);
+  g.sx = sxl;
+  g.sw = s_wl;
+  g.A2 = xh;
+  g.lda2 = d_hi;
+  g.B2 = (const uint8_t*)wh_codes;
+  g.ldb2 = d_hi;
+  g.Kb2 = (int)d_hi;
+  g.sx2 = sxh;
+  g.sw2 = s_wh;
+  if (dl == 0) {  // all 8-bit: empty main segment, scales unused
+    g.A = xh;
+    g.B = (const uint8_t*)wh_codes;
+    g.sx = sxh;
+    g.sw = s_wh;
+  }
+  TQ_RUN("gemm_mp", stream, tq::launch_gemm(g, 4, tq::EPI_MP, stream));
+  return TQ_OK;
+}
+
+tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m, int bits,
+                              int32_t* acc, hipStream_t stream) {
+  if (bits != 4 && bits != 8) return TQ_ERR_BITS;
+  if (n < 0 || n > kMaxDim || k <= 0 || k > kMaxDim || m <= 0 || m > kMaxDim || k % (bits == 4 ? 32 : 16))
+    return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!x_codes || !w_codes || !acc) return TQ_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned16(w_codes) || !aligned16(acc)) return TQ_ERR_ALIGN;
+  GemmArgs g{};
+  g.A = (const uint8_t*)x_codes;
+  g.B = (const uint8_t*)w_codes;
+  g.lda = g.ldb = k * bits / 8;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(k * bits / 8);
+  g.acc = acc;
+  if (n <= kSmallN)
+    TQ_RUN("gemm_small_n_acc", stream, tq::launch_gemv(g, bits, tq::EPI_ACC, stream));
+  else
+    TQ_RUN("gemm_acc", stream, tq::launch_gemm(g, bits, tq::EPI_ACC, stream));
+  return TQ_OK;
+}
+
+tq_status tq_profile_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+  return TQ_OK;
+}
+
+int tq_profile_read(tq_kernel_stat* out, int max) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  std::vector<tq_kernel_stat> stats;
+  for (const ProfRecord& r : p.recs) {
+    if (hipEventSynchronize(r.e1) != hipSuccess) return TQ_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return TQ_ERR_HIP;
+    tq_kernel_stat* s = nullptr;
+    for (auto& x : stats)
+      if (r.name == x.name) s = &x;
+    if (!s) {
+      tq_kernel_stat z{};
+      strncpy(z.name, r.name.c_str(), sizeof(z.name) - 1);
+      stats.push_back(z);
+      s = &stats.back();
+    }
+    s->launches += 1;
+    s->total_ms += ms;
+  }
+  const int k = (int)stats.size();
+  if (out)
+    for (int i = 0; i < k && i < max; ++i) out[i] = stats[i];
+  return k;
+}
+
+tq_status tq_profile_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  for (const ProfRecord& r : p.recs) {
+    p.pool.push_back(r.e0);
+    p.pool.push_back(r.e1);
+  }
+  p.recs.clear();
+  return TQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+// Device-side helpers shared by the kernels of the rank-augmented W4A4 layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 8 consecutive activations loaded from memory as fp32 values.
+template <typename T>
+struct Load8;
+
+template <>
+struct Load8<bf16_t> {
+  // 16 bytes
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[8], uint4& raw) {
+    raw = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x);
+    v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+    v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z);
+    v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+  }
+};
+
+template <>
+struct Load8<float> {
+  // 32 bytes; raw receives the values rounded to bf16 (ties to even)
+  static __device__ __forceinline__ void load(const float* p, float (&v)[8], uint4& raw) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    raw.x = pack_bf16x2(v[0], v[1]);
+    raw.y = pack_bf16x2(v[2], v[3]);
+    raw.z = pack_bf16x2(v[4], v[5]);
+    raw.w = pack_bf16x2(v[6], v[7]);
+  }
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------------------
+// Symmetric quantiser: s = fl32(amax / qmax), code = clamp(rne(fl32(x / s))).
+//
+// Fast path (s in [2^-125, 2^125]): q0 = RN(x * RN(1/s)).  With t = x/s real,
+// |t| <= 7.0000005 (4 bits) or 127.00001 (8 bits), the two roundings give
+// |q0 - t| <= |t| * 2^-23 * (1 + 2^-24), i.e. < 2^-20 (4 bits) or < 2^-16
+// (8 bits), and |fl32(t) - t| <= ulp(t)/2 <= 2^-22 or 2^-18.  If q0 is
+// farther than NEAR (2^-18, resp. 2^-14) from every half-integer, then t and
+// fl32(t) lie strictly inside the same interval between consecutive
+// half-integers as q0, so rne(q0) == rne(fl32(x / s)).  Otherwise the code is
+// recomputed with the IEEE division.  rne(q0) is read from q0 + 1.5*2^23,
+// whose unit-spaced binade rounds to nearest even; its low bits are the
+// two's-complement code.  In the fast path |rne| <= qmax, so no clamp is
+// needed; the exact path clamps (it matters only for subnormal scales).
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct QTraits;
+template <>
+struct QTraits<4> {
+  static constexpr int QMAX = 7;
+  static constexpr float NEAR = 0x1p-18f;
+};
+template <>
+struct QTraits<8> {
+  static constexpr int QMAX = 127;
+  static constexpr float NEAR = 0x1p-14f;
+};
+
+struct RowScale {
+  float s;
+  float rcp;
+  bool fast;
+};
+
+template <int BITS>
+__device__ __forceinline__ RowScale row_scale(float amax) {
+  RowScale r;
+  r.s = amax / (float)QTraits<BITS>::QMAX;  // correctly rounded fp32 division
+  r.fast = (r.s >= 0x1p-125f) && (r.s <= 0x1p+125f);
+  r.rcp = r.fast ? 1.0f / r.s : 0.0f;
+  return r;
+}
+
+template <int BITS>
+__device__ __forceinline__ int code_exact(float x, float s) {
+  if (!(s > 0.0f)) return 0;
+  const float q = x / s;  // correctly rounded fp32 division
+  const int c = (int)rintf(q);
+  return min(max(c, -QTraits<BITS>::QMAX - 1), QTraits<BITS>::QMAX);
+}
+
+// Codes of 8 values of one row; each int holds the code (two's complement).
+template <int BITS>
+__device__ __forceinline__ void quant8(const float (&x)[8], const RowScale& rs, int (&c)[8]) {
+  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+  if (rs.fast) {
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = x[i] * rs.rcp;
+      const float t = q + MAGIC;
+      const float r = t - MAGIC;
+      const float e = fabsf(fabsf(q - r) - 0.5f);
+      near |= (e < QTraits<BITS>::NEAR);
+      c[i] = (int)(__float_as_uint(t) - 0x4B400000u);
+    }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = code_exact<BITS>(x[i], rs.s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = code_exact<BITS>(x[i], rs.s);
+  }
+}
+
+// 8 codes -> 8 nibbles (even index low) in one dword.
+__device__ __forceinline__ uint32_t pack_nibbles(const int (&c)[8]) {
+  uint32_t p = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p |= ((uint32_t)c[i] & 0xFu) << (4 * i);
+  return p;
+}
+// 8 codes -> 8 int8 bytes.
+__device__ __forceinline__ uint2 pack_bytes(const int (&c)[8]) {
+  uint2 p;
+  p.x = ((uint32_t)c[0] & 0xFFu) | (((uint32_t)c[1] & 0xFFu) << 8) | (((uint32_t)c[2] & 0xFFu) << 16) |
+        ((uint32_t)c[3] << 24);
+  p.y = ((uint32_t)c[4] & 0xFFu) | (((uint32_t)c[5] & 0xFFu) << 8) | (((uint32_t)c[6] & 0xFFu) << 16) |
+        ((uint32_t)c[7] << 24);
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// INT4 -> INT8 for the int8 MFMA: the nibble of every byte is moved to the
+// byte's high half, so each int8 lane holds 16 * code exactly.  Both operands
+// are scaled the same way, so products carry a factor 256 that the epilogue
+// removes with an exact arithmetic shift (|acc| <= 256 * 64 * K < 2^31 for
+// K <= 2^17).  lo gets the even-index codes, hi the odd-index codes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nib_lo(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t nib_hi(uint32_t w) { return w & 0xF0F0F0F0u; }
+
+// Two packed dwords (16 codes) -> one int8 MFMA operand of 16 lanes.
+__device__ __forceinline__ i32x4 unpack16(uint32_t w0, uint32_t w1) {
+  i32x4 r;
+  r[0] = (int)nib_lo(w0);
+  r[1] = (int)nib_hi(w0);
+  r[2] = (int)nib_lo(w1);
+  r[3] = (int)nib_hi(w1);
+  return r;
+}
+
+// Max of |x| over non-negative floats via their bit patterns.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace tq

@@ -1,0 +1,55 @@
+// Internal launcher interface between the C ABI (tq_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "tq_device.h"
+
+namespace tq {
+
+enum Epilogue { EPI_ACC = 0, EPI_LINEAR = 1, EPI_MP = 2 };
+
+// Arguments of the integer GEMM kernels: C = A B^T over K-contiguous codes.
+struct GemmArgs {
+  const uint8_t* A;  // x codes, M rows
+  const uint8_t* B;  // w codes, N rows
+  int64_t lda, ldb;  // bytes per row
+  int M, N, Kb;      // Kb: code bytes per row of the main segment
+  // second (8-bit) segment of the two-subspace layer
+  const uint8_t* A2;
+  const uint8_t* B2;
+  int64_t lda2, ldb2;
+  int Kb2;
+  const float* sx;   // M scales
+  const float* sw;   // N scales
+  const float* sx2;  // second-segment scales
+  const float* sw2;
+  const bf16_t* T;    // M x r_pad (bf16) or null
+  const bf16_t* L2t;  // N x r_pad (bf16) or null
+  int r_pad;
+  void* Y;
+  int64_t ldy;  // elements
+  int y_bf16;
+  int32_t* acc;  // EPI_ACC output, M x N
+};
+
+hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, void* codes, float* sw,
+                              hipStream_t st);
+hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, void* out,
+                               hipStream_t st);
+hipError_t launch_quant_rows(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
+                             float* sa, void* cb, float* sb, hipStream_t st);
+hipError_t launch_prologue_prefill(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, void* xc,
+                                   float* sx, void* Tout, hipStream_t st);
+hipError_t launch_prologue_decode(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, int kc,
+                                  int nchunk, void* xc, float* sx, float* P, void* Tout, unsigned* counters,
+                                  hipStream_t st);
+// Integer GEMM (n > 32 tile kernel) with the given epilogue; bits of the main segment.
+hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
+// Small-n integer GEMM (M <= 32).
+hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
+
+}  // namespace tq

@@ -1,0 +1,228 @@
+"""Thin Python binding of the C ABI in ``include/tq.h`` (libtq.so).
+
+Argument marshalling only: every computation runs in the HIP library.
+PyTorch provides device memory (tensors) and the current stream.  Each
+function has the name of the C entry point it calls; outputs that are not
+passed in are allocated with ``torch.empty`` / ``torch.zeros``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+TQ_F32, TQ_BF16 = 0, 1
+
+_STATUS = {
+    0: "TQ_OK", -1: "TQ_ERR_NULL", -2: "TQ_ERR_SHAPE", -3: "TQ_ERR_DTYPE", -4: "TQ_ERR_BITS",
+    -5: "TQ_ERR_ALIGN", -6: "TQ_ERR_WORKSPACE", -7: "TQ_ERR_HIP",
+}
+
+EXPORTS = (
+    "tq_status_string", "tq_version", "tq_codes_bytes", "tq_pack_weight", "tq_lowrank_bytes",
+    "tq_pack_lowrank", "tq_quantize_act", "tq_linear_workspace_bytes", "tq_linear_workspace_offsets", "tq_linear",
+    "tq_linear_mp_workspace_bytes", "tq_linear_mp", "tq_debug_accumulate", "tq_profile_enable",
+    "tq_profile_read", "tq_profile_reset",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libtq.so (built in-tree by ``python -m rank_augmented_quantized_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB
+    if not os.path.exists(path):
+        raise ImportError(
+            f"HIP library {path} is missing; build it with `python -m rank_augmented_quantized_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, ptr, st, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_size_t
+    sigs = {
+        "tq_status_string": (ctypes.c_char_p, [c_int]),
+        "tq_version": (c_int, []),
+        "tq_codes_bytes": (sz, [i64, i64, c_int]),
+        "tq_pack_weight": (st, [ptr, c_int, i64, i64, c_int, ptr, ptr, ptr]),
+        "tq_lowrank_bytes": (sz, [i64, i64, i64]),
+        "tq_pack_lowrank": (st, [ptr, ptr, c_int, i64, i64, i64, ptr, ptr]),
+        "tq_quantize_act": (st, [ptr, c_int, i64, i64, c_int, ptr, ptr, ptr]),
+        "tq_linear_workspace_bytes": (sz, [i64, i64, i64, i64]),
+        "tq_linear": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
+        "tq_linear_workspace_offsets": (st, [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "tq_linear_mp_workspace_bytes": (sz, [i64, i64, i64]),
+        "tq_linear_mp": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
+        "tq_debug_accumulate": (st, [ptr, ptr, i64, i64, i64, c_int, ptr, ptr]),
+        "tq_profile_enable": (st, [c_int]),
+        "tq_profile_read": (c_int, [ctypes.POINTER(KernelStat), c_int]),
+        "tq_profile_reset": (st, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TQError(fn, status)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def tq_codes_bytes(rows: int, k: int, bits: int) -> int:
+    return load().tq_codes_bytes(rows, k, bits)
+
+
+def tq_pack_weight(W, bits: int = 4, w_codes=None, s_w=None):
+    """Per-output-channel quantisation of a d x m weight -> (codes m x d*bits/8 uint8, s_w fp32 m)."""
+    lib = load()
+    _need_cuda(W)
+    d, m = W.shape
+    if w_codes is None:
+        w_codes = torch.empty((m, d * bits // 8), dtype=torch.uint8, device=W.device)
+    if s_w is None:
+        s_w = torch.empty(m, dtype=torch.float32, device=W.device)
+    _check("tq_pack_weight", lib.tq_pack_weight(_p(W), _dt(W), d, m, bits, _p(w_codes), _p(s_w), _stream(W)))
+    return w_codes, s_w
+
+
+def tq_pack_lowrank(L1, L2, out=None):
+    """Lay out the low-rank factors (L1 d x r, L2 r x m) for tq_linear."""
+    lib = load()
+    _need_cuda(L1, L2)
+    d, r = L1.shape
+    m = L2.shape[1]
+    if out is None:
+        out = torch.empty(lib.tq_lowrank_bytes(d, m, r), dtype=torch.uint8, device=L1.device)
+    _check("tq_pack_lowrank", lib.tq_pack_lowrank(_p(L1), _p(L2), _dt(L1), d, m, r, _p(out), _stream(L1)))
+    return out
+
+
+def tq_quantize_act(X, bits: int = 4, x_codes=None, s_x=None):
+    """Per-token quantisation of n x d activations -> (codes n x d*bits/8 uint8, s_x fp32 n)."""
+    lib = load()
+    _need_cuda(X)
+    n, d = X.shape
+    if x_codes is None:
+        x_codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=X.device)
+    if s_x is None:
+        s_x = torch.empty(n, dtype=torch.float32, device=X.device)
+    _check("tq_quantize_act", lib.tq_quantize_act(_p(X), _dt(X), n, d, bits, _p(x_codes), _p(s_x), _stream(X)))
+    return x_codes, s_x
+
+
+def tq_linear_workspace_bytes(n: int, d: int, m: int, r: int) -> int:
+    return load().tq_linear_workspace_bytes(n, d, m, r)
+
+
+def tq_linear_workspace_offsets(n: int, d: int, m: int, r: int) -> dict:
+    """Byte offsets of s_x, the activation codes and T inside tq_linear's workspace."""
+    off = (ctypes.c_size_t * 3)()
+    _check("tq_linear_workspace_offsets", load().tq_linear_workspace_offsets(n, d, m, r, off))
+    return {"s_x": off[0], "x_codes": off[1], "T": off[2]}
+
+
+def linear_workspace(n: int, d: int, m: int, r: int, device) -> torch.Tensor:
+    """A zero-filled workspace for tq_linear (its counter block must start at zero)."""
+    return torch.zeros(max(1, tq_linear_workspace_bytes(n, d, m, r)), dtype=torch.uint8, device=device)
+
+
+def tq_linear(X, w_codes, s_w, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
+    """Y = s_x s_w (Q4(X) Q4(R)) + (X L1) L2 for X n x d."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, lowrank, Y, ws)
+    n, d = X.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = linear_workspace(n, d, m, r, X.device)
+    _check("tq_linear", lib.tq_linear(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
+                                      _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    return Y
+
+
+def tq_linear_mp_workspace_bytes(n: int, d: int, d_hi: int) -> int:
+    return load().tq_linear_mp_workspace_bytes(n, d, d_hi)
+
+
+def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtype=torch.bfloat16, Y=None, ws=None):
+    """Y = Q4(X_l) Q4(W_l) + Q8(X_h) Q8(W_h), X_h = the last d_hi columns of Xrot."""
+    lib = load()
+    _need_cuda(Xrot, wl_codes, s_wl, wh_codes, s_wh, Y, ws)
+    n, d = Xrot.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=Xrot.device)
+    if ws is None:
+        ws = torch.empty(max(1, tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=Xrot.device)
+    _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
+                                            _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                            _stream(Xrot)))
+    return Y
+
+
+def tq_debug_accumulate(x_codes, w_codes, k: int, bits: int = 4, acc=None):
+    """Exact int32 product of code matrices (x n x k, w m x k) -> n x m."""
+    lib = load()
+    _need_cuda(x_codes, w_codes, acc)
+    n, m = x_codes.shape[0], w_codes.shape[0]
+    if acc is None:
+        acc = torch.empty((n, m), dtype=torch.int32, device=x_codes.device)
+    _check("tq_debug_accumulate", lib.tq_debug_accumulate(_p(x_codes), _p(w_codes), n, k, m, bits, _p(acc),
+                                                          _stream(x_codes)))
+    return acc
+
+
+def tq_profile_enable(on: bool = True):
+    _check("tq_profile_enable", load().tq_profile_enable(1 if on else 0))
+
+
+def tq_profile_reset():
+    _check("tq_profile_reset", load().tq_profile_reset())
+
+
+def tq_profile_read() -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded while enabled."""
+    lib = load()
+    buf = (KernelStat * 64)()
+    k = lib.tq_profile_read(buf, 64)
+    if k < 0:
+        raise TQError("tq_profile_read", k)
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(k, 64))}

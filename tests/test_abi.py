@@ -1,0 +1,137 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+that include/tq.h declares, and rejects bad arguments before any HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+from rank_augmented_quantized_amd import tq as tqb  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tqb.LIB):
+        pytest.skip("libtq.so not built (run __graft_entry__.build())")
+    return tqb.load()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(tqb.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", tqb.LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tq_version() == 100
+    for code in range(-7, 1):
+        assert lib.tq_status_string(code)
+    assert b"unknown" in lib.tq_status_string(-99)
+
+
+def test_size_queries(lib):
+    assert lib.tq_codes_bytes(3, 64, 4) == 96
+    assert lib.tq_codes_bytes(3, 64, 8) == 192
+    assert lib.tq_codes_bytes(3, 63, 4) == 0
+    assert lib.tq_codes_bytes(3, 64, 5) == 0
+    # packed low-rank: r padded to a power of two >= 32
+    assert lib.tq_lowrank_bytes(512, 512, 16) == (32 * 512 + 512 * 32) * 2
+    assert lib.tq_lowrank_bytes(4096, 14336, 64) == (64 * 4096 + 14336 * 64) * 2
+    assert lib.tq_lowrank_bytes(512, 512, 257) == 0
+    ws = lib.tq_linear_workspace_bytes(16, 512, 512, 16)
+    assert ws >= 256 + 16 * 4 + 16 * 256 + 16 * 32 * 2
+    off = tqb.tq_linear_workspace_offsets(16, 512, 512, 16)
+    assert off["s_x"] >= 256 and off["x_codes"] >= off["s_x"] + 64 and off["T"] >= off["x_codes"] + 16 * 256
+    assert all(v % 256 == 0 for v in off.values())
+    assert lib.tq_linear_mp_workspace_bytes(8, 256, 64) >= 8 * 96 + 8 * 64 + 64
+
+
+# Fake, aligned, non-null device addresses: every call below must fail its
+# argument check and return before touching them.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = None
+S = None  # null stream
+
+
+def test_pack_weight_validation(lib):
+    assert lib.tq_pack_weight(A, 0, 512, 64, 5, B, C, S) == -4
+    assert lib.tq_pack_weight(A, 7, 512, 64, 4, B, C, S) == -3
+    assert lib.tq_pack_weight(A, 0, 100, 64, 4, B, C, S) == -2
+    assert lib.tq_pack_weight(A, 0, 512, 0, 4, B, C, S) == -2
+    assert lib.tq_pack_weight(NUL, 0, 512, 64, 4, B, C, S) == -1
+    assert lib.tq_pack_weight(A, 0, 512, 64, 4, MIS, C, S) == -5
+
+
+def test_quantize_act_validation(lib):
+    assert lib.tq_quantize_act(A, 1, 0, 512, 4, NUL, NUL, S) == 0  # n == 0 is a no-op
+    assert lib.tq_quantize_act(A, 1, 4, 48, 4, B, C, S) == -2  # d % 32
+    assert lib.tq_quantize_act(A, 1, 4, 48, 8, MIS, C, S) == -5  # 8 bits accepts d % 16
+    assert lib.tq_quantize_act(A, 1, -1, 512, 4, B, C, S) == -2
+    assert lib.tq_quantize_act(A, 1, 4, 512, 3, B, C, S) == -4
+    assert lib.tq_quantize_act(A, 1, 4, 512, 4, B, NUL, S) == -1
+
+
+def test_linear_validation(lib):
+    n, d, m, r = 64, 512, 256, 16
+    need = lib.tq_linear_workspace_bytes(n, d, m, r)
+    assert lib.tq_linear(A, 2, n, d, m, r, B, C, A, B, 1, C, need, S) == -3
+    assert lib.tq_linear(A, 1, n, 500, m, r, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear(A, 1, n, d, m, 300, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear(A, 1, n, d, 0, r, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, NUL, B, 1, C, need, S) == -1  # r > 0 needs the low-rank factors
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, NUL, 1, C, need, S) == -1
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, MIS, need, S) == -5
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, C, need - 1, S) == -6
+    assert lib.tq_linear(A, 1, 0, d, m, r, NUL, NUL, NUL, NUL, 1, NUL, 0, S) == 0
+
+
+def test_linear_mp_validation(lib):
+    n, d, dh, m = 64, 512, 64, 256
+    need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp(A, 1, n, d, 40, m, B, C, A, B, C, 1, A, need, S) == -2  # d_hi % 16
+    assert lib.tq_linear_mp(A, 1, n, 520, 64, m, B, C, A, B, C, 1, A, need, S) == -2  # (d - d_hi) % 32
+    assert lib.tq_linear_mp(A, 1, n, d, d + 16, m, B, C, A, B, C, 1, A, need, S) == -2
+    assert lib.tq_linear_mp(A, 1, n, d, dh, m, B, C, NUL, B, C, 1, A, need, S) == -1
+    assert lib.tq_linear_mp(A, 1, n, d, dh, m, B, C, A, B, C, 1, A, need - 1, S) == -6
+
+
+def test_debug_accumulate_validation(lib):
+    assert lib.tq_debug_accumulate(A, B, 4, 48, 8, 4, C, S) == -2
+    assert lib.tq_debug_accumulate(A, B, 4, 64, 8, 6, C, S) == -4
+    assert lib.tq_debug_accumulate(A, NUL, 4, 64, 8, 4, C, S) == -1
+    assert lib.tq_debug_accumulate(A, B, 4, 64, 8, 4, MIS, S) == -5
+
+
+def test_profile_record_without_launches(lib):
+    assert lib.tq_profile_reset() == 0
+    assert lib.tq_profile_enable(1) == 0
+    assert tqb.tq_profile_read() == {}
+    assert lib.tq_profile_enable(0) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(tqb, "_lib", None)
+    with pytest.raises(ImportError, match="missing"):
+        tqb.load(str(tmp_path / "nope.so"))

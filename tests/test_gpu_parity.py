@@ -1,0 +1,328 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: codes, scales and int32 accumulators bit-exact; Y within
+max|Y - Y_ref| <= 1e-2 * max|Y_ref| (fp64 oracle).  Inputs come from the
+seeded generators; expected values only from ``oracle``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle.tq_oracle as tqo  # noqa: E402
+import rank_augmented_quantized_amd as tq  # noqa: E402
+from workloads import WORKLOADS, draw_custom, draw_linear, draw_two_subspace, draw_two_subspace_custom  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tq.load()  # fails loudly if libtq.so is missing
+
+
+def _t(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def _x_tensor(x, x_dtype):
+    return _t(x, torch.bfloat16 if x_dtype == "bf16" else torch.float32)
+
+
+def _codes_np(t, k, bits):
+    """Device code bytes -> int codes (oracle unpacking)."""
+    b = t.cpu().numpy()
+    return tqo.unpack_int4(b) if bits == 4 else b.view(np.int8).astype(np.int16)
+
+
+def _assert_y(y_gpu, y_ref, what=""):
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(y_ref, dtype=np.float64)
+    scale = np.abs(ref).max()
+    err = np.abs(y - ref).max()
+    print(f"  {what} max|Y-Yref|/max|Yref| = {err / max(scale, 1e-300):.3e}", flush=True)
+    assert err <= TOL * scale, (what, err, scale)
+
+
+# ----------------------------------------------------------------------------
+# quantisation
+# ----------------------------------------------------------------------------
+
+def _golden_rows(d):
+    rows = []
+    import test_oracle_pins as pins
+
+    for name, bits, vals, _, _ in pins.read_golden("quantizer_examples.txt"):
+        if int(bits) != 4:
+            continue
+        v = [float(t) for t in vals.split()]
+        rows.append(v + [0.0] * (d - len(v)))
+    return np.array(rows, dtype=np.float32)
+
+
+QCASES = [
+    # (name, n, d, x_kind, x_dtype, outliers, bits)
+    ("small_f32", 16, 512, "normal", "f32", 4, 4),
+    ("bf16_ragged_outliers", 77, 4096, "normal", "bf16", 4, 4),
+    ("bf16_plain_full_range", 37, 4096, "normal", "bf16", 0, 4),
+    ("student_t_d14336", 5, 14336, "student_t", "bf16", 0, 4),
+    ("int8_bf16", 33, 2048, "normal", "bf16", 4, 8),
+    ("int8_f32_d48", 9, 48, "normal", "f32", 0, 8),
+]
+
+
+@pytest.mark.parametrize("case", QCASES, ids=[c[0] for c in QCASES])
+def test_quantize_act_bitexact(case):
+    name, n, d, kind, xdt, nout, bits = case
+    print(f"case {name}", flush=True)
+    x = draw_custom(n, d, 8, 1, seed=100 + n, x_kind=kind, x_dtype=xdt, outlier_count=nout, outlier_scale=30.0)["X"]
+    x = x.copy()
+    x[n // 2] = 0.0  # an all-zero row
+    codes, sx = tq.tq_quantize_act(_x_tensor(x, xdt), bits)
+    torch.cuda.synchronize()
+    c_ref, s_ref = tqo.quantize_rows(x, bits)
+    assert np.array_equal(sx.cpu().numpy(), s_ref)
+    got = _codes_np(codes, d, bits)
+    bad = np.argwhere(got != c_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def test_quantize_golden_rows_including_subnormal_scale():
+    x = _golden_rows(32)
+    codes, sx = tq.tq_quantize_act(_t(x), 4)
+    torch.cuda.synchronize()
+    c_ref, s_ref = tqo.quantize_rows(x, 4)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(_codes_np(codes, 32, 4), c_ref)
+
+
+def test_quantize_rounding_boundaries():
+    """Values placed exactly on and next to the half-integer boundaries of x/s."""
+    rng = np.random.default_rng(5)
+    n, d = 64, 512
+    amax = rng.uniform(0.5, 40.0, size=n).astype(np.float32)
+    s = (amax / np.float32(7)).astype(np.float32)
+    half = (rng.integers(-7, 7, size=(n, d)) + 0.5).astype(np.float32)
+    x = (half * s[:, None]).astype(np.float32)
+    # nudge by -2..2 ulps
+    bits = x.view(np.int32) + rng.integers(-2, 3, size=(n, d)).astype(np.int32)
+    x = bits.view(np.float32)
+    x = np.clip(x, -amax[:, None], amax[:, None])
+    x[:, 0] = amax
+    codes, sx = tq.tq_quantize_act(_t(x), 4)
+    torch.cuda.synchronize()
+    c_ref, s_ref = tqo.quantize_rows(x, 4)
+    assert np.array_equal(sx.cpu().numpy(), s_ref)
+    assert np.array_equal(_codes_np(codes, d, 4), c_ref)
+
+
+# ----------------------------------------------------------------------------
+# weight packing
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,m,dtype,bits", [(512, 512, "f32", 4), (4096, 200, "f32", 4), (1024, 96, "bf16", 4),
+                                            (128, 300, "f32", 8), (8064, 64, "f32", 4)])
+def test_pack_weight_bitexact(d, m, dtype, bits):
+    print(f"case d={d} m={m} {dtype} bits={bits}", flush=True)
+    case = draw_custom(4, d, m, 1, seed=d + m)
+    w = case["R"].copy()
+    w[:, 3] = 0.0  # an all-zero output channel
+    if dtype == "bf16":
+        from workloads import to_bf16_values
+
+        w = to_bf16_values(w)
+    codes, sw = tq.tq_pack_weight(_x_tensor(w, dtype), bits)
+    torch.cuda.synchronize()
+    c_ref, s_ref = tqo.quantize_weight(w, bits)
+    assert np.array_equal(sw.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), tqo.pack_codes(c_ref, bits))
+
+
+# ----------------------------------------------------------------------------
+# exact integer accumulation (both main loops)
+# ----------------------------------------------------------------------------
+
+ACASES = [
+    (1, 512, 16, 4), (16, 4096, 100, 4), (17, 512, 33, 4), (32, 14336, 48, 4), (33, 512, 130, 4),
+    (200, 4064, 300, 4), (130, 8064, 257, 4), (64, 128, 200, 8), (5, 128, 40, 8), (300, 1024, 160, 8),
+]
+
+
+@pytest.mark.parametrize("n,k,m,bits", ACASES)
+def test_accumulate_bitexact(n, k, m, bits):
+    print(f"case n={n} k={k} m={m} bits={bits}", flush=True)
+    rng = np.random.default_rng(n * 7 + k + m)
+    lo, hi = (-8, 7) if bits == 4 else (-128, 127)
+    cx = rng.integers(lo, hi + 1, size=(n, k))
+    cw = rng.integers(lo, hi + 1, size=(m, k))
+    cx[0, :] = lo  # extreme magnitudes in one row / column
+    cw[0, :] = lo
+    acc = tq.tq_debug_accumulate(_t(tqo.pack_codes(cx, bits)), _t(tqo.pack_codes(cw, bits)), k, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), tqo.int_matmul(cx, cw))
+
+
+# ----------------------------------------------------------------------------
+# the layer on small shapes (several tiles, ragged tails)
+# ----------------------------------------------------------------------------
+
+def _run_linear(x, xdt, r_w, l1, l2, y_dtype=torch.bfloat16):
+    n, d = x.shape
+    m = r_w.shape[1]
+    r = 0 if l1 is None else l1.shape[1]
+    wc, sw = tq.tq_pack_weight(_t(r_w), 4)
+    lowrank = tq.tq_pack_lowrank(_t(l1, torch.bfloat16), _t(l2, torch.bfloat16)) if r else None
+    ws = tq.linear_workspace(n, d, m, r, DEV)
+    y = tq.tq_linear(_x_tensor(x, xdt), wc, sw, lowrank, m, r, y_dtype=y_dtype, ws=ws)
+    torch.cuda.synchronize()
+    return y, ws, wc, sw
+
+
+def _ws_codes(ws, n, d, m, r):
+    off = tq.tq_linear_workspace_offsets(n, d, m, r)
+    b = ws.cpu().numpy()
+    sx = b[off["s_x"]: off["s_x"] + 4 * n].view(np.float32)
+    xc = b[off["x_codes"]: off["x_codes"] + n * d // 2].reshape(n, d // 2)
+    return sx, tqo.unpack_int4(xc)
+
+
+LCASES = [
+    # (name, n, d, m, r, x_kind, x_dtype, outliers)
+    ("small_linear", 16, 512, 512, 16, "normal", "f32", 4),
+    ("n1_ragged_m", 1, 512, 200, 16, "normal", "bf16", 4),
+    ("n33_r0", 33, 256, 130, 0, "normal", "bf16", 0),
+    ("n150_tiles", 150, 544, 272, 32, "normal", "bf16", 2),
+    ("n200_r64", 200, 1024, 384, 64, "normal", "bf16", 0),
+    ("n7_r96", 7, 1024, 100, 96, "student_t", "bf16", 0),
+    ("n32_decode_edge", 32, 2048, 64, 64, "normal", "bf16", 2),
+    ("n129_f32_out", 129, 512, 160, 32, "normal", "f32", 0),
+]
+
+
+@pytest.mark.parametrize("case", LCASES, ids=[c[0] for c in LCASES])
+def test_linear_small(case):
+    name, n, d, m, r, kind, xdt, nout = case
+    print(f"case {name}", flush=True)
+    c = draw_custom(n, d, m, max(r, 1), seed=1000 + n + d, x_kind=kind, x_dtype=xdt, outlier_count=nout,
+                    outlier_scale=30.0)
+    l1 = c["L1"] if r else None
+    l2 = c["L2"] if r else None
+    ydt = torch.float32 if name.endswith("f32_out") else torch.bfloat16
+    y, ws, wc, sw = _run_linear(c["X"], xdt, c["R"], l1, l2, ydt)
+    ref = tqo.tq_linear_ref(c["X"], c["R"], l1, l2)
+    sx, codes = _ws_codes(ws, n, d, m, r)
+    assert np.array_equal(sx, ref["s_x"])
+    assert np.array_equal(codes, ref["codes_x"])
+    # the product path's accumulators, exported from the same codes
+    xc = ws[tq.tq_linear_workspace_offsets(n, d, m, r)["x_codes"]:][: n * d // 2].view(n, d // 2)
+    acc = tq.tq_debug_accumulate(xc.contiguous(), wc, d, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    _assert_y(y, ref["Y"], name)
+
+
+def test_linear_r0_is_pure_w4a4_and_deterministic():
+    c = draw_custom(70, 512, 96, 16, seed=77)
+    y0a, *_ = _run_linear(c["X"], "bf16", c["R"], None, None, torch.float32)
+    y0b, *_ = _run_linear(c["X"], "bf16", c["R"], None, None, torch.float32)
+    assert torch.equal(y0a, y0b)
+    ref = tqo.tq_linear_ref(c["X"], c["R"])
+    _assert_y(y0a, ref["Y"], "r0")
+    # a zero L2 gives the same output as r = 0
+    y1, *_ = _run_linear(c["X"], "bf16", c["R"], c["L1"], np.zeros_like(c["L2"]), torch.float32)
+    assert torch.allclose(y1, y0a, rtol=0, atol=0)
+
+
+def test_small_n_and_tile_paths_agree():
+    c = draw_custom(33, 1024, 128, 32, seed=78)
+    y33, *_ = _run_linear(c["X"], "bf16", c["R"], c["L1"], c["L2"], torch.float32)
+    y32, *_ = _run_linear(c["X"][:32], "bf16", c["R"], c["L1"], c["L2"], torch.float32)
+    a = y33[:32].cpu().numpy()
+    b = y32.cpu().numpy()
+    assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max()
+
+
+# ----------------------------------------------------------------------------
+# the workloads at full size (sampled outputs)
+# ----------------------------------------------------------------------------
+
+def _sample(n, m, rng, k_rows=24, k_cols=48):
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=min(n, k_rows))]))
+    cols = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, size=min(m, k_cols))]))
+    return rows, cols
+
+
+WCASES = [("attn_proj", 4096, True), ("attn_proj", 4096, False), ("mlp_gate_up", 1, True),
+          ("mlp_gate_up", 16, True), ("mlp_gate_up", 256, True), ("mlp_gate_up", 4096, True),
+          ("mlp_gate_up", 16, False), ("mlp_down", 1, True), ("mlp_down", 8, True), ("mlp_down", 32, True),
+          ("small", 16, True)]
+
+
+@pytest.mark.parametrize("wl,n,outl", WCASES, ids=[f"{w}-n{n}-{'outliers' if o else 'plain'}" for w, n, o in WCASES])
+def test_linear_workload(wl, n, outl):
+    w = WORKLOADS[wl]
+    print(f"case {w.title} n={n} outliers={outl}", flush=True)
+    c = draw_linear(w, n=n, outliers=outl)
+    d, m, r = w.d, w.m, w.r
+    y, ws, wc, sw = _run_linear(c["X"], w.x_dtype, c["R"], c["L1"], c["L2"])
+    rng = np.random.default_rng(n)
+    rows, cols = _sample(n, m, rng)
+    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"], rows=rows, cols=cols)
+    # scales and codes of every token, bit-exact
+    cx_all, sx_all = tqo.quantize_rows(c["X"], 4)
+    sx, codes = _ws_codes(ws, n, d, m, r)
+    assert np.array_equal(sx, sx_all)
+    assert np.array_equal(codes, cx_all)
+    # weight scales / codes of the sampled channels
+    assert np.array_equal(sw.cpu().numpy()[cols], ref["s_w"])
+    # accumulators of the sampled outputs, bit-exact
+    xc = ws[tq.tq_linear_workspace_offsets(n, d, m, r)["x_codes"]:][: n * d // 2].view(n, d // 2).contiguous()
+    acc = tq.tq_debug_accumulate(xc, wc, d, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), ref["acc"])
+    _assert_y(y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)], ref["Y"], f"{wl} n={n}")
+
+
+# ----------------------------------------------------------------------------
+# two-subspace layer
+# ----------------------------------------------------------------------------
+
+def _run_mp(xrot, wrot, d_hi):
+    n, d = xrot.shape
+    m = wrot.shape[1]
+    dl = d - d_hi
+    wlc, swl = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[:dl])), 4) if dl else (None, None)
+    whc, swh = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[dl:])), 8) if d_hi else (None, None)
+    y = tq.tq_linear_mp(_t(xrot, torch.bfloat16), d_hi, wlc, swl, whc, swh, m)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("n,d,m,dh", [(40, 512, 96, 64), (130, 1024, 272, 128), (16, 256, 64, 0),
+                                      (70, 256, 80, 256), (9, 8192, 48, 128)])
+def test_linear_mp_small(n, d, m, dh):
+    print(f"case mp n={n} d={d} m={m} d_hi={dh}", flush=True)
+    c = draw_two_subspace_custom(n, d, m, dh, seed=n + d + m, outlier_count=2)
+    y = _run_mp(c["Xrot"], c["Wrot"], dh)
+    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], dh)
+    _assert_y(y, ref["Y"], f"mp n={n} d={d} dh={dh}")
+
+
+def test_linear_mp_workload():
+    w = WORKLOADS["two_subspace"]
+    print(f"case {w.title}", flush=True)
+    c = draw_two_subspace(w)
+    y = _run_mp(c["Xrot"], c["Wrot"], w.d_hi)
+    rows, cols = _sample(w.n, w.m, np.random.default_rng(4))
+    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], w.d_hi, rows=rows, cols=cols)
+    _assert_y(y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)], ref["Y"], "two_subspace")

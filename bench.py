@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copies", type=int, default=16, help="weight copies cycled through (defeats the MALL)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (scales rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding is a "
@@ -187,8 +189,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    tq.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
+        return
+    tq.load()
     wl = WORKLOADS[args.workload]
     n, d, m, r = wl.n, wl.d, wl.m, wl.r
 

@@ -128,11 +128,11 @@ size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
  *   Y        out: n x m, element type y_dt (TQ_BF16 or TQ_F32), rounded to
  *            nearest even from the fp32 epilogue.
  *   ws       device workspace of at least tq_linear_workspace_bytes(n,d,m,r)
- *            bytes.  Its first 256 bytes are completion counters of the
- *            small-n path (n <= 32): they must be zero before the first call
- *            that uses this workspace (e.g. hipMemset once after allocating
- *            it), and every call leaves them zero.  The rest is scratch whose
- *            contents on entry are ignored.
+ *            bytes.  It starts with completion counters of the low-rank
+ *            stage: zero-fill the workspace once before its first use (e.g.
+ *            hipMemset after allocating it); every call leaves the counters
+ *            zero again, and the rest is scratch whose contents on entry are
+ *            ignored.
  * For n <= 32 the call runs a memory-bound path (weight codes streamed once);
  * otherwise a tiled MFMA path.  Both produce bit-identical integer
  * accumulators.

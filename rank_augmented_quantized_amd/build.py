@@ -34,6 +34,8 @@ def compile_flags():
         "-O3",
         "-std=c++17",
         "-fPIC",
+        # floating-point operations exactly as written (fused only where fmaf says so)
+        "-ffp-contract=off",
         # no packed fp32 VALU instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",

@@ -16,7 +16,6 @@ namespace {
 using tq::GemmArgs;
 
 constexpr int kSmallN = 32;       // n <= kSmallN takes the memory-bound small-n path
-constexpr int kDecodeChunk = 512;  // k per partial block of the small-n low-rank stage
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -64,9 +63,9 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   Profiler& p = prof();
   if (!p.on) return launch();
   hipEvent_t e0 = p.get(), e1 = p.get();
-  if (e0) hipEventRecord(e0, st);
+  if (e0) (void)hipEventRecord(e0, st);
   hipError_t err = launch();
-  if (e1) hipEventRecord(e1, st);
+  if (e1) (void)hipEventRecord(e1, st);
   if (e0 && e1)
     p.recs.push_back({name, e0, e1});
   return err;
@@ -80,8 +79,9 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
 
 struct LinearWs {
   size_t ctr, sx, xc, t, p, total;
-  int r_pad, nchunk;
+  int r_pad;
   bool small;
+  tq::ProloguePlan plan;
 };
 
 LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
@@ -89,10 +89,10 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
   LinearWs w{};
   w.small = n <= kSmallN;
   w.r_pad = (int)r_padded(r);
-  w.nchunk = (int)((d + kDecodeChunk - 1) / kDecodeChunk);
+  w.plan = tq::plan_prologue((int)n, (int)d, w.r_pad);
   size_t o = 0;
   w.ctr = o;
-  o += 256;
+  o = align256(o + (size_t)w.plan.counters * 4 + 1);
   w.sx = o;
   o = align256(o + (size_t)n * 4);
   w.xc = o;
@@ -100,7 +100,7 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
   w.t = o;
   o = align256(o + (size_t)n * (size_t)w.r_pad * 2);
   w.p = o;
-  if (w.small && w.r_pad > 0) o = align256(o + (size_t)w.nchunk * (size_t)n * (size_t)w.r_pad * 4);
+  if (w.plan.ntb > 0 && w.plan.nchunk > 1) o = align256(o + (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4);
   w.total = o;
   return w;
 }
@@ -190,7 +190,7 @@ tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, in
   if (!X || !x_codes || !s_x) return TQ_ERR_NULL;
   if (!aligned16(X) || !aligned16(x_codes) || !aligned16(s_x)) return TQ_ERR_ALIGN;
   TQ_RUN("quant_rows", stream,
-         tq::launch_quant_rows(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, bits, bits, x_codes, s_x, nullptr, nullptr,
+         tq::launch_quant_rows_fast(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, bits, bits, x_codes, s_x, nullptr, nullptr,
                                stream));
   return TQ_OK;
 }
@@ -241,16 +241,12 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
 
-  if (L.small) {
-    TQ_RUN("prologue_small_n", stream,
-           tq::launch_prologue_decode(X, xb, (int)n, (int)d, L1t, L.r_pad, kDecodeChunk, L.nchunk, xc, sx, P, T, ctr,
-                                      stream));
+  TQ_RUN("prologue", stream,
+         tq::launch_prologue(X, xb, (int)n, (int)d, L1t, L.r_pad, L.plan, xc, sx, P, T, ctr, stream));
+  if (L.small)
     TQ_RUN("gemm_small_n", stream, tq::launch_gemv(g, 4, tq::EPI_LINEAR, stream));
-  } else {
-    TQ_RUN("prologue_prefill", stream,
-           tq::launch_prologue_prefill(X, xb, (int)n, (int)d, L1t, L.r_pad, xc, sx, T, stream));
+  else
     TQ_RUN("gemm_w4a4", stream, tq::launch_gemm(g, 4, tq::EPI_LINEAR, stream));
-  }
   return TQ_OK;
 }
 
@@ -293,13 +289,13 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   const bool xb = x_dt == TQ_BF16;
   if (dl > 0 && d_hi > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)dl, 4, 8, xl, sxl, xh, sxh, stream));
+           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)dl, 4, 8, xl, sxl, xh, sxh, stream));
   } else if (dl > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)d, 4, 4, xl, sxl, nullptr, nullptr, stream));
+           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 4, 4, xl, sxl, nullptr, nullptr, stream));
   } else {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
+           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
   }
   GemmArgs g{};
   g.M = (int)n;

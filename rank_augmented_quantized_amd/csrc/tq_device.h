@@ -66,17 +66,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 // ---------------------------------------------------------------------------
 // Symmetric quantiser: s = fl32(amax / qmax), code = clamp(rne(fl32(x / s))).
 //
-// Fast path (s in [2^-125, 2^125]): q0 = RN(x * RN(1/s)).  With t = x/s real,
-// |t| <= 7.0000005 (4 bits) or 127.00001 (8 bits), the two roundings give
-// |q0 - t| <= |t| * 2^-23 * (1 + 2^-24), i.e. < 2^-20 (4 bits) or < 2^-16
-// (8 bits), and |fl32(t) - t| <= ulp(t)/2 <= 2^-22 or 2^-18.  If q0 is
-// farther than NEAR (2^-18, resp. 2^-14) from every half-integer, then t and
-// fl32(t) lie strictly inside the same interval between consecutive
-// half-integers as q0, so rne(q0) == rne(fl32(x / s)).  Otherwise the code is
-// recomputed with the IEEE division.  rne(q0) is read from q0 + 1.5*2^23,
-// whose unit-spaced binade rounds to nearest even; its low bits are the
-// two's-complement code.  In the fast path |rne| <= qmax, so no clamp is
-// needed; the exact path clamps (it matters only for subnormal scales).
+// Fast path (s in [2^-125, 2^125]): with y = RN(1/s) and the exact product
+// p = x * y (formed inside an FMA, never rounded on its own), and t = x / s
+// real, |t| <= 7.0000005 (4 bits) or 127.00001 (8 bits) and
+// |p - t| = |t| |y s - 1| <= |t| 2^-24, i.e. < 2^-21 (4 bits) or < 2^-17
+// (8 bits), while |fl32(t) - t| <= ulp(t) / 2 <= 2^-22 (resp. 2^-18).
+//   c = fma(x, y, 1.5 * 2^23) = RN(p + 1.5 * 2^23): its unit-spaced binade
+//       rounds p to the nearest integer, ties to even; the low bits of c are
+//       that integer in two's complement;
+//   d = fma(x, y, -(c - 1.5 * 2^23)) = RN(p - rne(p)), |d| <= 1/2;
+//   e = | |d| - 1/2 | estimates the distance of p to the nearest
+//       half-integer within 2^-25.
+// If e >= NEAR (2^-18, resp. 2^-14) then t and fl32(t) lie strictly inside
+// the same interval between consecutive half-integers as p, so
+// rne(p) == rne(fl32(x / s)); otherwise the codes are recomputed with the
+// IEEE division.  In the fast path |rne(p)| <= qmax, so no clamp is needed;
+// the exact path clamps (it matters only for subnormal scales).
 // ---------------------------------------------------------------------------
 template <int BITS>
 struct QTraits;
@@ -114,29 +119,34 @@ __device__ __forceinline__ int code_exact(float x, float s) {
   return min(max(c, -QTraits<BITS>::QMAX - 1), QTraits<BITS>::QMAX);
 }
 
+template <int BITS>
+__device__ __forceinline__ void quant8_exact(const float (&x)[8], float s, int (&c)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = code_exact<BITS>(x[i], s);
+}
+
+template <int BITS>
+__device__ __forceinline__ void quant8_fast(const float (&x)[8], const RowScale& rs, int (&c)[8]) {
+  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = __builtin_fmaf(x[i], rs.rcp, MAGIC);
+    const float d = __builtin_fmaf(x[i], rs.rcp, -(t - MAGIC));
+    const float e = fabsf(fabsf(d) - 0.5f);
+    near |= (e < QTraits<BITS>::NEAR);
+    c[i] = (int)(__float_as_uint(t) - 0x4B400000u);
+  }
+  if (__builtin_expect(near, 0)) quant8_exact<BITS>(x, rs.s, c);
+}
+
 // Codes of 8 values of one row; each int holds the code (two's complement).
 template <int BITS>
 __device__ __forceinline__ void quant8(const float (&x)[8], const RowScale& rs, int (&c)[8]) {
-  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-  if (rs.fast) {
-    bool near = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q = x[i] * rs.rcp;
-      const float t = q + MAGIC;
-      const float r = t - MAGIC;
-      const float e = fabsf(fabsf(q - r) - 0.5f);
-      near |= (e < QTraits<BITS>::NEAR);
-      c[i] = (int)(__float_as_uint(t) - 0x4B400000u);
-    }
-    if (__builtin_expect(near, 0)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = code_exact<BITS>(x[i], rs.s);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = code_exact<BITS>(x[i], rs.s);
-  }
+  if (rs.fast)
+    quant8_fast<BITS>(x, rs, c);
+  else
+    quant8_exact<BITS>(x, rs.s, c);
 }
 
 // 8 codes -> 8 nibbles (even index low) in one dword.

@@ -16,69 +16,106 @@
 // sums are exact in any order, which leaves the k order inside a fragment
 // free.
 
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "tq_kernels.h"
 
 namespace tq {
 
 // ---------------------------------------------------------------------------
 // Tile kernel (any M; chosen for M > 32).
-//   256 threads = 4 waves in a 2 x 2 grid; wave tile (BM/2) x (BN/2) made of
-//   32 x 32 MFMA blocks.  One k-stage = 128 code bytes per row (256 k at 4
-//   bits, 128 k at 8 bits), double-buffered in LDS; the next stage is loaded
-//   from global into registers while the current one is multiplied.
-//   LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored
-//   at position c ^ (r & 7) ^ ((r >> 3) & 1) so that the 16-byte fragment
-//   reads of 8 or 16 consecutive rows hit distinct banks.
-//   4-bit codes stay packed in LDS and are unpacked in registers
-//   (nib_lo / nib_hi: each int8 lane = 16 * code, so acc = 256 * true sum).
+//   The MFMA tile's rows are output channels (weight codes) and its columns
+//   are tokens (activation codes), so each lane of a 32x32 result block holds
+//   four consecutive channels of one token and the epilogue writes Y with
+//   8-byte (bf16) or 16-byte (fp32) stores.
+//   One k-stage = 128 k.  Codes are loaded from global one stage ahead into
+//   registers and, when staged into LDS, 4-bit codes are unpacked once to
+//   int8 (16 * code, see nib_lo / nib_hi): a 16-byte chunk of 32 packed codes
+//   becomes two 16-byte LDS chunks (even k, odd k), so the MFMA fragments are
+//   read from LDS ready to use.  LDS rows are 128 bytes = 8 chunks; chunk c of
+//   row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the
+//   fragment reads of 8 or 16 consecutive rows on distinct banks.
+//   Waves: WGM x WGN, wave tile (BM / WGM) x (BN / WGN) of 32x32 blocks.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
-template <int BITS, int EPI, int BM, int BN>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int LA = BM / 32, LB = BN / 32;  // 16-byte global loads per thread per stage
+// Tile order: consecutive blocks are dispatched round-robin over the 8 XCDs,
+// each with its own L2, so the block index is first regrouped per XCD
+// (when the tile count is a multiple of 8) and the tiles of one XCD are then
+// walked in groups of GM tile-rows, keeping the tiles a group shares in that
+// XCD's L2.
+__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 4;
+  const int T = tiles_m * tiles_n;
+  int b = bid;
+  if ((T & 7) == 0) b = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int gsz = GM * tiles_n;
+  const int first = (b / gsz) * GM;
+  const int gm = min(tiles_m - first, GM);
+  const int r = b % gsz;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+template <int BITS, int EPI, int BM, int BN, int WGM, int WGN, bool PK>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(GemmArgs g) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  // PK: 4-bit codes stay packed in LDS (256-k stages) and are unpacked when a
+  // fragment is read; otherwise they are unpacked once when staged (128-k).
+  constexpr bool PACKED = PK && BITS == 4;
+  constexpr int CPR = (BITS == 4 && !PACKED) ? 4 : 8;  // 16-byte code chunks per row per stage
+  constexpr int RPS = NT / CPR;             // rows per load pass
+  constexpr int LA = BM / RPS, LB = BN / RPS;
   constexpr int STAGE = (BM + BN) * 128;
+  static_assert(FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, lgrp = lane >> 5;
 
-  const int tiles_n = (g.N + BN - 1) / BN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  // rows of the tile: channels (g.B, g.N of them); columns: tokens (g.A, g.M)
+  int tm, tn;
+  tile_of_block(blockIdx.x, (g.N + BM - 1) / BM, (g.M + BN - 1) / BN, tm, tn);
+  const int ch0 = tm * BM, tk0 = tn * BN;
 
-  const int lc = tid & 7, lr = tid >> 3;
-  const uint8_t* pa[LA];
-  const uint8_t* pb[LB];
+  const int lc = tid % CPR, lr = tid / CPR;
+  const uint8_t* pw[LA];
+  const uint8_t* px[LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) pa[i] = g.A + (size_t)min(m0 + lr + 32 * i, g.M - 1) * g.lda + 16 * lc;
+  for (int i = 0; i < LA; ++i) pw[i] = g.B + (size_t)min(ch0 + lr + RPS * i, g.N - 1) * g.ldb + 16 * lc;
 #pragma unroll
-  for (int i = 0; i < LB; ++i) pb[i] = g.B + (size_t)min(n0 + lr + 32 * i, g.N - 1) * g.ldb + 16 * lc;
+  for (int i = 0; i < LB; ++i) px[i] = g.A + (size_t)min(tk0 + lr + RPS * i, g.M - 1) * g.lda + 16 * lc;
 
-  uint4 ra[LA], rb[LB];
-  auto gload = [&](int kt, int Kb) {
-    const int kb = kt * 128;
+  uint4 rw[LA], rx[LB];
+  auto gload = [&](const uint8_t* const (&qw)[LA], const uint8_t* const (&qx)[LB], int kt, int Kb) {
+    const int kb = kt * CPR * 16;
     const bool ok = kb + 16 * lc < Kb;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) ra[i] = ok ? *reinterpret_cast<const uint4*>(pa[i] + kb) : uint4{0, 0, 0, 0};
+    for (int i = 0; i < LA; ++i) rw[i] = ok ? *reinterpret_cast<const uint4*>(qw[i] + kb) : uint4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < LB; ++i) rb[i] = ok ? *reinterpret_cast<const uint4*>(pb[i] + kb) : uint4{0, 0, 0, 0};
+    for (int i = 0; i < LB; ++i) rx[i] = ok ? *reinterpret_cast<const uint4*>(qx[i] + kb) : uint4{0, 0, 0, 0};
   };
-  auto sstore = [&](int buf) {
-    uint8_t* sA = smem + buf * STAGE;
-    uint8_t* sB = sA + BM * 128;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = lr + 32 * i;
-      *reinterpret_cast<uint4*>(sA + r * 128 + 16 * swz(lc, r)) = ra[i];
+  auto put = [&](uint8_t* base, int r, const uint4& v, auto bits) {
+    if constexpr (decltype(bits)::value == 4 && !PACKED) {
+      const uint4 lo = {nib_lo(v.x), nib_lo(v.y), nib_lo(v.z), nib_lo(v.w)};
+      const uint4 hi = {nib_hi(v.x), nib_hi(v.y), nib_hi(v.z), nib_hi(v.w)};
+      *reinterpret_cast<uint4*>(base + r * 128 + 16 * swz(2 * lc, r)) = lo;
+      *reinterpret_cast<uint4*>(base + r * 128 + 16 * swz(2 * lc + 1, r)) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(base + r * 128 + 16 * swz(lc, r)) = v;
     }
+  };
+  auto sstore = [&](int buf, auto bits) {
+    uint8_t* sW = smem + buf * STAGE;
+    uint8_t* sX = sW + BM * 128;
 #pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = lr + 32 * i;
-      *reinterpret_cast<uint4*>(sB + r * 128 + 16 * swz(lc, r)) = rb[i];
-    }
+    for (int i = 0; i < LA; ++i) put(sW, lr + RPS * i, rw[i], bits);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) put(sX, lr + RPS * i, rx[i], bits);
   };
 
   i32x16 acc[FM][FN];
@@ -89,179 +126,246 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0;
 
-  auto compute = [&](int buf, int bits) {
-    const uint8_t* sA = smem + buf * STAGE;
-    const uint8_t* sB = sA + BM * 128;
+  // One stage: 4 k-steps of 32; lane group g reads LDS chunk 2j + g (16 int8).
+  auto mma_block = [&](int buf, int a, int b, i32x16& c) {
+    const uint8_t* sW = smem + buf * STAGE;
+    const uint8_t* sX = sW + BM * 128;
+    const int rW = wm * WM + 32 * a + l32, rX = wn * WN + 32 * b + l32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = 2 * j + lgrp;
-      uint4 fa[FM], fb[FN];
+      const int cc = 2 * j + lgrp;
+      const uint4 fa = *reinterpret_cast<const uint4*>(sW + rW * 128 + 16 * swz(cc, rW));
+      const uint4 fb = *reinterpret_cast<const uint4*>(sX + rX * 128 + 16 * swz(cc, rX));
+      c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa), __builtin_bit_cast(i32x4, fb), c, 0, 0,
+                                                0);
+    }
+  };
+  // Fragments of one 32-k step (lane group g reads LDS chunk 2j + g); packed
+  // 16-byte chunks hold 32 codes = two MFMA k-steps, int8 chunks one.
+  auto read_frags = [&](int buf, int j, uint4 (&fa)[FM], uint4 (&fb)[FN]) {
+    const uint8_t* sW = smem + buf * STAGE;
+    const uint8_t* sX = sW + BM * 128;
+    const int cc = 2 * j + lgrp;
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int r = wm * WM + 32 * f + l32;
-        fa[f] = *reinterpret_cast<const uint4*>(sA + r * 128 + 16 * swz(c, r));
-      }
+    for (int f = 0; f < FM; ++f) {
+      const int r = wm * WM + 32 * f + l32;
+      fa[f] = *reinterpret_cast<const uint4*>(sW + r * 128 + 16 * swz(cc, r));
+    }
 #pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int r = wn * WN + 32 * f + l32;
-        fb[f] = *reinterpret_cast<const uint4*>(sB + r * 128 + 16 * swz(c, r));
-      }
-      if (bits == 4) {
+    for (int f = 0; f < FN; ++f) {
+      const int r = wn * WN + 32 * f + l32;
+      fb[f] = *reinterpret_cast<const uint4*>(sX + r * 128 + 16 * swz(cc, r));
+    }
+  };
+  auto mma_step = [&](const uint4 (&fa)[FM], const uint4 (&fb)[FN]) {
+    if constexpr (PACKED) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          i32x4 oa[FM], ob[FN];
+      for (int h = 0; h < 2; ++h) {
+        i32x4 oa[FM], ob[FN];
 #pragma unroll
-          for (int f = 0; f < FM; ++f) oa[f] = h ? unpack16(fa[f].z, fa[f].w) : unpack16(fa[f].x, fa[f].y);
+        for (int f = 0; f < FM; ++f) oa[f] = h ? unpack16(fa[f].z, fa[f].w) : unpack16(fa[f].x, fa[f].y);
 #pragma unroll
-          for (int f = 0; f < FN; ++f) ob[f] = h ? unpack16(fb[f].z, fb[f].w) : unpack16(fb[f].x, fb[f].y);
-#pragma unroll
-          for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-              acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[a], ob[b], acc[a][b], 0, 0, 0);
-        }
-      } else {
+        for (int f = 0; f < FN; ++f) ob[f] = h ? unpack16(fb[f].z, fb[f].w) : unpack16(fb[f].x, fb[f].y);
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
           for (int b = 0; b < FN; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[a]),
-                                                              __builtin_bit_cast(i32x4, fb[b]), acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(oa[a], ob[b], acc[a][b], 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa[a]),
+                                                            __builtin_bit_cast(i32x4, fb[b]), acc[a][b], 0, 0, 0);
     }
   };
+  // One stage, software-pipelined: the fragments of step j + 1 are read from
+  // LDS while the MFMAs of step j run; step 0's fragments come in loaded.
+  uint4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto compute = [&](int buf) {
+    read_frags(buf, 1, fa1, fb1);
+    mma_step(fa0, fb0);
+    read_frags(buf, 2, fa0, fb0);
+    mma_step(fa1, fb1);
+    read_frags(buf, 3, fa1, fb1);
+    mma_step(fa0, fb0);
+    mma_step(fa1, fb1);
+  };
 
-  // ---- main loop over the first segment ----
-  const int KT = (g.Kb + 127) / 128;
+  // ---- main loop ----
+  const int KT = (g.Kb + CPR * 16 - 1) / (CPR * 16);
+  using bits_t = std::integral_constant<int, BITS>;
   if (KT > 0) {
-    gload(0, g.Kb);
-    sstore(0);
+    gload(pw, px, 0, g.Kb);
+    sstore(0, bits_t{});
   }
   __syncthreads();
+  if (KT > 0) read_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < KT; ++kt) {
     const bool more = kt + 1 < KT;
-    if (more) gload(kt + 1, g.Kb);
-    compute(kt & 1, BITS);
-    if (more) sstore((kt + 1) & 1);
+    if (more) gload(pw, px, kt + 1, g.Kb);
+    compute(kt & 1);
+    if (more) sstore((kt + 1) & 1, bits_t{});
     __syncthreads();
+    if (more) read_frags((kt + 1) & 1, 0, fa0, fb0);
   }
 
   // ---- epilogue ----
-  // 32x32 MFMA result layout: lane l, element i -> row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+  // 32x32 result layout: lane l, element e -> row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32;
+  // here row = channel, column = token.  ch(a, e4): first of the 4 channels of group e4.
+  auto chan = [&](int a, int e4) { return ch0 + wm * WM + 32 * a + 8 * e4 + 4 * lgrp; };
+  auto tok = [&](int b) { return tk0 + wn * WN + 32 * b + l32; };
+  auto load4 = [&](const float* p, int c) -> float4 {  // p[c..c+3], clamped at the channel tail
+    if (c + 3 < g.N) return *reinterpret_cast<const float4*>(p + c);
+    return float4{p[min(c, g.N - 1)], p[min(c + 1, g.N - 1)], p[min(c + 2, g.N - 1)], p[min(c + 3, g.N - 1)]};
+  };
+  auto store4 = [&](int t, int c, float y0, float y1, float y2, float y3) {
+    if (t >= g.M) return;
+    if (g.y_bf16) {
+      bf16_t* yp = reinterpret_cast<bf16_t*>(g.Y) + (size_t)t * g.ldy + c;
+      if (c + 3 < g.N && ((g.ldy & 3) == 0)) {
+        *reinterpret_cast<uint2*>(yp) = uint2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+      } else {
+        const float v[4] = {y0, y1, y2, y3};
+        for (int q = 0; q < 4; ++q)
+          if (c + q < g.N) yp[q] = (bf16_t)f32_to_bf16_bits(v[q]);
+      }
+    } else {
+      float* yp = reinterpret_cast<float*>(g.Y) + (size_t)t * g.ldy + c;
+      if (c + 3 < g.N && ((g.ldy & 3) == 0)) {
+        *reinterpret_cast<float4*>(yp) = float4{y0, y1, y2, y3};
+      } else {
+        const float v[4] = {y0, y1, y2, y3};
+        for (int q = 0; q < 4; ++q)
+          if (c + q < g.N) yp[q] = v[q];
+      }
+    }
+  };
+  constexpr int SH = (BITS == 4) ? 8 : 0;  // int8 lanes carry 16 * code: acc = 256 * sum
+
   if constexpr (EPI == EPI_ACC) {
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
-        const int col = n0 + wn * WN + 32 * b + l32;
+        const int t = tok(b);
+        if (t >= g.M) continue;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = m0 + wm * WM + 32 * a + 8 * (i >> 2) + 4 * lgrp + (i & 3);
-          if (row < g.M && col < g.N) g.acc[(size_t)row * g.N + col] = (BITS == 4) ? (acc[a][b][i] >> 8) : acc[a][b][i];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = chan(a, e4);
+          int32_t* op = g.acc + (size_t)t * g.N + c;
+          const int v0 = acc[a][b][4 * e4] >> SH, v1 = acc[a][b][4 * e4 + 1] >> SH;
+          const int v2 = acc[a][b][4 * e4 + 2] >> SH, v3 = acc[a][b][4 * e4 + 3] >> SH;
+          if (c + 3 < g.N && (g.N & 3) == 0) {
+            *reinterpret_cast<int4*>(op) = int4{v0, v1, v2, v3};
+          } else {
+            const int v[4] = {v0, v1, v2, v3};
+            for (int q = 0; q < 4; ++q)
+              if (c + q < g.N) op[q] = v[q];
+          }
         }
       }
     return;
   } else {
-    f32x16 y[FM][FN];
+    // One 32x32 block at a time: dequantise (y = acc * s_w[channel] * s_x[token]),
+    // add the second low-rank stage (rank-augmented layer) or the high-subspace
+    // product (two-subspace layer), store.  Only one block's outputs are live.
+    const int KT2 = (EPI == EPI_MP) ? (g.Kb2 + 127) / 128 : 0;
+    if constexpr (EPI == EPI_MP) {
+      if (KT2 > 0) {
+        // stage the first 256 k of the high subspace (8-bit codes) into the two buffers
+        constexpr int RPS8 = NT / 8, LA8 = BM / RPS8, LB8 = BN / RPS8;
+        const int lc8 = tid & 7, lr8 = tid >> 3;
 #pragma unroll
-    for (int a = 0; a < FM; ++a)
+        for (int h = 0; h < 2; ++h) {
+          const int kb = h * 128;
+          const bool ok = (h < KT2) && (kb + 16 * lc8 < g.Kb2);
+          uint8_t* sW = smem + h * STAGE;
+          uint8_t* sX = sW + BM * 128;
 #pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        const int col = min(n0 + wn * WN + 32 * b + l32, g.N - 1);
-        const float swc = g.sw[col];
+          for (int i = 0; i < LA8; ++i) {
+            const int r = lr8 + RPS8 * i;
+            const uint8_t* p = g.B2 + (size_t)min(ch0 + r, g.N - 1) * g.ldb2 + 16 * lc8 + kb;
+            *reinterpret_cast<uint4*>(sW + r * 128 + 16 * swz(lc8, r)) =
+                ok ? *reinterpret_cast<const uint4*>(p) : uint4{0, 0, 0, 0};
+          }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = min(m0 + wm * WM + 32 * a + 8 * (i >> 2) + 4 * lgrp + (i & 3), g.M - 1);
-          const int v = (BITS == 4) ? (acc[a][b][i] >> 8) : acc[a][b][i];
-          y[a][b][i] = (float)v * (g.sx[row] * swc);
-        }
-      }
-
-    if constexpr (EPI == EPI_LINEAR) {
-      if (g.r_pad > 0) {
-        // second low-rank stage on the bf16 MFMA, accumulated onto the dequantised tile
-#pragma unroll
-        for (int a = 0; a < FM; ++a) {
-          const int arow = min(m0 + wm * WM + 32 * a + l32, g.M - 1);
-          const bf16_t* tp = g.T + (size_t)arow * g.r_pad + 8 * lgrp;
-#pragma unroll
-          for (int b = 0; b < FN; ++b) {
-            const int col = min(n0 + wn * WN + 32 * b + l32, g.N - 1);
-            const bf16_t* lp = g.L2t + (size_t)col * g.r_pad + 8 * lgrp;
-            for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
-              const uint4 av = *reinterpret_cast<const uint4*>(tp + t0);
-              const uint4 bv = *reinterpret_cast<const uint4*>(lp + t0);
-              y[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), y[a][b], 0, 0, 0);
-            }
+          for (int i = 0; i < LB8; ++i) {
+            const int r = lr8 + RPS8 * i;
+            const uint8_t* p = g.A2 + (size_t)min(tk0 + r, g.M - 1) * g.lda2 + 16 * lc8 + kb;
+            *reinterpret_cast<uint4*>(sX + r * 128 + 16 * swz(lc8, r)) =
+                ok ? *reinterpret_cast<const uint4*>(p) : uint4{0, 0, 0, 0};
           }
         }
-      }
-    } else if constexpr (EPI == EPI_MP) {
-      // high-precision (8-bit) segment: its own integer product per 32x32 block
-      const int KT2 = (g.Kb2 + 127) / 128;
-      const uint8_t* pa2[LA];
-      const uint8_t* pb2[LB];
-#pragma unroll
-      for (int i = 0; i < LA; ++i) pa2[i] = g.A2 + (size_t)min(m0 + lr + 32 * i, g.M - 1) * g.lda2 + 16 * lc;
-#pragma unroll
-      for (int i = 0; i < LB; ++i) pb2[i] = g.B2 + (size_t)min(n0 + lr + 32 * i, g.N - 1) * g.ldb2 + 16 * lc;
-      for (int kt = 0; kt < KT2; ++kt) {
-        const int kb = kt * 128;
-        const bool ok = kb + 16 * lc < g.Kb2;
-#pragma unroll
-        for (int i = 0; i < LA; ++i) ra[i] = ok ? *reinterpret_cast<const uint4*>(pa2[i] + kb) : uint4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < LB; ++i) rb[i] = ok ? *reinterpret_cast<const uint4*>(pb2[i] + kb) : uint4{0, 0, 0, 0};
-        sstore(0);
-        __syncthreads();
-        const uint8_t* sA = smem;
-        const uint8_t* sB = smem + BM * 128;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-          for (int b = 0; b < FN; ++b) {
-            i32x16 t;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) t[i] = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = 2 * j + lgrp;
-              const int rA = wm * WM + 32 * a + l32;
-              const int rB = wn * WN + 32 * b + l32;
-              const uint4 fa = *reinterpret_cast<const uint4*>(sA + rA * 128 + 16 * swz(c, rA));
-              const uint4 fb = *reinterpret_cast<const uint4*>(sB + rB * 128 + 16 * swz(c, rB));
-              t = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa), __builtin_bit_cast(i32x4, fb),
-                                                        t, 0, 0, 0);
-            }
-            const int col = min(n0 + wn * WN + 32 * b + l32, g.N - 1);
-            const float swc = g.sw2[col];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int row = min(m0 + wm * WM + 32 * a + 8 * (i >> 2) + 4 * lgrp + (i & 3), g.M - 1);
-              y[a][b][i] += (float)t[i] * (g.sx2[row] * swc);
-            }
-          }
         __syncthreads();
       }
     }
-
-    // ---- single store of Y ----
 #pragma unroll
-    for (int a = 0; a < FM; ++a)
+    for (int a = 0; a < FM; ++a) {
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
-        const int col = n0 + wn * WN + 32 * b + l32;
-        if (col >= g.N) continue;
+        const int tt = min(tok(b), g.M - 1);
+        const float sx = g.sx[tt];
+        f32x16 y;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = m0 + wm * WM + 32 * a + 8 * (i >> 2) + 4 * lgrp + (i & 3);
-          if (row >= g.M) continue;
-          if (g.y_bf16)
-            reinterpret_cast<bf16_t*>(g.Y)[(size_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_bits(y[a][b][i]);
-          else
-            reinterpret_cast<float*>(g.Y)[(size_t)row * g.ldy + col] = y[a][b][i];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 w = load4(g.sw, chan(a, e4));
+          y[4 * e4 + 0] = (float)(acc[a][b][4 * e4 + 0] >> SH) * (w.x * sx);
+          y[4 * e4 + 1] = (float)(acc[a][b][4 * e4 + 1] >> SH) * (w.y * sx);
+          y[4 * e4 + 2] = (float)(acc[a][b][4 * e4 + 2] >> SH) * (w.z * sx);
+          y[4 * e4 + 3] = (float)(acc[a][b][4 * e4 + 3] >> SH) * (w.w * sx);
         }
+        if constexpr (EPI == EPI_LINEAR) {
+          // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16 MFMA
+          if (g.r_pad > 0) {
+            const int c = min(ch0 + wm * WM + 32 * a + l32, g.N - 1);
+            const bf16_t* lp = g.L2t + (size_t)c * g.r_pad + 8 * lgrp;
+            const bf16_t* tp = g.T + (size_t)tt * g.r_pad + 8 * lgrp;
+            for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
+              const uint4 av = *reinterpret_cast<const uint4*>(lp + t0);
+              const uint4 bv = *reinterpret_cast<const uint4*>(tp + t0);
+              y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), y, 0, 0, 0);
+            }
+          }
+        } else {
+          if (KT2 > 0) {
+            i32x16 t;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = 0;
+            mma_block(0, a, b, t);
+            if (KT2 > 1) mma_block(1, a, b, t);
+            // k beyond the 256 staged in LDS: fragments straight from global (L2)
+            for (int kk = 2; kk < KT2; ++kk) {
+              const int cw = min(ch0 + wm * WM + 32 * a + l32, g.N - 1);
+              const uint8_t* pw2 = g.B2 + (size_t)cw * g.ldb2 + kk * 128 + 16 * lgrp;
+              const uint8_t* px2 = g.A2 + (size_t)tt * g.lda2 + kk * 128 + 16 * lgrp;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const bool ok = kk * 128 + 32 * j + 16 * lgrp < g.Kb2;
+                const uint4 fa = ok ? *reinterpret_cast<const uint4*>(pw2 + 32 * j) : uint4{0, 0, 0, 0};
+                const uint4 fb = ok ? *reinterpret_cast<const uint4*>(px2 + 32 * j) : uint4{0, 0, 0, 0};
+                t = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, fa), __builtin_bit_cast(i32x4, fb),
+                                                          t, 0, 0, 0);
+              }
+            }
+            const float sxh = g.sx2[tt];
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const float4 w = load4(g.sw2, chan(a, e4));
+              y[4 * e4 + 0] += (float)t[4 * e4 + 0] * (w.x * sxh);
+              y[4 * e4 + 1] += (float)t[4 * e4 + 1] * (w.y * sxh);
+              y[4 * e4 + 2] += (float)t[4 * e4 + 2] * (w.z * sxh);
+              y[4 * e4 + 3] += (float)t[4 * e4 + 3] * (w.w * sxh);
+            }
+          }
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) store4(tok(b), chan(a, e4), y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
   }
 }
 
@@ -275,7 +379,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // ---------------------------------------------------------------------------
 template <int BITS, int EPI, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemmArgs g) {
-  constexpr int U = 4;  // steps in flight per wave
+  constexpr int U = 16;  // weight loads in flight per lane
   __shared__ int red[WAVES][2][4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -284,32 +388,38 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemmArgs g) {
   const uint8_t* bp = g.B + (size_t)min(n0 + l16, g.N - 1) * g.ldb + 16 * lg;
   const uint8_t* ap0 = g.A + (size_t)min(l16, g.M - 1) * g.lda + 16 * lg;
   const uint8_t* ap1 = g.A + (size_t)min(16 + l16, g.M - 1) * g.lda + 16 * lg;
+  // each wave streams one contiguous k-range of the block's 16 columns
   const int KS = (g.Kb + 63) / 64;
+  const int per = (KS + WAVES - 1) / WAVES;
+  const int sbeg = wave * per, send = min(KS, sbeg + per);
   i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  for (int s0 = wave * U; s0 < KS; s0 += WAVES * U) {
-    uint4 bv[U], av0[U], av1[U];
+  for (int s0 = sbeg; s0 < send; s0 += U) {
+    uint4 bv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = (s0 + u) * 64;
-      const bool ok = (s0 + u < KS) && (kb + 16 * lg < g.Kb);
+      const bool ok = (s0 + u < send) && (kb + 16 * lg < g.Kb);
       bv[u] = ok ? *reinterpret_cast<const uint4*>(bp + kb) : uint4{0, 0, 0, 0};
-      av0[u] = ok ? *reinterpret_cast<const uint4*>(ap0 + kb) : uint4{0, 0, 0, 0};
-      av1[u] = (ok && two) ? *reinterpret_cast<const uint4*>(ap1 + kb) : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (s0 + u >= send) break;
+      const int kb = (s0 + u) * 64;
+      const bool ok = kb + 16 * lg < g.Kb;
+      const uint4 av0 = ok ? *reinterpret_cast<const uint4*>(ap0 + kb) : uint4{0, 0, 0, 0};
+      const uint4 av1 = (ok && two) ? *reinterpret_cast<const uint4*>(ap1 + kb) : uint4{0, 0, 0, 0};
       if (BITS == 4) {
         const i32x4 b0 = unpack16(bv[u].x, bv[u].y), b1 = unpack16(bv[u].z, bv[u].w);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].x, av0[u].y), b0, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].z, av0[u].w), b1, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0.x, av0.y), b0, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0.z, av0.w), b1, acc0, 0, 0, 0);
         if (two) {
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].x, av1[u].y), b0, acc1, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].z, av1[u].w), b1, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1.x, av1.y), b0, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1.z, av1.w), b1, acc1, 0, 0, 0);
         }
       } else {
         const i32x4 b0 = __builtin_bit_cast(i32x4, bv[u]);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0[u]), b0, acc0, 0, 0, 0);
-        if (two) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av1[u]), b0, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0), b0, acc0, 0, 0, 0);
+        if (two) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av1), b0, acc1, 0, 0, 0);
       }
     }
   }
@@ -359,11 +469,35 @@ __global__ __launch_bounds__(WAVES * 64) void k_gemv(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Tile-kernel variants; the default is the fastest measured on MI355X, the
+// TQ_GEMM_VARIANT environment variable (read once) overrides it for tuning:
+//   0: 256x256 tile, 8 waves of 128x64, int8 LDS (128-k stages)
+//   1: 256x256 tile, 8 waves of 128x64, packed LDS (256-k stages)
+//   2: 256x256 tile, 4 waves of 128x128, packed LDS
+//   3: 256x256 tile, 4 waves of 128x128, int8 LDS
+static int gemm_variant() {
+  static const int v = [] {
+    const char* e = getenv("TQ_GEMM_VARIANT");
+    return e ? atoi(e) : 1;
+  }();
+  return v;
+}
+
 template <int BITS, int EPI>
 static hipError_t gemm_tiles(const GemmArgs& g, hipStream_t st) {
-  constexpr int BM = 128, BN = 128;
-  const unsigned blocks = (unsigned)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  hipLaunchKernelGGL((k_gemm<BITS, EPI, BM, BN>), dim3(blocks), dim3(256), 0, st, g);
+  const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const dim3 grid((unsigned)big);
+  if (big >= 224) {
+    switch (gemm_variant()) {
+      case 0: hipLaunchKernelGGL((k_gemm<BITS, EPI, 256, 256, 2, 4, false>), grid, dim3(512), 0, st, g); break;
+      case 2: hipLaunchKernelGGL((k_gemm<BITS, EPI, 256, 256, 2, 2, true>), grid, dim3(256), 0, st, g); break;
+      case 3: hipLaunchKernelGGL((k_gemm<BITS, EPI, 256, 256, 2, 2, false>), grid, dim3(256), 0, st, g); break;
+      default: hipLaunchKernelGGL((k_gemm<BITS, EPI, 256, 256, 2, 4, true>), grid, dim3(512), 0, st, g); break;
+    }
+  } else {
+    const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 127) / 128));
+    hipLaunchKernelGGL((k_gemm<BITS, EPI, 128, 128, 2, 2, true>), dim3(blocks), dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 
@@ -383,7 +517,7 @@ hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st
 template <int BITS, int EPI>
 static hipError_t gemv_cols(const GemmArgs& g, hipStream_t st) {
   const unsigned blocks = (unsigned)((g.N + 15) / 16);
-  if (g.Kb >= 4096)
+  if (g.Kb > 2048)
     hipLaunchKernelGGL((k_gemv<BITS, EPI, 8>), dim3(blocks), dim3(512), 0, st, g);
   else
     hipLaunchKernelGGL((k_gemv<BITS, EPI, 4>), dim3(blocks), dim3(256), 0, st, g);

@@ -42,11 +42,17 @@ hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d,
                                hipStream_t st);
 hipError_t launch_quant_rows(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
                              float* sa, void* cb, float* sb, hipStream_t st);
-hipError_t launch_prologue_prefill(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, void* xc,
-                                   float* sx, void* Tout, hipStream_t st);
-hipError_t launch_prologue_decode(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, int kc,
-                                  int nchunk, void* xc, float* sx, float* P, void* Tout, unsigned* counters,
-                                  hipStream_t st);
+// Work split of the tq_linear prologue (quantisation + T = X L1).
+struct ProloguePlan {
+  int kc, nchunk, qs, nqg, ntb, nqb, counters;
+  bool quant_in_prologue;
+};
+ProloguePlan plan_prologue(int n, int d, int r_pad);
+hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
+                           void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st);
+// Per-token quantiser with one wave per row (falls back to a block per row for very long rows).
+hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
+                                  float* sa, void* cb, float* sb, hipStream_t st);
 // Integer GEMM (n > 32 tile kernel) with the given epilogue; bits of the main segment.
 hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
 // Small-n integer GEMM (M <= 32).

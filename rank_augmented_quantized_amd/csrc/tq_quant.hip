@@ -179,181 +179,266 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ X, int
 }
 
 // ---------------------------------------------------------------------------
-// Prefill prologue: 16 rows per block.  Pass A streams the rows once in the
-// bf16 MFMA A-operand layout (lane: row lane%16, 8 consecutive k at
-// 32*step + 8*(lane/16)), keeping each row's max|x| and accumulating
-// T = X L1 with v_mfma_f32_16x16x32_bf16 against L1^T (same k layout for the
-// B operand, so the pairing of k between A and B is the identity).  Waves
-// take the 32-k steps round-robin.  Pass B re-reads the rows (L2 hits) and
-// writes the 4-bit codes.  NQ = r_pad / 16 output slices of T.
+// One row quantised by one wave, the whole row held in registers (CH chunks
+// of 8 values per lane, chunk index lane + 64 i), so X is read exactly once.
+// Columns [0, dl) use BA bits, [dl, d) BB bits with their own scale.
 // ---------------------------------------------------------------------------
-template <typename T, int NQ>
-__global__ __launch_bounds__(256) void k_prologue_prefill(const T* __restrict__ X, int n, int d,
-                                                          const bf16_t* __restrict__ L1t, int r_pad,
-                                                          uint8_t* __restrict__ xc, float* __restrict__ sx,
-                                                          bf16_t* __restrict__ Tout) {
-  constexpr int RP = NQ * 16 > 0 ? NQ * 16 : 1;
-  __shared__ float smax[4][16];
-  __shared__ float sT[16][RP];
-  __shared__ float s_s[16], s_r[16];
-  __shared__ int s_f[16];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int row0 = blockIdx.x * 16;
-  const int row = min(row0 + lr, n - 1);
-  const T* xr = X + (size_t)row * d;
-  const int nsteps = d >> 5;
+template <typename T>
+struct Row8;
+template <>
+struct Row8<bf16_t> {
+  uint4 r;
+  __device__ __forceinline__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z); v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+  }
+};
+template <>
+struct Row8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
 
-  f32x4 acc[NQ > 0 ? NQ : 1];
+template <typename T, int BA, int BB, int CH>
+__device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, int dl, uint8_t* __restrict__ ca,
+                                               float* __restrict__ sa, uint8_t* __restrict__ cb,
+                                               float* __restrict__ sb) {
+  const int lane = threadIdx.x & 63;
+  const int nch = d >> 3, nchl = dl >> 3;
+  Row8<T> c[CH];
 #pragma unroll
-  for (int q = 0; q < (NQ > 0 ? NQ : 1); ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float amax = 0.0f;
-  for (int s = w; s < nsteps; s += 4) {
-    const int k = 32 * s + 8 * lg;
-    float v[8];
-    uint4 raw;
-    Load8<T>::load(xr + k, v, raw);
+  for (int i = 0; i < CH; ++i) {
+    const int ch = lane + 64 * i;
+    if (ch < nch) c[i].load(x + 8 * ch);
+  }
+  float ma = 0.0f, mb = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    if constexpr (NQ > 0) {
-      const bf16x8 a = as_bf16x8(raw);
+  for (int i = 0; i < CH; ++i) {
+    const int ch = lane + 64 * i;
+    if (ch < nch) {
+      float v[8];
+      c[i].get(v);
+      float mx = 0.0f;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const uint4 b = *reinterpret_cast<const uint4*>(L1t + (size_t)(16 * q + lr) * d + k);
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(b), acc[q], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+      if (ch < nchl)
+        ma = fmaxf(ma, mx);
+      else
+        mb = fmaxf(mb, mx);
     }
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  if (lg == 0) smax[w][lr] = amax;
-  // T partials of the four waves summed in a fixed order (deterministic).
-  if constexpr (NQ > 0) {
-    for (int ww = 0; ww < 4; ++ww) {
-      if (w == ww) {
+  ma = wave_max(ma);
+  mb = wave_max(mb);
+  const RowScale ra = row_scale<BA>(ma);
+  const RowScale rb = row_scale<BB>(mb);
+  if (lane == 0) {
+    *sa = ra.s;
+    if (dl < d) *sb = rb.s;
+  }
+  // The scales are the same in every lane: one scalar branch per row picks
+  // the reciprocal fast path (with its rare per-chunk exact fallback) or the
+  // division path, so neither is evaluated speculatively for the other.
+  auto store = [&](int ch, const int (&q)[8]) {
+    if (ch < nchl) {
+      if (BA == 4)
+        *reinterpret_cast<uint32_t*>(ca + (size_t)ch * 4) = pack_nibbles(q);
+      else
+        *reinterpret_cast<uint2*>(ca + (size_t)ch * 8) = pack_bytes(q);
+    } else {
+      if (BB == 4)
+        *reinterpret_cast<uint32_t*>(cb + (size_t)(ch - nchl) * 4) = pack_nibbles(q);
+      else
+        *reinterpret_cast<uint2*>(cb + (size_t)(ch - nchl) * 8) = pack_bytes(q);
+    }
+  };
+  const bool fast = ra.fast && (dl == d || rb.fast);
+  if (__builtin_amdgcn_readfirstlane(fast ? 1 : 0)) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float& dst = sT[4 * lg + i][16 * q + lr];
-            dst = (ww == 0) ? acc[q][i] : dst + acc[q][i];
-          }
+    for (int i = 0; i < CH; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) {
+        float v[8];
+        int q[8];
+        c[i].get(v);
+        if (ch < nchl)
+          quant8_fast<BA>(v, ra, q);
+        else
+          quant8_fast<BB>(v, rb, q);
+        store(ch, q);
       }
-      __syncthreads();
     }
   } else {
-    __syncthreads();
-  }
-  if (tid < 16) {
-    const float m = fmaxf(fmaxf(smax[0][tid], smax[1][tid]), fmaxf(smax[2][tid], smax[3][tid]));
-    const RowScale rs = row_scale<4>(m);
-    s_s[tid] = rs.s;
-    s_r[tid] = rs.rcp;
-    s_f[tid] = rs.fast ? 1 : 0;
-    if (row0 + tid < n) sx[row0 + tid] = rs.s;
-  }
-  if constexpr (NQ > 0) {
-    for (int e = tid; e < 16 * RP; e += 256) {
-      const int rr = e / RP, cc = e % RP;
-      if (row0 + rr < n) Tout[(size_t)(row0 + rr) * r_pad + cc] = (bf16_t)f32_to_bf16_bits(sT[rr][cc]);
-    }
-  }
-  __syncthreads();
-  const int nch = d >> 3;
-  const int rows_here = min(16, n - row0);
-  for (int rr = 0; rr < rows_here; ++rr) {
-    const RowScale rs = {s_s[rr], s_r[rr], s_f[rr] != 0};
-    const T* xp = X + (size_t)(row0 + rr) * d;
-    uint8_t* cp = xc + (size_t)(row0 + rr) * (d >> 1);
-    for (int ch = tid; ch < nch; ch += 256) {
-      float v[8];
-      uint4 raw;
-      int q[8];
-      Load8<T>::load(xp + 8 * ch, v, raw);
-      quant8<4>(v, rs, q);
-      *reinterpret_cast<uint32_t*>(cp + 4 * ch) = pack_nibbles(q);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) {
+        float v[8];
+        int q[8];
+        c[i].get(v);
+        if (ch < nchl)
+          quant8_exact<BA>(v, ra.s, q);
+        else
+          quant8_exact<BB>(v, rb.s, q);
+        store(ch, q);
+      }
     }
   }
 }
 
+// 4 rows per 256-thread block, one per wave.
+template <typename T, int BA, int BB, int CH>
+__global__ __launch_bounds__(256) void k_quant_rows_wave(const T* __restrict__ X, int n, int d, int dl,
+                                                         uint8_t* __restrict__ ca, float* __restrict__ sa,
+                                                         uint8_t* __restrict__ cb, float* __restrict__ sb) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const size_t lda = (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
+  quant_row_wave<T, BA, BB, CH>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row, cb ? cb + row * ldb : nullptr,
+                                sb ? sb + row : nullptr);
+}
+
 // ---------------------------------------------------------------------------
-// Small-n prologue (n <= 32).  Blocks [0, n) quantise one row each.  Blocks
-// [n, n + nchunk * nq) compute a K-chunk partial of one 16-column slice of
-// T for all rows (two 16-row MFMA tiles), write it to P, and the last block
-// to finish a slice (agent-scope counter) sums the nchunk partials in chunk
-// order into T and resets the counter.
+// Prologue of tq_linear: one launch, two kinds of blocks.
+//  * blocks [0, nqb): 4 rows each, one per wave, 4-bit codes and s_x
+//    (skipped, nqb = 0, when the row does not fit in registers);
+//  * blocks [nqb, nqb + ntb): the first low-rank stage T = X L1 on
+//    v_mfma_f32_16x16x32_bf16.  Block (rt, c, qg) takes rows 16 rt..16 rt+15,
+//    the k-range [c kc, (c+1) kc) and the QS 16-column slices of group qg;
+//    its 4 waves take the 32-k steps round-robin and are summed through LDS
+//    in a fixed order.  With one k-chunk the block writes T directly;
+//    otherwise it writes its fp32 partial to P and the last block of the
+//    (rt, qg) group to finish (agent-scope counter) sums the partials in
+//    chunk order into T and resets the counter.
+// MFMA operand layout: lane l supplies row (or T column) l % 16 and the 8
+// consecutive k at 32 step + 8 (l / 16), for X and L1^T alike.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_prologue_decode(const T* __restrict__ X, int n, int d,
-                                                         const bf16_t* __restrict__ L1t, int r_pad, int kc,
-                                                         int nchunk, uint8_t* __restrict__ xc,
-                                                         float* __restrict__ sx, float* __restrict__ P,
-                                                         bf16_t* __restrict__ Tout, unsigned* __restrict__ counters) {
-  __shared__ float red[16];
-  __shared__ float sP[32][17];
+struct PrologueArgs {
+  const void* X;
+  int n, d;
+  const bf16_t* L1t;
+  int r_pad, kc, nchunk, qs, nqg, nqb;
+  uint8_t* xc;
+  float* sx;
+  float* P;
+  bf16_t* T;
+  unsigned* counters;
+};
+
+template <typename T, int CH, int QS>
+__global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
+  constexpr int U = 8 / QS;  // 32-k steps per wave: all of them in flight at once
+  __shared__ float sP[16][65];
   __shared__ int s_last;
   const int b = blockIdx.x;
-  if (b < n) {
-    quant_row_block<T, 4, 4>(X + (size_t)b * d, d, d, xc + (size_t)b * (d >> 1), sx + b, nullptr, nullptr, red);
+  const T* X = (const T*)a.X;
+  if (b < a.nqb) {
+    const int row = b * 4 + (threadIdx.x >> 6);
+    if (row < a.n)
+      quant_row_wave<T, 4, 4, CH>(X + (size_t)row * a.d, a.d, a.d, a.xc + (size_t)row * (a.d >> 1), a.sx + row,
+                                  nullptr, nullptr);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int nq = r_pad >> 4;
-  const int bb = b - n, c = bb / nq, q = bb % nq;
-  const int s0 = (c * kc) >> 5, s1 = min(d, (c + 1) * kc) >> 5;
-  const bool two = n > 16;
-  const T* x0 = X + (size_t)min(lr, n - 1) * d;
-  const T* x1 = X + (size_t)min(16 + lr, n - 1) * d;
-  const bf16_t* lp = L1t + (size_t)(16 * q + lr) * d;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s = s0 + w; s < s1; s += 4) {
+  const int tb = b - a.nqb;
+  const int per_rt = a.nchunk * a.nqg;
+  const int rt = tb / per_rt, c = (tb % per_rt) / a.nqg, qg = tb % a.nqg;
+  const int d = a.d, n = a.n;
+  // k-chunk c covers the 32-k steps [c * 4U, (c + 1) * 4U); wave w takes every 4th
+  const int s0 = c * 4 * U, s1 = min(d >> 5, s0 + 4 * U);
+  const T* xr = X + (size_t)min(16 * rt + lr, n - 1) * d;
+  const bf16_t* lp = a.L1t + (size_t)(16 * qg * QS + lr) * d;
+
+  f32x4 acc[QS];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 xa[U];
+  uint4 lb[U][QS];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = s0 + w + 4 * u;
     const int k = 32 * s + 8 * lg;
-    const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(lp + k));
-    float v[8];
-    uint4 raw;
-    Load8<T>::load(x0 + k, v, raw);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(raw), bv, acc0, 0, 0, 0);
-    if (two) {
-      Load8<T>::load(x1 + k, v, raw);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(raw), bv, acc1, 0, 0, 0);
+    if (s < s1) {
+      float v[8];
+      Load8<T>::load(xr + k, v, xa[u]);
+#pragma unroll
+      for (int q = 0; q < QS; ++q) lb[u][q] = *reinterpret_cast<const uint4*>(lp + (size_t)16 * q * d + k);
     }
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (s0 + w + 4 * u < s1) {
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(lb[u][q]), acc[q], 0, 0, 0);
+    }
+  }
+  // 16x16 result layout: lane l, element i -> row 4 (l / 16) + i, column l % 16.
   for (int ww = 0; ww < 4; ++ww) {
     if (w == ww) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float& d0 = sP[4 * lg + i][lr];
-        float& d1 = sP[16 + 4 * lg + i][lr];
-        d0 = (ww == 0) ? acc0[i] : d0 + acc0[i];
-        d1 = (ww == 0) ? acc1[i] : d1 + acc1[i];
-      }
+      for (int q = 0; q < QS; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float& dst = sP[4 * lg + i][16 * q + lr];
+            dst = (ww == 0) ? acc[q][i] : dst + acc[q][i];
+          }
     }
     __syncthreads();
   }
-  // partial of chunk c: P[c][row][16q + col]
-  for (int e = tid; e < n * 16; e += 256) {
-    const int rr = e >> 4, cc = e & 15;
-    P[((size_t)c * n + rr) * r_pad + 16 * q + cc] = sP[rr][cc];
+  const int rows = min(16, n - 16 * rt);
+  constexpr int cols = 16 * QS;
+  const int col0 = 16 * qg * QS;
+  if (a.nchunk == 1) {
+    for (int e = tid; e < rows * cols; e += 256) {
+      const int rr = e / cols, cc = e % cols;
+      a.T[(size_t)(16 * rt + rr) * a.r_pad + col0 + cc] = (bf16_t)f32_to_bf16_bits(sP[rr][cc]);
+    }
+    return;
   }
-  __threadfence();
+  // Cross-block sum without device-wide cache maintenance: partials are
+  // written and read with agent-scope atomic stores / loads, which go to the
+  // device's point of coherence, and the barrier below waits until every
+  // wave's stores have completed before the counter is bumped.
+  for (int e = tid; e < rows * cols; e += 256) {
+    const int rr = e / cols, cc = e % cols;
+    __hip_atomic_store(&a.P[((size_t)c * n + 16 * rt + rr) * a.r_pad + col0 + cc], sP[rr][cc], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  unsigned* ctr = a.counters + rt * a.nqg + qg;
   if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(&counters[q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == (unsigned)(nchunk - 1)) ? 1 : 0;
+    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == (unsigned)(a.nchunk - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  for (int e = tid; e < n * 16; e += 256) {
-    const int rr = e >> 4, cc = e & 15;
+  for (int e = tid; e < rows * cols; e += 256) {
+    const int rr = e / cols, cc = e % cols;
+    const float* pp = a.P + (size_t)(16 * rt + rr) * a.r_pad + col0 + cc;
+    const size_t stride = (size_t)n * a.r_pad;
+    const int nc = a.nchunk;
     float sum = 0.0f;
-    for (int cc2 = 0; cc2 < nchunk; ++cc2)
-      sum += __hip_atomic_load(&P[((size_t)cc2 * n + rr) * r_pad + 16 * q + cc], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    Tout[(size_t)rr * r_pad + 16 * q + cc] = (bf16_t)f32_to_bf16_bits(sum);
+    for (int k0 = 0; k0 < nc; k0 += 8) {  // chunk order, 8 loads in flight
+      float part[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < nc) part[k] = __hip_atomic_load(pp + (k0 + k) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k0 + k < nc) sum += part[k];
+    }
+    a.T[(size_t)(16 * rt + rr) * a.r_pad + col0 + cc] = (bf16_t)f32_to_bf16_bits(sum);
   }
-  if (tid == 0) __hip_atomic_store(&counters[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,43 +496,107 @@ hipError_t launch_quant_rows(const void* X, bool bf16, int n, int d, int dl, int
               : launch_quant_rows_t<float>(X, n, d, dl, bits_a, bits_b, ca, sa, cb, sb, st);
 }
 
-template <typename T>
-static hipError_t launch_prologue_prefill_t(const void* X, int n, int d, const void* L1t, int r_pad, void* xc,
-                                            float* sx, void* Tout, hipStream_t st) {
-  dim3 grid((n + 15) / 16), block(256);
+static int chunks_for(int d) {
+  int ch = 1;
+  while (ch * 512 < d) ch <<= 1;
+  return ch;  // 1, 2, 4, ...: row of d values in ch chunks of 8 per lane
+}
+
+template <typename T, int BA, int BB>
+static hipError_t launch_quant_rows_wave_t(const void* X, int n, int d, int dl, void* ca, float* sa, void* cb,
+                                           float* sb, hipStream_t st) {
+  dim3 grid((n + 3) / 4), block(256);
   const T* x = (const T*)X;
-  const bf16_t* l = (const bf16_t*)L1t;
-  uint8_t* c = (uint8_t*)xc;
-  bf16_t* t = (bf16_t*)Tout;
-  switch (r_pad) {
-    case 0: hipLaunchKernelGGL((k_prologue_prefill<T, 0>), grid, block, 0, st, x, n, d, l, r_pad, c, sx, t); break;
-    case 32: hipLaunchKernelGGL((k_prologue_prefill<T, 2>), grid, block, 0, st, x, n, d, l, r_pad, c, sx, t); break;
-    case 64: hipLaunchKernelGGL((k_prologue_prefill<T, 4>), grid, block, 0, st, x, n, d, l, r_pad, c, sx, t); break;
-    case 128: hipLaunchKernelGGL((k_prologue_prefill<T, 8>), grid, block, 0, st, x, n, d, l, r_pad, c, sx, t); break;
-    case 256: hipLaunchKernelGGL((k_prologue_prefill<T, 16>), grid, block, 0, st, x, n, d, l, r_pad, c, sx, t); break;
-    default: return hipErrorInvalidValue;
+  uint8_t* a = (uint8_t*)ca;
+  uint8_t* b = (uint8_t*)cb;
+  switch (chunks_for(d)) {
+    case 1: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 1>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 2: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 2>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 4: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 4>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 8: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 16: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 16>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 32: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 32>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    default: return launch_quant_rows_t<T>(X, n, d, dl, BA, BB, ca, sa, cb, sb, st);  // rows beyond 16384 values
   }
   return hipGetLastError();
 }
 
-hipError_t launch_prologue_prefill(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, void* xc,
-                                   float* sx, void* Tout, hipStream_t st) {
-  return bf16 ? launch_prologue_prefill_t<bf16_t>(X, n, d, L1t, r_pad, xc, sx, Tout, st)
-              : launch_prologue_prefill_t<float>(X, n, d, L1t, r_pad, xc, sx, Tout, st);
+hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
+                                  float* sa, void* cb, float* sb, hipStream_t st) {
+#define TQ_QR(T)                                                                                          \
+  if (bits_a == 4 && bits_b == 8) return launch_quant_rows_wave_t<T, 4, 8>(X, n, d, dl, ca, sa, cb, sb, st); \
+  if (bits_a == 4) return launch_quant_rows_wave_t<T, 4, 4>(X, n, d, dl, ca, sa, cb, sb, st);               \
+  return launch_quant_rows_wave_t<T, 8, 8>(X, n, d, dl, ca, sa, cb, sb, st);
+  if (bf16) {
+    TQ_QR(bf16_t)
+  } else {
+    TQ_QR(float)
+  }
+#undef TQ_QR
 }
 
-hipError_t launch_prologue_decode(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, int kc,
-                                  int nchunk, void* xc, float* sx, float* P, void* Tout, unsigned* counters,
-                                  hipStream_t st) {
+ProloguePlan plan_prologue(int n, int d, int r_pad) {
+  ProloguePlan p{};
   const int nq = r_pad / 16;
-  dim3 grid(n + (r_pad > 0 ? nchunk * nq : 0)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL((k_prologue_decode<bf16_t>), grid, block, 0, st, (const bf16_t*)X, n, d,
-                       (const bf16_t*)L1t, r_pad, kc, nchunk, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters);
-  else
-    hipLaunchKernelGGL((k_prologue_decode<float>), grid, block, 0, st, (const float*)X, n, d, (const bf16_t*)L1t,
-                       r_pad, kc, nchunk, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters);
+  const int nrt = (n + 15) / 16;
+  const int steps = (d + 31) / 32;  // 32-k MFMA steps along d
+  if (nq == 0) {
+    p.qs = 1;
+    p.nqg = 0;
+    p.nchunk = 1;
+    p.kc = d;
+    p.ntb = 0;
+  } else {
+    // QS 16-column slices of T per block (all of them in one block when rows
+    // are many, one per block otherwise); each of the 4 waves then issues all
+    // of its 8 / QS steps at once, so a block covers 4 * 8 / QS steps of k.
+    p.qs = (nrt >= 64) ? std::min(nq, 4) : 1;
+    p.nqg = nq / p.qs;
+    const int chunk_steps = 4 * (8 / p.qs);
+    p.kc = 32 * chunk_steps;
+    p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
+    p.ntb = nrt * p.nchunk * p.nqg;
+  }
+  p.quant_in_prologue = chunks_for(d) <= 32;
+  p.nqb = p.quant_in_prologue ? (n + 3) / 4 : 0;
+  p.counters = (p.nchunk > 1) ? nrt * std::max(p.nqg, 1) : 0;
+  return p;
+}
+
+template <typename T, int QS>
+static hipError_t launch_prologue_q(const PrologueArgs& a, int ch, hipStream_t st) {
+  const dim3 grid(a.nqb + (unsigned)(a.nqg ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0)), block(256);
+  switch (ch) {
+    case 1: hipLaunchKernelGGL((k_prologue<T, 1, QS>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_prologue<T, 2, QS>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_prologue<T, 4, QS>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_prologue<T, 8, QS>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_prologue<T, 16, QS>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_prologue<T, 32, QS>), grid, block, 0, st, a); break;
+  }
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_prologue_t(const PrologueArgs& a, int ch, hipStream_t st) {
+  switch (a.qs) {
+    case 1: return launch_prologue_q<T, 1>(a, ch, st);
+    case 2: return launch_prologue_q<T, 2>(a, ch, st);
+    default: return launch_prologue_q<T, 4>(a, ch, st);
+  }
+}
+
+hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
+                           void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st) {
+  if (!p.quant_in_prologue) {
+    hipError_t e = launch_quant_rows(X, bf16, n, d, d, 4, 4, xc, sx, nullptr, nullptr, st);
+    if (e != hipSuccess) return e;
+    if (p.ntb == 0) return hipSuccess;
+  }
+  PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, p.nqb, (uint8_t*)xc, sx, P,
+                 (bf16_t*)Tout, counters};
+  const int ch = std::min(chunks_for(d), 32);
+  return bf16 ? launch_prologue_t<bf16_t>(a, ch, st) : launch_prologue_t<float>(a, ch, st);
 }
 
 }  // namespace tq

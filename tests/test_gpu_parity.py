@@ -196,6 +196,28 @@ def _ws_codes(ws, n, d, m, r):
     return sx, tqo.unpack_int4(xc)
 
 
+def _r_pad(r):
+    p = 32
+    while p < r:
+        p *= 2
+    return p if r else 0
+
+
+def _assert_t(ws, x, l1, n, d, m, r, rows=None):
+    """T = X L1 from the workspace against the fp64 oracle branch (bf16 rounding of X and T)."""
+    if not r:
+        return
+    rp = _r_pad(r)
+    off = tq.tq_linear_workspace_offsets(n, d, m, r)["T"]
+    t = ws[off: off + n * rp * 2].view(torch.bfloat16).view(n, rp).float().cpu().numpy()[:, :r]
+    rows = np.arange(n) if rows is None else rows
+    t_ref, _ = tqo.lowrank_branch(x[rows], l1, np.zeros((r, 1)))
+    scale = np.abs(t_ref).max(axis=1, keepdims=True) + 1e-30
+    err = np.abs(t[rows] - t_ref) / scale
+    print(f"  T max rel err {err.max():.3e}", flush=True)
+    assert err.max() <= 2e-2, err.max()
+
+
 LCASES = [
     # (name, n, d, m, r, x_kind, x_dtype, outliers)
     ("small_linear", 16, 512, 512, 16, "normal", "f32", 4),
@@ -228,6 +250,7 @@ def test_linear_small(case):
     acc = tq.tq_debug_accumulate(xc.contiguous(), wc, d, 4)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
+    _assert_t(ws, c["X"], l1, n, d, m, r)
     _assert_y(y, ref["Y"], name)
 
 
@@ -290,6 +313,7 @@ def test_linear_workload(wl, n, outl):
     acc = tq.tq_debug_accumulate(xc, wc, d, 4)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), ref["acc"])
+    _assert_t(ws, c["X"], c["L1"], n, d, m, r, rows)
     _assert_y(y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)], ref["Y"], f"{wl} n={n}")
 
 
@@ -309,12 +333,17 @@ def _run_mp(xrot, wrot, d_hi):
 
 
 @pytest.mark.parametrize("n,d,m,dh", [(40, 512, 96, 64), (130, 1024, 272, 128), (16, 256, 64, 0),
-                                      (70, 256, 80, 256), (9, 8192, 48, 128)])
+                                      (70, 256, 80, 256), (9, 8192, 48, 128), (70, 1024, 80, 512),
+                                      (300, 1024, 200, 384), (512, 1024, 28672, 512), (512, 1024, 28672, 128)])
 def test_linear_mp_small(n, d, m, dh):
+    """Ragged tails; high subspaces of 0 .. 512 columns; the 256 x 256 tile (n = 512, m = 28672)."""
     print(f"case mp n={n} d={d} m={m} d_hi={dh}", flush=True)
     c = draw_two_subspace_custom(n, d, m, dh, seed=n + d + m, outlier_count=2)
     y = _run_mp(c["Xrot"], c["Wrot"], dh)
-    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], dh)
+    rows, cols = (None, None) if m < 4096 else _sample(n, m, np.random.default_rng(n), 64, 512)
+    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], dh, rows=rows, cols=cols)
+    if rows is not None:
+        y = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
     _assert_y(y, ref["Y"], f"mp n={n} d={d} dh={dh}")
 
 

@@ -186,11 +186,20 @@ __device__ __forceinline__ i32x4 unpack16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// Max of |x| over non-negative floats via their bit patterns.
+// Maximum of non-negative floats over the 64 lanes of a wave, returned in
+// every lane.  Non-negative floats order like their bit patterns as signed
+// ints.  DPP steps inside each 16-lane row (swap neighbours, swap pairs,
+// mirror half-rows, mirror rows) leave the row maximum in every lane of the
+// row; the four row maxima are then read as scalars.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  int x = __float_as_int(v);
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  const int m = max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+                    max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+  return __int_as_float(m);
 }
 
 }  // namespace tq

@@ -235,7 +235,7 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
     }
   }
   ma = wave_max(ma);
-  mb = wave_max(mb);
+  if (dl < d) mb = wave_max(mb);
   const RowScale ra = row_scale<BA>(ma);
   const RowScale rb = row_scale<BB>(mb);
   if (lane == 0) {
@@ -351,33 +351,35 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   const int per_rt = a.nchunk * a.nqg;
   const int rt = tb / per_rt, c = (tb % per_rt) / a.nqg, qg = tb % a.nqg;
   const int d = a.d, n = a.n;
-  // k-chunk c covers the 32-k steps [c * 4U, (c + 1) * 4U); wave w takes every 4th
-  const int s0 = c * 4 * U, s1 = min(d >> 5, s0 + 4 * U);
+  // k-chunk c covers the 32-k steps [c * kc / 32, (c + 1) * kc / 32); wave w takes every 4th
+  const int s0 = c * (a.kc >> 5), s1 = min(d >> 5, s0 + (a.kc >> 5));
   const T* xr = X + (size_t)min(16 * rt + lr, n - 1) * d;
   const bf16_t* lp = a.L1t + (size_t)(16 * qg * QS + lr) * d;
 
   f32x4 acc[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 xa[U];
-  uint4 lb[U][QS];
+  for (int sb = s0 + w; sb < s1; sb += 4 * U) {  // batches of U steps, all loads in flight
+    uint4 xa[U];
+    uint4 lb[U][QS];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = s0 + w + 4 * u;
-    const int k = 32 * s + 8 * lg;
-    if (s < s1) {
-      float v[8];
-      Load8<T>::load(xr + k, v, xa[u]);
+    for (int u = 0; u < U; ++u) {
+      const int s = sb + 4 * u;
+      const int k = 32 * s + 8 * lg;
+      if (s < s1) {
+        float v[8];
+        Load8<T>::load(xr + k, v, xa[u]);
 #pragma unroll
-      for (int q = 0; q < QS; ++q) lb[u][q] = *reinterpret_cast<const uint4*>(lp + (size_t)16 * q * d + k);
+        for (int q = 0; q < QS; ++q) lb[u][q] = *reinterpret_cast<const uint4*>(lp + (size_t)16 * q * d + k);
+      }
     }
-  }
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (s0 + w + 4 * u < s1) {
+    for (int u = 0; u < U; ++u) {
+      if (sb + 4 * u < s1) {
 #pragma unroll
-      for (int q = 0; q < QS; ++q)
-        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(lb[u][q]), acc[q], 0, 0, 0);
+        for (int q = 0; q < QS; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(lb[u][q]), acc[q], 0, 0, 0);
+      }
     }
   }
   // 16x16 result layout: lane l, element i -> row 4 (l / 16) + i, column l % 16.
@@ -552,9 +554,18 @@ ProloguePlan plan_prologue(int n, int d, int r_pad) {
     // of its 8 / QS steps at once, so a block covers 4 * 8 / QS steps of k.
     p.qs = (nrt >= 64) ? std::min(nq, 4) : 1;
     p.nqg = nq / p.qs;
-    const int chunk_steps = 4 * (8 / p.qs);
-    p.kc = 32 * chunk_steps;
-    p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
+    if (nrt * p.nqg >= 128) {
+      // many row tiles: one block per (row tile, slice group) over all of k,
+      // no partial sums to combine across blocks
+      p.kc = 32 * steps;
+      p.nchunk = 1;
+    } else {
+      // few row tiles: split k so that each wave issues all of its 8 / QS
+      // steps at once, and combine the partials across blocks
+      const int chunk_steps = 4 * (8 / p.qs);
+      p.kc = 32 * chunk_steps;
+      p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
+    }
     p.ntb = nrt * p.nchunk * p.nqg;
   }
   p.quant_in_prologue = chunks_for(d) <= 32;

@@ -110,8 +110,9 @@ tq_status tq_pack_lowrank(const void* L1, const void* L2, tq_dtype dt, int64_t d
  * tq_quantize_act -- per-token symmetric quantisation of activations.
  *   X       n x d, element type x_dt.  bits 4 or 8.
  *   x_codes out: n x (d*bits/8) bytes.   s_x out: n fp32 scales.
- * "The residual GEMM quantizes activations concurrently" (TwinQuant notes
- * section 04.C); per-token activation scales (CoQuant protocol).
+ * In the fused layer the activations are quantised inside the residual
+ * GEMM's launch sequence (TwinQuant notes section 04.C); the scales are per
+ * token (CoQuant, experimental protocol).
  */
 tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int bits,
                           void* x_codes, float* s_x, hipStream_t stream);

@@ -245,6 +245,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(GemmArgs g) {
   };
   constexpr int SH = (BITS == 4) ? 8 : 0;  // int8 lanes carry 16 * code: acc = 256 * sum
 
+  // bf16 output of the rank-augmented epilogue is staged per wave in LDS (the
+  // main loop's buffers are free by then): WN token rows of WM channels.
+  // Row r, 16-byte chunk j (8 channels) sits at chunk j ^ sw(r) (sw = r % 16
+  // for 256-byte rows, (r / 2) % 8 for 128-byte rows, whose odd rows already
+  // sit on the other 32 banks), and rows with bit 4 set swap the two 8-byte
+  // halves of each chunk, so the 8-byte writes of 32 consecutive rows and
+  // the 16-byte reads of whole rows both touch every bank once per pass.
+  constexpr bool STAGE_Y = EPI == EPI_LINEAR;
+  constexpr int YCH = WM / 8;  // 16-byte chunks per staged row
+  static_assert(!STAGE_Y || (WGM * WGN * WN * WM * 2 <= 2 * STAGE), "staged Y tile exceeds LDS");
+  static_assert(!STAGE_Y || (YCH == 8 || YCH == 16), "staged row width");
+  uint8_t* sYw = smem + wave * (WN * WM * 2);
+  auto ychunk = [&](int row, int j) -> int {
+    const int sw = (YCH == 16) ? (row & 15) : ((row >> 1) & 7);
+    return row * (WM * 2) + 16 * (j ^ sw);
+  };
+  auto yslot = [&](int row, int j, int half) -> int { return ychunk(row, j) + 8 * (half ^ ((row >> 4) & 1)); };
+
   if constexpr (EPI == EPI_ACC) {
 #pragma unroll
     for (int a = 0; a < FM; ++a)
@@ -361,9 +379,46 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(GemmArgs g) {
             }
           }
         }
+        if (STAGE_Y && g.y_bf16) {
+          // bf16 result into the wave's LDS tile (see the write-out below)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) store4(tok(b), chan(a, e4), y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]);
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int row = 32 * b + l32;
+            *reinterpret_cast<uint2*>(sYw + yslot(row, 4 * a + e4, lgrp)) =
+                uint2{pack_bf16x2(y[4 * e4], y[4 * e4 + 1]), pack_bf16x2(y[4 * e4 + 2], y[4 * e4 + 3])};
+          }
+        } else {
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4)
+            store4(tok(b), chan(a, e4), y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (STAGE_Y && g.y_bf16) {
+      // Write-out of the wave's WN tokens x WM channels: 16 bytes per lane,
+      // WM / 8 lanes per token row, so each token's WM * 2 contiguous bytes of
+      // Y go out as whole cache lines.
+      __syncthreads();
+      constexpr int RPI = 64 / YCH;  // token rows per instruction
+      const int jc = lane % YCH, rsub = lane / YCH;
+      const int c = ch0 + wm * WM + 8 * jc;
+#pragma unroll 4
+      for (int r0 = 0; r0 < WN; r0 += RPI) {
+        const int row = r0 + rsub;
+        const int t = tk0 + wn * WN + row;
+        uint4 v = *reinterpret_cast<const uint4*>(sYw + ychunk(row, jc));
+        if ((row >> 4) & 1) v = uint4{v.z, v.w, v.x, v.y};
+        if (t < g.M) {
+          bf16_t* yp = reinterpret_cast<bf16_t*>(g.Y) + (size_t)t * g.ldy + c;
+          if (c + 7 < g.N && (g.ldy & 7) == 0) {
+            *reinterpret_cast<uint4*>(yp) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 8; ++q)
+              if (c + q < g.N) yp[q] = (bf16_t)((q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xFFFFu));
+          }
+        }
       }
     }
   }

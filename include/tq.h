@@ -129,13 +129,18 @@ size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
  *   Y        out: n x m, element type y_dt (TQ_BF16 or TQ_F32), rounded to
  *            nearest even from the fp32 epilogue.
  *   ws       device workspace of at least tq_linear_workspace_bytes(n,d,m,r)
- *            bytes.  It starts with completion counters of the low-rank
- *            stage: zero-fill the workspace once before its first use (e.g.
+ *            bytes.  It starts with completion counters (of the low-rank
+ *            stage, and of the hand-off inside the few-token launch):
+ *            zero-fill the workspace once before its first use (e.g.
  *            hipMemset after allocating it); every call leaves the counters
  *            zero again, and the rest is scratch whose contents on entry are
- *            ignored.
- * For n <= 32 the call runs a memory-bound path (weight codes streamed once);
- * otherwise a tiled MFMA path.  Both produce bit-identical integer
+ *            ignored.  Calls that share a workspace must be ordered (one
+ *            stream, or synchronised streams).
+ * For n <= 32 the call runs a memory-bound path (weight codes streamed once;
+ * for n <= 2 and d <= 4096 in one launch, whose weight-streaming blocks
+ * wait for the blocks that compute T with a bounded wait that sets the third
+ * word at off[3] of tq_linear_workspace_offsets instead of hanging);
+ * otherwise a tiled MFMA path.  All paths produce bit-identical integer
  * accumulators.
  */
 tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
@@ -147,9 +152,12 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
  * results inside the workspace, for inspection after a call:
  *   off[0] s_x (n fp32), off[1] activation codes (n x d/2 bytes),
  *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
- *   >= 32; absent when r == 0).  Returns TQ_ERR_SHAPE for invalid sizes.
+ *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words of
+ *   the one-launch path (all zero between calls; the third word is set if a
+ *   wait hit its limit).
+ *   Returns TQ_ERR_SHAPE for invalid sizes.
  */
-tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[3]);
+tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]);
 
 /* Workspace bytes tq_linear_mp needs for these sizes. */
 size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);

@@ -78,10 +78,11 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   } while (0)
 
 struct LinearWs {
-  size_t ctr, sx, xc, t, p, total;
+  size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;
-  bool small;
+  bool small, fused;
   tq::ProloguePlan plan;
+  tq::SmallPlan splan;
 };
 
 LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
@@ -89,10 +90,24 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
   LinearWs w{};
   w.small = n <= kSmallN;
   w.r_pad = (int)r_padded(r);
-  w.plan = tq::plan_prologue((int)n, (int)d, w.r_pad);
+  w.fused = w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
+  size_t psize = 0;
+  int counters = 0;
+  if (w.fused) {
+    w.splan = tq::plan_small((int)n, (int)d, w.r_pad);
+    psize = (size_t)w.splan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
+  } else {
+    w.plan = tq::plan_prologue((int)n, (int)d, w.r_pad, w.small,
+                               w.small ? tq::gemv_max_chunks((int)n, (int)(d / 2), w.r_pad) : 1);
+    counters = w.plan.counters;
+    if (w.plan.ntb > 0 && (w.plan.nchunk > 1 || w.plan.partial))
+      psize = (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
+  }
   size_t o = 0;
+  w.sync = o;  // hand-off counters of the few-token launch
+  o = tq::kSyncBytes;
   w.ctr = o;
-  o = align256(o + (size_t)w.plan.counters * 4 + 1);
+  o = align256(o + (size_t)counters * 4 + 1);
   w.sx = o;
   o = align256(o + (size_t)n * 4);
   w.xc = o;
@@ -100,7 +115,7 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
   w.t = o;
   o = align256(o + (size_t)n * (size_t)w.r_pad * 2);
   w.p = o;
-  if (w.plan.ntb > 0 && w.plan.nchunk > 1) o = align256(o + (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4);
+  o = align256(o + psize);
   w.total = o;
   return w;
 }
@@ -224,6 +239,33 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   const tq::bf16_t* L2t = lowrank ? L1t + (size_t)L.r_pad * d : nullptr;
   const bool xb = x_dt == TQ_BF16;
 
+  if (L.fused) {
+    tq::SmallArgs a{};
+    a.X = X;
+    a.n = (int)n;
+    a.d = (int)d;
+    a.m = (int)m;
+    a.wc = (const uint8_t*)w_codes;
+    a.sw = s_w;
+    a.L1t = L1t;
+    a.L2t = L2t;
+    a.r_pad = L.r_pad;
+    a.nt = L.splan.nt;
+    a.nchunk = L.splan.nchunk;
+    a.kc = L.splan.kc;
+    a.qs = L.splan.qs;
+    a.nqg = L.splan.nqg;
+    a.xc = xc;
+    a.sx = sx;
+    a.P = P;
+    a.Tout = L.r_pad ? T : nullptr;
+    a.sync = (unsigned*)(base + L.sync);
+    a.Y = Y;
+    a.y_bf16 = y_dt == TQ_BF16;
+    TQ_RUN("linear_small", stream, tq::launch_linear_small(a, xb, stream));
+    return TQ_OK;
+  }
+
   GemmArgs g{};
   g.A = xc;
   g.lda = d / 2;
@@ -237,6 +279,11 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   g.T = L.r_pad ? T : nullptr;
   g.L2t = L2t;
   g.r_pad = L.r_pad;
+  if (L.r_pad && L.plan.partial) {
+    g.P = P;
+    g.nchunk = L.plan.nchunk;
+    g.Tout = T;
+  }
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
@@ -250,13 +297,14 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   return TQ_OK;
 }
 
-tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[3]) {
+tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]) {
   if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256 || d % 32) return TQ_ERR_SHAPE;
   if (!off) return TQ_ERR_NULL;
   const LinearWs L = linear_ws(n, d, m, r);
   off[0] = L.sx;
   off[1] = L.xc;
   off[2] = L.t;
+  off[3] = L.sync;
   return TQ_OK;
 }
 

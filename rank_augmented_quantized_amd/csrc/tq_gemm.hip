@@ -426,99 +426,224 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // Small-n kernel (M <= 32): memory-bound on the weight codes.
-//   Block: 16 output columns, WAVES waves splitting K in 64-byte steps (each
-//   lane group of 16 lanes loads 16 bytes per column per step).  MFMA
-//   16x16x64 int8 with up to two 16-row tiles sharing each weight fragment.
-//   The waves' int32 partials are summed exactly through LDS; the epilogue
-//   (dequantisation + T L2 on the VALU) produces one Y value per thread.
+//   Block: 16 output channels; WAVES waves split K into contiguous ranges of
+//   64-byte steps (lane group g of 16 lanes loads bytes 16 g .. 16 g + 15 of
+//   each step for channel lane % 16).  Every load of a batch of U steps --
+//   weights, the matching activation codes, and the low-rank operands -- is
+//   issued before the first wait, so a block pays one memory round trip per
+//   batch.  MFMA 16x16x64 int8 (TWO: a second 16-token tile shares each
+//   weight fragment); the waves' int32 partials are summed exactly through
+//   LDS in wave order.
+//   Epilogue: T is the sum over the k-chunks of the fp32 partials of X L1
+//   written by the prologue (P; chunk order, then rounded to bf16; block 0
+//   also writes it to Tout); T L2 for the block's 16 channels
+//   is one 16x16 bf16 MFMA chain whose result layout matches the integer
+//   accumulator's (lane l, element i -> token 4 (l / 16) + i, channel l % 16).
 // ---------------------------------------------------------------------------
-template <int BITS, int EPI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_gemv(GemmArgs g) {
-  constexpr int U = 16;  // weight loads in flight per lane
-  __shared__ int red[WAVES][2][4][64];
+template <int BITS, int EPI, int WAVES, bool TWO>
+__global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g) {
+  constexpr int U = (WAVES == 4 || TWO) ? 8 : 16;  // 64-byte steps per wave per batch
+  constexpr int NT = WAVES * 64;
+  constexpr int MT = TWO ? 32 : 16;  // token rows held for the low-rank stage
+  constexpr bool LR = EPI == EPI_LINEAR;
+  __shared__ int red[WAVES][TWO ? 2 : 1][4][64];
+  __shared__ __attribute__((aligned(16))) bf16_t sT[LR ? MT * 256 : 1];
+  __shared__ __attribute__((aligned(16))) bf16_t sL[LR ? 16 * 256 : 1];
+  __shared__ __attribute__((aligned(16))) float4 sPart[LR ? NT : 1][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16;
-  const bool two = g.M > 16;
   const uint8_t* bp = g.B + (size_t)min(n0 + l16, g.N - 1) * g.ldb + 16 * lg;
   const uint8_t* ap0 = g.A + (size_t)min(l16, g.M - 1) * g.lda + 16 * lg;
   const uint8_t* ap1 = g.A + (size_t)min(16 + l16, g.M - 1) * g.lda + 16 * lg;
-  // each wave streams one contiguous k-range of the block's 16 columns
   const int KS = (g.Kb + 63) / 64;
   const int per = (KS + WAVES - 1) / WAVES;
   const int sbeg = wave * per, send = min(KS, sbeg + per);
-  i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  for (int s0 = sbeg; s0 < send; s0 += U) {
-    uint4 bv[U];
+  const int rp = LR ? g.r_pad : 0;
+  const int rq = rp / 8;  // 16-byte pieces (8 values) per low-rank row
+  // T pieces: NP = M rows x rq; G thread groups (no more than there are
+  // chunks) split the k-chunks of each piece, at most two chunks per group
+  const int NP = g.M * rq;
+  const int G = max(1, min(NT / max(NP, 1), LR ? g.nchunk : 1));
+
+  // Loads are unconditional, from clamped (always valid) addresses, and
+  // masked where used: conditional loads become branches whose register
+  // merges force early waits on every load in flight.
+  const int kb_last = max(0, min((max(send, sbeg + 1) - 1) * 64, g.Kb - 16 - 16 * lg));
+  uint4 bv[U], av0[U], av1[U];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) bv[u] = *reinterpret_cast<const uint4*>(bp + min((s0 + u) * 64, kb_last));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = (s0 + u) * 64;
-      const bool ok = (s0 + u < send) && (kb + 16 * lg < g.Kb);
-      bv[u] = ok ? *reinterpret_cast<const uint4*>(bp + kb) : uint4{0, 0, 0, 0};
+      const int kb = min((s0 + u) * 64, kb_last);
+      av0[u] = *reinterpret_cast<const uint4*>(ap0 + kb);
+      if (TWO) av1[u] = *reinterpret_cast<const uint4*>(ap1 + kb);
     }
+  };
+  i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  auto mma_batch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + u >= send) break;
-      const int kb = (s0 + u) * 64;
-      const bool ok = kb + 16 * lg < g.Kb;
-      const uint4 av0 = ok ? *reinterpret_cast<const uint4*>(ap0 + kb) : uint4{0, 0, 0, 0};
-      const uint4 av1 = (ok && two) ? *reinterpret_cast<const uint4*>(ap1 + kb) : uint4{0, 0, 0, 0};
+      if (s0 + u >= send) continue;
+      if ((s0 + u) * 64 + 16 * lg >= g.Kb) {  // this lane group's 16 bytes lie past the row: zero codes
+        bv[u] = uint4{0, 0, 0, 0};
+        av0[u] = uint4{0, 0, 0, 0};
+        av1[u] = uint4{0, 0, 0, 0};
+      }
       if (BITS == 4) {
         const i32x4 b0 = unpack16(bv[u].x, bv[u].y), b1 = unpack16(bv[u].z, bv[u].w);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0.x, av0.y), b0, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0.z, av0.w), b1, acc0, 0, 0, 0);
-        if (two) {
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1.x, av1.y), b0, acc1, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1.z, av1.w), b1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].x, av0[u].y), b0, acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].z, av0[u].w), b1, acc0, 0, 0, 0);
+        if (TWO) {
+          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].x, av1[u].y), b0, acc1, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].z, av1[u].w), b1, acc1, 0, 0, 0);
         }
       } else {
         const i32x4 b0 = __builtin_bit_cast(i32x4, bv[u]);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0), b0, acc0, 0, 0, 0);
-        if (two) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av1), b0, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0[u]), b0, acc0, 0, 0, 0);
+        if (TWO) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av1[u]), b0, acc1, 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- issue every load of the first batch before any wait ----
+  float sxv[4], swv = 0.0f;  // epilogue scales
+  if (LR) {
+    swv = g.sw[min(n0 + l16, g.N - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
+  }
+  load_batch(sbeg);
+  // Low-rank operands, with clamped (always valid) indices, masked where used,
+  // so that none of them needs a wait before the integer product: piece
+  // tid of L2^T (16 x rp), and for thread (piece p, group q), q < G, of T
+  // the chunks q and q + G of the prologue's fp32 partials.
+  uint4 lv;
+  float4 pv[2][2];
+  if (LR && rp > 0) {
+    const int el = min(tid, 16 * rq - 1);
+    lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
+    if (tid < NP * G) {
+      const int pc = tid % NP, grp = tid / NP;
+      const int rowt = pc / rq, qt = pc % rq;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = min(grp + G * j, g.nchunk - 1);
+        const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)c * g.M + rowt) * rp + 8 * qt);
+        pv[j][0] = pp[0];
+        pv[j][1] = pp[1];
       }
     }
   }
+
+  // ---- integer product ----
+  mma_batch(sbeg);
+  for (int s0 = sbeg + U; s0 < send; s0 += U) {
+    load_batch(s0);
+    mma_batch(s0);
+  }
+
+  // ---- low-rank operands into LDS (T rows >= M are zero) ----
+  if (LR && rp > 0) {
+    if (tid < 16 * rq) *reinterpret_cast<uint4*>(sL + tid * 8) = (n0 + tid / rq < g.N) ? lv : uint4{0, 0, 0, 0};
+    for (int e = tid + NT; e < 16 * rq; e += NT) {
+      const int c = e / rq, q = e % rq;
+      uint4 v = uint4{0, 0, 0, 0};
+      if (n0 + c < g.N) v = *reinterpret_cast<const uint4*>(g.L2t + (size_t)(n0 + c) * rp + 8 * q);
+      *reinterpret_cast<uint4*>(sL + e * 8) = v;
+    }
+    if (tid < NP * G) {
+      const int grp = tid / NP;
+      float4 t0 = float4{0.f, 0.f, 0.f, 0.f}, t1 = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (grp + G * j < g.nchunk) {
+          t0.x += pv[j][0].x; t0.y += pv[j][0].y; t0.z += pv[j][0].z; t0.w += pv[j][0].w;
+          t1.x += pv[j][1].x; t1.y += pv[j][1].y; t1.z += pv[j][1].z; t1.w += pv[j][1].w;
+        }
+      }
+      sPart[tid][0] = t0;
+      sPart[tid][1] = t1;
+    }
+    __syncthreads();
+    // piece p: groups in order -> bf16; rows M .. MT - 1 zero
+    for (int pc = tid; pc < MT * rq; pc += NT) {
+      const int row = pc / rq, q = pc % rq;
+      uint4 v = uint4{0, 0, 0, 0};
+      if (row < g.M) {
+        float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (pc < NT) {
+          for (int gi = 0; gi < G; ++gi) {
+            const float4 x0 = sPart[gi * NP + pc][0], x1 = sPart[gi * NP + pc][1];
+            t[0] += x0.x; t[1] += x0.y; t[2] += x0.z; t[3] += x0.w;
+            t[4] += x1.x; t[5] += x1.y; t[6] += x1.z; t[7] += x1.w;
+          }
+        } else {  // pieces beyond the block's threads (G == 1): all chunks here
+          for (int k = 0; k < g.nchunk; ++k) {
+            const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)k * g.M + row) * rp + 8 * q);
+            const float4 x0 = pp[0], x1 = pp[1];
+            t[0] += x0.x; t[1] += x0.y; t[2] += x0.z; t[3] += x0.w;
+            t[4] += x1.x; t[5] += x1.y; t[6] += x1.z; t[7] += x1.w;
+          }
+        }
+        v = uint4{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]), pack_bf16x2(t[4], t[5]), pack_bf16x2(t[6], t[7])};
+        if (blockIdx.x == 0 && g.Tout) *reinterpret_cast<uint4*>(g.Tout + (size_t)row * rp + 8 * q) = v;
+      }
+      *reinterpret_cast<uint4*>(sT + pc * 8) = v;
+    }
+  }
+
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     red[wave][0][i][lane] = acc0[i];
-    red[wave][1][i][lane] = acc1[i];
+    if (TWO) red[wave][TWO ? 1 : 0][i][lane] = acc1[i];
   }
   __syncthreads();
-  // 16x16 MFMA result layout: lane l, element i -> row 4*(l/16) + i, column l%16.
-  for (int o = tid; o < 512; o += WAVES * 64) {
-    const int tile = o >> 8, ln = (o >> 2) & 63, i = o & 3;
-    const int row = 16 * tile + 4 * (ln >> 4) + i, col = n0 + (ln & 15);
-    if (row >= g.M || col >= g.N) continue;
-    int s = 0;
+  // wave t (t < number of 16-token tiles) finishes tile t
+  constexpr int TILES = TWO ? 2 : 1;
+  if (wave >= TILES) return;
+  const int tile = wave;
+  int sacc[4];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += red[w][tile][i][ln];
-    if (BITS == 4) s >>= 8;
-    if constexpr (EPI == EPI_ACC) {
-      g.acc[(size_t)row * g.N + col] = s;
-    } else {
-      float y = (float)s * (g.sx[row] * g.sw[col]);
-      if (g.r_pad > 0) {
-        const bf16_t* tp = g.T + (size_t)row * g.r_pad;
-        const bf16_t* lp = g.L2t + (size_t)col * g.r_pad;
-        for (int t = 0; t < g.r_pad; t += 8) {
-          const uint4 a = *reinterpret_cast<const uint4*>(tp + t);
-          const uint4 b = *reinterpret_cast<const uint4*>(lp + t);
-          y = fmaf(bf16_lo(a.x), bf16_lo(b.x), y);
-          y = fmaf(bf16_hi(a.x), bf16_hi(b.x), y);
-          y = fmaf(bf16_lo(a.y), bf16_lo(b.y), y);
-          y = fmaf(bf16_hi(a.y), bf16_hi(b.y), y);
-          y = fmaf(bf16_lo(a.z), bf16_lo(b.z), y);
-          y = fmaf(bf16_hi(a.z), bf16_hi(b.z), y);
-          y = fmaf(bf16_lo(a.w), bf16_lo(b.w), y);
-          y = fmaf(bf16_hi(a.w), bf16_hi(b.w), y);
-        }
-      }
+  for (int i = 0; i < 4; ++i) {
+    int v = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w][tile][i][lane];
+    sacc[i] = (BITS == 4) ? (v >> 8) : v;
+  }
+  const int col = n0 + l16;
+  if constexpr (EPI == EPI_ACC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * tile + 4 * lg + i;
+      if (row < g.M && col < g.N) g.acc[(size_t)row * g.N + col] = sacc[i];
+    }
+  } else {
+    f32x4 lr = {0.f, 0.f, 0.f, 0.f};
+    for (int t0 = 0; t0 < rp; t0 += 32) {
+      // A: T rows (tokens), B: L2^T rows (channels); 8 consecutive t per lane
+      const uint4 a8 = *reinterpret_cast<const uint4*>(sT + (16 * tile + l16) * rp + t0 + 8 * lg);
+      const uint4 b8 = *reinterpret_cast<const uint4*>(sL + l16 * rp + t0 + 8 * lg);
+      lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a8), as_bf16x8(b8), lr, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * tile + 4 * lg + i;
+      if (row >= g.M || col >= g.N) continue;
+      const float y = (float)sacc[i] * (sxv[i] * swv) + lr[i];
       if (g.y_bf16)
         reinterpret_cast<bf16_t*>(g.Y)[(size_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_bits(y);
       else
         reinterpret_cast<float*>(g.Y)[(size_t)row * g.ldy + col] = y;
     }
   }
+}
+
+int gemv_max_chunks(int M, int Kb, int r_pad) {
+  const int nt = (Kb > 2048 ? 8 : 4) * 64;
+  const int np = M * (r_pad / 8);
+  return 2 * std::max(1, nt / std::max(np, 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -569,14 +694,20 @@ hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-template <int BITS, int EPI>
-static hipError_t gemv_cols(const GemmArgs& g, hipStream_t st) {
+template <int BITS, int EPI, bool TWO>
+static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
   const unsigned blocks = (unsigned)((g.N + 15) / 16);
   if (g.Kb > 2048)
-    hipLaunchKernelGGL((k_gemv<BITS, EPI, 8>), dim3(blocks), dim3(512), 0, st, g);
+    hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO>), dim3(blocks), dim3(512), 0, st, g);
   else
-    hipLaunchKernelGGL((k_gemv<BITS, EPI, 4>), dim3(blocks), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO>), dim3(blocks), dim3(256), 0, st, g);
   return hipGetLastError();
+}
+
+template <int BITS, int EPI>
+static hipError_t gemv_cols(const GemmArgs& g, hipStream_t st) {
+  if (EPI == EPI_LINEAR && (g.r_pad > 256 || (g.r_pad > 0 && (!g.P || g.nchunk < 1)))) return hipErrorInvalidValue;
+  return g.M > 16 ? gemv_cols_t<BITS, EPI, true>(g, st) : gemv_cols_t<BITS, EPI, false>(g, st);
 }
 
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st) {

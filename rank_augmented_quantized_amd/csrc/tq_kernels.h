@@ -30,6 +30,11 @@ struct GemmArgs {
   const bf16_t* T;    // M x r_pad (bf16) or null
   const bf16_t* L2t;  // N x r_pad (bf16) or null
   int r_pad;
+  // small-n path: T comes as nchunk fp32 partials P[c][M][r_pad], summed in
+  // chunk order by the kernel, which also writes the bf16 sum to Tout
+  const float* P;
+  int nchunk;
+  bf16_t* Tout;
   void* Y;
   int64_t ldy;  // elements
   int y_bf16;
@@ -44,10 +49,16 @@ hipError_t launch_quant_rows(const void* X, bool bf16, int n, int d, int dl, int
                              float* sa, void* cb, float* sb, hipStream_t st);
 // Work split of the tq_linear prologue (quantisation + T = X L1).
 struct ProloguePlan {
-  int kc, nchunk, qs, nqg, ntb, nqb, counters;
+  int kc, nchunk, qs, nqg, ntb, nqb, counters, waves;
   bool quant_in_prologue;
+  bool partial;     // T left as fp32 partials per k-chunk (small-n path)
+  bool row_blocks;  // quantise one row per block (few tokens)
 };
-ProloguePlan plan_prologue(int n, int d, int r_pad);
+// small: few tokens (T as k-chunk partials for the small-n GEMM, which can sum
+// at most max_chunks of them in one pass).
+ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks);
+// Most k-chunk partials of T the small-n GEMM sums in one pass for M tokens.
+int gemv_max_chunks(int M, int Kb, int r_pad);
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st);
 // Per-token quantiser with one wave per row (falls back to a block per row for very long rows).
@@ -57,5 +68,36 @@ hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl
 hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
 // Small-n integer GEMM (M <= 32).
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
+
+// One- or two-token layer in one launch (tq_small.hip): producers (T
+// partials) and consumers (16 output channels each) in one grid.
+struct SmallPlan {
+  int nt;      // T-partial blocks (nchunk x nqg)
+  int nchunk;  // k-chunks of T
+  int kc;      // k values per chunk
+  int qs;      // 16-column slices of T per block
+  int nqg;     // column groups
+};
+struct SmallArgs {
+  const void* X;
+  int n, d, m;
+  const uint8_t* wc;
+  const float* sw;
+  const bf16_t* L1t;
+  const bf16_t* L2t;
+  int r_pad;
+  int nt, nchunk, kc, qs, nqg;
+  uint8_t* xc;     // n x d/2 activation codes (written by the first consumer)
+  float* sx;       // n scales (idem)
+  float* P;        // nchunk x n x r_pad fp32 partials of X L1
+  bf16_t* Tout;    // n x r_pad: the bf16 T (idem)
+  unsigned* sync;  // hand-off words, kSyncBytes: [0] producers done, [2] wait-limit flag, consumer shard counters
+  void* Y;
+  int y_bf16;
+};
+constexpr int kSyncBytes = 4096;  // workspace bytes of the hand-off words
+bool small_fused_ok(int n, int d, int r_pad);
+SmallPlan plan_small(int n, int d, int r_pad);
+hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);
 
 }  // namespace tq

@@ -183,29 +183,6 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ X, int
 // of 8 values per lane, chunk index lane + 64 i), so X is read exactly once.
 // Columns [0, dl) use BA bits, [dl, d) BB bits with their own scale.
 // ---------------------------------------------------------------------------
-template <typename T>
-struct Row8;
-template <>
-struct Row8<bf16_t> {
-  uint4 r;
-  __device__ __forceinline__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void get(float (&v)[8]) const {
-    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
-    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z); v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
-  }
-};
-template <>
-struct Row8<float> {
-  float4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = reinterpret_cast<const float4*>(p)[0];
-    b = reinterpret_cast<const float4*>(p)[1];
-  }
-  __device__ __forceinline__ void get(float (&v)[8]) const {
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
-};
-
 template <typename T, int BA, int BB, int CH>
 __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, int dl, uint8_t* __restrict__ ca,
                                                float* __restrict__ sa, uint8_t* __restrict__ cb,
@@ -305,17 +282,83 @@ __global__ __launch_bounds__(256) void k_quant_rows_wave(const T* __restrict__ X
 }
 
 // ---------------------------------------------------------------------------
+// One row quantised at 4 bits by a whole block, each thread holding CHB
+// chunks of 8 values (chunk tid + blockDim.x i) in registers, so X is read
+// once and the row's arithmetic is spread over all the block's waves (the
+// few-token case, where one wave per row would leave the GPU idle).  Every
+// thread of the block must call it (it contains a barrier).
+// ---------------------------------------------------------------------------
+template <typename T, int CHB>
+__device__ __forceinline__ void quant_row_block_reg(const T* __restrict__ x, int d, uint8_t* __restrict__ c,
+                                                    float* __restrict__ s, float* red) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, w = tid >> 6, nw = nthr >> 6;
+  const int nch = d >> 3;
+  Row8<T> r[CHB];
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    const int ch = tid + nthr * i;
+    if (ch < nch) r[i].load(x + 8 * ch);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    if (tid + nthr * i < nch) {
+      float v[8];
+      r[i].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = 0.0f;
+  for (int i = 0; i < nw; ++i) m = fmaxf(m, red[i]);
+  const RowScale rs = row_scale<4>(m);
+  if (tid == 0) *s = rs.s;
+  if (__builtin_amdgcn_readfirstlane(rs.fast ? 1 : 0)) {
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) {
+      const int ch = tid + nthr * i;
+      if (ch < nch) {
+        float v[8];
+        int q[8];
+        r[i].get(v);
+        quant8_fast<4>(v, rs, q);
+        *reinterpret_cast<uint32_t*>(c + (size_t)ch * 4) = pack_nibbles(q);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CHB; ++i) {
+      const int ch = tid + nthr * i;
+      if (ch < nch) {
+        float v[8];
+        int q[8];
+        r[i].get(v);
+        quant8_exact<4>(v, rs.s, q);
+        *reinterpret_cast<uint32_t*>(c + (size_t)ch * 4) = pack_nibbles(q);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Prologue of tq_linear: one launch, two kinds of blocks.
-//  * blocks [0, nqb): 4 rows each, one per wave, 4-bit codes and s_x
-//    (skipped, nqb = 0, when the row does not fit in registers);
+//  * blocks [0, nqb): 4-bit codes and s_x of WAVES rows, one per wave, or,
+//    for few tokens (row_blocks), of one row per block (skipped, nqb = 0,
+//    when the row does not fit in registers);
 //  * blocks [nqb, nqb + ntb): the first low-rank stage T = X L1 on
 //    v_mfma_f32_16x16x32_bf16.  Block (rt, c, qg) takes rows 16 rt..16 rt+15,
 //    the k-range [c kc, (c+1) kc) and the QS 16-column slices of group qg;
-//    its 4 waves take the 32-k steps round-robin and are summed through LDS
-//    in a fixed order.  With one k-chunk the block writes T directly;
-//    otherwise it writes its fp32 partial to P and the last block of the
-//    (rt, qg) group to finish (agent-scope counter) sums the partials in
-//    chunk order into T and resets the counter.
+//    its waves take the 32-k steps round-robin, U steps per wave in flight,
+//    and their partials are summed through LDS in wave order.
+//    - partial mode (few tokens): the block writes its fp32 partial to
+//      P[c]; the small-n GEMM sums the chunks;
+//    - one k-chunk: the block writes T directly;
+//    - otherwise the block writes its fp32 partial to P and the last block of
+//      the (rt, qg) group to finish (agent-scope counter) sums the partials
+//      in chunk order into T and resets the counter.
 // MFMA operand layout: lane l supplies row (or T column) l % 16 and the 8
 // consecutive k at 32 step + 8 (l / 16), for X and L1^T alike.
 // ---------------------------------------------------------------------------
@@ -323,7 +366,7 @@ struct PrologueArgs {
   const void* X;
   int n, d;
   const bf16_t* L1t;
-  int r_pad, kc, nchunk, qs, nqg, nqb;
+  int r_pad, kc, nchunk, qs, nqg, nqb, partial, row_blocks;
   uint8_t* xc;
   float* sx;
   float* P;
@@ -331,15 +374,22 @@ struct PrologueArgs {
   unsigned* counters;
 };
 
-template <typename T, int CH, int QS>
-__global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
-  constexpr int U = 8 / QS;  // 32-k steps per wave: all of them in flight at once
-  __shared__ float sP[16][65];
+template <typename T, int CH, int QS, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
+  constexpr int COLS = 16 * QS;
+  __shared__ float sP[WAVES][16][COLS + 1];
   __shared__ int s_last;
   const int b = blockIdx.x;
   const T* X = (const T*)a.X;
   if (b < a.nqb) {
-    const int row = b * 4 + (threadIdx.x >> 6);
+    if (a.row_blocks) {
+      // CH chunks per lane for one wave -> CH / WAVES per thread for the block
+      constexpr int CHB = (CH >= WAVES) ? CH / WAVES : 1;
+      __shared__ float red[WAVES];
+      quant_row_block_reg<T, CHB>(X + (size_t)b * a.d, a.d, a.xc + (size_t)b * (a.d >> 1), a.sx + b, red);
+      return;
+    }
+    const int row = b * WAVES + (threadIdx.x >> 6);
     if (row < a.n)
       quant_row_wave<T, 4, 4, CH>(X + (size_t)row * a.d, a.d, a.d, a.xc + (size_t)row * (a.d >> 1), a.sx + row,
                                   nullptr, nullptr);
@@ -351,7 +401,7 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   const int per_rt = a.nchunk * a.nqg;
   const int rt = tb / per_rt, c = (tb % per_rt) / a.nqg, qg = tb % a.nqg;
   const int d = a.d, n = a.n;
-  // k-chunk c covers the 32-k steps [c * kc / 32, (c + 1) * kc / 32); wave w takes every 4th
+  // k-chunk c covers the 32-k steps [c * kc / 32, (c + 1) * kc / 32); wave w takes every WAVES-th
   const int s0 = c * (a.kc >> 5), s1 = min(d >> 5, s0 + (a.kc >> 5));
   const T* xr = X + (size_t)min(16 * rt + lr, n - 1) * d;
   const bf16_t* lp = a.L1t + (size_t)(16 * qg * QS + lr) * d;
@@ -359,12 +409,12 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   f32x4 acc[QS];
 #pragma unroll
   for (int q = 0; q < QS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sb = s0 + w; sb < s1; sb += 4 * U) {  // batches of U steps, all loads in flight
+  for (int sb = s0 + w; sb < s1; sb += WAVES * U) {  // batches of U steps, all loads in flight
     uint4 xa[U];
     uint4 lb[U][QS];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = sb + 4 * u;
+      const int s = sb + WAVES * u;
       const int k = 32 * s + 8 * lg;
       if (s < s1) {
         float v[8];
@@ -375,7 +425,7 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (sb + 4 * u < s1) {
+      if (sb + WAVES * u < s1) {
 #pragma unroll
         for (int q = 0; q < QS; ++q)
           acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(lb[u][q]), acc[q], 0, 0, 0);
@@ -383,25 +433,30 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
     }
   }
   // 16x16 result layout: lane l, element i -> row 4 (l / 16) + i, column l % 16.
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
 #pragma unroll
-      for (int q = 0; q < QS; ++q)
+  for (int q = 0; q < QS; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float& dst = sP[4 * lg + i][16 * q + lr];
-            dst = (ww == 0) ? acc[q][i] : dst + acc[q][i];
-          }
-    }
-    __syncthreads();
-  }
+    for (int i = 0; i < 4; ++i) sP[w][4 * lg + i][16 * q + lr] = acc[q][i];
+  __syncthreads();
   const int rows = min(16, n - 16 * rt);
-  constexpr int cols = 16 * QS;
   const int col0 = 16 * qg * QS;
+  auto wave_sum = [&](int rr, int cc) {
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) v += sP[ww][rr][cc];
+    return v;
+  };
+  if (a.partial) {
+    for (int e = tid; e < rows * COLS; e += WAVES * 64) {
+      const int rr = e / COLS, cc = e % COLS;
+      a.P[((size_t)c * n + 16 * rt + rr) * a.r_pad + col0 + cc] = wave_sum(rr, cc);
+    }
+    return;
+  }
   if (a.nchunk == 1) {
-    for (int e = tid; e < rows * cols; e += 256) {
-      const int rr = e / cols, cc = e % cols;
-      a.T[(size_t)(16 * rt + rr) * a.r_pad + col0 + cc] = (bf16_t)f32_to_bf16_bits(sP[rr][cc]);
+    for (int e = tid; e < rows * COLS; e += WAVES * 64) {
+      const int rr = e / COLS, cc = e % COLS;
+      a.T[(size_t)(16 * rt + rr) * a.r_pad + col0 + cc] = (bf16_t)f32_to_bf16_bits(wave_sum(rr, cc));
     }
     return;
   }
@@ -409,9 +464,9 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   // written and read with agent-scope atomic stores / loads, which go to the
   // device's point of coherence, and the barrier below waits until every
   // wave's stores have completed before the counter is bumped.
-  for (int e = tid; e < rows * cols; e += 256) {
-    const int rr = e / cols, cc = e % cols;
-    __hip_atomic_store(&a.P[((size_t)c * n + 16 * rt + rr) * a.r_pad + col0 + cc], sP[rr][cc], __ATOMIC_RELAXED,
+  for (int e = tid; e < rows * COLS; e += WAVES * 64) {
+    const int rr = e / COLS, cc = e % COLS;
+    __hip_atomic_store(&a.P[((size_t)c * n + 16 * rt + rr) * a.r_pad + col0 + cc], wave_sum(rr, cc), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -423,8 +478,8 @@ __global__ __launch_bounds__(256) void k_prologue(PrologueArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  for (int e = tid; e < rows * cols; e += 256) {
-    const int rr = e / cols, cc = e % cols;
+  for (int e = tid; e < rows * COLS; e += WAVES * 64) {
+    const int rr = e / COLS, cc = e % COLS;
     const float* pp = a.P + (size_t)(16 * rt + rr) * a.r_pad + col0 + cc;
     const size_t stride = (size_t)n * a.r_pad;
     const int nc = a.nchunk;
@@ -537,21 +592,35 @@ hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl
 #undef TQ_QR
 }
 
-ProloguePlan plan_prologue(int n, int d, int r_pad) {
+ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) {
   ProloguePlan p{};
   const int nq = r_pad / 16;
   const int nrt = (n + 15) / 16;
   const int steps = (d + 31) / 32;  // 32-k MFMA steps along d
+  p.waves = small ? 8 : 4;
   if (nq == 0) {
     p.qs = 1;
     p.nqg = 0;
     p.nchunk = 1;
     p.kc = d;
     p.ntb = 0;
+  } else if (small) {
+    // few tokens: all (up to 64) columns per block, 8 waves with up to 8
+    // steps each in flight; k split into chunks of at least 16 steps, as
+    // many as the small-n GEMM can sum in one pass (max_chunks), so that L1
+    // is read by many CUs at once; fp32 partials per k-chunk, summed there
+    p.qs = std::min(nq, 4);
+    p.nqg = nq / p.qs;
+    const int nch = std::max(1, std::min((steps + 15) / 16, max_chunks));
+    const int chunk_steps = (steps + nch - 1) / nch;
+    p.kc = 32 * chunk_steps;
+    p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
+    p.partial = true;
+    p.ntb = nrt * p.nchunk * p.nqg;
   } else {
     // QS 16-column slices of T per block (all of them in one block when rows
-    // are many, one per block otherwise); each of the 4 waves then issues all
-    // of its 8 / QS steps at once, so a block covers 4 * 8 / QS steps of k.
+    // are many, one per block otherwise); each of the 4 waves issues 8 / QS
+    // steps at once.
     p.qs = (nrt >= 64) ? std::min(nq, 4) : 1;
     p.nqg = nq / p.qs;
     if (nrt * p.nqg >= 128) {
@@ -569,31 +638,33 @@ ProloguePlan plan_prologue(int n, int d, int r_pad) {
     p.ntb = nrt * p.nchunk * p.nqg;
   }
   p.quant_in_prologue = chunks_for(d) <= 32;
-  p.nqb = p.quant_in_prologue ? (n + 3) / 4 : 0;
-  p.counters = (p.nchunk > 1) ? nrt * std::max(p.nqg, 1) : 0;
+  p.row_blocks = small;  // few tokens: a block per row
+  p.nqb = p.quant_in_prologue ? (small ? n : (n + p.waves - 1) / p.waves) : 0;
+  p.counters = (p.ntb > 0 && !p.partial && p.nchunk > 1) ? nrt * std::max(p.nqg, 1) : 0;
   return p;
 }
 
-template <typename T, int QS>
+template <typename T, int QS, int WAVES, int U>
 static hipError_t launch_prologue_q(const PrologueArgs& a, int ch, hipStream_t st) {
-  const dim3 grid(a.nqb + (unsigned)(a.nqg ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0)), block(256);
+  const dim3 grid(a.nqb + (unsigned)(a.nqg ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0)), block(WAVES * 64);
   switch (ch) {
-    case 1: hipLaunchKernelGGL((k_prologue<T, 1, QS>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_prologue<T, 2, QS>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_prologue<T, 4, QS>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_prologue<T, 8, QS>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_prologue<T, 16, QS>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_prologue<T, 32, QS>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_prologue<T, 1, QS, WAVES, U>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_prologue<T, 2, QS, WAVES, U>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_prologue<T, 4, QS, WAVES, U>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_prologue<T, 8, QS, WAVES, U>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_prologue<T, 16, QS, WAVES, U>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_prologue<T, 32, QS, WAVES, U>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_prologue_t(const PrologueArgs& a, int ch, hipStream_t st) {
+static hipError_t launch_prologue_t(const PrologueArgs& a, int waves, int ch, hipStream_t st) {
+  if (waves == 8) return a.qs == 4 ? launch_prologue_q<T, 4, 8, 8>(a, ch, st) : launch_prologue_q<T, 2, 8, 8>(a, ch, st);
   switch (a.qs) {
-    case 1: return launch_prologue_q<T, 1>(a, ch, st);
-    case 2: return launch_prologue_q<T, 2>(a, ch, st);
-    default: return launch_prologue_q<T, 4>(a, ch, st);
+    case 1: return launch_prologue_q<T, 1, 4, 8>(a, ch, st);
+    case 2: return launch_prologue_q<T, 2, 4, 4>(a, ch, st);
+    default: return launch_prologue_q<T, 4, 4, 2>(a, ch, st);
   }
 }
 
@@ -604,10 +675,10 @@ hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L
     if (e != hipSuccess) return e;
     if (p.ntb == 0) return hipSuccess;
   }
-  PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, p.nqb, (uint8_t*)xc, sx, P,
-                 (bf16_t*)Tout, counters};
+  PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, p.nqb, p.partial ? 1 : 0,
+                 p.row_blocks ? 1 : 0, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters};
   const int ch = std::min(chunks_for(d), 32);
-  return bf16 ? launch_prologue_t<bf16_t>(a, ch, st) : launch_prologue_t<float>(a, ch, st);
+  return bf16 ? launch_prologue_t<bf16_t>(a, p.waves, ch, st) : launch_prologue_t<float>(a, p.waves, ch, st);
 }
 
 }  // namespace tq

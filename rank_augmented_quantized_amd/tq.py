@@ -154,10 +154,10 @@ def tq_linear_workspace_bytes(n: int, d: int, m: int, r: int) -> int:
 
 
 def tq_linear_workspace_offsets(n: int, d: int, m: int, r: int) -> dict:
-    """Byte offsets of s_x, the activation codes and T inside tq_linear's workspace."""
-    off = (ctypes.c_size_t * 3)()
+    """Byte offsets of s_x, the activation codes, T and the hand-off words inside tq_linear's workspace."""
+    off = (ctypes.c_size_t * 4)()
     _check("tq_linear_workspace_offsets", load().tq_linear_workspace_offsets(n, d, m, r, off))
-    return {"s_x": off[0], "x_codes": off[1], "T": off[2]}
+    return {"s_x": off[0], "x_codes": off[1], "T": off[2], "sync": off[3]}
 
 
 def linear_workspace(n: int, d: int, m: int, r: int, device) -> torch.Tensor:

@@ -228,6 +228,9 @@ LCASES = [
     ("n7_r96", 7, 1024, 100, 96, "student_t", "bf16", 0),
     ("n32_decode_edge", 32, 2048, 64, 64, "normal", "bf16", 2),
     ("n129_f32_out", 129, 512, 160, 32, "normal", "f32", 0),
+    # d above the single-launch limit: the two-launch few-token path
+    ("n4_d32800_two_launch", 4, 32800, 64, 32, "normal", "bf16", 3),
+    ("n24_r256", 24, 1024, 48, 256, "normal", "bf16", 0),
 ]
 
 
@@ -264,6 +267,35 @@ def test_linear_r0_is_pure_w4a4_and_deterministic():
     # a zero L2 gives the same output as r = 0
     y1, *_ = _run_linear(c["X"], "bf16", c["R"], c["L1"], np.zeros_like(c["L2"]), torch.float32)
     assert torch.allclose(y1, y0a, rtol=0, atol=0)
+
+
+def _sync_words(ws, n, d, m, r):
+    """The hand-off words of the one-launch path (counters and the wait-limit flag; 4 KiB)."""
+    off = tq.tq_linear_workspace_offsets(n, d, m, r)["sync"]
+    return ws[off: off + 4096].view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 2048, 200, 64), (1, 4064, 64, 32), (2, 512, 40, 0),
+                                     (2, 1024, 48, 256), (1, 14336, 64, 32), (5, 2048, 200, 64)])
+def test_small_n_single_launch_handoff(n, d, m, r):
+    """One or two tokens (d <= 4096) run in one launch whose consumers wait for its producers: every call leaves the
+    hand-off counters at zero, the wait never hits its limit, and calls repeated on one workspace give identical
+    outputs (the d = 14336 and n = 5 cases take the two-launch path and must leave the words untouched)."""
+    print(f"case n={n} d={d} m={m} r={r}", flush=True)
+    c = draw_custom(n, d, m, max(r, 1), seed=90 + n)
+    wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+    lowrank = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16)) if r else None
+    ws = tq.linear_workspace(n, d, m, r, DEV)
+    x = _x_tensor(c["X"], "bf16")
+    ys = []
+    for _ in range(4):
+        ys.append(tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws))
+        torch.cuda.synchronize()
+        assert not _sync_words(ws, n, d, m, r).any()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"] if r else None, c["L2"] if r else None)
+    _assert_y(ys[0], ref["Y"], f"n{n}")
 
 
 def test_small_n_and_tile_paths_agree():

@@ -150,7 +150,11 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
 /*
  * tq_linear_workspace_offsets -- where tq_linear keeps its intermediate
  * results inside the workspace, for inspection after a call:
- *   off[0] s_x (n fp32), off[1] activation codes (n x d/2 bytes),
+ *   off[0] s_x (n fp32), off[1] activation codes: nibble-packed (n x d/2
+ *   bytes) for n <= 32; for n > 32 one byte per code holding 16 x code, each
+ *   row of d bytes listing, for every 8 consecutive k, the 4 even-k codes
+ *   and then the 4 odd-k codes (the order in which the tile GEMM consumes
+ *   them),
  *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
  *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words of
  *   the one-launch path (all zero between calls; the third word is set if a

@@ -110,8 +110,8 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
   o = align256(o + (size_t)counters * 4 + 1);
   w.sx = o;
   o = align256(o + (size_t)n * 4);
-  w.xc = o;
-  o = align256(o + (size_t)n * (size_t)d / 2);
+  w.xc = o;  // activation codes: int8 (d bytes per row) for the tile GEMM, else packed
+  o = align256(o + (size_t)n * (size_t)(w.small ? d / 2 : d));
   w.t = o;
   o = align256(o + (size_t)n * (size_t)w.r_pad * 2);
   w.p = o;
@@ -290,10 +290,12 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
 
   TQ_RUN("prologue", stream,
          tq::launch_prologue(X, xb, (int)n, (int)d, L1t, L.r_pad, L.plan, xc, sx, P, T, ctr, stream));
-  if (L.small)
+  if (L.small) {
     TQ_RUN("gemm_small_n", stream, tq::launch_gemv(g, 4, tq::EPI_LINEAR, stream));
-  else
-    TQ_RUN("gemm_w4a4", stream, tq::launch_gemm(g, 4, tq::EPI_LINEAR, stream));
+  } else {
+    g.lda = d;  // int8 activation codes
+    TQ_RUN("gemm_w4a4", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, stream));
+  }
   return TQ_OK;
 }
 
@@ -394,6 +396,8 @@ tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t 
   g.acc = acc;
   if (n <= kSmallN)
     TQ_RUN("gemm_small_n_acc", stream, tq::launch_gemv(g, bits, tq::EPI_ACC, stream));
+  else if (bits == 4)  // the main loop of tq_linear's tile GEMM, on packed activation codes
+    TQ_RUN("gemm_acc", stream, tq::launch_gemm8(g, tq::EPI_ACC, false, stream));
   else
     TQ_RUN("gemm_acc", stream, tq::launch_gemm(g, bits, tq::EPI_ACC, stream));
   return TQ_OK;

@@ -180,6 +180,19 @@ __device__ __forceinline__ uint32_t pack_nibbles(const int (&c)[8]) {
   for (int i = 0; i < 8; ++i) p |= ((uint32_t)c[i] & 0xFu) << (4 * i);
   return p;
 }
+// 8 codes of k = 8 ch .. 8 ch + 7 of a 4-bit row, stored for the int8 tile
+// GEMM: each byte holds 16 x code, the 4 even-k codes first, then the 4
+// odd-k codes (the order in which two packed dwords expand, unpack16); row is
+// the start of the row (d bytes).
+__device__ __forceinline__ void store_codes_int8(uint8_t* row, int ch, const int (&c)[8]) {
+  uint32_t e = 0, o = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e |= ((uint32_t)c[2 * i] & 15u) << (8 * i + 4);
+    o |= ((uint32_t)c[2 * i + 1] & 15u) << (8 * i + 4);
+  }
+  *reinterpret_cast<uint2*>(row + 8 * ch) = uint2{e, o};
+}
 // 8 codes -> 8 int8 bytes.
 __device__ __forceinline__ uint2 pack_bytes(const int (&c)[8]) {
   uint2 p;

@@ -39,26 +39,6 @@ namespace tq {
 //   fragment reads of 8 or 16 consecutive rows on distinct banks.
 //   Waves: WGM x WGN, wave tile (BM / WGM) x (BN / WGN) of 32x32 blocks.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
-
-// Tile order: consecutive blocks are dispatched round-robin over the 8 XCDs,
-// each with its own L2, so the block index is first regrouped per XCD
-// (when the tile count is a multiple of 8) and the tiles of one XCD are then
-// walked in groups of GM tile-rows, keeping the tiles a group shares in that
-// XCD's L2.
-__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = 4;
-  const int T = tiles_m * tiles_n;
-  int b = bid;
-  if ((T & 7) == 0) b = (bid & 7) * (T >> 3) + (bid >> 3);
-  const int gsz = GM * tiles_n;
-  const int first = (b / gsz) * GM;
-  const int gm = min(tiles_m - first, GM);
-  const int r = b % gsz;
-  tm = first + r % gm;
-  tn = r / gm;
-}
-
 template <int BITS, int EPI, int BM, int BN, int WGM, int WGN, bool PK>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(GemmArgs g) {
   constexpr int NT = WGM * WGN * 64;

@@ -1,0 +1,388 @@
+// Tile GEMM of the rank-augmented W4A4 layer (gfx950): operands staged from
+// HBM straight into LDS, weights kept nibble-packed in LDS and expanded to
+// int8 at fragment read, activation codes consumed as int8.
+//
+// acc[i][j] = sum_k cx[i][k] cw[j][k], exact in int32 on v_mfma_i32_32x32x32_i8
+// (TwinQuant notes, "TwinQuant: Learnable Subspace Decomposition for W4A4 LLM
+// Quantization", section 02 note on INT32 accumulation, section 04.C and
+// Figure 4), then one epilogue: s_x s_w dequantisation plus the second
+// low-rank stage T L2 on the bf16 MFMA, and a single store of Y.
+//
+// Why this shape on gfx950:
+//  * staging uses buffer_load ... lds (16 bytes per lane, written to LDS at
+//    M0 + 16 x lane): no VGPRs, no VALU and no LDS stores are spent on it, so
+//    three 128-k stages can be in flight: the loads of stage k + 2 are issued
+//    while stage k is multiplied;
+//  * a wave64 VALU instruction occupies its SIMD for 4 cycles and overlaps an
+//    int8 MFMA (32 cycles) only partly, so the inner loop keeps VALU work low:
+//    activation codes arrive as int8 (16 x code, written that way by the
+//    quantiser) and each wave expands only the packed weight fragments it
+//    reads, 6 VALU per 32 x 32 x 32 fragment that feeds FN MFMAs;
+//  * the direct loads cannot permute bytes within a lane's 16, so the LDS
+//    XOR swizzles (chosen so that fragment reads of 8 or 16 consecutive rows
+//    hit distinct banks) are applied to the global addresses instead;
+//  * rows past the matrix end and chunks past the row end are fetched with
+//    offsets beyond the buffer resource's size, which the hardware turns into
+//    zeros: no clamping or masking in the loop.
+//
+// int8 code order: within every 8 consecutive k, the 4 codes of even k and
+// then the 4 codes of odd k, one byte each holding 16 x code.  Two packed
+// dwords (16 codes, even k in the low nibbles) expand to exactly this order
+// (unpack16), so a lane's 16 activation bytes and its expanded weight bytes
+// pair equal k in every MFMA slot; the int32 sum is 256 x the code product
+// and is shifted back exactly.
+//
+// Tile: 256 channels x BN tokens (BN = 256 or 128) per block of 8 waves, as a
+// 4 x 2 grid of 64 x BN/2 wave tiles.  Stage: 128 k; LDS per stage: packed
+// weights 256 rows x 64 bytes, activations BN rows x 128 bytes (int8) or
+// x 64 bytes (packed, the integer check entry point).
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+// Raw (stride 0) buffer resource over [base, base + bytes); loads at offsets
+// at or past `bytes` return zeros.  Word 3 is the gfx9-family dword format.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+constexpr int kOutOfRange = (int)0x80000000;  // voffset that no buffer here reaches
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 x lane
+// (buffer_load_dwordx4 ... lds, LDS base in M0).  Written as asm so that the
+// compiler does not track it: its own tracking would wait for every
+// outstanding direct load before any LDS read.  Completion is waited for
+// explicitly (wait_vmcnt); the data goes to LDS, so no VGPR is written.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+// Workgroup barrier without the memory-model fences of __syncthreads (which
+// would wait for all outstanding vector memory operations); the memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Packed LDS rows (64 bytes = 4 chunks per stage): chunk c of row r sits at
+// slot c ^ psw(r); any 8 or 16 consecutive rows read one chunk each on
+// distinct banks.
+__device__ __forceinline__ int psw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int EPI, bool XP, int BN>
+__global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
+  constexpr int BM = 256;                        // channels per tile
+  constexpr int WGM = 4;                         // wave grid: 4 (channels) x 2 (tokens)
+  constexpr int WM = BM / WGM, WN = BN / 2;      // wave tile 64 x BN/2
+  constexpr int FM = WM / 32, FN = WN / 32;      // 32 x 32 blocks per wave tile
+  constexpr int XROW = XP ? 64 : 128;            // LDS bytes per activation row per stage
+  constexpr int WPL = BM * 64, XPL = BN * XROW;  // stage planes
+  constexpr int SPL = WPL + XPL;
+  constexpr int NST = 3;
+  constexpr int WI = WPL / 1024 / 8, XI = XPL / 1024 / 8;  // direct loads per wave per stage
+  static_assert(WI >= 1 && XI >= 1, "each wave fills whole 1 KB pieces");
+  static_assert(EPI == EPI_ACC || 8 * WN * WM * 2 <= NST * SPL, "Y staging fits in the stage buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * SPL];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l32 = lane & 31, lg = lane >> 5;
+  int tm, tn;
+  tile_of_block(blockIdx.x, (g.N + BM - 1) / BM, (g.M + BN - 1) / BN, tm, tn);
+  const int ch0 = tm * BM, tk0 = tn * BN;
+  const int Kb = g.Kb;                // packed weight bytes per row (K / 2)
+  const int Kx = XP ? Kb : 2 * Kb;    // activation bytes per row
+
+  const i32x4 rw = buffer_rsrc(g.B + (size_t)ch0 * g.ldb, (uint32_t)(min(BM, g.N - ch0) * g.ldb));
+  const i32x4 rx = buffer_rsrc(g.A + (size_t)tk0 * g.lda, (uint32_t)(min(BN, g.M - tk0) * g.lda));
+
+  // ---- direct loads: load i of wave w fills 1 KB of a plane; lane L writes
+  // its 16 bytes at 16 L, so it fetches the chunk whose swizzled slot that is.
+  // Packed planes: 16 rows of 64 bytes per load, rows 16 (w + 8 i) + L / 4.
+  const int cpk = (lane & 3) ^ (((lane >> 3) ^ (2 * (wave & 1) + (lane >> 5))) & 3);
+  int vw[WI], vx[XI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) vw[i] = (int)((16 * (wave + 8 * i) + (lane >> 2)) * g.ldb) + 16 * cpk;
+  // int8 plane: 8 rows of 128 bytes per load, rows 8 (w + 8 i) + L / 8
+  const int c8 = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  const int cx = XP ? cpk : c8;
+#pragma unroll
+  for (int i = 0; i < XI; ++i)
+    vx[i] = XP ? (int)((16 * (wave + 8 * i) + (lane >> 2)) * g.lda) + 16 * cpk
+               : (int)((8 * (wave + 8 * i) + (lane >> 3)) * g.lda) + 16 * c8;
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int kt, int buf) {
+    const uint32_t base = lds0 + buf * SPL;
+    const int sw = 64 * kt, sx = (XP ? 64 : 128) * kt;
+    const bool okw = sw + 16 * cpk < Kb, okx = sx + 16 * cx < Kx;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+      load_lds16(rw, base + 1024 * (wave + 8 * i), okw ? vw[i] : kOutOfRange, sw);
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      load_lds16(rx, base + WPL + 1024 * (wave + 8 * i), okx ? vx[i] : kOutOfRange, sx);
+  };
+
+  // ---- fragments.  Step s (0..3) of a stage covers, for lane group lg,
+  // the codes of packed chunk 2 (s / 2) + lg, half s % 2 (16 codes), which
+  // is int8 chunk 4 (s / 2) + 2 lg + s % 2.  Weight lanes read the whole
+  // packed chunk (both halves) once per pair of steps.  The 32-row blocks of
+  // a wave are 2048 (packed) or 4096 (int8) bytes apart with equal swizzle.
+  int fa[2], fb[XP ? 2 : 4];
+  {
+    const int ra = wm * WM + l32, rb = wn * WN + l32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) fa[p] = ra * 64 + 16 * ((2 * p + lg) ^ psw(ra));
+    if constexpr (XP) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) fb[p] = WPL + rb * 64 + 16 * ((2 * p + lg) ^ psw(rb));
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) fb[s] = WPL + rb * 128 + 16 * swz(4 * (s >> 1) + 2 * lg + (s & 1), rb);
+    }
+  }
+  constexpr int XF = XP ? 2048 : 4096;
+
+  i32x16 acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0;
+
+  auto compute = [&](int buf) {
+    const uint8_t* s0 = smem + buf * SPL;
+    uint4 pa[2][FM];
+    uint4 pb[2][FN];  // packed activation chunks (XP)
+    i32x4 xb[2][FN];  // int8 activation fragments of steps s and s + 1
+#pragma unroll
+    for (int f = 0; f < FM; ++f) pa[0][f] = *reinterpret_cast<const uint4*>(s0 + fa[0] + 2048 * f);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      if constexpr (XP)
+        pb[0][f] = *reinterpret_cast<const uint4*>(s0 + fb[0] + XF * f);
+      else
+        xb[0][f] = *reinterpret_cast<const i32x4*>(s0 + fb[0] + XF * f);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int p = s >> 1, h = s & 1;
+      if (s == 0) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) pa[1][f] = *reinterpret_cast<const uint4*>(s0 + fa[1] + 2048 * f);
+        if constexpr (XP) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f) pb[1][f] = *reinterpret_cast<const uint4*>(s0 + fb[1] + XF * f);
+        }
+      }
+      if constexpr (!XP) {
+        if (s + 1 < 4) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+            xb[(s + 1) & 1][f] = *reinterpret_cast<const i32x4*>(s0 + fb[s + 1] + XF * f);
+        }
+      }
+      i32x4 av[FM], bv[FN];
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+        av[f] = h ? unpack16(pa[p][f].z, pa[p][f].w) : unpack16(pa[p][f].x, pa[p][f].y);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        if constexpr (XP)
+          bv[f] = h ? unpack16(pb[p][f].z, pb[p][f].w) : unpack16(pb[p][f].x, pb[p][f].y);
+        else
+          bv[f] = xb[s & 1][f];
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: stage kt sits in buffer kt % 3.  Each wave waits for its
+  // own loads of stage kt (the loads of stage kt + 1 may stay in flight); the
+  // barrier then publishes stage kt to all waves and frees the buffer of
+  // stage kt - 1, which receives stage kt + 2.
+  const int KT = (Kb + 63) / 64;
+  if (KT > 0) issue(0, 0);
+  if (KT > 1) issue(1, 1);
+  int buf = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT)
+      wait_vmcnt<WI + XI>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + 2 < KT) issue(kt + 2, buf == 0 ? 2 : buf - 1);
+    compute(buf);
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+
+  // ---- epilogue ----
+  // 32x32 result layout: lane l, element e -> row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32;
+  // here row = channel, column = token.  chan(a, e4): first of the 4 channels of group e4.
+  constexpr int SH = 8;  // both operands carry 16 x code: acc = 256 x the code product
+  auto chan = [&](int a, int e4) { return ch0 + wm * WM + 32 * a + 8 * e4 + 4 * lg; };
+  auto tok = [&](int b) { return tk0 + wn * WN + 32 * b + l32; };
+  if constexpr (EPI == EPI_ACC) {
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b) {
+        const int t = tok(b);
+        if (t >= g.M) continue;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = chan(a, e4);
+          int32_t* op = g.acc + (size_t)t * g.N + c;
+          const int v0 = acc[a][b][4 * e4] >> SH, v1 = acc[a][b][4 * e4 + 1] >> SH;
+          const int v2 = acc[a][b][4 * e4 + 2] >> SH, v3 = acc[a][b][4 * e4 + 3] >> SH;
+          if (c + 3 < g.N && (g.N & 3) == 0) {
+            *reinterpret_cast<int4*>(op) = int4{v0, v1, v2, v3};
+          } else {
+            const int v[4] = {v0, v1, v2, v3};
+            for (int q = 0; q < 4; ++q)
+              if (c + q < g.N) op[q] = v[q];
+          }
+        }
+      }
+  } else {
+    auto load4 = [&](const float* p, int c) -> float4 {  // p[c..c+3], clamped at the channel tail
+      if (c + 3 < g.N) return *reinterpret_cast<const float4*>(p + c);
+      return float4{p[min(c, g.N - 1)], p[min(c + 1, g.N - 1)], p[min(c + 2, g.N - 1)], p[min(c + 3, g.N - 1)]};
+    };
+    // bf16 Y is staged per wave in LDS (WN token rows of WM channels, 128-byte
+    // rows: chunk j of row r at slot j ^ ((r >> 1) & 7), and rows with bit 4
+    // set swap the 8-byte halves of each chunk, so the 32 rows a store
+    // instruction touches land on distinct banks) and written as whole
+    // 128-byte row pieces; fp32 Y is stored directly.
+    if (g.y_bf16) __syncthreads();  // every wave is done with the stage buffers
+    uint8_t* sYw = smem + wave * (WN * WM * 2);
+    auto ychunk = [&](int row, int j) -> int { return row * (WM * 2) + 16 * (j ^ ((row >> 1) & 7)); };
+    auto yslot = [&](int row, int j, int half) -> int { return ychunk(row, j) + 8 * (half ^ ((row >> 4) & 1)); };
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+      for (int b = 0; b < FN; ++b) {
+        const int tt = min(tok(b), g.M - 1);
+        const float sxt = g.sx[tt];
+        f32x16 y;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const float4 w = load4(g.sw, chan(a, e4));
+          y[4 * e4 + 0] = (float)(acc[a][b][4 * e4 + 0] >> SH) * (w.x * sxt);
+          y[4 * e4 + 1] = (float)(acc[a][b][4 * e4 + 1] >> SH) * (w.y * sxt);
+          y[4 * e4 + 2] = (float)(acc[a][b][4 * e4 + 2] >> SH) * (w.z * sxt);
+          y[4 * e4 + 3] = (float)(acc[a][b][4 * e4 + 3] >> SH) * (w.w * sxt);
+        }
+        if (g.r_pad > 0) {
+          // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16 MFMA
+          const int c = min(ch0 + wm * WM + 32 * a + l32, g.N - 1);
+          const bf16_t* lp = g.L2t + (size_t)c * g.r_pad + 8 * lg;
+          const bf16_t* tp = g.T + (size_t)tt * g.r_pad + 8 * lg;
+          for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
+            const uint4 av = *reinterpret_cast<const uint4*>(lp + t0);
+            const uint4 bv = *reinterpret_cast<const uint4*>(tp + t0);
+            y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), y, 0, 0, 0);
+          }
+        }
+        if (g.y_bf16) {
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int row = 32 * b + l32;
+            *reinterpret_cast<uint2*>(sYw + yslot(row, 4 * a + e4, lg)) =
+                uint2{pack_bf16x2(y[4 * e4], y[4 * e4 + 1]), pack_bf16x2(y[4 * e4 + 2], y[4 * e4 + 3])};
+          }
+        } else {
+          const int t = tok(b);
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int c = chan(a, e4);
+            if (t >= g.M) continue;
+            float* yp = reinterpret_cast<float*>(g.Y) + (size_t)t * g.ldy + c;
+            if (c + 3 < g.N && (g.ldy & 3) == 0) {
+              *reinterpret_cast<float4*>(yp) = float4{y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]};
+            } else {
+              for (int q = 0; q < 4; ++q)
+                if (c + q < g.N) yp[q] = y[4 * e4 + q];
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (g.y_bf16) {
+      // 16 bytes per lane, 8 lanes per token row of WM channels; a wave reads
+      // only its own staging area, so a wave-level LDS wait suffices
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      const int jc = lane & 7, rsub = lane >> 3;
+      const int c = ch0 + wm * WM + 8 * jc;
+#pragma unroll 4
+      for (int r0 = 0; r0 < WN; r0 += 8) {
+        const int row = r0 + rsub;
+        const int t = tk0 + wn * WN + row;
+        uint4 v = *reinterpret_cast<const uint4*>(sYw + ychunk(row, jc));
+        if ((row >> 4) & 1) v = uint4{v.z, v.w, v.x, v.y};
+        if (t < g.M) {
+          bf16_t* yp = reinterpret_cast<bf16_t*>(g.Y) + (size_t)t * g.ldy + c;
+          if (c + 7 < g.N && (g.ldy & 7) == 0) {
+            *reinterpret_cast<uint4*>(yp) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int q = 0; q < 8; ++q)
+              if (c + q < g.N) yp[q] = (bf16_t)((q & 1) ? (w[q >> 1] >> 16) : (w[q >> 1] & 0xFFFFu));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, bool XP>
+hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
+  const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  if (big >= 224) {
+    hipLaunchKernelGGL((k_gemm8<EPI, XP, 256>), dim3((unsigned)big), dim3(512), 0, st, g);
+  } else {
+    const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
+    hipLaunchKernelGGL((k_gemm8<EPI, XP, 128>), dim3(blocks), dim3(512), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Channels x tokens tiles of 256 x 256 (256 x 128 for small grids); x_int8:
+// activation codes as int8 in the order above (lda bytes per row), else
+// nibble-packed like the weights.  Buffer offsets are 32-bit: a tile's rows
+// of codes must span less than 2 GiB.
+hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, hipStream_t st) {
+  if ((int64_t)256 * g.ldb >= (1ll << 31) || (int64_t)256 * g.lda >= (1ll << 31)) return hipErrorInvalidValue;
+  if (epi == EPI_LINEAR && x_int8) return launch_t<EPI_LINEAR, false>(g, st);
+  if (epi == EPI_ACC && x_int8) return launch_t<EPI_ACC, false>(g, st);
+  if (epi == EPI_ACC && !x_int8) return launch_t<EPI_ACC, true>(g, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

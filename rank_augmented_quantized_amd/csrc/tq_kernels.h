@@ -12,6 +12,29 @@ namespace tq {
 
 enum Epilogue { EPI_ACC = 0, EPI_LINEAR = 1, EPI_MP = 2 };
 
+// LDS rows of the tile kernels are 128 bytes = 8 chunks of 16 bytes; chunk c
+// of row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the
+// fragment reads of 8 or 16 consecutive rows on distinct banks.
+__device__ __forceinline__ int swz(int c, int r) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+
+// Tile order: consecutive blocks are dispatched round-robin over the 8 XCDs,
+// each with its own L2, so the block index is first regrouped per XCD
+// (when the tile count is a multiple of 8) and the tiles of one XCD are then
+// walked in groups of GM tile-rows, keeping the tiles a group shares in that
+// XCD's L2.
+__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GM = 4;
+  const int T = tiles_m * tiles_n;
+  int b = bid;
+  if ((T & 7) == 0) b = (bid & 7) * (T >> 3) + (bid >> 3);
+  const int gsz = GM * tiles_n;
+  const int first = (b / gsz) * GM;
+  const int gm = min(tiles_m - first, GM);
+  const int r = b % gsz;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
 // Arguments of the integer GEMM kernels: C = A B^T over K-contiguous codes.
 struct GemmArgs {
   const uint8_t* A;  // x codes, M rows
@@ -66,6 +89,9 @@ hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl
                                   float* sa, void* cb, float* sb, hipStream_t st);
 // Integer GEMM (n > 32 tile kernel) with the given epilogue; bits of the main segment.
 hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
+// 4-bit tile GEMM with int8 operands in LDS (tq_gemm8.hip): x_int8 means the
+// activation codes come as int8 (16 x code, split order, lda bytes per row).
+hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, hipStream_t st);
 // Small-n integer GEMM (M <= 32).
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
 

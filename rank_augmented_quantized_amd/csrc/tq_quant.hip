@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void k_pack_lowrank(const T* __restrict__ L1, 
 // split); dl == d for a single segment.  Two passes over the row: the second
 // is served by L2 (the block read the same bytes a moment earlier).
 // ---------------------------------------------------------------------------
-template <typename T, int BA, int BB>
+template <typename T, int BA, int BB, bool X8 = false>
 __device__ __forceinline__ void quant_row_block(const T* __restrict__ x, int d, int dl, uint8_t* __restrict__ ca,
                                                 float* __restrict__ sa, uint8_t* __restrict__ cb,
                                                 float* __restrict__ sb, float* red) {
@@ -153,7 +153,9 @@ __device__ __forceinline__ void quant_row_block(const T* __restrict__ x, int d, 
     Load8<T>::load(x + 8 * ch, v, raw);
     if (ch < nchl) {
       quant8<BA>(v, ra, q);
-      if (BA == 4)
+      if (BA == 4 && X8)
+        store_codes_int8(ca, ch, q);
+      else if (BA == 4)
         *reinterpret_cast<uint32_t*>(ca + (size_t)ch * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(ca + (size_t)ch * 8) = pack_bytes(q);
@@ -167,15 +169,15 @@ __device__ __forceinline__ void quant_row_block(const T* __restrict__ x, int d, 
   }
 }
 
-template <typename T, int BA, int BB>
+template <typename T, int BA, int BB, bool X8 = false>
 __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ X, int n, int d, int dl,
                                                     uint8_t* __restrict__ ca, float* __restrict__ sa,
                                                     uint8_t* __restrict__ cb, float* __restrict__ sb) {
   __shared__ float red[16];
   const int row = blockIdx.x;
-  const size_t lda = (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
-  quant_row_block<T, BA, BB>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row, cb ? cb + row * ldb : nullptr,
-                             sb ? sb + row : nullptr, red);
+  const size_t lda = X8 ? (size_t)dl : (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
+  quant_row_block<T, BA, BB, X8>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row, cb ? cb + row * ldb : nullptr,
+                                 sb ? sb + row : nullptr, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ X, int
 // of 8 values per lane, chunk index lane + 64 i), so X is read exactly once.
 // Columns [0, dl) use BA bits, [dl, d) BB bits with their own scale.
 // ---------------------------------------------------------------------------
-template <typename T, int BA, int BB, int CH>
+template <typename T, int BA, int BB, int CH, bool X8 = false>
 __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, int dl, uint8_t* __restrict__ ca,
                                                float* __restrict__ sa, uint8_t* __restrict__ cb,
                                                float* __restrict__ sb) {
@@ -224,7 +226,9 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
   // division path, so neither is evaluated speculatively for the other.
   auto store = [&](int ch, const int (&q)[8]) {
     if (ch < nchl) {
-      if (BA == 4)
+      if (BA == 4 && X8)
+        store_codes_int8(ca, ch, q);
+      else if (BA == 4)
         *reinterpret_cast<uint32_t*>(ca + (size_t)ch * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(ca + (size_t)ch * 8) = pack_bytes(q);
@@ -347,7 +351,8 @@ __device__ __forceinline__ void quant_row_block_reg(const T* __restrict__ x, int
 // Prologue of tq_linear: one launch, two kinds of blocks.
 //  * blocks [0, nqb): 4-bit codes and s_x of WAVES rows, one per wave, or,
 //    for few tokens (row_blocks), of one row per block (skipped, nqb = 0,
-//    when the row does not fit in registers);
+//    when the row does not fit in registers); X8: codes as int8 in the order
+//    of the int8 tile GEMM (d bytes per row), else nibble-packed;
 //  * blocks [nqb, nqb + ntb): the first low-rank stage T = X L1 on
 //    v_mfma_f32_16x16x32_bf16.  Block (rt, c, qg) takes rows 16 rt..16 rt+15,
 //    the k-range [c kc, (c+1) kc) and the QS 16-column slices of group qg;
@@ -374,7 +379,7 @@ struct PrologueArgs {
   unsigned* counters;
 };
 
-template <typename T, int CH, int QS, int WAVES, int U>
+template <typename T, int CH, int QS, int WAVES, int U, bool X8>
 __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
   constexpr int COLS = 16 * QS;
   __shared__ float sP[WAVES][16][COLS + 1];
@@ -391,8 +396,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
     }
     const int row = b * WAVES + (threadIdx.x >> 6);
     if (row < a.n)
-      quant_row_wave<T, 4, 4, CH>(X + (size_t)row * a.d, a.d, a.d, a.xc + (size_t)row * (a.d >> 1), a.sx + row,
-                                  nullptr, nullptr);
+      quant_row_wave<T, 4, 4, CH, X8>(X + (size_t)row * a.d, a.d, a.d,
+                                      a.xc + (size_t)row * (X8 ? a.d : (a.d >> 1)), a.sx + row, nullptr, nullptr);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -644,34 +649,48 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) 
   return p;
 }
 
-template <typename T, int QS, int WAVES, int U>
+template <typename T, int QS, int WAVES, int U, bool X8>
 static hipError_t launch_prologue_q(const PrologueArgs& a, int ch, hipStream_t st) {
   const dim3 grid(a.nqb + (unsigned)(a.nqg ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0)), block(WAVES * 64);
   switch (ch) {
-    case 1: hipLaunchKernelGGL((k_prologue<T, 1, QS, WAVES, U>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_prologue<T, 2, QS, WAVES, U>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_prologue<T, 4, QS, WAVES, U>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_prologue<T, 8, QS, WAVES, U>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_prologue<T, 16, QS, WAVES, U>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_prologue<T, 32, QS, WAVES, U>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_prologue<T, 1, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_prologue<T, 2, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_prologue<T, 4, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_prologue<T, 8, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
+    case 16: hipLaunchKernelGGL((k_prologue<T, 16, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_prologue<T, 32, QS, WAVES, U, X8>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
 }
 
+// few tokens (8 waves): nibble-packed codes for the small-n GEMM; otherwise
+// int8 codes for the int8 tile GEMM
 template <typename T>
 static hipError_t launch_prologue_t(const PrologueArgs& a, int waves, int ch, hipStream_t st) {
-  if (waves == 8) return a.qs == 4 ? launch_prologue_q<T, 4, 8, 8>(a, ch, st) : launch_prologue_q<T, 2, 8, 8>(a, ch, st);
+  if (waves == 8)
+    return a.qs == 4 ? launch_prologue_q<T, 4, 8, 8, false>(a, ch, st) : launch_prologue_q<T, 2, 8, 8, false>(a, ch, st);
   switch (a.qs) {
-    case 1: return launch_prologue_q<T, 1, 4, 8>(a, ch, st);
-    case 2: return launch_prologue_q<T, 2, 4, 4>(a, ch, st);
-    default: return launch_prologue_q<T, 4, 4, 2>(a, ch, st);
+    case 1: return launch_prologue_q<T, 1, 4, 8, true>(a, ch, st);
+    case 2: return launch_prologue_q<T, 2, 4, 4, true>(a, ch, st);
+    default: return launch_prologue_q<T, 4, 4, 2, true>(a, ch, st);
   }
 }
 
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st) {
   if (!p.quant_in_prologue) {
-    hipError_t e = launch_quant_rows(X, bf16, n, d, d, 4, 4, xc, sx, nullptr, nullptr, st);
+    hipError_t e;
+    if (p.waves == 8) {
+      e = launch_quant_rows(X, bf16, n, d, d, 4, 4, xc, sx, nullptr, nullptr, st);
+    } else {  // int8 codes for the tile GEMM
+      if (bf16)
+        hipLaunchKernelGGL((k_quant_rows<bf16_t, 4, 4, true>), dim3(n), dim3(256), 0, st, (const bf16_t*)X, n, d, d,
+                           (uint8_t*)xc, sx, nullptr, nullptr);
+      else
+        hipLaunchKernelGGL((k_quant_rows<float, 4, 4, true>), dim3(n), dim3(256), 0, st, (const float*)X, n, d, d,
+                           (uint8_t*)xc, sx, nullptr, nullptr);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     if (p.ntb == 0) return hipSuccess;
   }

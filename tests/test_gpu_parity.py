@@ -188,12 +188,32 @@ def _run_linear(x, xdt, r_w, l1, l2, y_dtype=torch.bfloat16):
     return y, ws, wc, sw
 
 
+def _int8_codes(b):
+    """Decode tq_linear's int8 activation codes for the tile GEMM (n > 32): bytes hold 16 x code; every 8-k group
+    lists its 4 even-k codes, then its 4 odd-k codes (include/tq.h, tq_linear_workspace_offsets)."""
+    n, d = b.shape
+    v = (b.view(np.int8).astype(np.int16) >> 4).reshape(n, d // 8, 2, 4)
+    out = np.empty((n, d // 8, 4, 2), np.int16)
+    out[..., 0] = v[:, :, 0, :]
+    out[..., 1] = v[:, :, 1, :]
+    return out.reshape(n, d)
+
+
 def _ws_codes(ws, n, d, m, r):
+    """s_x and the activation codes tq_linear left in its workspace."""
     off = tq.tq_linear_workspace_offsets(n, d, m, r)
     b = ws.cpu().numpy()
     sx = b[off["s_x"]: off["s_x"] + 4 * n].view(np.float32)
-    xc = b[off["x_codes"]: off["x_codes"] + n * d // 2].reshape(n, d // 2)
-    return sx, tqo.unpack_int4(xc)
+    if n <= 32:
+        xc = b[off["x_codes"]: off["x_codes"] + n * d // 2].reshape(n, d // 2)
+        return sx, tqo.unpack_int4(xc)
+    return sx, _int8_codes(b[off["x_codes"]: off["x_codes"] + n * d].reshape(n, d))
+
+
+def _ws_packed_codes(ws, n, d, m, r):
+    """The workspace activation codes as nibble-packed rows (device tensor), for tq_debug_accumulate."""
+    _, codes = _ws_codes(ws, n, d, m, r)
+    return _t(tqo.pack_int4(codes))
 
 
 def _r_pad(r):
@@ -249,8 +269,8 @@ def test_linear_small(case):
     assert np.array_equal(sx, ref["s_x"])
     assert np.array_equal(codes, ref["codes_x"])
     # the product path's accumulators, exported from the same codes
-    xc = ws[tq.tq_linear_workspace_offsets(n, d, m, r)["x_codes"]:][: n * d // 2].view(n, d // 2)
-    acc = tq.tq_debug_accumulate(xc.contiguous(), wc, d, 4)
+    xc = _ws_packed_codes(ws, n, d, m, r)
+    acc = tq.tq_debug_accumulate(xc, wc, d, 4)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
     _assert_t(ws, c["X"], l1, n, d, m, r)
@@ -341,8 +361,7 @@ def test_linear_workload(wl, n, outl):
     # weight scales / codes of the sampled channels
     assert np.array_equal(sw.cpu().numpy()[cols], ref["s_w"])
     # accumulators of the sampled outputs, bit-exact
-    xc = ws[tq.tq_linear_workspace_offsets(n, d, m, r)["x_codes"]:][: n * d // 2].view(n, d // 2).contiguous()
-    acc = tq.tq_debug_accumulate(xc, wc, d, 4)
+    acc = tq.tq_debug_accumulate(_ws_packed_codes(ws, n, d, m, r), wc, d, 4)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), ref["acc"])
     _assert_t(ws, c["X"], c["L1"], n, d, m, r, rows)

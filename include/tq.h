@@ -43,7 +43,9 @@
  *    k dimension contiguous ("K-contiguous").
  *  - Shapes: n == 0 is a valid no-op.  d must be a positive multiple of 32 and
  *    m positive; any n and m are handled (no tile multiple needed).  r may be
- *    0..256.  Non-finite inputs are outside the contract (codes unspecified).
+ *    0..256.  Reduction lengths (d of tq_linear and tq_linear_mp, k of
+ *    tq_debug_accumulate) are at most 65536, which keeps every int32
+ *    accumulator exact.  Non-finite inputs are outside the contract (codes unspecified).
  *  - Calls that share a workspace must not overlap in time.
  */
 #ifndef TQ_H_
@@ -151,10 +153,9 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
  * tq_linear_workspace_offsets -- where tq_linear keeps its intermediate
  * results inside the workspace, for inspection after a call:
  *   off[0] s_x (n fp32), off[1] activation codes: nibble-packed (n x d/2
- *   bytes) for n <= 32; for n > 32 one byte per code holding 16 x code, each
- *   row of d bytes listing, for every 8 consecutive k, the 4 even-k codes
- *   and then the 4 odd-k codes (the order in which the tile GEMM consumes
- *   them),
+ *   bytes) for n <= 32; for n > 32 one int8 byte per code, each row of d
+ *   bytes listing, for every 8 consecutive k, the 4 even-k codes and then
+ *   the 4 odd-k codes (the order in which the tile GEMM consumes them),
  *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
  *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words of
  *   the one-launch path (all zero between calls; the third word is set if a

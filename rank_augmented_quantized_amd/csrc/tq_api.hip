@@ -17,6 +17,10 @@ using tq::GemmArgs;
 
 constexpr int kSmallN = 32;       // n <= kSmallN takes the memory-bound small-n path
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Longest reduction: |sum of k code products| <= 128 * 128 * k (8-bit) or, in
+// the 4-bit GEMM whose operands carry 16 x code, 256 * 64 * k; both stay below
+// 2^31 (exact int32) for k <= 2^16.
+constexpr int64_t kMaxK = (int64_t)1 << 16;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -219,7 +223,7 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
                     const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
   if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
-  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxDim || m <= 0 || m > kMaxDim || d % 32 || r < 0 || r > 256)
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || m <= 0 || m > kMaxDim || d % 32 || r < 0 || r > 256)
     return TQ_ERR_SHAPE;
   if (n == 0) return TQ_OK;
   if (!X || !w_codes || !s_w || !Y || !ws || (r > 0 && !lowrank)) return TQ_ERR_NULL;
@@ -320,7 +324,7 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
                        tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
   const int64_t dl = d - d_hi;
-  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxDim || m <= 0 || m > kMaxDim || d_hi < 0 || d_hi > d || dl % 32 ||
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || m <= 0 || m > kMaxDim || d_hi < 0 || d_hi > d || dl % 32 ||
       d_hi % 16)
     return TQ_ERR_SHAPE;
   if (n == 0) return TQ_OK;
@@ -381,7 +385,7 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
 tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m, int bits,
                               int32_t* acc, hipStream_t stream) {
   if (bits != 4 && bits != 8) return TQ_ERR_BITS;
-  if (n < 0 || n > kMaxDim || k <= 0 || k > kMaxDim || m <= 0 || m > kMaxDim || k % (bits == 4 ? 32 : 16))
+  if (n < 0 || n > kMaxDim || k <= 0 || k > kMaxK || m <= 0 || m > kMaxDim || k % (bits == 4 ? 32 : 16))
     return TQ_ERR_SHAPE;
   if (n == 0) return TQ_OK;
   if (!x_codes || !w_codes || !acc) return TQ_ERR_NULL;

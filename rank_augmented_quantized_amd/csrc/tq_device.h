@@ -8,6 +8,7 @@ namespace tq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -26,8 +27,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // 8 consecutive activations loaded from memory as fp32 values.
@@ -74,6 +78,7 @@ struct Row8<bf16_t> {
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
     v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z); v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
   }
+  __device__ __forceinline__ uint4 bf16() const { return r; }  // the 8 values as bf16 (exact)
 };
 template <>
 struct Row8<float> {
@@ -84,6 +89,9 @@ struct Row8<float> {
   }
   __device__ __forceinline__ void get(float (&v)[8]) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ uint4 bf16() const {  // rounded to bf16, ties to even
+    return uint4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
   }
 };
 
@@ -181,17 +189,50 @@ __device__ __forceinline__ uint32_t pack_nibbles(const int (&c)[8]) {
   return p;
 }
 // 8 codes of k = 8 ch .. 8 ch + 7 of a 4-bit row, stored for the int8 tile
-// GEMM: each byte holds 16 x code, the 4 even-k codes first, then the 4
-// odd-k codes (the order in which two packed dwords expand, unpack16); row is
-// the start of the row (d bytes).
-__device__ __forceinline__ void store_codes_int8(uint8_t* row, int ch, const int (&c)[8]) {
+// GEMM: one int8 byte per code, the 4 even-k codes first, then the 4 odd-k
+// codes (the order in which two packed weight dwords expand, unpack16); row
+// is the start of the row (d bytes).
+__device__ __forceinline__ uint2 codes_int8(const int (&c)[8]) {
   uint32_t e = 0, o = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    e |= ((uint32_t)c[2 * i] & 15u) << (8 * i + 4);
-    o |= ((uint32_t)c[2 * i + 1] & 15u) << (8 * i + 4);
+    e |= ((uint32_t)c[2 * i] & 0xFFu) << (8 * i);
+    o |= ((uint32_t)c[2 * i + 1] & 0xFFu) << (8 * i);
   }
-  *reinterpret_cast<uint2*>(row + 8 * ch) = uint2{e, o};
+  return uint2{e, o};
+}
+__device__ __forceinline__ void store_codes_int8(uint8_t* row, int ch, const int (&c)[8]) {
+  *reinterpret_cast<uint2*>(row + 8 * ch) = codes_int8(c);
+}
+
+// The 4-bit codes of 8 values of one row (the same codes as quant8<4>),
+// returned as the 8 int8 bytes of store_codes_int8.  Fast path: the
+// near-half-integer test of quant8_fast is folded into one running minimum,
+// and each code's byte is the low byte of t = fma(x, y, 1.5 * 2^23), whose
+// bits are bits(1.5 * 2^23) + code with zero low mantissa bits in the
+// constant; v_perm_b32 gathers the 4 bytes of a dword.
+__device__ __forceinline__ uint2 quant8_int8(const float (&x)[8], const RowScale& rs) {
+  if (rs.fast) {
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    uint32_t t[8];
+    float em = 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float tf = __builtin_fmaf(x[i], rs.rcp, MAGIC);
+      const float d = __builtin_fmaf(x[i], rs.rcp, -(tf - MAGIC));
+      em = fminf(em, fabsf(fabsf(d) - 0.5f));
+      t[i] = __float_as_uint(tf);
+    }
+    if (__builtin_expect(!(em < QTraits<4>::NEAR), 1)) {
+      // bytes [b0 of t0, t2, t4, t6] and [b0 of t1, t3, t5, t7]
+      const uint32_t e = __builtin_amdgcn_perm(t[2], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[6], t[4], 0x04000c0cu);
+      const uint32_t o = __builtin_amdgcn_perm(t[3], t[1], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[5], 0x04000c0cu);
+      return uint2{e, o};
+    }
+  }
+  int c[8];
+  quant8_exact<4>(x, rs.s, c);
+  return codes_int8(c);
 }
 // 8 codes -> 8 int8 bytes.
 __device__ __forceinline__ uint2 pack_bytes(const int (&c)[8]) {

@@ -15,8 +15,8 @@
 //    while stage k is multiplied;
 //  * a wave64 VALU instruction occupies its SIMD for 4 cycles and overlaps an
 //    int8 MFMA (32 cycles) only partly, so the inner loop keeps VALU work low:
-//    activation codes arrive as int8 (16 x code, written that way by the
-//    quantiser) and each wave expands only the packed weight fragments it
+//    activation codes arrive as int8 (written that way by the quantiser)
+//    and each wave expands only the packed weight fragments it
 //    reads, 6 VALU per 32 x 32 x 32 fragment that feeds FN MFMAs;
 //  * the direct loads cannot permute bytes within a lane's 16, so the LDS
 //    XOR swizzles (chosen so that fragment reads of 8 or 16 consecutive rows
@@ -26,11 +26,12 @@
 //    zeros: no clamping or masking in the loop.
 //
 // int8 code order: within every 8 consecutive k, the 4 codes of even k and
-// then the 4 codes of odd k, one byte each holding 16 x code.  Two packed
+// then the 4 codes of odd k, one int8 byte per code.  Two packed weight
 // dwords (16 codes, even k in the low nibbles) expand to exactly this order
-// (unpack16), so a lane's 16 activation bytes and its expanded weight bytes
-// pair equal k in every MFMA slot; the int32 sum is 256 x the code product
-// and is shifted back exactly.
+// (unpack16, 16 x code per byte), so a lane's 16 activation bytes and its
+// expanded weight bytes pair equal k in every MFMA slot; the int32 sum is
+// 16 x the code product (256 x when the activations come packed and are
+// expanded the same way) and is shifted back exactly.
 //
 // Tile: 256 channels x BN tokens (BN = 256 or 128) per block of 8 waves, as a
 // 4 x 2 grid of 64 x BN/2 wave tiles.  Stage: 128 k; LDS per stage: packed
@@ -128,17 +129,18 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
                : (int)((8 * (wave + 8 * i) + (lane >> 3)) * g.lda) + 16 * c8;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue = [&](int kt, int buf) {
+  // load i (0 .. WI + XI - 1) of stage kt into buffer buf: weights first
+  auto issue_one = [&](int i, int kt, int buf) {
     const uint32_t base = lds0 + buf * SPL;
-    const int sw = 64 * kt, sx = (XP ? 64 : 128) * kt;
-    const bool okw = sw + 16 * cpk < Kb, okx = sx + 16 * cx < Kx;
-#pragma unroll
-    for (int i = 0; i < WI; ++i)
-      load_lds16(rw, base + 1024 * (wave + 8 * i), okw ? vw[i] : kOutOfRange, sw);
-#pragma unroll
-    for (int i = 0; i < XI; ++i)
-      load_lds16(rx, base + WPL + 1024 * (wave + 8 * i), okx ? vx[i] : kOutOfRange, sx);
+    if (i < WI) {
+      const int sw = 64 * kt;
+      load_lds16(rw, base + 1024 * (wave + 8 * i), sw + 16 * cpk < Kb ? vw[i] : kOutOfRange, sw);
+    } else {
+      const int sx = (XP ? 64 : 128) * kt;
+      load_lds16(rx, base + WPL + 1024 * (wave + 8 * (i - WI)), sx + 16 * cx < Kx ? vx[i - WI] : kOutOfRange, sx);
+    }
   };
+  constexpr int NL = WI + XI;
 
   // ---- fragments.  Step s (0..3) of a stage covers, for lane group lg,
   // the codes of packed chunk 2 (s / 2) + lg, half s % 2 (16 codes), which
@@ -168,7 +170,11 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0;
 
-  auto compute = [&](int buf) {
+  // Multiply the stage in buffer buf.  The direct loads of stage kn (if
+  // kn >= 0) into buffer nb are spread over the four k-steps, issued between
+  // MFMAs: a wave that issues a whole stage's loads at once stalls on the
+  // memory pipeline while its SIMD's MFMA unit idles.
+  auto compute = [&](int buf, int kn, int nb) {
     const uint8_t* s0 = smem + buf * SPL;
     uint4 pa[2][FM];
     uint4 pb[2][FN];  // packed activation chunks (XP)
@@ -212,10 +218,15 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
           bv[f] = xb[s & 1][f];
       }
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
+      for (int a = 0; a < FM; ++a) {
 #pragma unroll
         for (int b = 0; b < FN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[a], bv[b], acc[a][b], 0, 0, 0);
+        if (a == 0 && kn >= 0) {
+#pragma unroll
+          for (int i = NL * s / 4; i < NL * (s + 1) / 4; ++i) issue_one(i, kn, nb);
+        }
+      }
     }
   };
 
@@ -224,24 +235,31 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   // barrier then publishes stage kt to all waves and frees the buffer of
   // stage kt - 1, which receives stage kt + 2.
   const int KT = (Kb + 63) / 64;
-  if (KT > 0) issue(0, 0);
-  if (KT > 1) issue(1, 1);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (KT > 0) issue_one(i, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (KT > 1) issue_one(i, 1, 1);
+  }
   int buf = 0;
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + 1 < KT)
-      wait_vmcnt<WI + XI>();
+      wait_vmcnt<NL>();
     else
       wait_vmcnt<0>();
     stage_barrier();
-    if (kt + 2 < KT) issue(kt + 2, buf == 0 ? 2 : buf - 1);
-    compute(buf);
+    compute(buf, kt + 2 < KT ? kt + 2 : -1, buf == 0 ? 2 : buf - 1);
     buf = buf == 2 ? 0 : buf + 1;
   }
 
   // ---- epilogue ----
   // 32x32 result layout: lane l, element e -> row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32;
   // here row = channel, column = token.  chan(a, e4): first of the 4 channels of group e4.
-  constexpr int SH = 8;  // both operands carry 16 x code: acc = 256 x the code product
+  // the weights carry 16 x code, and so do packed activations once expanded:
+  // acc = 16 (int8 activations) or 256 (packed) x the code product
+  constexpr int SH = XP ? 8 : 4;
   auto chan = [&](int a, int e4) { return ch0 + wm * WM + 32 * a + 8 * e4 + 4 * lg; };
   auto tok = [&](int b) { return tk0 + wn * WN + 32 * b + l32; };
   if constexpr (EPI == EPI_ACC) {
@@ -276,6 +294,54 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     // set swap the 8-byte halves of each chunk, so the 32 rows a store
     // instruction touches land on distinct banks) and written as whole
     // 128-byte row pieces; fp32 Y is stored directly.
+    // Dequantisation: the int32 sums carry the factor 2^SH, folded exactly
+    // into s_x; acc is converted in place to the fp32 tile y.
+    f32x16 y[FM][FN];
+    {
+      float4 swv[FM][4];
+      float sxv[FN];
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) swv[a][e4] = load4(g.sw, chan(a, e4));
+#pragma unroll
+      for (int b = 0; b < FN; ++b) sxv[b] = g.sx[min(tok(b), g.M - 1)] * (1.0f / (1 << SH));
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            y[a][b][4 * e4 + 0] = (float)acc[a][b][4 * e4 + 0] * (swv[a][e4].x * sxv[b]);
+            y[a][b][4 * e4 + 1] = (float)acc[a][b][4 * e4 + 1] * (swv[a][e4].y * sxv[b]);
+            y[a][b][4 * e4 + 2] = (float)acc[a][b][4 * e4 + 2] * (swv[a][e4].z * sxv[b]);
+            y[a][b][4 * e4 + 3] = (float)acc[a][b][4 * e4 + 3] * (swv[a][e4].w * sxv[b]);
+          }
+    }
+    if (g.r_pad > 0) {
+      // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16
+      // MFMA, 16 t per step; the L2 fragment of each channel block and the T
+      // fragment of each token block are loaded once per step
+      const bf16_t* lp[FM];
+      const bf16_t* tp[FN];
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+        lp[a] = g.L2t + (size_t)min(ch0 + wm * WM + 32 * a + l32, g.N - 1) * g.r_pad + 8 * lg;
+#pragma unroll
+      for (int b = 0; b < FN; ++b) tp[b] = g.T + (size_t)min(tok(b), g.M - 1) * g.r_pad + 8 * lg;
+      for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
+        uint4 av[FM], bv[FN];
+#pragma unroll
+        for (int a = 0; a < FM; ++a) av[a] = *reinterpret_cast<const uint4*>(lp[a] + t0);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) bv[b] = *reinterpret_cast<const uint4*>(tp[b] + t0);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int b = 0; b < FN; ++b)
+            y[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[a]), as_bf16x8(bv[b]), y[a][b], 0, 0, 0);
+      }
+    }
     if (g.y_bf16) __syncthreads();  // every wave is done with the stage buffers
     uint8_t* sYw = smem + wave * (WN * WM * 2);
     auto ychunk = [&](int row, int j) -> int { return row * (WM * 2) + 16 * (j ^ ((row >> 1) & 7)); };
@@ -284,34 +350,13 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     for (int a = 0; a < FM; ++a) {
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
-        const int tt = min(tok(b), g.M - 1);
-        const float sxt = g.sx[tt];
-        f32x16 y;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const float4 w = load4(g.sw, chan(a, e4));
-          y[4 * e4 + 0] = (float)(acc[a][b][4 * e4 + 0] >> SH) * (w.x * sxt);
-          y[4 * e4 + 1] = (float)(acc[a][b][4 * e4 + 1] >> SH) * (w.y * sxt);
-          y[4 * e4 + 2] = (float)(acc[a][b][4 * e4 + 2] >> SH) * (w.z * sxt);
-          y[4 * e4 + 3] = (float)(acc[a][b][4 * e4 + 3] >> SH) * (w.w * sxt);
-        }
-        if (g.r_pad > 0) {
-          // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16 MFMA
-          const int c = min(ch0 + wm * WM + 32 * a + l32, g.N - 1);
-          const bf16_t* lp = g.L2t + (size_t)c * g.r_pad + 8 * lg;
-          const bf16_t* tp = g.T + (size_t)tt * g.r_pad + 8 * lg;
-          for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
-            const uint4 av = *reinterpret_cast<const uint4*>(lp + t0);
-            const uint4 bv = *reinterpret_cast<const uint4*>(tp + t0);
-            y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), y, 0, 0, 0);
-          }
-        }
         if (g.y_bf16) {
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
             const int row = 32 * b + l32;
             *reinterpret_cast<uint2*>(sYw + yslot(row, 4 * a + e4, lg)) =
-                uint2{pack_bf16x2(y[4 * e4], y[4 * e4 + 1]), pack_bf16x2(y[4 * e4 + 2], y[4 * e4 + 3])};
+                uint2{pack_bf16x2(y[a][b][4 * e4], y[a][b][4 * e4 + 1]),
+                      pack_bf16x2(y[a][b][4 * e4 + 2], y[a][b][4 * e4 + 3])};
           }
         } else {
           const int t = tok(b);
@@ -321,14 +366,14 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
             if (t >= g.M) continue;
             float* yp = reinterpret_cast<float*>(g.Y) + (size_t)t * g.ldy + c;
             if (c + 3 < g.N && (g.ldy & 3) == 0) {
-              *reinterpret_cast<float4*>(yp) = float4{y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]};
+              *reinterpret_cast<float4*>(yp) =
+                  float4{y[a][b][4 * e4], y[a][b][4 * e4 + 1], y[a][b][4 * e4 + 2], y[a][b][4 * e4 + 3]};
             } else {
               for (int q = 0; q < 4; ++q)
-                if (c + q < g.N) yp[q] = y[4 * e4 + q];
+                if (c + q < g.N) yp[q] = y[a][b][4 * e4 + q];
             }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (g.y_bf16) {

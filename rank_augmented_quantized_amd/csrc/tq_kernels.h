@@ -76,6 +76,7 @@ struct ProloguePlan {
   bool quant_in_prologue;
   bool partial;     // T left as fp32 partials per k-chunk (small-n path)
   bool row_blocks;  // quantise one row per block (few tokens)
+  bool fused;       // many tokens: one pass over X makes codes, s_x and T (16-row blocks)
 };
 // small: few tokens (T as k-chunk partials for the small-n GEMM, which can sum
 // at most max_chunks of them in one pass).

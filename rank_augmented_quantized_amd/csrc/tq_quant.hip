@@ -597,6 +597,184 @@ hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl
 #undef TQ_QR
 }
 
+// ---------------------------------------------------------------------------
+// Prologue of tq_linear for many tokens, reading X once.  A block of 16
+// waves takes 16 rows, one per wave:
+//  * each wave, on its own (no block barrier, so a wave quantises while
+//    others still wait for their rows): loads its row, takes the absmax
+//    (wave reduction) and s_x, writes the int8 codes of the tile GEMM (same
+//    quantiser as quant_row_wave) and leaves the row as bf16 in LDS (rows
+//    padded by 16 bytes, so the 16 rows of an MFMA operand read hit distinct
+//    banks);
+//  * after one barrier, the first low-rank stage T = X L1 on
+//    v_mfma_f32_16x16x32_bf16 (lane l: row or T column l % 16, the 8 k at
+//    32 s + 8 (l / 16)), wave w taking the 32-k steps s = w mod 16, with
+//    its first L1 operands fetched before the barrier; the 16 wave partials
+//    are summed through LDS in wave order and rounded once to bf16.
+// TwinQuant notes, "TwinQuant: Learnable Subspace Decomposition for W4A4
+// LLM Quantization", section 04.C (per-token scales, T = X L1 feeding the
+// shared epilogue).
+// ---------------------------------------------------------------------------
+struct FusedArgs {
+  const void* X;
+  int n, d;
+  const bf16_t* L1t;
+  int r_pad;
+  uint8_t* xc;
+  float* sx;
+  bf16_t* T;
+};
+constexpr int kFusedWaves = 16;
+constexpr int kFusedMaxD = 4096;  // the 16 bf16 rows fill at most 128 KiB of LDS
+
+__host__ __device__ constexpr int fused_row_bytes(int d) { return 2 * d + 16; }
+__host__ __device__ constexpr int fused_lds_bytes(int d, int qs) {
+  const int x = kFusedWaves * fused_row_bytes(d), p = kFusedWaves * 16 * (16 * qs + 1) * 4;
+  return x > p ? x : p;
+}
+
+template <typename T, int CH, int QS>
+__global__ __launch_bounds__(1024) void k_prologue_rows(FusedArgs a) {
+  constexpr int WAVES = kFusedWaves, COLS = 16 * QS;
+  constexpr int U = QS <= 2 ? 4 : (QS <= 4 ? 2 : 1);  // L1 steps fetched ahead
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int d = a.d, nch = d >> 3, XS = fused_row_bytes(d);
+  const int row0 = 16 * blockIdx.x;
+
+  // ---- per wave: one row -> s_x, codes, bf16 copy in LDS ----
+  {
+    const int row = row0 + w;
+    uint8_t* sx_row = lds + w * XS;
+    if (row < a.n) {
+      const T* x = (const T*)a.X + (size_t)row * d;
+      Row8<T> r[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int ch = lane + 64 * i;
+        if (ch < nch) r[i].load(x + 8 * ch);
+      }
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (lane + 64 * i < nch) {
+          float v[8];
+          r[i].get(v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+        }
+      }
+      const RowScale rs = row_scale<4>(wave_max(mx));
+      if (lane == 0) a.sx[row] = rs.s;
+      uint8_t* cr = a.xc + (size_t)row * d;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int ch = lane + 64 * i;
+        if (ch < nch) {
+          float v[8];
+          r[i].get(v);
+          *reinterpret_cast<uint2*>(cr + 8 * ch) = quant8_int8(v, rs);
+          if constexpr (QS > 0) *reinterpret_cast<uint4*>(sx_row + 16 * ch) = r[i].bf16();
+        }
+      }
+    } else if constexpr (QS > 0) {
+      for (int ch = lane; ch < nch; ch += 64) *reinterpret_cast<uint4*>(sx_row + 16 * ch) = uint4{0, 0, 0, 0};
+    }
+  }
+  if constexpr (QS == 0) return;
+
+  // ---- T = X L1 over the 16 rows in LDS ----
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nsteps = d >> 5;
+  const bf16_t* lp = a.L1t + (size_t)lr * d + 8 * lg;
+  uint4 lb[U][QS > 0 ? QS : 1];
+  auto load_l1 = [&](int j) {
+    const int s = w + WAVES * j;
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+      lb[j % U][q] = *reinterpret_cast<const uint4*>(lp + (size_t)16 * q * d + 32 * s);
+  };
+  constexpr int SJ = (kFusedMaxD / 32 + WAVES - 1) / WAVES;  // steps per wave at most
+#pragma unroll
+  for (int j = 0; j < U; ++j)
+    if (w + WAVES * j < nsteps) load_l1(j);
+  __syncthreads();
+  f32x4 acc[QS > 0 ? QS : 1];
+#pragma unroll
+  for (int q = 0; q < QS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* ap = lds + lr * XS + 16 * lg;
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) {
+    const int s = w + WAVES * j;
+    if (s < nsteps) {
+      const uint4 xa = *reinterpret_cast<const uint4*>(ap + 64 * s);
+      uint4 b[QS > 0 ? QS : 1];
+#pragma unroll
+      for (int q = 0; q < QS; ++q) b[q] = lb[j % U][q];
+      if (j + U < SJ && s + WAVES * U < nsteps) load_l1(j + U);
+#pragma unroll
+      for (int q = 0; q < QS; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(b[q]), acc[q], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // the LDS rows are free: partials go there
+  float* sP = reinterpret_cast<float*>(lds);  // [WAVES][16][COLS + 1]
+  // 16x16 result layout: lane l, element i -> row 4 (l / 16) + i, column l % 16
+#pragma unroll
+  for (int q = 0; q < QS; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sP[(w * 16 + 4 * lg + i) * (COLS + 1) + 16 * q + lr] = acc[q][i];
+  __syncthreads();
+  const int rows = min(16, a.n - row0);
+  for (int e = tid; e < rows * COLS; e += WAVES * 64) {
+    const int rr = e / COLS, cc = e % COLS;
+    float v = sP[rr * (COLS + 1) + cc];
+#pragma unroll
+    for (int ww = 1; ww < WAVES; ++ww) v += sP[(ww * 16 + rr) * (COLS + 1) + cc];
+    a.T[(size_t)(row0 + rr) * a.r_pad + cc] = (bf16_t)f32_to_bf16_bits(v);
+  }
+}
+
+static bool fused_fits(int d, int qs) {
+  return d <= kFusedMaxD && (qs == 0 || qs == 2 || qs == 4 || qs == 8) && fused_lds_bytes(d, qs) <= 160 * 1024;
+}
+
+template <typename T, int CH>
+static hipError_t launch_rows_ch(const FusedArgs& a, int qs, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * kFusedWaves);
+  const unsigned lds = (unsigned)fused_lds_bytes(a.d, qs);
+  switch (qs) {
+    case 0: hipLaunchKernelGGL((k_prologue_rows<T, CH, 0>), grid, block, lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_prologue_rows<T, CH, 2>), grid, block, lds, st, a); break;
+    case 4: hipLaunchKernelGGL((k_prologue_rows<T, CH, 4>), grid, block, lds, st, a); break;
+    case 8: hipLaunchKernelGGL((k_prologue_rows<T, CH, 8>), grid, block, lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_rows_t(const FusedArgs& a, int qs, hipStream_t st) {
+  switch (chunks_for(a.d)) {
+    case 1: return launch_rows_ch<T, 1>(a, qs, st);
+    case 2: return launch_rows_ch<T, 2>(a, qs, st);
+    case 4: return launch_rows_ch<T, 4>(a, qs, st);
+    case 8: return launch_rows_ch<T, 8>(a, qs, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static hipError_t launch_prologue_fused(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad,
+                                        void* xc, float* sx, void* Tout, hipStream_t st) {
+  const FusedArgs a{X, n, d, (const bf16_t*)L1t, r_pad, (uint8_t*)xc, sx, (bf16_t*)Tout};
+  const int qs = r_pad / 16;
+  if (!fused_fits(d, qs)) return hipErrorInvalidValue;
+  return bf16 ? launch_rows_t<bf16_t>(a, qs, st) : launch_rows_t<float>(a, qs, st);
+}
+
+// Fewest tokens for the fused prologue.
+constexpr int kFusedMinRows = 1024;
+
 ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) {
   ProloguePlan p{};
   const int nq = r_pad / 16;
@@ -644,6 +822,13 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) 
   }
   p.quant_in_prologue = chunks_for(d) <= 32;
   p.row_blocks = small;  // few tokens: a block per row
+  if (!small && n >= kFusedMinRows && fused_fits(d, nq)) {
+    ProloguePlan f{};
+    f.fused = true;
+    f.qs = nq;
+    f.waves = kFusedWaves;
+    return f;
+  }
   p.nqb = p.quant_in_prologue ? (small ? n : (n + p.waves - 1) / p.waves) : 0;
   p.counters = (p.ntb > 0 && !p.partial && p.nchunk > 1) ? nrt * std::max(p.nqg, 1) : 0;
   return p;
@@ -678,6 +863,7 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, int waves, int ch, hi
 
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st) {
+  if (p.fused) return launch_prologue_fused(X, bf16, n, d, L1t, r_pad, xc, sx, Tout, st);
   if (!p.quant_in_prologue) {
     hipError_t e;
     if (p.waves == 8) {

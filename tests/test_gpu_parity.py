@@ -189,10 +189,10 @@ def _run_linear(x, xdt, r_w, l1, l2, y_dtype=torch.bfloat16):
 
 
 def _int8_codes(b):
-    """Decode tq_linear's int8 activation codes for the tile GEMM (n > 32): bytes hold 16 x code; every 8-k group
+    """Decode tq_linear's int8 activation codes for the tile GEMM (n > 32): one int8 byte per code; every 8-k group
     lists its 4 even-k codes, then its 4 odd-k codes (include/tq.h, tq_linear_workspace_offsets)."""
     n, d = b.shape
-    v = (b.view(np.int8).astype(np.int16) >> 4).reshape(n, d // 8, 2, 4)
+    v = b.view(np.int8).astype(np.int16).reshape(n, d // 8, 2, 4)
     out = np.empty((n, d // 8, 4, 2), np.int16)
     out[..., 0] = v[:, :, 0, :]
     out[..., 1] = v[:, :, 1, :]
@@ -251,6 +251,12 @@ LCASES = [
     # d above the single-launch limit: the two-launch few-token path
     ("n4_d32800_two_launch", 4, 32800, 64, 32, "normal", "bf16", 3),
     ("n24_r256", 24, 1024, 48, 256, "normal", "bf16", 0),
+    # many tokens: the one-pass prologue (16 rows per block, one per wave; rows
+    # longer than 4096 take the two-kind prologue)
+    ("n1030_d544_r128_fused", 1030, 544, 96, 128, "normal", "bf16", 2),
+    ("n1100_f32_fused", 1100, 1024, 80, 32, "student_t", "f32", 0),
+    ("n1040_r0_fused", 1040, 256, 64, 0, "normal", "bf16", 1),
+    ("n1024_d8192_r32_long_rows", 1024, 8192, 64, 32, "normal", "bf16", 3),
 ]
 
 

@@ -8,10 +8,12 @@ HBM.  Prints ONE JSON line (stdout); progress goes to stderr.
 
   value     effective int ops/s of the whole call, 2 n d m / t, in TOPS
   roofline  the integer GEMM kernel: algorithmic 2 n d m per launch over its
-            average launch duration (HIP events on the launch stream),
-            against the MI355X dense int8 MFMA peak (5.0 POP/s)
+            average launch duration (HIP events on the launch stream, taken
+            by the dispatch itself via hipExtLaunchKernelGGL), against the
+            MI355X dense int8 MFMA peak (5.0 POP/s)
   cpu_baseline  the CPU oracle on the same workload (a bounded sample)
-  sweep     the other workloads (decode rows against the 8 TB/s HBM peak)
+  sweep     the other workloads (decode rows against the 8 TB/s HBM peak,
+            also with the calls captured in a HIP graph and replayed)
 """
 
 from __future__ import annotations
@@ -120,6 +122,31 @@ class LinearCase:
         wc, sw, lr = self.w[i % len(self.w)]
         self.tq.tq_linear(self.X, wc, sw, lr, self.m, self.r, Y=self.Y, ws=self.ws)
 
+    def graph_ms(self, torch, replays=20):
+        """Per-call time with the calls (one per weight copy) captured in a HIP graph and replayed: the GPU time a
+        serving loop that captures its decode step sees, without per-launch host overhead."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(self.w)):
+                self(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(len(self.w)):
+                self(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / (replays * len(self.w))
+
 
 class MpCase:
     def __init__(self, wl, torch, tq, dev):
@@ -142,8 +169,9 @@ class MpCase:
                              ws=self.ws)
 
 
-def cpu_baseline(wl, rows):
-    """The oracle as it stands, timed on the host on the first `rows` tokens."""
+def cpu_baseline(wl, rows, seconds):
+    """The oracle as it stands, timed on the host: the layer on the first `rows` tokens, repeated until about
+    `seconds` of CPU work have been timed."""
     import oracle.tq_oracle as tqo
     from workloads import draw_linear
 
@@ -154,13 +182,17 @@ def cpu_baseline(wl, rows):
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
     c = draw_linear(wl, n=rows)
-    t0 = time.perf_counter()
-    tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
-    dt = time.perf_counter() - t0
-    ops = 2.0 * rows * wl.d * wl.m
+    reps, dt = 0, 0.0
+    while dt < seconds and reps < 100:
+        t0 = time.perf_counter()
+        tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
+        dt += time.perf_counter() - t0
+        reps += 1
+    ops = 2.0 * rows * wl.d * wl.m * reps
     return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {rows} of {wl.n} tokens, all {wl.m} output channels; numpy/fp64 oracle incl. "
-                      f"weight and activation quantisation, exact integer product, fp64 epilogue; {dt:.2f} s"}
+            "sample": f"first {rows} of {wl.n} tokens, all {wl.m} output channels, {reps} repetitions; numpy/fp64 "
+                      f"oracle incl. weight and activation quantisation, exact integer product, fp64 epilogue; "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -172,7 +204,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--copies", type=int, default=16, help="weight copies cycled through (defeats the MALL)")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time to accumulate (repetitions)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scales rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -236,6 +269,10 @@ def main():
                        "GBps": round(b / (t * 1e-3) / 1e9, 1), "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
                        "pct_hbm": round(100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                        "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+                if nn <= 32:
+                    tg = c.graph_ms(torch)
+                    row.update({"graph_us": round(tg * 1e3, 2), "graph_GBps": round(b / (tg * 1e-3) / 1e9, 1),
+                                "graph_pct_hbm": round(100 * b / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)})
                 sweep.append(row)
                 log(f"[bench] sweep {row}")
                 del c
@@ -258,7 +295,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} tokens")
-        cpu = cpu_baseline(wl, args.cpu_rows)
+        cpu = cpu_baseline(wl, min(args.cpu_rows, n), args.cpu_seconds)
         log(f"[bench] cpu baseline {cpu}")
 
     out = {

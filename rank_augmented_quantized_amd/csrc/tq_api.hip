@@ -61,17 +61,41 @@ Profiler& prof() {
   return p;
 }
 
-// Wraps one kernel launch; returns the launcher's error.
+}  // namespace
+
+namespace tq {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace tq
+
+namespace {
+
+// Wraps one kernel launch; returns the launcher's error.  Stream events are
+// recorded around the launch; a launcher that takes the dispatch-timestamp
+// events (tq::launch_kernel) makes those the record instead.
 template <typename F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   Profiler& p = prof();
   if (!p.on) return launch();
-  hipEvent_t e0 = p.get(), e1 = p.get();
+  hipEvent_t e0 = p.get(), e1 = p.get(), x0 = p.get(), x1 = p.get();
+  tq::LaunchEvents& ev = tq::launch_events();
+  ev = tq::LaunchEvents{x0, x1, false};
   if (e0) (void)hipEventRecord(e0, st);
   hipError_t err = launch();
   if (e1) (void)hipEventRecord(e1, st);
-  if (e0 && e1)
-    p.recs.push_back({name, e0, e1});
+  const bool used = ev.used;
+  ev = tq::LaunchEvents{};
+  if (used) {
+    p.recs.push_back({name, x0, x1});
+    if (e0) p.pool.push_back(e0);
+    if (e1) p.pool.push_back(e1);
+  } else {
+    if (e0 && e1) p.recs.push_back({name, e0, e1});
+    if (x0) p.pool.push_back(x0);
+    if (x1) p.pool.push_back(x1);
+  }
   return err;
 }
 

@@ -408,10 +408,10 @@ template <int EPI, bool XP>
 hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
   const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
   if (big >= 224) {
-    hipLaunchKernelGGL((k_gemm8<EPI, XP, 256>), dim3((unsigned)big), dim3(512), 0, st, g);
+    launch_kernel(k_gemm8<EPI, XP, 256>, dim3((unsigned)big), dim3(512), 0, st, g);
   } else {
     const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
-    hipLaunchKernelGGL((k_gemm8<EPI, XP, 128>), dim3(blocks), dim3(512), 0, st, g);
+    launch_kernel(k_gemm8<EPI, XP, 128>, dim3(blocks), dim3(512), 0, st, g);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Internal launcher interface between the C ABI (tq_api.hip) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,6 +12,27 @@
 namespace tq {
 
 enum Epilogue { EPI_ACC = 0, EPI_LINEAR = 1, EPI_MP = 2 };
+
+// Timing events for the next launch, set by the library's profiler.  A
+// launcher that supports them (hipExtLaunchKernelGGL: timestamps taken by
+// the dispatch itself, without the gap of stream-recorded events) takes them
+// and marks them used; otherwise the profiler's stream events stand.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchEvents& launch_events();
+
+template <typename K, typename... Args>
+void launch_kernel(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t st, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.start && ev.stop && !ev.used) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.start, ev.stop, 0, args...);
+    ev.used = true;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 // LDS rows of the tile kernels are 128 bytes = 8 chunks of 16 bytes; chunk c
 // of row r sits at position c ^ (r & 7) ^ ((r >> 3) & 1), which keeps the

@@ -744,10 +744,10 @@ static hipError_t launch_rows_ch(const FusedArgs& a, int qs, hipStream_t st) {
   const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * kFusedWaves);
   const unsigned lds = (unsigned)fused_lds_bytes(a.d, qs);
   switch (qs) {
-    case 0: hipLaunchKernelGGL((k_prologue_rows<T, CH, 0>), grid, block, lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_prologue_rows<T, CH, 2>), grid, block, lds, st, a); break;
-    case 4: hipLaunchKernelGGL((k_prologue_rows<T, CH, 4>), grid, block, lds, st, a); break;
-    case 8: hipLaunchKernelGGL((k_prologue_rows<T, CH, 8>), grid, block, lds, st, a); break;
+    case 0: launch_kernel(k_prologue_rows<T, CH, 0>, grid, block, lds, st, a); break;
+    case 2: launch_kernel(k_prologue_rows<T, CH, 2>, grid, block, lds, st, a); break;
+    case 4: launch_kernel(k_prologue_rows<T, CH, 4>, grid, block, lds, st, a); break;
+    case 8: launch_kernel(k_prologue_rows<T, CH, 8>, grid, block, lds, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -324,6 +324,41 @@ def test_small_n_single_launch_handoff(n, d, m, r):
     _assert_y(ys[0], ref["Y"], f"n{n}")
 
 
+@pytest.mark.parametrize("n,d,m,r", [(1, 2048, 300, 64), (16, 1024, 200, 32), (40, 512, 96, 32),
+                                     (1030, 512, 80, 32)])
+def test_graph_replay_matches_eager(n, d, m, r):
+    """tq_linear captured in a HIP graph (as a serving loop would run it): every replay, with eager calls and
+    synchronisations in between, gives the eager output bit for bit and leaves the hand-off words at zero."""
+    print(f"case n={n} d={d} m={m} r={r}", flush=True)
+    c = draw_custom(n, d, m, r, seed=500 + n)
+    wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+    lowrank = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+    x = _x_tensor(c["X"], "bf16")
+    ws_e = tq.linear_workspace(n, d, m, r, DEV)
+    y_e = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws_e)
+    torch.cuda.synchronize()
+    ws_g = tq.linear_workspace(n, d, m, r, DEV)
+    y_g = torch.empty_like(y_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tq.tq_linear(x, wc, sw, lowrank, m, r, Y=y_g, ws=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tq.tq_linear(x, wc, sw, lowrank, m, r, Y=y_g, ws=ws_g)
+    for rep in range(3):
+        y_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"replay {rep}"
+        assert not _sync_words(ws_g, n, d, m, r).any()
+        y_again = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws_e)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y_again, y_e)
+
+
 def test_small_n_and_tile_paths_agree():
     c = draw_custom(33, 1024, 128, 32, seed=78)
     y33, *_ = _run_linear(c["X"], "bf16", c["R"], c["L1"], c["L2"], torch.float32)

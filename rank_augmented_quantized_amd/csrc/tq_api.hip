@@ -160,8 +160,8 @@ MpWs mp_ws(int64_t n, int64_t d, int64_t d_hi) {
   o = align256(o + (size_t)n * 4);
   w.sxh = o;
   o = align256(o + (size_t)n * 4);
-  w.xl = o;
-  o = align256(o + (size_t)n * (size_t)dl / 2);
+  w.xl = o;  // 4-bit codes as int8 in the order of the tile GEMM
+  o = align256(o + (size_t)n * (size_t)dl);
   w.xh = o;
   o = align256(o + (size_t)n * (size_t)d_hi);
   w.total = o;
@@ -322,7 +322,7 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
     TQ_RUN("gemm_small_n", stream, tq::launch_gemv(g, 4, tq::EPI_LINEAR, stream));
   } else {
     g.lda = d;  // int8 activation codes
-    TQ_RUN("gemm_w4a4", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, stream));
+    TQ_RUN("gemm_w4a4", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, 4, stream));
   }
   return TQ_OK;
 }
@@ -367,10 +367,10 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   const bool xb = x_dt == TQ_BF16;
   if (dl > 0 && d_hi > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)dl, 4, 8, xl, sxl, xh, sxh, stream));
+           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)dl, 8, xl, sxl, xh, sxh, stream));
   } else if (dl > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 4, 4, xl, sxl, nullptr, nullptr, stream));
+           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)d, 4, xl, sxl, nullptr, nullptr, stream));
   } else {
     TQ_RUN("quant_rows_mp", stream,
            tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
@@ -382,13 +382,13 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
   // low subspace is the main (4-bit) segment, the high subspace the second (8-bit) segment
-  g.A = xl;
-  g.lda = dl / 2;
-  g.B = (const uint8_t*)wl_codes;
-  g.ldb = dl / 2;
+  g.A = dl > 0 ? xl : xh;
+  g.lda = dl > 0 ? dl : 16;  // int8 activation codes
+  g.B = dl > 0 ? (const uint8_t*)wl_codes : (const uint8_t*)wh_codes;
+  g.ldb = dl > 0 ? dl / 2 : 16;
   g.Kb = (int)(dl / 2);
-  g.sx = sxl;
-  g.sw = s_wl;
+  g.sx = dl > 0 ? sxl : sxh;
+  g.sw = dl > 0 ? s_wl : s_wh;
   g.A2 = xh;
   g.lda2 = d_hi;
   g.B2 = (const uint8_t*)wh_codes;
@@ -396,13 +396,7 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   g.Kb2 = (int)d_hi;
   g.sx2 = sxh;
   g.sw2 = s_wh;
-  if (dl == 0) {  // all 8-bit: empty main segment, scales unused
-    g.A = xh;
-    g.B = (const uint8_t*)wh_codes;
-    g.sx = sxh;
-    g.sw = s_wh;
-  }
-  TQ_RUN("gemm_mp", stream, tq::launch_gemm(g, 4, tq::EPI_MP, stream));
+  TQ_RUN("gemm_mp", stream, tq::launch_gemm8(g, tq::EPI_MP, true, 4, stream));
   return TQ_OK;
 }
 
@@ -424,10 +418,8 @@ tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t 
   g.acc = acc;
   if (n <= kSmallN)
     TQ_RUN("gemm_small_n_acc", stream, tq::launch_gemv(g, bits, tq::EPI_ACC, stream));
-  else if (bits == 4)  // the main loop of tq_linear's tile GEMM, on packed activation codes
-    TQ_RUN("gemm_acc", stream, tq::launch_gemm8(g, tq::EPI_ACC, false, stream));
-  else
-    TQ_RUN("gemm_acc", stream, tq::launch_gemm(g, bits, tq::EPI_ACC, stream));
+  else  // the main loop of tq_linear's tile GEMM (4-bit: on packed activation codes)
+    TQ_RUN("gemm_acc", stream, tq::launch_gemm8(g, tq::EPI_ACC, bits == 8, bits, stream));
   return TQ_OK;
 }
 

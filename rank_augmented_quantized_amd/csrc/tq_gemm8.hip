@@ -86,19 +86,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int EPI, bool XP, int BN>
+template <int EPI, bool XP, int BN, bool W8 = false>
 __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
+  static_assert(!W8 || (EPI == EPI_ACC && !XP), "8-bit weights: the integer check only");
   constexpr int BM = 256;                        // channels per tile
   constexpr int WGM = 4;                         // wave grid: 4 (channels) x 2 (tokens)
   constexpr int WM = BM / WGM, WN = BN / 2;      // wave tile 64 x BN/2
   constexpr int FM = WM / 32, FN = WN / 32;      // 32 x 32 blocks per wave tile
   constexpr int XROW = XP ? 64 : 128;            // LDS bytes per activation row per stage
-  constexpr int WPL = BM * 64, XPL = BN * XROW;  // stage planes
+  constexpr int WROW = W8 ? 128 : 64;            // LDS bytes per weight row per stage
+  constexpr int WPL = BM * WROW, XPL = BN * XROW;  // stage planes
   constexpr int SPL = WPL + XPL;
-  constexpr int NST = 3;
+  constexpr int NST = W8 ? 2 : 3;                // stage buffers; NST - 1 stages in flight
+  constexpr int AHEAD = NST - 1;
   constexpr int WI = WPL / 1024 / 8, XI = XPL / 1024 / 8;  // direct loads per wave per stage
   static_assert(WI >= 1 && XI >= 1, "each wave fills whole 1 KB pieces");
   static_assert(EPI == EPI_ACC || 8 * WN * WM * 2 <= NST * SPL, "Y staging fits in the stage buffers");
+  static_assert(EPI != EPI_MP || (BM + BN) * 128 <= NST * SPL, "a 128-k chunk of the 8-bit subspace fits");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * SPL];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,8 +111,8 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   int tm, tn;
   tile_of_block(blockIdx.x, (g.N + BM - 1) / BM, (g.M + BN - 1) / BN, tm, tn);
   const int ch0 = tm * BM, tk0 = tn * BN;
-  const int Kb = g.Kb;                // packed weight bytes per row (K / 2)
-  const int Kx = XP ? Kb : 2 * Kb;    // activation bytes per row
+  const int Kb = g.Kb;                       // weight code bytes per row (K / 2, or K for 8-bit)
+  const int Kx = (XP || W8) ? Kb : 2 * Kb;   // activation bytes per row
 
   const i32x4 rw = buffer_rsrc(g.B + (size_t)ch0 * g.ldb, (uint32_t)(min(BM, g.N - ch0) * g.ldb));
   const i32x4 rx = buffer_rsrc(g.A + (size_t)tk0 * g.lda, (uint32_t)(min(BN, g.M - tk0) * g.lda));
@@ -117,11 +121,14 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   // its 16 bytes at 16 L, so it fetches the chunk whose swizzled slot that is.
   // Packed planes: 16 rows of 64 bytes per load, rows 16 (w + 8 i) + L / 4.
   const int cpk = (lane & 3) ^ (((lane >> 3) ^ (2 * (wave & 1) + (lane >> 5))) & 3);
+  // int8 planes: 8 rows of 128 bytes per load, rows 8 (w + 8 i) + L / 8
+  const int c8 = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  const int cw = W8 ? c8 : cpk;
   int vw[WI], vx[XI];
 #pragma unroll
-  for (int i = 0; i < WI; ++i) vw[i] = (int)((16 * (wave + 8 * i) + (lane >> 2)) * g.ldb) + 16 * cpk;
-  // int8 plane: 8 rows of 128 bytes per load, rows 8 (w + 8 i) + L / 8
-  const int c8 = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  for (int i = 0; i < WI; ++i)
+    vw[i] = W8 ? (int)((8 * (wave + 8 * i) + (lane >> 3)) * g.ldb) + 16 * c8
+               : (int)((16 * (wave + 8 * i) + (lane >> 2)) * g.ldb) + 16 * cpk;
   const int cx = XP ? cpk : c8;
 #pragma unroll
   for (int i = 0; i < XI; ++i)
@@ -133,8 +140,8 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   auto issue_one = [&](int i, int kt, int buf) {
     const uint32_t base = lds0 + buf * SPL;
     if (i < WI) {
-      const int sw = 64 * kt;
-      load_lds16(rw, base + 1024 * (wave + 8 * i), sw + 16 * cpk < Kb ? vw[i] : kOutOfRange, sw);
+      const int sw = WROW * kt;
+      load_lds16(rw, base + 1024 * (wave + 8 * i), sw + 16 * cw < Kb ? vw[i] : kOutOfRange, sw);
     } else {
       const int sx = (XP ? 64 : 128) * kt;
       load_lds16(rx, base + WPL + 1024 * (wave + 8 * (i - WI)), sx + 16 * cx < Kx ? vx[i - WI] : kOutOfRange, sx);
@@ -147,11 +154,16 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   // is int8 chunk 4 (s / 2) + 2 lg + s % 2.  Weight lanes read the whole
   // packed chunk (both halves) once per pair of steps.  The 32-row blocks of
   // a wave are 2048 (packed) or 4096 (int8) bytes apart with equal swizzle.
-  int fa[2], fb[XP ? 2 : 4];
+  int fa[W8 ? 4 : 2], fb[XP ? 2 : 4];
   {
     const int ra = wm * WM + l32, rb = wn * WN + l32;
+    if constexpr (W8) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) fa[p] = ra * 64 + 16 * ((2 * p + lg) ^ psw(ra));
+      for (int s = 0; s < 4; ++s) fa[s] = ra * 128 + 16 * swz(4 * (s >> 1) + 2 * lg + (s & 1), ra);
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) fa[p] = ra * 64 + 16 * ((2 * p + lg) ^ psw(ra));
+    }
     if constexpr (XP) {
 #pragma unroll
       for (int p = 0; p < 2; ++p) fb[p] = WPL + rb * 64 + 16 * ((2 * p + lg) ^ psw(rb));
@@ -161,6 +173,7 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     }
   }
   constexpr int XF = XP ? 2048 : 4096;
+  constexpr int WF = W8 ? 4096 : 2048;  // bytes between a wave's 32-row weight blocks
 
   i32x16 acc[FM][FN];
 #pragma unroll
@@ -179,8 +192,14 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     uint4 pa[2][FM];
     uint4 pb[2][FN];  // packed activation chunks (XP)
     i32x4 xb[2][FN];  // int8 activation fragments of steps s and s + 1
+    i32x4 wb[2][FM];  // int8 weight fragments of steps s and s + 1 (W8)
 #pragma unroll
-    for (int f = 0; f < FM; ++f) pa[0][f] = *reinterpret_cast<const uint4*>(s0 + fa[0] + 2048 * f);
+    for (int f = 0; f < FM; ++f) {
+      if constexpr (W8)
+        wb[0][f] = *reinterpret_cast<const i32x4*>(s0 + fa[0] + WF * f);
+      else
+        pa[0][f] = *reinterpret_cast<const uint4*>(s0 + fa[0] + WF * f);
+    }
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       if constexpr (XP)
@@ -191,9 +210,9 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int p = s >> 1, h = s & 1;
-      if (s == 0) {
+      if (s == 0 && !W8) {
 #pragma unroll
-        for (int f = 0; f < FM; ++f) pa[1][f] = *reinterpret_cast<const uint4*>(s0 + fa[1] + 2048 * f);
+        for (int f = 0; f < FM; ++f) pa[1][f] = *reinterpret_cast<const uint4*>(s0 + fa[1] + WF * f);
         if constexpr (XP) {
 #pragma unroll
           for (int f = 0; f < FN; ++f) pb[1][f] = *reinterpret_cast<const uint4*>(s0 + fb[1] + XF * f);
@@ -206,10 +225,21 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
             xb[(s + 1) & 1][f] = *reinterpret_cast<const i32x4*>(s0 + fb[s + 1] + XF * f);
         }
       }
+      if constexpr (W8) {
+        if (s + 1 < 4) {
+#pragma unroll
+          for (int f = 0; f < FM; ++f)
+            wb[(s + 1) & 1][f] = *reinterpret_cast<const i32x4*>(s0 + fa[s + 1] + WF * f);
+        }
+      }
       i32x4 av[FM], bv[FN];
 #pragma unroll
-      for (int f = 0; f < FM; ++f)
-        av[f] = h ? unpack16(pa[p][f].z, pa[p][f].w) : unpack16(pa[p][f].x, pa[p][f].y);
+      for (int f = 0; f < FM; ++f) {
+        if constexpr (W8)
+          av[f] = wb[s & 1][f];
+        else
+          av[f] = h ? unpack16(pa[p][f].z, pa[p][f].w) : unpack16(pa[p][f].x, pa[p][f].y);
+      }
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         if constexpr (XP)
@@ -230,28 +260,27 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     }
   };
 
-  // ---- main loop: stage kt sits in buffer kt % 3.  Each wave waits for its
-  // own loads of stage kt (the loads of stage kt + 1 may stay in flight); the
-  // barrier then publishes stage kt to all waves and frees the buffer of
-  // stage kt - 1, which receives stage kt + 2.
-  const int KT = (Kb + 63) / 64;
+  // ---- main loop: stage kt (128 k) sits in buffer kt % NST.  Each wave
+  // waits for its own loads of stage kt (those of the next stage may stay in
+  // flight); the barrier then publishes stage kt to all waves and frees the
+  // buffer of stage kt - 1, which receives stage kt + AHEAD.
+  const int KT = (Kb + WROW - 1) / WROW;
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    if (KT > 0) issue_one(i, 0, 0);
-  }
+  for (int j = 0; j < AHEAD; ++j) {
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    if (KT > 1) issue_one(i, 1, 1);
+    for (int i = 0; i < NL; ++i) {
+      if (j < KT) issue_one(i, j, j);
+    }
   }
   int buf = 0;
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT)
-      wait_vmcnt<NL>();
+    if (AHEAD >= 2 && kt + 1 < KT)
+      wait_vmcnt<(AHEAD >= 2 ? NL : 0)>();
     else
       wait_vmcnt<0>();
     stage_barrier();
-    compute(buf, kt + 2 < KT ? kt + 2 : -1, buf == 0 ? 2 : buf - 1);
-    buf = buf == 2 ? 0 : buf + 1;
+    compute(buf, kt + AHEAD < KT ? kt + AHEAD : -1, buf == 0 ? NST - 1 : buf - 1);
+    buf = buf == NST - 1 ? 0 : buf + 1;
   }
 
   // ---- epilogue ----
@@ -259,7 +288,7 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   // here row = channel, column = token.  chan(a, e4): first of the 4 channels of group e4.
   // the weights carry 16 x code, and so do packed activations once expanded:
   // acc = 16 (int8 activations) or 256 (packed) x the code product
-  constexpr int SH = XP ? 8 : 4;
+  constexpr int SH = W8 ? 0 : (XP ? 8 : 4);
   auto chan = [&](int a, int e4) { return ch0 + wm * WM + 32 * a + 8 * e4 + 4 * lg; };
   auto tok = [&](int b) { return tk0 + wn * WN + 32 * b + l32; };
   if constexpr (EPI == EPI_ACC) {
@@ -306,6 +335,14 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
         for (int e4 = 0; e4 < 4; ++e4) swv[a][e4] = load4(g.sw, chan(a, e4));
 #pragma unroll
       for (int b = 0; b < FN; ++b) sxv[b] = g.sx[min(tok(b), g.M - 1)] * (1.0f / (1 << SH));
+      if (EPI == EPI_MP && g.Kb == 0) {  // no 4-bit subspace (its scales are never written)
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) swv[a][e4] = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < FN; ++b) sxv[b] = 0.0f;
+      }
 #pragma unroll
       for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -318,7 +355,7 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
             y[a][b][4 * e4 + 3] = (float)acc[a][b][4 * e4 + 3] * (swv[a][e4].w * sxv[b]);
           }
     }
-    if (g.r_pad > 0) {
+    if (EPI == EPI_LINEAR && g.r_pad > 0) {
       // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16
       // MFMA, 16 t per step; the L2 fragment of each channel block and the T
       // fragment of each token block are loaded once per step
@@ -340,6 +377,84 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
 #pragma unroll
           for (int b = 0; b < FN; ++b)
             y[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[a]), as_bf16x8(bv[b]), y[a][b], 0, 0, 0);
+      }
+    }
+    if constexpr (EPI == EPI_MP) {
+      // Two-subspace layer: add the 8-bit subspace, s_x2 s_w2 (Q8(X_h) Q8(W_h))
+      // (CoQuant notes, "CoQuant: Joint Weight-Activation Subspace Projection
+      // for Mixed-Precision LLMs", Eq. 9, the high-precision term).  Its
+      // int8 code rows (Kb2 bytes) are staged like the activation plane, one
+      // 128-k chunk of both operands per pass into the now idle stage
+      // buffers, and each 32 x 32 block takes its exact int32 product over
+      // the chunk (no factor: both operands are plain codes); chunks beyond
+      // the first (Kb2 > 128) add in fp32.
+      const int K2 = g.Kb2;
+      if (K2 > 0) {
+        constexpr int PW = BM / 64, PX = BN / 64;  // 1 KB pieces per wave per plane
+        const i32x4 rwh = buffer_rsrc(g.B2 + (size_t)ch0 * g.ldb2, (uint32_t)(min(BM, g.N - ch0) * g.ldb2));
+        const i32x4 rxh = buffer_rsrc(g.A2 + (size_t)tk0 * g.lda2, (uint32_t)(min(BN, g.M - tk0) * g.lda2));
+        const int rw8 = 8 * wave + (lane >> 3);  // row of piece wave (+ 64 i) for this lane
+        float sx2[FN];
+#pragma unroll
+        for (int b = 0; b < FN; ++b) sx2[b] = g.sx2[min(tok(b), g.M - 1)];
+        float4 sw2[FM][4];
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int c = chan(a, e4);
+            sw2[a][e4] = c + 3 < g.N ? *reinterpret_cast<const float4*>(g.sw2 + c)
+                                     : float4{g.sw2[min(c, g.N - 1)], g.sw2[min(c + 1, g.N - 1)],
+                                              g.sw2[min(c + 2, g.N - 1)], g.sw2[min(c + 3, g.N - 1)]};
+          }
+        for (int k0 = 0; k0 < K2; k0 += 128) {
+          stage_barrier();  // every wave is done with the LDS of the main loop or the last chunk
+          {
+            const bool ok = k0 + 16 * c8 < K2;
+#pragma unroll
+            for (int i = 0; i < PW; ++i)
+              load_lds16(rwh, lds0 + 1024 * (wave + 8 * i),
+                         ok ? (int)((rw8 + 64 * i) * g.ldb2) + 16 * c8 : kOutOfRange, k0);
+#pragma unroll
+            for (int i = 0; i < PX; ++i)
+              load_lds16(rxh, lds0 + BM * 128 + 1024 * (wave + 8 * i),
+                         ok ? (int)((rw8 + 64 * i) * g.lda2) + 16 * c8 : kOutOfRange, k0);
+          }
+          wait_vmcnt<0>();
+          stage_barrier();
+#pragma unroll
+          for (int a = 0; a < FM; ++a) {
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+              // fragments as in the main loop: step s of lane group lg takes
+              // chunk 4 (s / 2) + 2 lg + s % 2 of the rows (plain int8 codes)
+              i32x16 acc2;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc2[i] = 0;
+              // empty asm fences on acc2 keep the blocks' MFMA chains in
+              // sequence (interleaved, their accumulators would not fit)
+              asm volatile("" : "+v"(acc2));
+#pragma unroll
+              for (int st = 0; st < 4; ++st) {
+                if (k0 + 32 * st < K2) {
+                  // weight rows wm WM + 32 a + l32 have the swizzle of token rows wn WN + l32
+                  const i32x4 av = *reinterpret_cast<const i32x4*>(smem + (fb[st] - WPL) +
+                                                                   (wm * WM - wn * WN + 32 * a) * 128);
+                  const i32x4 bv = *reinterpret_cast<const i32x4*>(smem + BM * 128 + (fb[st] - WPL) + 4096 * b);
+                  acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc2, 0, 0, 0);
+                }
+              }
+#pragma unroll
+              for (int e4 = 0; e4 < 4; ++e4) {
+                y[a][b][4 * e4 + 0] += (float)acc2[4 * e4 + 0] * (sw2[a][e4].x * sx2[b]);
+                y[a][b][4 * e4 + 1] += (float)acc2[4 * e4 + 1] * (sw2[a][e4].y * sx2[b]);
+                y[a][b][4 * e4 + 2] += (float)acc2[4 * e4 + 2] * (sw2[a][e4].z * sx2[b]);
+                y[a][b][4 * e4 + 3] += (float)acc2[4 * e4 + 3] * (sw2[a][e4].w * sx2[b]);
+              }
+              asm volatile("" : "+v"(acc2));
+            }
+          }
+        }
       }
     }
     if (g.y_bf16) __syncthreads();  // every wave is done with the stage buffers
@@ -404,29 +519,39 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   }
 }
 
-template <int EPI, bool XP>
+template <int EPI, bool XP, bool W8 = false>
 hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
   const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
-  if (big >= 224) {
-    launch_kernel(k_gemm8<EPI, XP, 256>, dim3((unsigned)big), dim3(512), 0, st, g);
-  } else {
+  // the two-subspace epilogue keeps a 64 x 64 fp32 tile per wave (256 x 128
+  // tiles): with 64 x 128 it would not fit the registers beside the 8-bit product
+  if constexpr (EPI != EPI_MP) {
+    if (big >= 224) {
+      launch_kernel(k_gemm8<EPI, XP, 256, W8>, dim3((unsigned)big), dim3(512), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  {
     const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
-    launch_kernel(k_gemm8<EPI, XP, 128>, dim3(blocks), dim3(512), 0, st, g);
+    launch_kernel(k_gemm8<EPI, XP, 128, W8>, dim3(blocks), dim3(512), 0, st, g);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Channels x tokens tiles of 256 x 256 (256 x 128 for small grids); x_int8:
-// activation codes as int8 in the order above (lda bytes per row), else
-// nibble-packed like the weights.  Buffer offsets are 32-bit: a tile's rows
-// of codes must span less than 2 GiB.
-hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, hipStream_t st) {
+// Channels x tokens tiles of 256 x 256 (256 x 128 for small grids and the
+// two-subspace layer); x_int8: activation codes as int8 in the order above
+// (lda bytes per row), else nibble-packed like the weights; w_bits 8: int8
+// weight codes and activation codes in natural k order (the integer check
+// only).  Buffer offsets are 32-bit: a tile's rows of codes must span less
+// than 2 GiB.
+hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, int w_bits, hipStream_t st) {
   if ((int64_t)256 * g.ldb >= (1ll << 31) || (int64_t)256 * g.lda >= (1ll << 31)) return hipErrorInvalidValue;
+  if (w_bits == 8) return (epi == EPI_ACC && x_int8) ? launch_t<EPI_ACC, false, true>(g, st) : hipErrorInvalidValue;
+  if (w_bits != 4) return hipErrorInvalidValue;
   if (epi == EPI_LINEAR && x_int8) return launch_t<EPI_LINEAR, false>(g, st);
-  if (epi == EPI_ACC && x_int8) return launch_t<EPI_ACC, false>(g, st);
   if (epi == EPI_ACC && !x_int8) return launch_t<EPI_ACC, true>(g, st);
+  if (epi == EPI_MP && x_int8) return launch_t<EPI_MP, false>(g, st);
   return hipErrorInvalidValue;
 }
 

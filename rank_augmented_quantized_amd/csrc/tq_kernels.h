@@ -107,14 +107,17 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks);
 int gemv_max_chunks(int M, int Kb, int r_pad);
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st);
+// The same with the 4-bit codes of columns [0, dl) as int8 in the order of the
+// int8 tile GEMM (dl bytes per row); columns [dl, d) take bits_b bits.
+hipError_t launch_quant_rows_i8(const void* X, bool bf16, int n, int d, int dl, int bits_b, void* ca, float* sa,
+                                void* cb, float* sb, hipStream_t st);
 // Per-token quantiser with one wave per row (falls back to a block per row for very long rows).
 hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
                                   float* sa, void* cb, float* sb, hipStream_t st);
-// Integer GEMM (n > 32 tile kernel) with the given epilogue; bits of the main segment.
-hipError_t launch_gemm(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
-// 4-bit tile GEMM with int8 operands in LDS (tq_gemm8.hip): x_int8 means the
-// activation codes come as int8 (16 x code, split order, lda bytes per row).
-hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, hipStream_t st);
+// Tile GEMM with operands staged HBM -> LDS by direct loads (tq_gemm8.hip):
+// x_int8: activation codes as int8 (lda bytes per row), else nibble-packed;
+// w_bits: 4 (nibble-packed weights) or 8 (int8 weights, EPI_ACC only).
+hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, int w_bits, hipStream_t st);
 // Small-n integer GEMM (M <= 32).
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
 

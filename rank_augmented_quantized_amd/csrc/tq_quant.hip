@@ -274,15 +274,15 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
 }
 
 // 4 rows per 256-thread block, one per wave.
-template <typename T, int BA, int BB, int CH>
+template <typename T, int BA, int BB, int CH, bool X8 = false>
 __global__ __launch_bounds__(256) void k_quant_rows_wave(const T* __restrict__ X, int n, int d, int dl,
                                                          uint8_t* __restrict__ ca, float* __restrict__ sa,
                                                          uint8_t* __restrict__ cb, float* __restrict__ sb) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  const size_t lda = (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
-  quant_row_wave<T, BA, BB, CH>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row, cb ? cb + row * ldb : nullptr,
-                                sb ? sb + row : nullptr);
+  const size_t lda = X8 ? (size_t)dl : (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
+  quant_row_wave<T, BA, BB, CH, X8>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row,
+                                    cb ? cb + row * ldb : nullptr, sb ? sb + row : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,7 +564,7 @@ static int chunks_for(int d) {
   return ch;  // 1, 2, 4, ...: row of d values in ch chunks of 8 per lane
 }
 
-template <typename T, int BA, int BB>
+template <typename T, int BA, int BB, bool X8 = false>
 static hipError_t launch_quant_rows_wave_t(const void* X, int n, int d, int dl, void* ca, float* sa, void* cb,
                                            float* sb, hipStream_t st) {
   dim3 grid((n + 3) / 4), block(256);
@@ -572,15 +572,28 @@ static hipError_t launch_quant_rows_wave_t(const void* X, int n, int d, int dl, 
   uint8_t* a = (uint8_t*)ca;
   uint8_t* b = (uint8_t*)cb;
   switch (chunks_for(d)) {
-    case 1: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 1>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    case 2: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 2>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    case 4: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 4>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    case 8: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    case 16: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 16>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    case 32: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 32>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
-    default: return launch_quant_rows_t<T>(X, n, d, dl, BA, BB, ca, sa, cb, sb, st);  // rows beyond 16384 values
+    case 1: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 1, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 2: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 2, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 4: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 4, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 8: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 8, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 16: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 16, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    case 32: hipLaunchKernelGGL((k_quant_rows_wave<T, BA, BB, 32, X8>), grid, block, 0, st, x, n, d, dl, a, sa, b, sb); break;
+    default:  // rows beyond 16384 values: a block per row
+      if constexpr (X8)
+        hipLaunchKernelGGL((k_quant_rows<T, BA, BB, true>), dim3(n), dim3(256), 0, st, x, n, d, dl, a, sa, b, sb);
+      else
+        return launch_quant_rows_t<T>(X, n, d, dl, BA, BB, ca, sa, cb, sb, st);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_i8(const void* X, bool bf16, int n, int d, int dl, int bits_b, void* ca, float* sa,
+                                void* cb, float* sb, hipStream_t st) {
+  if (bf16)
+    return bits_b == 8 ? launch_quant_rows_wave_t<bf16_t, 4, 8, true>(X, n, d, dl, ca, sa, cb, sb, st)
+                       : launch_quant_rows_wave_t<bf16_t, 4, 4, true>(X, n, d, dl, ca, sa, cb, sb, st);
+  return bits_b == 8 ? launch_quant_rows_wave_t<float, 4, 8, true>(X, n, d, dl, ca, sa, cb, sb, st)
+                     : launch_quant_rows_wave_t<float, 4, 4, true>(X, n, d, dl, ca, sa, cb, sb, st);
 }
 
 hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,

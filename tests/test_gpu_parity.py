@@ -155,6 +155,8 @@ def test_pack_weight_bitexact(d, m, dtype, bits):
 ACASES = [
     (1, 512, 16, 4), (16, 4096, 100, 4), (17, 512, 33, 4), (32, 14336, 48, 4), (33, 512, 130, 4),
     (200, 4064, 300, 4), (130, 8064, 257, 4), (64, 128, 200, 8), (5, 128, 40, 8), (300, 1024, 160, 8),
+    # ragged last 128-k stage of the tile GEMM (8-bit: 16-byte chunks past k read as zeros)
+    (40, 272, 96, 8), (70, 416, 64, 4),
 ]
 
 

@@ -248,6 +248,10 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
         float v[8];
         int q[8];
         c[i].get(v);
+        if (BA == 4 && X8 && ch < nchl) {
+          *reinterpret_cast<uint2*>(ca + 8 * ch) = quant8_int8(v, ra);
+          continue;
+        }
         if (ch < nchl)
           quant8_fast<BA>(v, ra, q);
         else

@@ -25,7 +25,9 @@ namespace tq {
 //   each step for channel lane % 16).  Every load of a batch of U steps --
 //   weights, the matching activation codes, and the low-rank operands -- is
 //   issued before the first wait, so a block pays one memory round trip per
-//   batch.  MFMA 16x16x64 int8 (TWO: a second 16-token tile shares each
+//   batch.  XL: when the activation codes of all M rows fit in a few KB of
+//   LDS, the block copies them there first and the product reads them from
+//   LDS, so the vector memory stream carries only the weights.  MFMA 16x16x64 int8 (TWO: a second 16-token tile shares each
 //   weight fragment); the waves' int32 partials are summed exactly through
 //   LDS in wave order.
 //   Epilogue: T is the sum over the k-chunks of the fp32 partials of X L1
@@ -34,9 +36,14 @@ namespace tq {
 //   is one 16x16 bf16 MFMA chain whose result layout matches the integer
 //   accumulator's (lane l, element i -> token 4 (l / 16) + i, channel l % 16).
 // ---------------------------------------------------------------------------
-template <int BITS, int EPI, int WAVES, bool TWO>
+// Most bytes of activation codes the small-n GEMM stages in LDS: what
+// leaves the blocks per CU of its launch bounds (2 of 8 waves, 4 of 4 waves)
+// within the 160 KB of LDS next to the static arrays.
+__host__ __device__ constexpr int gemv_xl_bytes(int waves) { return waves == 8 ? 24576 : 12288; }
+
+template <int BITS, int EPI, int WAVES, bool TWO, bool XL>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g) {
-  constexpr int U = (WAVES == 4 || TWO) ? 8 : 16;  // 64-byte steps per wave per batch
+  constexpr int U = (WAVES == 4 && TWO && !XL) ? 4 : ((WAVES == 4 || TWO) ? 8 : 16);  // 64-byte steps per wave per batch
   constexpr int NT = WAVES * 64;
   constexpr int MT = TWO ? 32 : 16;  // token rows held for the low-rank stage
   constexpr bool LR = EPI == EPI_LINEAR;
@@ -60,6 +67,21 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   const int NP = g.M * rq;
   const int G = max(1, min(NT / max(NP, 1), LR ? g.nchunk : 1));
 
+  // XL: the M rows of activation codes, row stride Kb + 16 bytes (rows of a
+  // 16-row operand read then fall on distinct banks); XLN 16-byte pieces per
+  // thread cover the largest staging the launcher allows
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl_lds[];
+  constexpr int XLN = XL ? gemv_xl_bytes(WAVES) / 16 / NT : 1;
+  const int XS = g.Kb + 16, kp = g.Kb >> 4;
+  uint4 xst[XLN];
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XLN; ++i) {
+      const int idx = min(tid + NT * i, g.M * kp - 1);
+      xst[i] = *reinterpret_cast<const uint4*>(g.A + (size_t)(idx / kp) * g.lda + 16 * (idx % kp));
+    }
+  }
+
   // Loads are unconditional, from clamped (always valid) addresses, and
   // masked where used: conditional loads become branches whose register
   // merges force early waits on every load in flight.
@@ -68,6 +90,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   auto load_batch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) bv[u] = *reinterpret_cast<const uint4*>(bp + min((s0 + u) * 64, kb_last));
+    if (XL) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kb = min((s0 + u) * 64, kb_last);
@@ -75,11 +98,18 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
       if (TWO) av1[u] = *reinterpret_cast<const uint4*>(ap1 + kb);
     }
   };
+  const uint8_t* xl0 = xl_lds + min(l16, g.M - 1) * XS + 16 * lg;
+  const uint8_t* xl1 = xl_lds + min(16 + l16, g.M - 1) * XS + 16 * lg;
   i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   auto mma_batch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u >= send) continue;
+      if (XL) {
+        const int kb = min((s0 + u) * 64, kb_last);
+        av0[u] = *reinterpret_cast<const uint4*>(xl0 + kb);
+        if (TWO) av1[u] = *reinterpret_cast<const uint4*>(xl1 + kb);
+      }
       if ((s0 + u) * 64 + 16 * lg >= g.Kb) {  // this lane group's 16 bytes lie past the row: zero codes
         bv[u] = uint4{0, 0, 0, 0};
         av0[u] = uint4{0, 0, 0, 0};
@@ -129,6 +159,15 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
         pv[j][1] = pp[1];
       }
     }
+  }
+
+  if (XL) {
+#pragma unroll
+    for (int i = 0; i < XLN; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < g.M * kp) *reinterpret_cast<uint4*>(xl_lds + (idx / kp) * XS + 16 * (idx % kp)) = xst[i];
+    }
+    __syncthreads();
   }
 
   // ---- integer product ----
@@ -246,10 +285,19 @@ int gemv_max_chunks(int M, int Kb, int r_pad) {
 template <int BITS, int EPI, bool TWO>
 static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
   const unsigned blocks = (unsigned)((g.N + 15) / 16);
-  if (g.Kb > 2048)
-    hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO>), dim3(blocks), dim3(512), 0, st, g);
-  else
-    hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO>), dim3(blocks), dim3(256), 0, st, g);
+  const size_t xl = (size_t)g.M * (size_t)(g.Kb + 16);  // activation codes in LDS
+  const bool use_xl = xl <= (size_t)gemv_xl_bytes(g.Kb > 2048 ? 8 : 4) && g.Kb % 16 == 0;
+  if (g.Kb > 2048) {
+    if (use_xl)
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, true>), dim3(blocks), dim3(512), xl, st, g);
+    else
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, false>), dim3(blocks), dim3(512), 0, st, g);
+  } else {
+    if (use_xl)
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, true>), dim3(blocks), dim3(256), xl, st, g);
+    else
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, false>), dim3(blocks), dim3(256), 0, st, g);
+  }
   return hipGetLastError();
 }
 

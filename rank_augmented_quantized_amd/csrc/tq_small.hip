@@ -63,7 +63,7 @@ __device__ __forceinline__ void signal_done(unsigned* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T, int WAVES>
+template <typename T, int WAVES, int NR>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_small(SmallArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int U = (WAVES == 4) ? 8 : 16;  // 64-byte weight steps per wave per batch
@@ -190,12 +190,12 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
   //    then overlaps the weight stream, memory counters being in order), the
   //    weight codes, scales and L2^T
   const int nch = d >> 3;
-  Row8<T> r8[2][CHX];
+  Row8<T> r8[NR][CHX];  // NR = n: one or two token rows
 #pragma unroll
   for (int i = 0; i < CHX; ++i) {
     const int ch = min(tid + NT * i, nch - 1);
-    r8[0][i].load(X + 8 * ch);
-    r8[1][i].load(X + (size_t)(n > 1 ? d : 0) + 8 * ch);
+#pragma unroll
+    for (int row = 0; row < NR; ++row) r8[row][i].load(X + (size_t)row * d + 8 * ch);
   }
   load_w(sbeg);
   const float swv = a.sw[min(n0 + lr, m - 1)];
@@ -209,8 +209,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
   //    few KB of L2-resident input); the first consumer also writes s_x and
   //    the codes out
 #pragma unroll
-  for (int row = 0; row < 2; ++row) {
-    if (row >= n) break;
+  for (int row = 0; row < NR; ++row) {
     float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < CHX; ++i) {
@@ -430,7 +429,10 @@ template <typename T>
 static hipError_t launch_small_t(const SmallArgs& a, hipStream_t st) {
   if (!small_fused_ok(a.n, a.d, a.r_pad)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.nt + (a.m + 15) / 16));
-  hipLaunchKernelGGL((k_linear_small<T, 4>), grid, dim3(256), 0, st, a);
+  if (a.n == 1)
+    hipLaunchKernelGGL((k_linear_small<T, 4, 1>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_linear_small<T, 4, 2>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -86,7 +86,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int EPI, bool XP, int BN, bool W8 = false>
+// KF: every row's code bytes are a whole number of stages, so no direct load
+// needs the per-lane end-of-row test (which costs VALU slots next to the MFMAs)
+template <int EPI, bool XP, int BN, bool W8 = false, bool KF = false>
 __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   static_assert(!W8 || (EPI == EPI_ACC && !XP), "8-bit weights: the integer check only");
   constexpr int BM = 256;                        // channels per tile
@@ -141,10 +143,11 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     const uint32_t base = lds0 + buf * SPL;
     if (i < WI) {
       const int sw = WROW * kt;
-      load_lds16(rw, base + 1024 * (wave + 8 * i), sw + 16 * cw < Kb ? vw[i] : kOutOfRange, sw);
+      load_lds16(rw, base + 1024 * (wave + 8 * i), (KF || sw + 16 * cw < Kb) ? vw[i] : kOutOfRange, sw);
     } else {
       const int sx = (XP ? 64 : 128) * kt;
-      load_lds16(rx, base + WPL + 1024 * (wave + 8 * (i - WI)), sx + 16 * cx < Kx ? vx[i - WI] : kOutOfRange, sx);
+      load_lds16(rx, base + WPL + 1024 * (wave + 8 * (i - WI)), (KF || sx + 16 * cx < Kx) ? vx[i - WI] : kOutOfRange,
+                 sx);
     }
   };
   constexpr int NL = WI + XI;
@@ -326,6 +329,29 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     // Dequantisation: the int32 sums carry the factor 2^SH, folded exactly
     // into s_x; acc is converted in place to the fp32 tile y.
     f32x16 y[FM][FN];
+    // The low-rank operands of the first TQ 16-t steps are loaded with the
+    // scales, before the dequantisation, so the epilogue pays one L2 round
+    // trip for both instead of one per step.
+    constexpr int TQ = 2;
+    const bf16_t* lp[FM];
+    const bf16_t* tp[FN];
+    uint4 lav[TQ][FM], lbv[TQ][FN];
+    const bool lr_on = EPI == EPI_LINEAR && g.r_pad > 0;
+    if (lr_on) {
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+        lp[a] = g.L2t + (size_t)min(ch0 + wm * WM + 32 * a + l32, g.N - 1) * g.r_pad + 8 * lg;
+#pragma unroll
+      for (int b = 0; b < FN; ++b) tp[b] = g.T + (size_t)min(tok(b), g.M - 1) * g.r_pad + 8 * lg;
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        const int t0 = min(16 * q, g.r_pad - 16);  // r_pad >= 32: in range
+#pragma unroll
+        for (int a = 0; a < FM; ++a) lav[q][a] = *reinterpret_cast<const uint4*>(lp[a] + t0);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) lbv[q][b] = *reinterpret_cast<const uint4*>(tp[b] + t0);
+      }
+    }
     {
       float4 swv[FM][4];
       float sxv[FN];
@@ -355,28 +381,29 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
             y[a][b][4 * e4 + 3] = (float)acc[a][b][4 * e4 + 3] * (swv[a][e4].w * sxv[b]);
           }
     }
-    if (EPI == EPI_LINEAR && g.r_pad > 0) {
+    if (lr_on) {
       // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16
-      // MFMA, 16 t per step; the L2 fragment of each channel block and the T
-      // fragment of each token block are loaded once per step
-      const bf16_t* lp[FM];
-      const bf16_t* tp[FN];
+      // MFMA, 16 t per step (r_pad is a multiple of 32); the L2 fragment of
+      // each channel block and the T fragment of each token block are loaded
+      // once per step, TQ steps at a time
+      for (int t00 = 0; t00 < g.r_pad; t00 += 16 * TQ) {
+        if (t00 > 0) {
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
-        lp[a] = g.L2t + (size_t)min(ch0 + wm * WM + 32 * a + l32, g.N - 1) * g.r_pad + 8 * lg;
+          for (int q = 0; q < TQ; ++q) {
 #pragma unroll
-      for (int b = 0; b < FN; ++b) tp[b] = g.T + (size_t)min(tok(b), g.M - 1) * g.r_pad + 8 * lg;
-      for (int t0 = 0; t0 < g.r_pad; t0 += 16) {
-        uint4 av[FM], bv[FN];
+            for (int a = 0; a < FM; ++a) lav[q][a] = *reinterpret_cast<const uint4*>(lp[a] + t00 + 16 * q);
 #pragma unroll
-        for (int a = 0; a < FM; ++a) av[a] = *reinterpret_cast<const uint4*>(lp[a] + t0);
+            for (int b = 0; b < FN; ++b) lbv[q][b] = *reinterpret_cast<const uint4*>(tp[b] + t00 + 16 * q);
+          }
+        }
 #pragma unroll
-        for (int b = 0; b < FN; ++b) bv[b] = *reinterpret_cast<const uint4*>(tp[b] + t0);
+        for (int q = 0; q < TQ; ++q)
 #pragma unroll
-        for (int a = 0; a < FM; ++a)
+          for (int a = 0; a < FM; ++a)
 #pragma unroll
-          for (int b = 0; b < FN; ++b)
-            y[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[a]), as_bf16x8(bv[b]), y[a][b], 0, 0, 0);
+            for (int b = 0; b < FN; ++b)
+              y[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lav[q][a]), as_bf16x8(lbv[q][b]), y[a][b],
+                                                                0, 0, 0);
       }
     }
     if constexpr (EPI == EPI_MP) {
@@ -519,22 +546,29 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   }
 }
 
-template <int EPI, bool XP, bool W8 = false>
-hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
+template <int EPI, bool XP, bool W8, bool KF>
+hipError_t launch_kf(const GemmArgs& g, hipStream_t st) {
   const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
   // the two-subspace epilogue keeps a 64 x 64 fp32 tile per wave (256 x 128
   // tiles): with 64 x 128 it would not fit the registers beside the 8-bit product
   if constexpr (EPI != EPI_MP) {
     if (big >= 224) {
-      launch_kernel(k_gemm8<EPI, XP, 256, W8>, dim3((unsigned)big), dim3(512), 0, st, g);
+      launch_kernel(k_gemm8<EPI, XP, 256, W8, KF>, dim3((unsigned)big), dim3(512), 0, st, g);
       return hipGetLastError();
     }
   }
   {
     const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
-    launch_kernel(k_gemm8<EPI, XP, 128, W8>, dim3(blocks), dim3(512), 0, st, g);
+    launch_kernel(k_gemm8<EPI, XP, 128, W8, KF>, dim3(blocks), dim3(512), 0, st, g);
   }
   return hipGetLastError();
+}
+
+template <int EPI, bool XP, bool W8 = false>
+hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
+  // whole stages: WROW weight bytes per row per stage, and then also whole
+  // activation stages (XROW = 2 WROW for int8 activations, WROW otherwise)
+  return g.Kb % (W8 ? 128 : 64) == 0 ? launch_kf<EPI, XP, W8, true>(g, st) : launch_kf<EPI, XP, W8, false>(g, st);
 }
 
 }  // namespace

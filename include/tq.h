@@ -109,6 +109,54 @@ tq_status tq_pack_lowrank(const void* L1, const void* L2, tq_dtype dt, int64_t d
                           int64_t r, void* lowrank, hipStream_t stream);
 
 /*
+ * Layers that share one input (CoQuant notes, "CoQuant: Joint Weight-
+ * Activation Subspace Projection for Mixed-Precision LLMs", the grouping of
+ * linear layers with identical input activations around Eq. 14: Q/K/V, and
+ * gate/up).  G layers of m[0..G-1] output channels and a common rank r are
+ * stacked along the output channels: one quantisation of X and one T for
+ * all of them, then one integer GEMM over m_total = sum m[g] channels.
+ * Shapes: 1 <= G <= 8; every m[g] but the last a multiple of 256;
+ * G * r_pad <= 256 (r_pad = r rounded up to a power of two, at least 32).
+ */
+
+/* Bytes of the packed low-rank factors of tq_pack_lowrank_group (0 for invalid shapes). */
+size_t tq_lowrank_group_bytes(int64_t d, const int64_t* m, int64_t G, int64_t r);
+
+/*
+ * tq_pack_lowrank_group -- lays out the G layers' low-rank factors (offline).
+ *   L1[g]   d x r, L2[g] r x m[g] (host array of G device pointers each),
+ *           element type dt, rounded or copied to bf16 as in tq_pack_lowrank.
+ *   m       host array of G channel counts.
+ *   lowrank out: tq_lowrank_group_bytes(d, m, G, r) bytes, an opaque bf16
+ *           layout (all L1 transposed and stacked, then all L2 transposed and
+ *           stacked in channel order, zero-padded).
+ */
+tq_status tq_pack_lowrank_group(const void* const* L1, const void* const* L2, tq_dtype dt, int64_t d,
+                                const int64_t* m, int64_t G, int64_t r, void* lowrank,
+                                hipStream_t stream);
+
+/* Workspace bytes tq_linear_group needs for these sizes (0 for invalid shapes). */
+size_t tq_linear_group_workspace_bytes(int64_t n, int64_t d, const int64_t* m, int64_t G,
+                                       int64_t r);
+
+/*
+ * tq_linear_group -- G layers on one input X (n x d, x_dt):
+ *   Y[:, M_g + j] = layer g's tq_linear output, channel j (M_g = sum of m[h], h < g).
+ *   w_codes  m_total x d/2 bytes: the G layers' tq_pack_weight codes stacked in
+ *            channel order (layer g at row M_g); s_w m_total fp32 likewise.
+ *   lowrank  from tq_pack_lowrank_group, or NULL iff r == 0.
+ *   Y        out, n x m_total row-major, y_dt.
+ *   ws       device workspace of at least tq_linear_group_workspace_bytes,
+ *            zero-filled once before first use (as for tq_linear).
+ * Every layer's codes, scales and Y are those tq_linear gives for it alone.
+ * Errors as tq_linear, plus TQ_ERR_SHAPE for group shapes outside the above.
+ */
+tq_status tq_linear_group(const void* X, tq_dtype x_dt, int64_t n, int64_t d, const int64_t* m,
+                          int64_t G, int64_t r, const void* w_codes, const float* s_w,
+                          const void* lowrank, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * tq_quantize_act -- per-token symmetric quantisation of activations.
  *   X       n x d, element type x_dt.  bits 4 or 8.
  *   x_codes out: n x (d*bits/8) bytes.   s_x out: n fp32 scales.

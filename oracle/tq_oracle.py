@@ -18,7 +18,9 @@ It evaluates the plain definition of the layer, step by step, in numpy:
   unquantised activations;
 * exact integer accumulation of the residual product -- TwinQuant notes,
   section 02 (note on INT32 accumulation) and section 04.C, Figure 4;
-* the two-subspace mixed-precision output -- CoQuant Eq. 3-9.
+* the two-subspace mixed-precision output -- CoQuant Eq. 3-9;
+* layers that share one input, grouped -- CoQuant, the grouping paragraph
+  around Eq. 14.
 
 Readings of points the pages leave open (each one is also listed in the
 design notes): q_max = 7 / 127; "round" is round-half-to-even; the scale is
@@ -191,6 +193,26 @@ def tq_linear_ref(x, r, l1=None, l2=None, rows=None, cols=None, bits: int = 4):
         t, ylr = lowrank_branch(x, l1, l2)
         y = y + ylr
     return {"codes_x": cx, "s_x": s_x, "codes_w": cw, "s_w": s_w, "acc": acc, "T": t, "Y": y}
+
+
+def tq_linear_group_ref(x, rs, l1s=None, l2s=None, rows=None, bits: int = 4):
+    """Reference output of G layers that share one input.
+
+    The CoQuant notes group the linear layers whose input activations are
+    identical (query/key/value, gate/up; the paragraph around Eq. 14).  Layer
+    g is the layer of ``tq_linear_ref`` on the same X with its own weight
+    rs[g] (d x m_g) and factors l1s[g], l2s[g]; the outputs sit side by side,
+    layer g in the m_g columns after those of layers 0 .. g-1.  X is
+    quantised once: its codes and scales are every layer's.
+    """
+    outs = []
+    for g, r in enumerate(rs):
+        l1 = None if l1s is None else l1s[g]
+        l2 = None if l2s is None else l2s[g]
+        outs.append(tq_linear_ref(x, r, l1, l2, rows=rows, bits=bits))
+    y = np.concatenate([o["Y"] for o in outs], axis=1)
+    t = None if outs[0]["T"] is None else np.concatenate([o["T"] for o in outs], axis=1)
+    return {"codes_x": outs[0]["codes_x"], "s_x": outs[0]["s_x"], "layers": outs, "T": t, "Y": y}
 
 
 def tq_linear_mp_ref(xrot, wrot, d_hi: int, rows=None, cols=None, bits_lo: int = 4, bits_hi: int = 8):

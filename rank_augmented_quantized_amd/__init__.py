@@ -6,16 +6,21 @@ The computation lives in the HIP library ``libtq.so`` (C ABI: include/tq.h);
 
 from .tq import (  # noqa: F401
     TQError,
+    linear_group_workspace,
     linear_workspace,
     load,
     tq_codes_bytes,
     tq_debug_accumulate,
     tq_linear,
+    tq_linear_group,
+    tq_linear_group_workspace_bytes,
     tq_linear_mp,
     tq_linear_mp_workspace_bytes,
     tq_linear_workspace_bytes,
     tq_linear_workspace_offsets,
+    tq_lowrank_group_bytes,
     tq_pack_lowrank,
+    tq_pack_lowrank_group,
     tq_pack_weight,
     tq_profile_enable,
     tq_profile_read,

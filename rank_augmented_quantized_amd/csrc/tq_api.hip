@@ -107,17 +107,19 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
 
 struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
-  int r_pad;
+  int r_pad;  // columns of T
   bool small, fused;
   tq::ProloguePlan plan;
   tq::SmallPlan splan;
 };
 
-LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t r) {
+// tcols: columns of T (r_pad of one layer; a power of two covering all the
+// layers of a group)
+LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols) {
   (void)m;
   LinearWs w{};
   w.small = n <= kSmallN;
-  w.r_pad = (int)r_padded(r);
+  w.r_pad = (int)tcols;
   w.fused = w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
   size_t psize = 0;
   int counters = 0;
@@ -188,7 +190,7 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 100; }
+int tq_version(void) { return 101; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
   if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
@@ -206,6 +208,9 @@ tq_status tq_pack_weight(const void* W, tq_dtype w_dt, int64_t d, int64_t m, int
   return TQ_OK;
 }
 
+// T columns of G layers of rank r: G r_pad rounded up to a power of two.
+int64_t group_tcols(int64_t G, int64_t r) { return G <= 1 ? r_padded(r) : r_padded(G * r_padded(r)); }
+
 size_t tq_lowrank_bytes(int64_t d, int64_t m, int64_t r) {
   if (d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
   const int64_t rp = r_padded(r);
@@ -220,7 +225,8 @@ tq_status tq_pack_lowrank(const void* L1, const void* L2, tq_dtype dt, int64_t d
   if (!aligned16(lowrank)) return TQ_ERR_ALIGN;
   const int rp = (int)r_padded(r);
   TQ_RUN("pack_lowrank", stream,
-         tq::launch_pack_lowrank(L1, L2, dt == TQ_BF16, (int)d, (int)m, (int)r, rp, lowrank, stream));
+         tq::launch_pack_lowrank(L1, L2, dt == TQ_BF16, (int)d, (int)m, (int)r, rp, rp, lowrank,
+                                 (uint8_t*)lowrank + (size_t)rp * d * 2, stream));
   return TQ_OK;
 }
 
@@ -240,21 +246,20 @@ tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, in
 
 size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r) {
   if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
-  return linear_ws(n, d, m, r).total;
+  return linear_ws(n, d, m, r_padded(r)).total;
 }
 
-tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
-                    const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
-  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
-  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || m <= 0 || m > kMaxDim || d % 32 || r < 0 || r > 256)
-    return TQ_ERR_SHAPE;
-  if (n == 0) return TQ_OK;
-  if (!X || !w_codes || !s_w || !Y || !ws || (r > 0 && !lowrank)) return TQ_ERR_NULL;
-  if (!aligned16(X) || !aligned16(w_codes) || !aligned16(s_w) || !aligned16(Y) || !aligned16(ws) ||
-      (r > 0 && !aligned16(lowrank)))
-    return TQ_ERR_ALIGN;
-  const LinearWs L = linear_ws(n, d, m, r);
+}  // extern "C"
+
+namespace {
+
+// The layer (or G layers stacked along the channels, sharing X) once the
+// arguments are checked: ms[g] channels per layer, m = their sum.
+tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, int G,
+                     const int64_t* ms, const void* w_codes, const float* s_w, const void* lowrank, void* Y,
+                     tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int rp = (int)r_padded(r);
+  const LinearWs L = linear_ws(n, d, m, group_tcols(G, r));
   if (ws_bytes < L.total) return TQ_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
@@ -266,6 +271,9 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   const tq::bf16_t* L1t = (const tq::bf16_t*)lowrank;
   const tq::bf16_t* L2t = lowrank ? L1t + (size_t)L.r_pad * d : nullptr;
   const bool xb = x_dt == TQ_BF16;
+  tq::Groups groups{};
+  groups.n = G;
+  for (int g = 0; g < G; ++g) groups.start[g + 1] = groups.start[g] + (int)ms[g];
 
   if (L.fused) {
     tq::SmallArgs a{};
@@ -277,7 +285,9 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
     a.sw = s_w;
     a.L1t = L1t;
     a.L2t = L2t;
-    a.r_pad = L.r_pad;
+    a.r_pad = rp;
+    a.ldt = L.r_pad;
+    a.groups = groups;
     a.nt = L.splan.nt;
     a.nchunk = L.splan.nchunk;
     a.kc = L.splan.kc;
@@ -306,7 +316,9 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   g.sw = s_w;
   g.T = L.r_pad ? T : nullptr;
   g.L2t = L2t;
-  g.r_pad = L.r_pad;
+  g.r_pad = rp;
+  g.ldt = L.r_pad;
+  g.groups = groups;
   if (L.r_pad && L.plan.partial) {
     g.P = P;
     g.nchunk = L.plan.nchunk;
@@ -327,10 +339,100 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   return TQ_OK;
 }
 
+// Checks shared by tq_linear and tq_linear_group.
+tq_status linear_check(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                       const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws) {
+  if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || m <= 0 || m > kMaxDim || d % 32 || r < 0 || r > 256)
+    return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!X || !w_codes || !s_w || !Y || !ws || (r > 0 && !lowrank)) return TQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(w_codes) || !aligned16(s_w) || !aligned16(Y) || !aligned16(ws) ||
+      (r > 0 && !aligned16(lowrank)))
+    return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+// Group shapes: 1 <= G <= 8 layers, each but the last a whole number of
+// 256-channel tiles, G r_pad <= 256; m_total = their sum.
+tq_status group_check(const int64_t* ms, int64_t G, int64_t r, int64_t* m_total) {
+  if (!ms) return TQ_ERR_NULL;
+  if (G < 1 || G > tq::kMaxGroups || r < 0 || r > 256 || G * r_padded(r) > 256) return TQ_ERR_SHAPE;
+  int64_t t = 0;
+  for (int64_t g = 0; g < G; ++g) {
+    if (ms[g] <= 0 || (g + 1 < G && ms[g] % 256)) return TQ_ERR_SHAPE;
+    t += ms[g];
+  }
+  if (t > kMaxDim) return TQ_ERR_SHAPE;
+  *m_total = t;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                    const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  const int64_t ms[1] = {m};
+  return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream);
+}
+
+size_t tq_lowrank_group_bytes(int64_t d, const int64_t* m, int64_t G, int64_t r) {
+  int64_t mt = 0;
+  if (d <= 0 || r < 1 || group_check(m, G, r, &mt) != TQ_OK) return 0;
+  return (size_t)(group_tcols(G, r) * d + mt * r_padded(r)) * 2;
+}
+
+tq_status tq_pack_lowrank_group(const void* const* L1, const void* const* L2, tq_dtype dt, int64_t d,
+                                const int64_t* m, int64_t G, int64_t r, void* lowrank, hipStream_t stream) {
+  if (!valid_dtype(dt)) return TQ_ERR_DTYPE;
+  int64_t mt = 0;
+  const tq_status gs = group_check(m, G, r, &mt);
+  if (gs != TQ_OK) return gs;
+  if (d <= 0 || d > kMaxDim || d % 32 || r < 1) return TQ_ERR_SHAPE;
+  if (!L1 || !L2 || !lowrank) return TQ_ERR_NULL;
+  for (int64_t g = 0; g < G; ++g)
+    if (!L1[g] || !L2[g]) return TQ_ERR_NULL;
+  if (!aligned16(lowrank)) return TQ_ERR_ALIGN;
+  const int rp = (int)r_padded(r), tc = (int)group_tcols(G, r);
+  uint8_t* l1 = (uint8_t*)lowrank;
+  uint8_t* l2 = l1 + (size_t)tc * d * 2;
+  for (int64_t g = 0; g < G; ++g) {
+    // the last layer also zero-fills the rows of T past G r_pad
+    const int rows1 = g + 1 < G ? rp : tc - (int)(G - 1) * rp;
+    TQ_RUN("pack_lowrank", stream,
+           tq::launch_pack_lowrank(L1[g], L2[g], dt == TQ_BF16, (int)d, (int)m[g], (int)r, rp, rows1,
+                                   l1 + (size_t)g * rp * d * 2, l2, stream));
+    l2 += (size_t)m[g] * rp * 2;
+  }
+  return TQ_OK;
+}
+
+size_t tq_linear_group_workspace_bytes(int64_t n, int64_t d, const int64_t* m, int64_t G, int64_t r) {
+  int64_t mt = 0;
+  if (n < 0 || d <= 0 || group_check(m, G, r, &mt) != TQ_OK) return 0;
+  return linear_ws(n, d, mt, group_tcols(G, r)).total;
+}
+
+tq_status tq_linear_group(const void* X, tq_dtype x_dt, int64_t n, int64_t d, const int64_t* m, int64_t G,
+                          int64_t r, const void* w_codes, const float* s_w, const void* lowrank, void* Y,
+                          tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t mt = 0;
+  const tq_status gs = group_check(m, G, r, &mt);
+  if (gs != TQ_OK) return gs;
+  const tq_status st = linear_check(X, x_dt, n, d, mt, r, w_codes, s_w, lowrank, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  return linear_run(X, x_dt, n, d, mt, r, (int)G, m, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream);
+}
+
 tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]) {
   if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256 || d % 32) return TQ_ERR_SHAPE;
   if (!off) return TQ_ERR_NULL;
-  const LinearWs L = linear_ws(n, d, m, r);
+  const LinearWs L = linear_ws(n, d, m, r_padded(r));
   off[0] = L.sx;
   off[1] = L.xc;
   off[2] = L.t;

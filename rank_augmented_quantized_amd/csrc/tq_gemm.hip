@@ -62,6 +62,9 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   const int sbeg = wave * per, send = min(KS, sbeg + per);
   const int rp = LR ? g.r_pad : 0;
   const int rq = rp / 8;  // 16-byte pieces (8 values) per low-rank row
+  const int grp0 = LR ? group_of(g.groups, n0) : 0;
+  const int toff = grp0 * rp;                          // this block's layer in T and the partials
+  const bool tfirst = LR && n0 == g.groups.start[grp0];  // first block of its layer writes T
   // T pieces: NP = M rows x rq; G thread groups (no more than there are
   // chunks) split the k-chunks of each piece, at most two chunks per group
   const int NP = g.M * rq;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = min(grp + G * j, g.nchunk - 1);
-        const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)c * g.M + rowt) * rp + 8 * qt);
+        const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)c * g.M + rowt) * g.ldt + toff + 8 * qt);
         pv[j][0] = pp[0];
         pv[j][1] = pp[1];
       }
@@ -214,14 +217,14 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
           }
         } else {  // pieces beyond the block's threads (G == 1): all chunks here
           for (int k = 0; k < g.nchunk; ++k) {
-            const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)k * g.M + row) * rp + 8 * q);
+            const float4* pp = reinterpret_cast<const float4*>(g.P + ((size_t)k * g.M + row) * g.ldt + toff + 8 * q);
             const float4 x0 = pp[0], x1 = pp[1];
             t[0] += x0.x; t[1] += x0.y; t[2] += x0.z; t[3] += x0.w;
             t[4] += x1.x; t[5] += x1.y; t[6] += x1.z; t[7] += x1.w;
           }
         }
         v = uint4{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]), pack_bf16x2(t[4], t[5]), pack_bf16x2(t[6], t[7])};
-        if (blockIdx.x == 0 && g.Tout) *reinterpret_cast<uint4*>(g.Tout + (size_t)row * rp + 8 * q) = v;
+        if (tfirst && g.Tout) *reinterpret_cast<uint4*>(g.Tout + (size_t)row * g.ldt + toff + 8 * q) = v;
       }
       *reinterpret_cast<uint4*>(sT + pc * 8) = v;
     }

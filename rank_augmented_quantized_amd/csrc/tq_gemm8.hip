@@ -341,8 +341,9 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
 #pragma unroll
       for (int a = 0; a < FM; ++a)
         lp[a] = g.L2t + (size_t)min(ch0 + wm * WM + 32 * a + l32, g.N - 1) * g.r_pad + 8 * lg;
+      const int toff = group_of(g.groups, ch0) * g.r_pad;  // this tile's layer
 #pragma unroll
-      for (int b = 0; b < FN; ++b) tp[b] = g.T + (size_t)min(tok(b), g.M - 1) * g.r_pad + 8 * lg;
+      for (int b = 0; b < FN; ++b) tp[b] = g.T + (size_t)min(tok(b), g.M - 1) * g.ldt + toff + 8 * lg;
 #pragma unroll
       for (int q = 0; q < TQ; ++q) {
         const int t0 = min(16 * q, g.r_pad - 16);  // r_pad >= 32: in range

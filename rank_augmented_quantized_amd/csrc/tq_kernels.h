@@ -57,6 +57,23 @@ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
   tn = r / gm;
 }
 
+// Layers that share one input (several weights stacked along the output
+// channels, one activation quantisation and one T for all of them): group g
+// holds channels [gstart[g], gstart[g + 1]), and its T columns start at
+// g * r_pad in rows of ldt.  Every group but the last spans whole 256-channel
+// tiles, so a tile or block never straddles two groups.
+constexpr int kMaxGroups = 8;
+struct Groups {
+  int n;                      // number of groups (1: a single layer)
+  int start[kMaxGroups + 1];  // first channel of each group; start[n] = all channels
+};
+__device__ __forceinline__ int group_of(const Groups& gr, int c) {
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i) g += (i < gr.n && c >= gr.start[i]) ? 1 : 0;
+  return g;
+}
+
 // Arguments of the integer GEMM kernels: C = A B^T over K-contiguous codes.
 struct GemmArgs {
   const uint8_t* A;  // x codes, M rows
@@ -72,11 +89,14 @@ struct GemmArgs {
   const float* sw;   // N scales
   const float* sx2;  // second-segment scales
   const float* sw2;
-  const bf16_t* T;    // M x r_pad (bf16) or null
+  const bf16_t* T;    // M rows of ldt (bf16); a layer's r_pad columns from its group's offset
   const bf16_t* L2t;  // N x r_pad (bf16) or null
-  int r_pad;
-  // small-n path: T comes as nchunk fp32 partials P[c][M][r_pad], summed in
-  // chunk order by the kernel, which also writes the bf16 sum to Tout
+  int r_pad;          // per layer
+  int ldt;            // T row length (r_pad for one layer)
+  Groups groups;
+  // small-n path: T comes as nchunk fp32 partials P[c][M][ldt], summed in
+  // chunk order by the kernel, which also writes the bf16 sum to Tout (the
+  // first block of each group, its columns)
   const float* P;
   int nchunk;
   bf16_t* Tout;
@@ -88,8 +108,9 @@ struct GemmArgs {
 
 hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, void* codes, float* sw,
                               hipStream_t st);
-hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, void* out,
-                               hipStream_t st);
+// L1^T (rows1 rows of d, rows r.. zero) to out1 and L2^T (m x r_pad) to out2, bf16.
+hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, int rows1,
+                               void* out1, void* out2, hipStream_t st);
 hipError_t launch_quant_rows(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
                              float* sa, void* cb, float* sb, hipStream_t st);
 // Work split of the tq_linear prologue (quantisation + T = X L1).
@@ -135,14 +156,16 @@ struct SmallArgs {
   int n, d, m;
   const uint8_t* wc;
   const float* sw;
-  const bf16_t* L1t;
-  const bf16_t* L2t;
-  int r_pad;
+  const bf16_t* L1t;   // ldt rows of d (all groups' L1^T)
+  const bf16_t* L2t;   // m x r_pad
+  int r_pad;           // per layer
+  int ldt;             // columns of T (and of the partials) over all groups
+  Groups groups;
   int nt, nchunk, kc, qs, nqg;
   uint8_t* xc;     // n x d/2 activation codes (written by the first consumer)
   float* sx;       // n scales (idem)
-  float* P;        // nchunk x n x r_pad fp32 partials of X L1
-  bf16_t* Tout;    // n x r_pad: the bf16 T (idem)
+  float* P;        // nchunk x n x ldt fp32 partials of X L1
+  bf16_t* Tout;    // n x ldt: the bf16 T (the first consumer of each group, its columns)
   unsigned* sync;  // hand-off words, kSyncBytes: [0] producers done, [2] wait-limit flag, consumer shard counters
   void* Y;
   int y_bf16;

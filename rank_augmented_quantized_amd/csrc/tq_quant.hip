@@ -84,21 +84,25 @@ __device__ __forceinline__ bf16_t to_bf16<float>(float v) { return (bf16_t)f32_t
 template <>
 __device__ __forceinline__ bf16_t to_bf16<bf16_t>(bf16_t v) { return v; }
 
+// L1^T into rows1 rows of d (rows r.. zero) at out1, L2^T into m rows of
+// r_pad (columns r.. zero) at out2.
 template <typename T>
 __global__ __launch_bounds__(256) void k_pack_lowrank(const T* __restrict__ L1, const T* __restrict__ L2, int d,
-                                                      int m, int r, int r_pad, bf16_t* __restrict__ out) {
-  const size_t n1 = (size_t)r_pad * d, n2 = (size_t)m * r_pad;
+                                                      int m, int r, int r_pad, int rows1, bf16_t* __restrict__ out1,
+                                                      bf16_t* __restrict__ out2) {
+  const size_t n1 = (size_t)rows1 * d, n2 = (size_t)m * r_pad;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * blockDim.x) {
     bf16_t v = 0;
     if (e < n1) {
       const int t = (int)(e / d), k = (int)(e % d);
       if (t < r) v = to_bf16<T>(L1[(size_t)k * r + t]);
+      out1[e] = v;
     } else {
       const size_t e2 = e - n1;
       const int jj = (int)(e2 / r_pad), t = (int)(e2 % r_pad);
       if (t < r) v = to_bf16<T>(L2[(size_t)t * m + jj]);
+      out2[e2] = v;
     }
-    out[e] = v;
   }
 }
 
@@ -527,16 +531,16 @@ hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, 
               : launch_pack_weight_t<float>(W, d, m, bits, codes, sw, st);
 }
 
-hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, void* out,
-                               hipStream_t st) {
-  const size_t total = (size_t)r_pad * d + (size_t)m * r_pad;
+hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, int rows1,
+                               void* out1, void* out2, hipStream_t st) {
+  const size_t total = (size_t)rows1 * d + (size_t)m * r_pad;
   const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
   if (bf16)
     hipLaunchKernelGGL((k_pack_lowrank<bf16_t>), dim3(blocks), dim3(256), 0, st, (const bf16_t*)L1,
-                       (const bf16_t*)L2, d, m, r, r_pad, (bf16_t*)out);
+                       (const bf16_t*)L2, d, m, r, r_pad, rows1, (bf16_t*)out1, (bf16_t*)out2);
   else
     hipLaunchKernelGGL((k_pack_lowrank<float>), dim3(blocks), dim3(256), 0, st, (const float*)L1,
-                       (const float*)L2, d, m, r, r_pad, (bf16_t*)out);
+                       (const float*)L2, d, m, r, r_pad, rows1, (bf16_t*)out1, (bf16_t*)out2);
   return hipGetLastError();
 }
 

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
     const int cols = 16 * qs, col0 = 16 * qg * qs;
     for (int e = tid; e < n * cols; e += NT) {
       const int rr = e / cols, cc = e % cols;
-      st_agent(a.P + ((size_t)c * n + rr) * a.r_pad + col0 + cc, sP[rr * 65 + cc]);
+      st_agent(a.P + ((size_t)c * n + rr) * a.ldt + col0 + cc, sP[rr * 65 + cc]);
     }
     signal_done(a.sync);
     return;
@@ -157,6 +157,9 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
   const int per = (KS + WAVES - 1) / WAVES;
   const int sbeg = wave * per, send = min(KS, sbeg + per);
   const int rp = a.r_pad, rq = rp / 8;
+  const int grp0 = group_of(a.groups, n0);
+  const int toff = grp0 * rp;                           // this block's layer in the partials and T
+  const bool tfirst = n0 == a.groups.start[grp0];      // first consumer of its layer writes T
   const int NP = n * rq;
   const int G = max(1, min(NT / max(NP, 1), max(a.nchunk, 1)));
 
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
       uint4 pv[2][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float* pp = a.P + ((size_t)min(grp + G * j, a.nchunk - 1) * n + row) * rp + 8 * q;
+        const float* pp = a.P + ((size_t)min(grp + G * j, a.nchunk - 1) * n + row) * a.ldt + toff + 8 * q;
         pv[j][0] = ld_agent_u128(pp);
         pv[j][1] = ld_agent_u128(pp + 4);
       }
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
           }
         } else {  // pieces beyond the block's threads (G == 1): all chunks here
           for (int k = 0; k < a.nchunk; ++k) {
-            const float* pp = a.P + ((size_t)k * n + row) * rp + 8 * q;
+            const float* pp = a.P + ((size_t)k * n + row) * a.ldt + toff + 8 * q;
             const uint4 x0 = ld_agent_u128(pp), x1 = ld_agent_u128(pp + 4);
             t[0] += __uint_as_float(x0.x); t[1] += __uint_as_float(x0.y);
             t[2] += __uint_as_float(x0.z); t[3] += __uint_as_float(x0.w);
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
           }
         }
         v = uint4{pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]), pack_bf16x2(t[4], t[5]), pack_bf16x2(t[6], t[7])};
-        if (b == nA && a.Tout) *reinterpret_cast<uint4*>(a.Tout + (size_t)row * rp + 8 * q) = v;
+        if (tfirst && a.Tout) *reinterpret_cast<uint4*>(a.Tout + (size_t)row * a.ldt + toff + 8 * q) = v;
       }
       *reinterpret_cast<uint4*>(sT + pc * 8) = v;
     }

@@ -26,7 +26,8 @@ EXPORTS = (
     "tq_status_string", "tq_version", "tq_codes_bytes", "tq_pack_weight", "tq_lowrank_bytes",
     "tq_pack_lowrank", "tq_quantize_act", "tq_linear_workspace_bytes", "tq_linear_workspace_offsets", "tq_linear",
     "tq_linear_mp_workspace_bytes", "tq_linear_mp", "tq_debug_accumulate", "tq_profile_enable",
-    "tq_profile_read", "tq_profile_reset",
+    "tq_profile_read", "tq_profile_reset", "tq_lowrank_group_bytes", "tq_pack_lowrank_group",
+    "tq_linear_group_workspace_bytes", "tq_linear_group",
 )
 
 
@@ -71,6 +72,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_profile_enable": (st, [c_int]),
         "tq_profile_read": (c_int, [ctypes.POINTER(KernelStat), c_int]),
         "tq_profile_reset": (st, []),
+        "tq_lowrank_group_bytes": (sz, [i64, ptr, i64, i64]),
+        "tq_pack_lowrank_group": (st, [ptr, ptr, c_int, i64, ptr, i64, i64, ptr, ptr]),
+        "tq_linear_group_workspace_bytes": (sz, [i64, i64, ptr, i64, i64]),
+        "tq_linear_group": (st, [ptr, c_int, i64, i64, ptr, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -195,6 +200,54 @@ def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtyp
     _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
                                             _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
                                             _stream(Xrot)))
+    return Y
+
+
+def _i64s(ms):
+    return (ctypes.c_int64 * len(ms))(*[int(v) for v in ms])
+
+
+def tq_lowrank_group_bytes(d: int, ms, r: int) -> int:
+    return load().tq_lowrank_group_bytes(d, _i64s(ms), len(ms), r)
+
+
+def tq_pack_lowrank_group(L1s, L2s, out=None):
+    """Lay out G layers' low-rank factors (L1s[g] d x r, L2s[g] r x m[g]) for tq_linear_group."""
+    lib = load()
+    _need_cuda(*L1s, *L2s)
+    d, r = L1s[0].shape
+    ms = [L2.shape[1] for L2 in L2s]
+    if out is None:
+        out = torch.empty(max(1, tq_lowrank_group_bytes(d, ms, r)), dtype=torch.uint8, device=L1s[0].device)
+    p1 = (ctypes.c_void_p * len(L1s))(*[t.data_ptr() for t in L1s])
+    p2 = (ctypes.c_void_p * len(L2s))(*[t.data_ptr() for t in L2s])
+    _check("tq_pack_lowrank_group", lib.tq_pack_lowrank_group(p1, p2, _dt(L1s[0]), d, _i64s(ms), len(ms), r,
+                                                              _p(out), _stream(L1s[0])))
+    return out
+
+
+def tq_linear_group_workspace_bytes(n: int, d: int, ms, r: int) -> int:
+    return load().tq_linear_group_workspace_bytes(n, d, _i64s(ms), len(ms), r)
+
+
+def linear_group_workspace(n: int, d: int, ms, r: int, device) -> torch.Tensor:
+    """A zero-filled workspace for tq_linear_group."""
+    return torch.zeros(max(1, tq_linear_group_workspace_bytes(n, d, ms, r)), dtype=torch.uint8, device=device)
+
+
+def tq_linear_group(X, w_codes, s_w, lowrank, ms, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
+    """G layers sharing X: w_codes / s_w stacked in channel order (ms[g] channels each); Y n x sum(ms)."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, lowrank, Y, ws)
+    n, d = X.shape
+    mt = int(sum(ms))
+    if Y is None:
+        Y = torch.empty((n, mt), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = linear_group_workspace(n, d, ms, r, X.device)
+    _check("tq_linear_group", lib.tq_linear_group(_p(X), _dt(X), n, d, _i64s(ms), len(ms), r, _p(w_codes),
+                                                  _p(s_w), _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                                  _stream(X)))
     return Y
 
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 100
+    assert lib.tq_version() == 101
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -105,6 +105,45 @@ def test_linear_validation(lib):
     assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, MIS, need, S) == -5
     assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, C, need - 1, S) == -6
     assert lib.tq_linear(A, 1, 0, d, m, r, NUL, NUL, NUL, NUL, 1, NUL, 0, S) == 0
+
+
+def _ms(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_group_size_queries(lib):
+    # gate/up: two layers of r 64 -> T of 128 columns, L2^T of all channels at r_pad 64
+    assert lib.tq_lowrank_group_bytes(4096, _ms(14336, 14336), 2, 64) == (128 * 4096 + 28672 * 64) * 2
+    # three layers of r 32: 96 T columns rounded up to 128
+    assert lib.tq_lowrank_group_bytes(512, _ms(512, 256, 256), 3, 32) == (128 * 512 + 1024 * 32) * 2
+    assert lib.tq_lowrank_group_bytes(512, _ms(300, 256), 2, 32) == 0  # a layer before the last off the 256 grid
+    assert lib.tq_lowrank_group_bytes(512, _ms(256, 300), 2, 32) == (64 * 512 + 556 * 32) * 2
+    assert lib.tq_lowrank_group_bytes(512, _ms(256, 256, 256), 3, 128) == 0  # 3 x 128 T columns > 256
+    assert lib.tq_lowrank_group_bytes(512, _ms(*([256] * 9)), 9, 16) == 0  # more than 8 layers
+    # the workspace of a group is that of one layer as wide as all of them with the group's T width
+    assert lib.tq_linear_group_workspace_bytes(64, 512, _ms(256, 256), 2, 64) == \
+        lib.tq_linear_workspace_bytes(64, 512, 512, 128)
+    assert lib.tq_linear_group_workspace_bytes(64, 512, _ms(256), 1, 16) == lib.tq_linear_workspace_bytes(64, 512, 256, 16)
+
+
+def test_linear_group_validation(lib):
+    n, d, r = 64, 512, 16
+    ms = _ms(256, 512)
+    need = lib.tq_linear_group_workspace_bytes(n, d, ms, 2, r)
+    assert lib.tq_linear_group(A, 1, n, d, ms, 2, r, B, C, A, B, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_group(A, 1, n, d, _ms(200, 256), 2, r, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear_group(A, 1, n, d, ms, 0, r, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear_group(A, 1, n, d, NUL, 2, r, B, C, A, B, 1, C, need, S) == -1
+    assert lib.tq_linear_group(A, 1, n, d, ms, 2, r, B, C, NUL, B, 1, C, need, S) == -1
+    assert lib.tq_linear_group(A, 1, n, d, ms, 2, r, B, C, A, B, 1, MIS, need, S) == -5
+    assert lib.tq_linear_group(A, 2, n, d, ms, 2, r, B, C, A, B, 1, C, need, S) == -3
+    assert lib.tq_linear_group(A, 1, 0, d, ms, 2, r, NUL, NUL, NUL, NUL, 1, NUL, 0, S) == 0
+    L = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    Ln = (ctypes.c_void_p * 2)(0x10000, None)
+    assert lib.tq_pack_lowrank_group(L, L, 1, d, ms, 2, r, MIS, S) == -5
+    assert lib.tq_pack_lowrank_group(L, Ln, 1, d, ms, 2, r, A, S) == -1
+    assert lib.tq_pack_lowrank_group(L, L, 1, d, ms, 2, 0, A, S) == -2
+    assert lib.tq_pack_lowrank_group(L, L, 5, d, ms, 2, r, A, S) == -3
 
 
 def test_linear_mp_validation(lib):

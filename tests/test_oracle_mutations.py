@@ -17,7 +17,7 @@ import test_oracle_pins as pins
 _orig = {name: getattr(tqo, name) for name in (
     "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
     "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
-    "subspace_split")}
+    "subspace_split", "tq_linear_group_ref")}
 
 
 def _q_reciprocal(a, bits=4):
@@ -167,6 +167,23 @@ def _split_swapped(x, w, u, d_hi):
     return x @ ul, x @ uh, ul.T @ w, uh.T @ w
 
 
+def _group_first_l2(x, rs, l1s=None, l2s=None, rows=None, bits=4):
+    # every layer's low-rank product taken with its own L1 but L2 columns of
+    # the first layer cut or padded to its width
+    l2x = [np.resize(l2s[0], l2.shape).astype(np.float32) for l2 in l2s]
+    return _orig["tq_linear_group_ref"](x, rs, l1s, l2x, rows, bits)
+
+
+def _group_reversed(x, rs, l1s=None, l2s=None, rows=None, bits=4):
+    out = _orig["tq_linear_group_ref"](x, rs[::-1], l1s[::-1], l2s[::-1], rows, bits)
+    out["layers"] = out["layers"][::-1]
+    return out
+
+
+def _group_l1_shared(x, rs, l1s=None, l2s=None, rows=None, bits=4):
+    return _orig["tq_linear_group_ref"](x, rs, [l1s[0]] * len(l1s), l2s, rows, bits)
+
+
 MUTANTS = {
     "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
     "quantize_weight": [_w_per_input_channel],
@@ -179,6 +196,7 @@ MUTANTS = {
     "hadamard": [_hadamard_bad],
     "block_rotation": [_rotation_no_norm],
     "subspace_split": [_split_swapped],
+    "tq_linear_group_ref": [_group_first_l2, _group_reversed, _group_l1_shared],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]

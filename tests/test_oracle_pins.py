@@ -351,6 +351,33 @@ def pin_two_subspace_lossless(seed=16):
     assert np.array_equal(tqo.tq_linear_mp_ref(x4, w4, 0)["Y"], tqo.tq_linear_ref(x4, w4)["Y"])
 
 
+def pin_group_stacking(seed=17):
+    """G layers on one X equal one layer whose weight stacks theirs side by side
+    and whose low-rank factors are [L1_0 | L1_1 | ...] and blockdiag(L2_0, L2_1, ...):
+    weight scales are per output channel, and the block-diagonal L2 keeps each
+    layer's T columns to its own channels."""
+    rng = np.random.default_rng(seed)
+    n, d, rk, ms = 6, 48, 3, (5, 7, 4)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    rs = [(0.02 * rng.standard_normal((d, m))).astype(np.float32) for m in ms]
+    l1s = [rng.standard_normal((d, rk)).astype(np.float32) for _ in ms]
+    l2s = [(0.02 * rng.standard_normal((rk, m))).astype(np.float32) for m in ms]
+    grp = tqo.tq_linear_group_ref(x, rs, l1s, l2s)
+    l2bd = np.zeros((rk * len(ms), sum(ms)), np.float32)
+    c0 = 0
+    for g, m in enumerate(ms):
+        l2bd[rk * g:rk * (g + 1), c0:c0 + m] = l2s[g]
+        c0 += m
+    one = tqo.tq_linear_ref(x, np.concatenate(rs, axis=1), np.concatenate(l1s, axis=1), l2bd)
+    assert np.array_equal(grp["codes_x"], one["codes_x"]) and np.array_equal(grp["s_x"], one["s_x"])
+    assert np.array_equal(np.concatenate([o["codes_w"] for o in grp["layers"]]), one["codes_w"])
+    assert np.array_equal(np.concatenate([o["acc"] for o in grp["layers"]], axis=1), one["acc"])
+    assert np.allclose(grp["Y"], one["Y"], rtol=1e-12, atol=1e-12 * np.abs(one["Y"]).max())
+    # one layer alone is the plain layer
+    assert np.array_equal(tqo.tq_linear_group_ref(x, rs[:1], l1s[:1], l2s[:1])["Y"],
+                          tqo.tq_linear_ref(x, rs[0], l1s[0], l2s[0])["Y"])
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -366,6 +393,7 @@ ALL_PINS = [
     pin_hadamard,
     pin_rotation_identities,
     pin_two_subspace_lossless,
+    pin_group_stacking,
 ]
 
 

@@ -10,6 +10,8 @@ from .synth import (  # noqa: F401
     Workload,
     draw_linear,
     draw_custom,
+    draw_group,
+    draw_group_custom,
     draw_two_subspace,
     draw_two_subspace_custom,
     to_bf16_values,

@@ -169,6 +169,37 @@ def draw_linear(wl: Workload | str, n: int | None = None, outliers: bool = True)
     return case
 
 
+def draw_group_custom(n, d, ms, r, seed, x_kind="normal", x_dtype="bf16", outlier_count=0,
+                      outlier_scale=1.0, outliers=True):
+    """G layers on one input: X as ``draw_custom(seed)``; layer g's R, L1, L2
+    (d x ms[g], d x r, r x ms[g]) from the weight streams of the sequence
+    seeded ``seed + 7919 g`` (layer 0: the same weights as ``draw_custom``)."""
+    s = _streams(seed)
+    x, chans = _draw_x(s[0], s[1], n, d, x_kind, x_dtype, outlier_count, outlier_scale, outliers)
+    rs, l1s, l2s = [], [], []
+    for g, m in enumerate(ms):
+        sg = _streams(seed + 7919 * g)
+        r_w, l1, l2 = _draw_weights(sg[2], sg[3], sg[4], d, m, r)
+        rs.append(r_w)
+        l1s.append(l1)
+        l2s.append(l2)
+    return {"X": x, "Rs": rs, "L1s": l1s, "L2s": l2s, "outlier_channels": chans}
+
+
+def draw_group(wl: "Workload | str", n: int | None = None, groups: int = 2, outliers: bool = True):
+    """Inputs of ``groups`` layers of a workload's shape sharing its X (gate and
+    up of an MLP), X sliced to the first ``n`` tokens."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    case = draw_group_custom(wl.n, wl.d, [wl.m] * groups, wl.r, wl.seed, wl.x_kind, wl.x_dtype,
+                             wl.outlier_count, wl.outlier_scale, outliers)
+    if n is not None:
+        if n > wl.n:
+            raise ValueError(f"n={n} exceeds the drawn {wl.n} tokens")
+        case["X"] = np.ascontiguousarray(case["X"][:n])
+    return case
+
+
 def _sylvester(k: int) -> np.ndarray:
     h = np.ones((1, 1), dtype=np.float64)
     while h.shape[0] < k:

@@ -13,7 +13,8 @@ HBM.  Prints ONE JSON line (stdout); progress goes to stderr.
             MI355X dense int8 MFMA peak (5.0 POP/s)
   cpu_baseline  the CPU oracle on the same workload (a bounded sample)
   sweep     the other workloads (decode rows against the 8 TB/s HBM peak,
-            also with the calls captured in a HIP graph and replayed)
+            also with the calls captured in a HIP graph and replayed), and
+            gate and up as one grouped call next to two separate calls
 """
 
 from __future__ import annotations
@@ -148,6 +149,48 @@ class LinearCase:
         return e0.elapsed_time(e1) / (replays * len(self.w))
 
 
+class GroupCase:
+    """Layers of one workload's shape that share X (gate and up), as one tq_linear_group call and, for
+    comparison, as one tq_linear call per layer on the same device data; `copies` weight sets cycled."""
+
+    def __init__(self, wl, n, groups, copies, torch, tq, dev):
+        from workloads import draw_group
+
+        c = draw_group(wl, n=n, groups=groups)
+        self.n, self.d, self.m, self.r, self.G = n, wl.d, wl.m, wl.r, groups
+        self.ms = [wl.m] * groups
+        self.X = torch.from_numpy(c["X"]).to(dev).bfloat16()
+        Rs = [torch.from_numpy(a).to(dev) for a in c["Rs"]]
+        L1s = [torch.from_numpy(a).to(dev).bfloat16() for a in c["L1s"]]
+        L2s = [torch.from_numpy(a).to(dev).bfloat16() for a in c["L2s"]]
+        self.w = []
+        for _ in range(copies):
+            packed = [tq.tq_pack_weight(R, 4) for R in Rs]
+            wc = torch.cat([p[0] for p in packed], dim=0).contiguous()
+            sw = torch.cat([p[1] for p in packed]).contiguous()
+            del packed
+            lr = tq.tq_pack_lowrank_group(L1s, L2s)
+            lrs = [tq.tq_pack_lowrank(L1s[g], L2s[g]) for g in range(groups)]
+            self.w.append((wc, sw, lr, lrs))
+        del Rs
+        self.Y = torch.empty((n, groups * wl.m), dtype=torch.bfloat16, device=dev)
+        self.Ys = [torch.empty((n, wl.m), dtype=torch.bfloat16, device=dev) for _ in range(groups)]
+        self.ws = tq.linear_group_workspace(n, wl.d, self.ms, wl.r, dev)
+        self.ws1 = tq.linear_workspace(n, wl.d, wl.m, wl.r, dev)
+        self.tq = tq
+
+    def __call__(self, i):
+        wc, sw, lr, _ = self.w[i % len(self.w)]
+        self.tq.tq_linear_group(self.X, wc, sw, lr, self.ms, self.r, Y=self.Y, ws=self.ws)
+
+    def separate(self, i):
+        wc, sw, _, lrs = self.w[i % len(self.w)]
+        m = self.m
+        for g in range(self.G):
+            self.tq.tq_linear(self.X, wc[g * m:(g + 1) * m], sw[g * m:(g + 1) * m], lrs[g], m, self.r,
+                              Y=self.Ys[g], ws=self.ws1)
+
+
 class MpCase:
     def __init__(self, wl, torch, tq, dev):
         from workloads import draw_two_subspace
@@ -277,6 +320,24 @@ def main():
                 log(f"[bench] sweep {row}")
                 del c
                 torch.cuda.empty_cache()
+        w = WORKLOADS["mlp_gate_up"]
+        for nn in (1, 16, 4096):
+            c = GroupCase(w, nn, 2, args.copies if nn <= 256 else 2, torch, tq, dev)
+            steps = max(20, args.steps // 2)
+            t = time_calls(c, steps, 10, torch)
+            t_sep = time_calls(c.separate, steps, 10, torch)
+            # X once; each layer's codes, scales, L1, L2 and its Y
+            b = nn * w.d * 2 + 2 * (w.d * w.m // 2 + 4 * w.m + 2 * w.d * w.r + 2 * w.r * w.m + 2 * nn * w.m)
+            o = 2.0 * nn * w.d * 2 * w.m
+            row = {"workload": f"{w.title}: gate and up as one group", "n": nn, "us": round(t * 1e3, 2),
+                   "separate_us": round(t_sep * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
+                   "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                   "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                   "pct_hbm": round(100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+            sweep.append(row)
+            log(f"[bench] sweep {row}")
+            del c
+            torch.cuda.empty_cache()
         w = WORKLOADS["two_subspace"]
         log(f"[bench] {w.title}: building inputs")
         c = MpCase(w, torch, tq, dev)

@@ -319,9 +319,9 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   g.r_pad = rp;
   g.ldt = L.r_pad;
   g.groups = groups;
-  if (L.r_pad && L.plan.partial) {
+  if (L.r_pad && (L.plan.partial || L.plan.sum_to_p0)) {
     g.P = P;
-    g.nchunk = L.plan.nchunk;
+    g.nchunk = L.plan.partial ? L.plan.nchunk : 1;
     g.Tout = T;
   }
   g.Y = Y;

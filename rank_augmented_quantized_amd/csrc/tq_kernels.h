@@ -118,6 +118,7 @@ struct ProloguePlan {
   int kc, nchunk, qs, nqg, ntb, nqb, counters, waves;
   bool quant_in_prologue;
   bool partial;     // T left as fp32 partials per k-chunk (small-n path)
+  bool sum_to_p0;   // small-n path with more chunks than the GEMM sums: the fp32 sum left in chunk 0
   bool row_blocks;  // quantise one row per block (few tokens)
   bool fused;       // many tokens: one pass over X makes codes, s_x and T (16-row blocks)
 };

@@ -380,6 +380,7 @@ struct PrologueArgs {
   int n, d;
   const bf16_t* L1t;
   int r_pad, kc, nchunk, qs, nqg, nqb, partial, row_blocks;
+  int sum_to_p0;  // the last block also leaves the fp32 sum of the chunks in chunk 0 of P
   uint8_t* xc;
   float* sx;
   float* P;
@@ -507,6 +508,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
         if (k0 + k < nc) sum += part[k];
     }
     a.T[(size_t)(16 * rt + rr) * a.r_pad + col0 + cc] = (bf16_t)f32_to_bf16_bits(sum);
+    // chunk 0 of this element was read above by this thread only
+    if (a.sum_to_p0) __hip_atomic_store(const_cast<float*>(pp), sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -795,6 +798,8 @@ static hipError_t launch_prologue_fused(const void* X, bool bf16, int n, int d, 
 
 // Fewest tokens for the fused prologue.
 constexpr int kFusedMinRows = 1024;
+// Most k-chunks of T the few-token prologue sums itself.
+constexpr int kMaxPrologueChunks = 64;
 
 ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) {
   ProloguePlan p{};
@@ -815,11 +820,16 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) 
     // is read by many CUs at once; fp32 partials per k-chunk, summed there
     p.qs = std::min(nq, 4);
     p.nqg = nq / p.qs;
-    const int nch = std::max(1, std::min((steps + 15) / 16, max_chunks));
+    const int want = std::max(1, (steps + 15) / 16);
+    // long rows with several row tiles want more chunks than the small-n
+    // GEMM sums in one pass: then the last block of each (row tile, slice
+    // group) sums them here and leaves the fp32 sum in chunk 0
+    const int nch = want <= max_chunks ? want : std::min(want, kMaxPrologueChunks);
     const int chunk_steps = (steps + nch - 1) / nch;
     p.kc = 32 * chunk_steps;
     p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
-    p.partial = true;
+    p.partial = p.nchunk <= max_chunks;
+    p.sum_to_p0 = !p.partial;
     p.ntb = nrt * p.nchunk * p.nqg;
   } else {
     // QS 16-column slices of T per block (all of them in one block when rows
@@ -902,7 +912,7 @@ hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L
     if (p.ntb == 0) return hipSuccess;
   }
   PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, p.nqb, p.partial ? 1 : 0,
-                 p.row_blocks ? 1 : 0, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters};
+                 p.row_blocks ? 1 : 0, p.sum_to_p0 ? 1 : 0, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters};
   const int ch = std::min(chunks_for(d), 32);
   return bf16 ? launch_prologue_t<bf16_t>(a, p.waves, ch, st) : launch_prologue_t<float>(a, p.waves, ch, st);
 }

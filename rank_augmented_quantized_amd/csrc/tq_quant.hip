@@ -660,7 +660,7 @@ __host__ __device__ constexpr int fused_lds_bytes(int d, int qs) {
 template <typename T, int CH, int QS>
 __global__ __launch_bounds__(1024) void k_prologue_rows(FusedArgs a) {
   constexpr int WAVES = kFusedWaves, COLS = 16 * QS;
-  constexpr int U = QS <= 2 ? 4 : (QS <= 4 ? 2 : 1);  // L1 steps fetched ahead
+  constexpr int U = QS <= 2 ? 8 : (QS <= 4 ? 4 : 1);  // L1 steps fetched ahead
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int d = a.d, nch = d >> 3, XS = fused_row_bytes(d);

@@ -278,6 +278,49 @@ def block_rotation(signs, block: int, perm=None) -> np.ndarray:
     return u
 
 
+def rht_rows(x, signs, perm, block: int = 128):
+    """The rotation X' = X U of ``block_rotation(signs, block, perm)`` evaluated
+    online in fp32, as the fused quantiser does it (the randomised Hadamard
+    transform of "Quantizing With Randomized Hadamard Transforms: Efficient
+    Heuristic Now Proven", in the block form of the CoQuant rotation after
+    Eq. 3):
+
+      v = x * signs                                  (exact: signs are +-1)
+      for h = 1, 2, 4, ..., block / 2, within every block of ``block`` columns:
+          (v[i], v[i + h]) <- (v[i] + v[i + h], v[i] - v[i + h])   for i with bit h clear
+      v = v * fl32(1 / sqrt(block))
+      X'[:, j] = v[:, perm[j]]
+
+    Every step is one correctly rounded fp32 operation in this order (the
+    fast Walsh-Hadamard transform, natural order, spans increasing), so the
+    result is a definite fp32 array that the device reproduces bit for bit.
+    """
+    v = np.asarray(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)[None, :]
+    n, d = v.shape
+    if d % block or block & (block - 1):
+        raise ValueError("d must be a multiple of a power-of-two block")
+    v = v.reshape(n, d // block, block).copy()
+    h = 1
+    while h < block:
+        w = v.reshape(n, d // block, block // (2 * h), 2, h)
+        a, b = w[:, :, :, 0, :].copy(), w[:, :, :, 1, :].copy()
+        w[:, :, :, 0, :] = a + b
+        w[:, :, :, 1, :] = a - b
+        h *= 2
+    v = v.reshape(n, d) * np.float32(1.0 / math.sqrt(block))
+    return np.ascontiguousarray(v[:, np.asarray(perm)], dtype=np.float32)
+
+
+def tq_linear_mp_rht_ref(x, signs, perm, wrot, d_hi: int, block: int = 128, rows=None, cols=None):
+    """Two-subspace output (CoQuant Eq. 9) on unrotated X: the rotation of
+    ``rht_rows`` in fp32, then ``tq_linear_mp_ref`` on X' (W' = U^T W is
+    rotated offline and given)."""
+    x = np.asarray(x, dtype=np.float32)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    return tq_linear_mp_ref(rht_rows(x, signs, perm, block), wrot, d_hi, cols=cols)
+
+
 def rotate(x, w, u):
     """Rotation invariance (CoQuant Eq. 3): returns (X U, U^T W), fp64."""
     u = np.asarray(u, dtype=np.float64)

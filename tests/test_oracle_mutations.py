@@ -17,7 +17,7 @@ import test_oracle_pins as pins
 _orig = {name: getattr(tqo, name) for name in (
     "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
     "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
-    "subspace_split", "tq_linear_group_ref")}
+    "subspace_split", "tq_linear_group_ref", "rht_rows")}
 
 
 def _q_reciprocal(a, bits=4):
@@ -184,6 +184,45 @@ def _group_l1_shared(x, rs, l1s=None, l2s=None, rows=None, bits=4):
     return _orig["tq_linear_group_ref"](x, rs, [l1s[0]] * len(l1s), l2s, rows, bits)
 
 
+def _rht_sub_swapped(x, signs, perm, block=128):
+    # butterfly difference taken the other way round: (v[i + h] - v[i])
+    return _rht_generic(x, signs, perm, block, flip=True)
+
+
+def _rht_generic(x, signs, perm, block=128, flip=False, inverse_perm=False, scale=None, signs_after=False):
+    v = np.asarray(x, dtype=np.float32)
+    if not signs_after:
+        v = v * np.asarray(signs, dtype=np.float32)[None, :]
+    n, d = v.shape
+    v = v.reshape(n, d // block, block).copy()
+    h = 1
+    while h < block:
+        w = v.reshape(n, d // block, block // (2 * h), 2, h)
+        a, b = w[:, :, :, 0, :].copy(), w[:, :, :, 1, :].copy()
+        w[:, :, :, 0, :] = a + b
+        w[:, :, :, 1, :] = (b - a) if flip else (a - b)
+        h *= 2
+    v = v.reshape(n, d) * np.float32(scale if scale is not None else 1.0 / np.sqrt(block))
+    if signs_after:
+        v = v * np.asarray(signs, dtype=np.float32)[None, :]
+    p = np.asarray(perm)
+    if inverse_perm:
+        p = np.argsort(p)
+    return np.ascontiguousarray(v[:, p], dtype=np.float32)
+
+
+def _rht_inverse_perm(x, signs, perm, block=128):
+    return _rht_generic(x, signs, perm, block, inverse_perm=True)
+
+
+def _rht_scale_by_block(x, signs, perm, block=128):
+    return _rht_generic(x, signs, perm, block, scale=1.0 / block)
+
+
+def _rht_signs_after(x, signs, perm, block=128):
+    return _rht_generic(x, signs, perm, block, signs_after=True)
+
+
 MUTANTS = {
     "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
     "quantize_weight": [_w_per_input_channel],
@@ -197,6 +236,7 @@ MUTANTS = {
     "block_rotation": [_rotation_no_norm],
     "subspace_split": [_split_swapped],
     "tq_linear_group_ref": [_group_first_l2, _group_reversed, _group_l1_shared],
+    "rht_rows": [_rht_sub_swapped, _rht_inverse_perm, _rht_scale_by_block, _rht_signs_after],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]

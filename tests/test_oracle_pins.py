@@ -378,6 +378,56 @@ def pin_group_stacking(seed=17):
                           tqo.tq_linear_ref(x, rs[0], l1s[0], l2s[0])["Y"])
 
 
+def pin_rht_rows(seed=18):
+    """The fp32 online rotation: exact on small integers (each butterfly and
+    the final single rounding), within fp32 error of X U from the dense fp64
+    basis, and H H = block I for the unscaled butterflies."""
+    rng = np.random.default_rng(seed)
+    n, d, block = 5, 512, 128
+    signs = np.where(rng.integers(0, 2, size=d) == 1, 1.0, -1.0)
+    perm = rng.permutation(d)
+    # small integers: every butterfly sum is exact, so X' = fl32(fl32(H (x signs)) / sqrt(block) as fl32) exactly
+    xi = rng.integers(-50, 51, size=(n, d)).astype(np.float32)
+    h = tqo.hadamard(block)
+    exact = np.concatenate([(xi[:, b:b + block].astype(np.int64) * signs[b:b + block].astype(np.int64)) @ h
+                            for b in range(0, d, block)], axis=1)
+    want = (exact.astype(np.float32) * np.float32(1.0 / np.sqrt(block)))[:, perm]
+    assert np.array_equal(tqo.rht_rows(xi, signs, perm, block), want)
+    # generic values: close to the fp64 dense rotation of block_rotation
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    u = tqo.block_rotation(signs, block, perm)
+    ref = x.astype(np.float64) @ u
+    got = tqo.rht_rows(x, signs, perm, block).astype(np.float64)
+    tol = 8 * np.finfo(np.float32).eps * np.sqrt(block) * np.abs(x).max()
+    assert np.abs(got - ref).max() <= tol
+    # H H = block I: the transform applied twice (signs +1, identity permutation) gives x back
+    ones, ident = np.ones(d), np.arange(d)
+    twice = tqo.rht_rows(tqo.rht_rows(xi, ones, ident, block), ones, ident, block)
+    assert np.allclose(twice, xi, rtol=1e-6, atol=1e-4)
+
+
+def pin_rht_layer_rotation_invariance(seed=19):
+    """The two-subspace layer on unrotated X with the rotation done online
+    equals X W up to the quantisers' error (CoQuant Eq. 3: (XU)(U^T W) = XW);
+    at d_hi = d both sides are 8-bit, so the error is small."""
+    rng = np.random.default_rng(seed)
+    n, d, m, block = 6, 256, 40, 128
+    signs = np.where(rng.integers(0, 2, size=d) == 1, 1.0, -1.0)
+    perm = rng.permutation(d)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((d, m))).astype(np.float32)
+    u = tqo.block_rotation(signs, block, perm)
+    wrot = (u.T @ w.astype(np.float64)).astype(np.float32)
+    ref = x.astype(np.float64) @ w.astype(np.float64)
+    for d_hi, tol in ((d, 2e-2), (128, 3.5e-1)):  # half the dimensions at 4 bits: a loose bound
+        y = tqo.tq_linear_mp_rht_ref(x, signs, perm, wrot, d_hi, block)["Y"]
+        assert np.abs(y - ref).max() <= tol * np.abs(ref).max(), d_hi
+    # the same codes as the pre-rotated layer fed with the fp32 rotated X
+    out = tqo.tq_linear_mp_rht_ref(x, signs, perm, wrot, 128, block)
+    pre = tqo.tq_linear_mp_ref(tqo.rht_rows(x, signs, perm, block), wrot, 128)
+    assert np.array_equal(out["codes_xl"], pre["codes_xl"]) and np.array_equal(out["codes_xh"], pre["codes_xh"])
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -394,6 +444,8 @@ ALL_PINS = [
     pin_rotation_identities,
     pin_two_subspace_lossless,
     pin_group_stacking,
+    pin_rht_rows,
+    pin_rht_layer_rotation_invariance,
 ]
 
 

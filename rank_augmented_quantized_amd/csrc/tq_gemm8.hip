@@ -464,7 +464,9 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
               asm volatile("" : "+v"(acc2));
 #pragma unroll
               for (int st = 0; st < 4; ++st) {
-                if (k0 + 32 * st < K2) {
+                // steps 2 p and 2 p + 1 together cover the 64 k from k0 + 64 p
+                // (interleaved chunks); chunks past K2 were fetched as zeros
+                if (k0 + 64 * (st >> 1) < K2) {
                   // weight rows wm WM + 32 a + l32 have the swizzle of token rows wn WN + l32
                   const i32x4 av = *reinterpret_cast<const i32x4*>(smem + (fb[st] - WPL) +
                                                                    (wm * WM - wn * WN + 32 * a) * 128);

@@ -428,11 +428,13 @@ def _run_mp(xrot, wrot, d_hi):
 
 @pytest.mark.parametrize("n,d,m,dh", [(40, 512, 96, 64), (130, 1024, 272, 128), (16, 256, 64, 0),
                                       (70, 256, 80, 256), (9, 8192, 48, 128), (70, 1024, 80, 512),
-                                      (300, 1024, 200, 384), (512, 1024, 28672, 512), (512, 1024, 28672, 128)])
+                                      (300, 1024, 200, 384), (512, 1024, 28672, 512), (512, 1024, 28672, 128),
+                                      (1, 128, 32, 32), (40, 560, 96, 48), (70, 1056, 80, 32), (33, 608, 64, 96)])
 def test_linear_mp_small(n, d, m, dh):
-    """Ragged tails; high subspaces of 0 .. 512 columns; the 256 x 256 tile (n = 512, m = 28672)."""
+    """Ragged tails; high subspaces of 0 .. 512 columns, including widths that are not a multiple of 64; the
+    256 x 256 tile (n = 512, m = 28672)."""
     print(f"case mp n={n} d={d} m={m} d_hi={dh}", flush=True)
-    c = draw_two_subspace_custom(n, d, m, dh, seed=n + d + m, outlier_count=2)
+    c = draw_two_subspace_custom(n, d, m, dh, seed=n + d + m, outlier_count=2, block=128 if d % 128 == 0 else 16)
     y = _run_mp(c["Xrot"], c["Wrot"], dh)
     rows, cols = (None, None) if m < 4096 else _sample(n, m, np.random.default_rng(n), 64, 512)
     ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], dh, rows=rows, cols=cols)

@@ -236,6 +236,49 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
                        hipStream_t stream);
 
 /*
+ * Byte offsets inside the tq_linear_mp (and tq_linear_mp_rht) workspace:
+ *   off[0] s_x of the 4-bit subspace (n fp32), off[1] s_x of the 8-bit
+ *   subspace (n fp32), off[2] the 4-bit codes (n x (d - d_hi) bytes, one int8
+ *   per code, per 8 columns the 4 even then the 4 odd ones), off[3] the
+ *   8-bit codes (n x d_hi int8).  TQ_ERR_SHAPE / TQ_ERR_NULL on bad arguments.
+ */
+tq_status tq_linear_mp_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[4]);
+
+/*
+ * Online rotation (CoQuant notes, the randomised block-Hadamard rotation after
+ * Eq. 3; "Quantizing With Randomized Hadamard Transforms: Efficient
+ * Heuristic Now Proven"): U = diag(signs) . blockdiag(H_128) / sqrt(128) . P,
+ * X' = X U with X'[:, j] = (X diag(signs) blockdiag(H_128) / sqrt(128))[:, perm[j]].
+ * d must be a multiple of 128 and at most 8192.
+ */
+
+/* Bytes of the packed rotation of tq_pack_rht (0 for unsupported d). */
+size_t tq_rht_bytes(int64_t d);
+
+/*
+ * tq_pack_rht -- lays out a rotation for tq_linear_mp_rht (offline).
+ *   signs  d fp32 values, +-1 (negative means -1).
+ *   perm   d int32: a permutation of 0 .. d-1 (position j takes rotated
+ *          coordinate perm[j]); for anything else the layer's output is
+ *          unspecified (no access leaves the buffers).
+ *   rot    out: tq_rht_bytes(d) bytes.
+ */
+tq_status tq_pack_rht(const float* signs, const int32_t* perm, int64_t d, void* rot, hipStream_t stream);
+
+/*
+ * tq_linear_mp_rht -- tq_linear_mp on unrotated X (n x d, x_dt): the rotation
+ * (from tq_pack_rht) is applied to every token row in fp32 inside the
+ * quantiser -- butterflies of increasing span, each (a + b, a - b), then one
+ * multiply by fl32(1 / sqrt(128)) -- and X' is never stored.  The weights are
+ * those of tq_linear_mp for the rotated weight U^T W.  Workspace and errors as
+ * tq_linear_mp, plus TQ_ERR_SHAPE for d outside the rotation's range.
+ */
+tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi,
+                           const void* rot, int64_t m, const void* wl_codes, const float* s_wl,
+                           const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
  * tq_debug_accumulate -- exact integer product of two code matrices, exported.
  *   x_codes  n x k codes, w_codes m x k codes (both bits wide, K-contiguous).
  *   acc      out: n x m int32, acc[i][j] = sum_t x[i][t] * w[j][t], exactly.

@@ -15,12 +15,15 @@ from .tq import (  # noqa: F401
     tq_linear_group,
     tq_linear_group_workspace_bytes,
     tq_linear_mp,
+    tq_linear_mp_rht,
     tq_linear_mp_workspace_bytes,
+    tq_linear_mp_workspace_offsets,
     tq_linear_workspace_bytes,
     tq_linear_workspace_offsets,
     tq_lowrank_group_bytes,
     tq_pack_lowrank,
     tq_pack_lowrank_group,
+    tq_pack_rht,
     tq_pack_weight,
     tq_profile_enable,
     tq_profile_read,

@@ -190,7 +190,7 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 101; }
+int tq_version(void) { return 102; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
   if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
@@ -445,38 +445,35 @@ size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi) {
   return mp_ws(n, d, d_hi).total;
 }
 
-tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
-                       const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
-                       tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the two-subspace layer (X is Xrot, or unrotated X with rot).
+tq_status mp_check(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_codes,
+                   const float* s_wl, const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws) {
   if (!valid_dtype(x_dt) || !valid_dtype(y_dt)) return TQ_ERR_DTYPE;
   const int64_t dl = d - d_hi;
   if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || m <= 0 || m > kMaxDim || d_hi < 0 || d_hi > d || dl % 32 ||
       d_hi % 16)
     return TQ_ERR_SHAPE;
   if (n == 0) return TQ_OK;
-  if (!Xrot || !Y || !ws || (dl > 0 && (!wl_codes || !s_wl)) || (d_hi > 0 && (!wh_codes || !s_wh)))
-    return TQ_ERR_NULL;
-  if (!aligned16(Xrot) || !aligned16(Y) || !aligned16(ws) || (dl > 0 && (!aligned16(wl_codes) || !aligned16(s_wl))) ||
+  if (!X || !Y || !ws || (dl > 0 && (!wl_codes || !s_wl)) || (d_hi > 0 && (!wh_codes || !s_wh))) return TQ_ERR_NULL;
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || (dl > 0 && (!aligned16(wl_codes) || !aligned16(s_wl))) ||
       (d_hi > 0 && (!aligned16(wh_codes) || !aligned16(s_wh))))
     return TQ_ERR_ALIGN;
-  const MpWs W = mp_ws(n, d, d_hi);
-  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
-  uint8_t* base = (uint8_t*)ws;
+  return TQ_OK;
+}
+
+// The two-subspace GEMM on the codes and scales in the workspace.
+tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_codes, const float* s_wl,
+                  const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, const MpWs& W, uint8_t* base,
+                  hipStream_t stream) {
+  const int64_t dl = d - d_hi;
   float* sxl = (float*)(base + W.sxl);
   float* sxh = (float*)(base + W.sxh);
   uint8_t* xl = base + W.xl;
   uint8_t* xh = base + W.xh;
-  const bool xb = x_dt == TQ_BF16;
-  if (dl > 0 && d_hi > 0) {
-    TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)dl, 8, xl, sxl, xh, sxh, stream));
-  } else if (dl > 0) {
-    TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)d, 4, xl, sxl, nullptr, nullptr, stream));
-  } else {
-    TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
-  }
   GemmArgs g{};
   g.M = (int)n;
   g.N = (int)m;
@@ -500,6 +497,79 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   g.sw2 = s_wh;
   TQ_RUN("gemm_mp", stream, tq::launch_gemm8(g, tq::EPI_MP, true, 4, stream));
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                       const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
+                       tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  const int64_t dl = d - d_hi;
+  const MpWs W = mp_ws(n, d, d_hi);
+  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  float* sxl = (float*)(base + W.sxl);
+  float* sxh = (float*)(base + W.sxh);
+  uint8_t* xl = base + W.xl;
+  uint8_t* xh = base + W.xh;
+  const bool xb = x_dt == TQ_BF16;
+  if (dl > 0 && d_hi > 0) {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)dl, 8, xl, sxl, xh, sxh, stream));
+  } else if (dl > 0) {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)d, 4, xl, sxl, nullptr, nullptr, stream));
+  } else {
+    TQ_RUN("quant_rows_mp", stream,
+           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
+  }
+  return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
+}
+
+tq_status tq_linear_mp_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[4]) {
+  if (n < 0 || d <= 0 || d_hi < 0 || d_hi > d) return TQ_ERR_SHAPE;
+  if (!off) return TQ_ERR_NULL;
+  const MpWs W = mp_ws(n, d, d_hi);
+  off[0] = W.sxl;
+  off[1] = W.sxh;
+  off[2] = W.xl;
+  off[3] = W.xh;
+  return TQ_OK;
+}
+
+size_t tq_rht_bytes(int64_t d) {
+  if (d <= 0 || d % 128 || d > tq::kRhtMaxD) return 0;
+  return tq::rht_bytes((int)d);
+}
+
+tq_status tq_pack_rht(const float* signs, const int32_t* perm, int64_t d, void* rot, hipStream_t stream) {
+  if (d <= 0 || d % 128 || d > tq::kRhtMaxD) return TQ_ERR_SHAPE;
+  if (!signs || !perm || !rot) return TQ_ERR_NULL;
+  if (!aligned16(rot)) return TQ_ERR_ALIGN;
+  TQ_RUN("pack_rht", stream, tq::launch_pack_rht(signs, perm, (int)d, rot, stream));
+  return TQ_OK;
+}
+
+tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, const void* rot,
+                           int64_t m, const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh,
+                           void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const tq_status st = mp_check(X, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
+  if (st != TQ_OK) return st;
+  if (d % 128 || d > tq::kRhtMaxD) return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!rot) return TQ_ERR_NULL;
+  if (!aligned16(rot)) return TQ_ERR_ALIGN;
+  const MpWs W = mp_ws(n, d, d_hi);
+  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  TQ_RUN("quant_rows_rht", stream,
+         tq::launch_quant_rows_rht(X, x_dt == TQ_BF16, (int)n, (int)d, (int)(d - d_hi), rot, base + W.xl,
+                                   (float*)(base + W.sxl), base + W.xh, (float*)(base + W.sxh), stream));
+  return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
 }
 
 tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m, int bits,

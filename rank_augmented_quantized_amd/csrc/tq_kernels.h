@@ -172,6 +172,18 @@ struct SmallArgs {
   int y_bf16;
 };
 constexpr int kSyncBytes = 4096;  // workspace bytes of the hand-off words
+
+// Online block-Hadamard rotation of the two-subspace quantiser: the packed
+// rotation holds the int8 signs (d bytes) and then, for each rotated
+// coordinate, its output position (uint16).  d % 128 == 0, d <= kRhtMaxD.
+constexpr int kRhtMaxD = 8192;
+__host__ __device__ constexpr size_t rht_signs_bytes(int d) { return ((size_t)d + 15) & ~(size_t)15; }
+__host__ __device__ constexpr size_t rht_bytes(int d) { return rht_signs_bytes(d) + (((size_t)d * 2 + 15) & ~(size_t)15); }
+hipError_t launch_pack_rht(const float* signs, const int32_t* perm, int d, void* rot, hipStream_t st);
+// X (n x d) rotated online and quantised: columns [0, dl) of X' at 4 bits as
+// int8 in the tile GEMM's order (dl bytes per row), [dl, d) at 8 bits.
+hipError_t launch_quant_rows_rht(const void* X, bool bf16, int n, int d, int dl, const void* rot, void* xl,
+                                 float* sxl, void* xh, float* sxh, hipStream_t st);
 bool small_fused_ok(int n, int d, int r_pad);
 SmallPlan plan_small(int n, int d, int r_pad);
 hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);

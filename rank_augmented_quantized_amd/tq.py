@@ -27,7 +27,8 @@ EXPORTS = (
     "tq_pack_lowrank", "tq_quantize_act", "tq_linear_workspace_bytes", "tq_linear_workspace_offsets", "tq_linear",
     "tq_linear_mp_workspace_bytes", "tq_linear_mp", "tq_debug_accumulate", "tq_profile_enable",
     "tq_profile_read", "tq_profile_reset", "tq_lowrank_group_bytes", "tq_pack_lowrank_group",
-    "tq_linear_group_workspace_bytes", "tq_linear_group",
+    "tq_linear_group_workspace_bytes", "tq_linear_group", "tq_linear_mp_workspace_offsets", "tq_rht_bytes",
+    "tq_pack_rht", "tq_linear_mp_rht",
 )
 
 
@@ -76,6 +77,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_pack_lowrank_group": (st, [ptr, ptr, c_int, i64, ptr, i64, i64, ptr, ptr]),
         "tq_linear_group_workspace_bytes": (sz, [i64, i64, ptr, i64, i64]),
         "tq_linear_group": (st, [ptr, c_int, i64, i64, ptr, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
+        "tq_linear_mp_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "tq_rht_bytes": (sz, [i64]),
+        "tq_pack_rht": (st, [ptr, ptr, i64, ptr, ptr]),
+        "tq_linear_mp_rht": (st, [ptr, c_int, i64, i64, i64, ptr, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz,
+                                  ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -248,6 +254,40 @@ def tq_linear_group(X, w_codes, s_w, lowrank, ms, r: int, y_dtype=torch.bfloat16
     _check("tq_linear_group", lib.tq_linear_group(_p(X), _dt(X), n, d, _i64s(ms), len(ms), r, _p(w_codes),
                                                   _p(s_w), _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(),
                                                   _stream(X)))
+    return Y
+
+
+def tq_linear_mp_workspace_offsets(n: int, d: int, d_hi: int) -> dict:
+    """Byte offsets of the two subspaces' scales and codes inside tq_linear_mp's workspace."""
+    off = (ctypes.c_size_t * 4)()
+    _check("tq_linear_mp_workspace_offsets", load().tq_linear_mp_workspace_offsets(n, d, d_hi, off))
+    return {"s_xl": off[0], "s_xh": off[1], "x_codes_l": off[2], "x_codes_h": off[3]}
+
+
+def tq_pack_rht(signs, perm, out=None):
+    """Lay out a rotation (signs fp32 +-1, perm int32, both of length d) for tq_linear_mp_rht."""
+    lib = load()
+    _need_cuda(signs, perm)
+    d = signs.shape[0]
+    if out is None:
+        out = torch.empty(max(1, lib.tq_rht_bytes(d)), dtype=torch.uint8, device=signs.device)
+    _check("tq_pack_rht", lib.tq_pack_rht(_p(signs), _p(perm), d, _p(out), _stream(signs)))
+    return out
+
+
+def tq_linear_mp_rht(X, d_hi: int, rot, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtype=torch.bfloat16, Y=None,
+                     ws=None):
+    """tq_linear_mp on unrotated X, the rotation (tq_pack_rht) applied inside the quantiser."""
+    lib = load()
+    _need_cuda(X, rot, wl_codes, s_wl, wh_codes, s_wh, Y, ws)
+    n, d = X.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = torch.empty(max(1, tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=X.device)
+    _check("tq_linear_mp_rht", lib.tq_linear_mp_rht(_p(X), _dt(X), n, d, d_hi, _p(rot), m, _p(wl_codes), _p(s_wl),
+                                                    _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                                    _stream(X)))
     return Y
 
 

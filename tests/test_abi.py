@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 101
+    assert lib.tq_version() == 102
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -144,6 +144,24 @@ def test_linear_group_validation(lib):
     assert lib.tq_pack_lowrank_group(L, Ln, 1, d, ms, 2, r, A, S) == -1
     assert lib.tq_pack_lowrank_group(L, L, 1, d, ms, 2, 0, A, S) == -2
     assert lib.tq_pack_lowrank_group(L, L, 5, d, ms, 2, r, A, S) == -3
+
+
+def test_rht_validation(lib):
+    assert lib.tq_rht_bytes(8192) == 8192 + 2 * 8192
+    assert lib.tq_rht_bytes(130) == 0 and lib.tq_rht_bytes(16384) == 0
+    assert lib.tq_pack_rht(A, B, 200, C, S) == -2
+    assert lib.tq_pack_rht(NUL, B, 256, C, S) == -1
+    assert lib.tq_pack_rht(A, B, 256, MIS, S) == -5
+    n, d, dh, m = 8, 512, 128, 64
+    need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp_rht(A, 1, n, 544, 160, B, m, A, B, C, A, B, 1, C, need, S) == -2  # d % 128
+    assert lib.tq_linear_mp_rht(A, 1, n, 16384, 128, B, m, A, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, NUL, m, A, B, C, A, B, 1, C, need, S) == -1
+    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, MIS, m, A, B, C, A, B, 1, C, need, S) == -5
+    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, B, m, A, B, C, A, B, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_mp_rht(A, 1, 0, d, dh, NUL, m, A, B, C, A, B, 1, C, 0, S) == 0
+    off = tqb.tq_linear_mp_workspace_offsets(n, d, dh)
+    assert off["x_codes_h"] >= off["x_codes_l"] + n * (d - dh) and all(v % 256 == 0 for v in off.values())
 
 
 def test_linear_mp_validation(lib):

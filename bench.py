@@ -192,13 +192,20 @@ class GroupCase:
 
 
 class MpCase:
-    def __init__(self, wl, torch, tq, dev):
+    """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
+    applied online inside the quantiser (tq_linear_mp_rht)."""
+
+    def __init__(self, wl, torch, tq, dev, rht=False):
         from workloads import draw_two_subspace
 
         c = draw_two_subspace(wl)
         self.n, self.d, self.m, self.dh = wl.n, wl.d, wl.m, wl.d_hi
         dl = self.d - self.dh
-        self.X = torch.from_numpy(c["Xrot"]).to(dev).bfloat16()
+        self.rht = rht
+        self.X = torch.from_numpy(c["X" if rht else "Xrot"]).to(dev).bfloat16()
+        if rht:
+            self.rot = tq.tq_pack_rht(torch.from_numpy(c["signs"].astype("float32")).to(dev),
+                                      torch.from_numpy(c["perm"].astype("int32")).to(dev))
         W = torch.from_numpy(c["Wrot"])
         self.wl = tq.tq_pack_weight(W[:dl].contiguous().to(dev), 4)
         self.wh = tq.tq_pack_weight(W[dl:].contiguous().to(dev), 8)
@@ -208,8 +215,12 @@ class MpCase:
         self.tq = tq
 
     def __call__(self, i):
-        self.tq.tq_linear_mp(self.X, self.dh, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m, Y=self.Y,
-                             ws=self.ws)
+        if self.rht:
+            self.tq.tq_linear_mp_rht(self.X, self.dh, self.rot, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m,
+                                     Y=self.Y, ws=self.ws)
+        else:
+            self.tq.tq_linear_mp(self.X, self.dh, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m, Y=self.Y,
+                                 ws=self.ws)
 
 
 def cpu_baseline(wl, rows, seconds):
@@ -339,19 +350,22 @@ def main():
             del c
             torch.cuda.empty_cache()
         w = WORKLOADS["two_subspace"]
-        log(f"[bench] {w.title}: building inputs")
-        c = MpCase(w, torch, tq, dev)
-        t = time_calls(c, 20, 3, torch)
-        km = kernel_ms(c, 10, torch, tq)
-        o = 2.0 * w.n * w.d * w.m
-        b = w.n * w.d * 2 + (w.d - w.d_hi) * w.m // 2 + w.d_hi * w.m + 8 * w.m + 2 * w.n * w.m
-        row = {"workload": w.title, "n": w.n, "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
-               "GBps": round(b / (t * 1e-3) / 1e9, 1), "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
-               "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
-        sweep.append(row)
-        log(f"[bench] sweep {row}")
-        del c
-        torch.cuda.empty_cache()
+        for rht in (False, True):
+            log(f"[bench] {w.title}{' (rotation online)' if rht else ''}: building inputs")
+            c = MpCase(w, torch, tq, dev, rht=rht)
+            t = time_calls(c, 20, 3, torch)
+            km = kernel_ms(c, 10, torch, tq)
+            o = 2.0 * w.n * w.d * w.m
+            b = w.n * w.d * 2 + (w.d - w.d_hi) * w.m // 2 + w.d_hi * w.m + 8 * w.m + 2 * w.n * w.m
+            row = {"workload": w.title + (": unrotated X, rotation inside the quantiser" if rht else ""), "n": w.n,
+                   "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
+                   "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                   "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                   "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+            sweep.append(row)
+            log(f"[bench] sweep {row}")
+            del c
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:

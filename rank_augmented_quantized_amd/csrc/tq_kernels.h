@@ -174,10 +174,11 @@ struct SmallArgs {
 constexpr int kSyncBytes = 4096;  // workspace bytes of the hand-off words
 
 // Online block-Hadamard rotation of the two-subspace quantiser: the packed
-// rotation holds the int8 signs (d bytes) and then, for each rotated
-// coordinate, its output position (uint16).  d % 128 == 0, d <= kRhtMaxD.
+// rotation holds the signs as bits (d / 8 bytes, padded to 16) and then, for
+// each rotated coordinate, its output position (uint16).  d % 128 == 0,
+// d <= kRhtMaxD.
 constexpr int kRhtMaxD = 8192;
-__host__ __device__ constexpr size_t rht_signs_bytes(int d) { return ((size_t)d + 15) & ~(size_t)15; }
+__host__ __device__ constexpr size_t rht_signs_bytes(int d) { return ((size_t)d / 8 + 15) & ~(size_t)15; }
 __host__ __device__ constexpr size_t rht_bytes(int d) { return rht_signs_bytes(d) + (((size_t)d * 2 + 15) & ~(size_t)15); }
 hipError_t launch_pack_rht(const float* signs, const int32_t* perm, int d, void* rot, hipStream_t st);
 // X (n x d) rotated online and quantised: columns [0, dl) of X' at 4 bits as

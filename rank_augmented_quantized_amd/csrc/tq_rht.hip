@@ -9,10 +9,11 @@
 // One wave per token row.  Lane L holds the 8-value chunks L + 64 i of the
 // row, so the 16 chunks of a 128-column block sit in 16 consecutive lanes:
 // the three butterfly stages of span 1, 2, 4 run inside a lane, those of span
-// 8 .. 64 between lanes L and L ^ 1 .. L ^ 8.  Each stage is the fp32 pair
-// (a + b, a - b), a the lower index, spans increasing, then one multiply by
-// fl32(1 / sqrt(128)) -- the order the fp32 oracle fixes, so X' is reproduced
-// bit for bit.  The absmax of each subspace (position j = pinv[k] of rotated
+// 8 .. 64 between lanes L and L ^ 1 .. L ^ 8 (DPP moves).  Each stage is the
+// fp32 pair (a + b, a - b), a the lower index, spans increasing, then one
+// multiply by fl32(1 / sqrt(128)) -- the order the fp32 oracle fixes, so X'
+// is reproduced bit for bit.  The row is rotated twice (for the absmax, then
+// for the codes) so that only its raw chunks stay in registers.  The absmax of each subspace (position j = pinv[k] of rotated
 // coordinate k below d - d_hi, or not) comes from wave reductions; the codes
 // are written byte by byte to a per-wave LDS row at their positions (4-bit
 // subspace in the int8 order of the tile GEMM, 8-bit subspace in natural
@@ -39,9 +40,27 @@ __device__ __forceinline__ int code_one(float x, const RowScale& rs) {
   return code_exact<BITS>(x, rs.s);
 }
 
+// v from lane L ^ m (m = 1, 2, 4, 8) through DPP moves, no LDS: quad
+// permutations, and for 4 and 8 the half-row / row mirror followed by one
+__device__ __forceinline__ float xor_lane(float v, int m) {
+  int x = __float_as_int(v);
+  if (m == 1) {
+    x = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if (m == 2) {
+    x = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else if (m == 4) {
+    x = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true);  // row_half_mirror: 7 - i
+    x = __builtin_amdgcn_update_dpp(0, x, 0x1B, 0xF, 0xF, true);   // quad_perm [3, 2, 1, 0]
+  } else {
+    x = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true);  // row_mirror: 15 - i
+    x = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  }
+  return __int_as_float(x);
+}
+
 template <typename T, int CH>
 __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __restrict__ X, int n, int d, int dl,
-                                                                  const int8_t* __restrict__ signs,
+                                                                  const uint8_t* __restrict__ sbits,
                                                                   const uint16_t* __restrict__ pinv,
                                                                   uint8_t* __restrict__ xl, float* __restrict__ sxl,
                                                                   uint8_t* __restrict__ xh, float* __restrict__ sxh) {
@@ -52,61 +71,63 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
   const int nch = d >> 3, dh = d - dl;
   const T* x = X + (size_t)row * d;
 
-  float v[CH][8];
-  uint4 pv[CH];
+  Row8<T> raw[CH];
+  uint32_t sg[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int ch = min(lane + 64 * i, nch - 1);
-    Row8<T> r;
-    r.load(x + 8 * ch);
-    const uint2 sg = *reinterpret_cast<const uint2*>(signs + 8 * ch);
-    pv[i] = *reinterpret_cast<const uint4*>(pinv + 8 * ch);
-    r.get(v[i]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sb = ((e < 4 ? sg.x : sg.y) >> (8 * (e & 3))) & 0x80u;  // sign bit of the int8 +-1
-      v[i][e] = __uint_as_float(__float_as_uint(v[i][e]) ^ (sb << 24));   // x * +-1, exactly
-    }
+    raw[i].load(x + 8 * ch);
+    sg[i] = sbits[ch];
   }
-  // butterflies of span 1, 2, 4 (inside the chunk), then 8 .. 64 (between lanes)
+  const float c = (float)(1.0 / 11.313708498984760390);  // fl32(1 / sqrt(128))
+  auto rotate = [&](int i, float (&v)[8]) {
+    raw[i].get(v);
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
+    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sg[i] >> e) & 1u) << 31));
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+    for (int h = 1; h < 8; h <<= 1)  // spans 1, 2, 4: inside the chunk
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (!(e & h)) {
-          const float a = v[i][e], b = v[i][e + h];
-          v[i][e] = a + b;
-          v[i][e + h] = a - b;
+          const float a = v[e], b = v[e + h];
+          v[e] = a + b;
+          v[e + h] = a - b;
         }
-  }
 #pragma unroll
-  for (int lm = 1; lm < 16; lm <<= 1) {
-    const bool upper = lane & lm;
+    for (int lm = 1; lm < 16; lm <<= 1) {  // spans 8 .. 64: between lanes L and L ^ lm
+      // lower lane: v + p; upper lane: p - v = p + (-v) (the same IEEE
+      // operation on the same operands): one add, its operand through DPP
+      const uint32_t flip = (lane & lm) ? 0x80000000u : 0u;
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+      for (int e = 0; e < 8; ++e) v[e] = xor_lane(v[e], lm) + __uint_as_float(__float_as_uint(v[e]) ^ flip);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __shfl_xor(v[i][e], lm, 64);
-        v[i][e] = upper ? p - v[i][e] : v[i][e] + p;
-      }
-  }
-  const float c = (float)(1.0 / 11.313708498984760390);  // fl32(1 / sqrt(128))
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * c;
+  };
+  auto position = [&](const uint4& pv, int e) {
+    const uint32_t wv = e < 2 ? pv.x : (e < 4 ? pv.y : (e < 6 ? pv.z : pv.w));
+    return min((int)((wv >> (16 * (e & 1))) & 0xFFFFu), d - 1);
+  };
+
+  // pass 1: the absmax of each subspace
   float ml = 0.0f, mh = 0.0f;
+  {
+    uint4 pv[CH];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const bool live = lane + 64 * i < nch;
-    const uint32_t pw[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+    for (int i = 0; i < CH; ++i) pv[i] = *reinterpret_cast<const uint4*>(pinv + 8 * min(lane + 64 * i, nch - 1));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[i][e] = v[i][e] * c;
-      const int j = min((int)((pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), d - 1);
-      const float a = live ? fabsf(v[i][e]) : 0.0f;
-      if (j < dl)
-        ml = fmaxf(ml, a);
-      else
-        mh = fmaxf(mh, a);
+    for (int i = 0; i < CH; ++i) {
+      float v[8];
+      rotate(i, v);
+      if (lane + 64 * i < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (position(pv[i], e) < dl)
+            ml = fmaxf(ml, fabsf(v[e]));
+          else
+            mh = fmaxf(mh, fabsf(v[e]));
+        }
+      }
     }
   }
   ml = wave_max(ml);
@@ -116,18 +137,26 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
     if (dl > 0) sxl[row] = rl.s;
     if (dh > 0) sxh[row] = rh.s;
   }
+  // pass 2: the same rotation again, codes to their positions in LDS
   uint8_t* rb = rowb[w];
+  {
+    uint4 pv[CH];
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    if (lane + 64 * i >= nch) continue;
-    const uint32_t pw[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+    for (int i = 0; i < CH; ++i) pv[i] = *reinterpret_cast<const uint4*>(pinv + 8 * min(lane + 64 * i, nch - 1));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = min((int)((pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), d - 1);
-      if (j < dl)  // 4-bit subspace: per 8 positions, the 4 even then the 4 odd
-        rb[(j & ~7) + 4 * (j & 1) + ((j & 7) >> 1)] = (uint8_t)code_one<4>(v[i][e], rl);
-      else
-        rb[j] = (uint8_t)code_one<8>(v[i][e], rh);
+    for (int i = 0; i < CH; ++i) {
+      float v[8];
+      rotate(i, v);
+      if (lane + 64 * i < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = position(pv[i], e);
+          if (j < dl)  // 4-bit subspace: per 8 positions, the 4 even then the 4 odd
+            rb[(j & ~7) + 4 * (j & 1) + ((j & 7) >> 1)] = (uint8_t)code_one<4>(v[e], rl);
+          else
+            rb[j] = (uint8_t)code_one<8>(v[e], rh);
+        }
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS bytes are written
@@ -138,27 +167,33 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
     *reinterpret_cast<uint4*>(xh + (size_t)row * dh + o) = *reinterpret_cast<const uint4*>(rb + dl + o);
 }
 
-// signs (fp32 +-1) -> int8 +-1; perm (position j -> rotated coordinate) ->
-// its inverse (coordinate -> position), uint16
+// signs (fp32 +-1) -> one bit per coordinate (set: -1; bit e of byte ch is
+// coordinate 8 ch + e); perm (position j -> rotated coordinate) -> its
+// inverse (coordinate -> position), uint16
 __global__ __launch_bounds__(256) void k_pack_rht(const float* __restrict__ signs, const int32_t* __restrict__ perm,
-                                                  int d, int8_t* __restrict__ s8, uint16_t* __restrict__ pinv) {
+                                                  int d, uint8_t* __restrict__ sbits, uint16_t* __restrict__ pinv) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d) return;
-  s8[j] = signs[j] < 0.0f ? (int8_t)-1 : (int8_t)1;
-  const int k = perm[j];
-  if (k >= 0 && k < d) pinv[k] = (uint16_t)j;
+  if (j < d) {
+    const int k = perm[j];
+    if (k >= 0 && k < d) pinv[k] = (uint16_t)j;
+  }
+  if (j < d / 8) {
+    uint32_t b = 0;
+    for (int e = 0; e < 8; ++e) b |= (signs[8 * j + e] < 0.0f ? 1u : 0u) << e;
+    sbits[j] = (uint8_t)b;
+  }
 }
 
 template <typename T>
 hipError_t launch_rht_t(const void* X, int n, int d, int dl, const void* rot, void* xl, float* sxl, void* xh,
                         float* sxh, hipStream_t st) {
-  const int8_t* s8 = (const int8_t*)rot;
+  const uint8_t* sb = (const uint8_t*)rot;
   const uint16_t* pinv = (const uint16_t*)((const uint8_t*)rot + rht_signs_bytes(d));
   const dim3 grid((unsigned)((n + kRhtWaves - 1) / kRhtWaves)), block(kRhtWaves * 64);
   const int nch = d / 8;
   const T* x = (const T*)X;
 #define TQ_RHT(C)                                                                                                \
-  hipLaunchKernelGGL((k_quant_rows_rht<T, C>), grid, block, 0, st, x, n, d, dl, s8, pinv, (uint8_t*)xl, sxl, \
+  hipLaunchKernelGGL((k_quant_rows_rht<T, C>), grid, block, 0, st, x, n, d, dl, sb, pinv, (uint8_t*)xl, sxl, \
                      (uint8_t*)xh, sxh)
   if (nch <= 64)
     TQ_RHT(1);
@@ -177,7 +212,7 @@ hipError_t launch_rht_t(const void* X, int n, int d, int dl, const void* rot, vo
 }  // namespace
 
 hipError_t launch_pack_rht(const float* signs, const int32_t* perm, int d, void* rot, hipStream_t st) {
-  hipLaunchKernelGGL(k_pack_rht, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, st, signs, perm, d, (int8_t*)rot,
+  hipLaunchKernelGGL(k_pack_rht, dim3((unsigned)((d + 255) / 256)), dim3(256), 0, st, signs, perm, d, (uint8_t*)rot,
                      (uint16_t*)((uint8_t*)rot + rht_signs_bytes(d)));
   return hipGetLastError();
 }

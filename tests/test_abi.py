@@ -147,7 +147,7 @@ def test_linear_group_validation(lib):
 
 
 def test_rht_validation(lib):
-    assert lib.tq_rht_bytes(8192) == 8192 + 2 * 8192
+    assert lib.tq_rht_bytes(8192) == 1024 + 2 * 8192  # sign bits, then uint16 positions
     assert lib.tq_rht_bytes(130) == 0 and lib.tq_rht_bytes(16384) == 0
     assert lib.tq_pack_rht(A, B, 200, C, S) == -2
     assert lib.tq_pack_rht(NUL, B, 256, C, S) == -1

@@ -13,7 +13,8 @@
 // fp32 pair (a + b, a - b), a the lower index, spans increasing, then one
 // multiply by fl32(1 / sqrt(128)) -- the order the fp32 oracle fixes, so X'
 // is reproduced bit for bit.  The row is rotated twice (for the absmax, then
-// for the codes) so that only its raw chunks stay in registers.  The absmax of each subspace (position j = pinv[k] of rotated
+// for the codes), one chunk slot at a time in a loop with the next slot
+// fetched ahead, which keeps the kernel body and its registers small.  The absmax of each subspace (position j = pinv[k] of rotated
 // coordinate k below d - d_hi, or not) comes from wave reductions; the codes
 // are written byte by byte to a per-wave LDS row at their positions (4-bit
 // subspace in the int8 order of the tile GEMM, 8-bit subspace in natural
@@ -58,7 +59,7 @@ __device__ __forceinline__ float xor_lane(float v, int m) {
   return __int_as_float(x);
 }
 
-template <typename T, int CH>
+template <typename T>
 __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __restrict__ X, int n, int d, int dl,
                                                                   const uint8_t* __restrict__ sbits,
                                                                   const uint16_t* __restrict__ pinv,
@@ -69,21 +70,27 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
   const int row = blockIdx.x * kRhtWaves + w;
   if (row >= n) return;
   const int nch = d >> 3, dh = d - dl;
+  const int slots = (nch + 63) >> 6;  // chunks per lane (the last slot may be partly past the row)
   const T* x = X + (size_t)row * d;
 
-  Row8<T> raw[CH];
-  uint32_t sg[CH];
+  // chunk slot i of this lane: raw values, sign bits, positions; fetched one
+  // slot ahead of its use (clamped in-row addresses, so no branch)
+  struct Chunk {
+    Row8<T> raw;
+    uint32_t sg;
+    uint4 pv;
+  };
+  auto fetch = [&](int i, Chunk& c) {
+    const int ch = min(lane + 64 * min(i, slots - 1), nch - 1);
+    c.raw.load(x + 8 * ch);
+    c.sg = sbits[ch];
+    c.pv = *reinterpret_cast<const uint4*>(pinv + 8 * ch);
+  };
+  const float sc = (float)(1.0 / 11.313708498984760390);  // fl32(1 / sqrt(128))
+  auto rotate = [&](const Chunk& c, float (&v)[8]) {
+    c.raw.get(v);
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int ch = min(lane + 64 * i, nch - 1);
-    raw[i].load(x + 8 * ch);
-    sg[i] = sbits[ch];
-  }
-  const float c = (float)(1.0 / 11.313708498984760390);  // fl32(1 / sqrt(128))
-  auto rotate = [&](int i, float (&v)[8]) {
-    raw[i].get(v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((sg[i] >> e) & 1u) << 31));
+    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__float_as_uint(v[e]) ^ (((c.sg >> e) & 1u) << 31));
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)  // spans 1, 2, 4: inside the chunk
 #pragma unroll
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
       for (int e = 0; e < 8; ++e) v[e] = xor_lane(v[e], lm) + __uint_as_float(__float_as_uint(v[e]) ^ flip);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * c;
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * sc;
   };
   auto position = [&](const uint4& pv, int e) {
     const uint32_t wv = e < 2 ? pv.x : (e < 4 ? pv.y : (e < 6 ? pv.z : pv.w));
@@ -111,24 +118,22 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
 
   // pass 1: the absmax of each subspace
   float ml = 0.0f, mh = 0.0f;
-  {
-    uint4 pv[CH];
+  Chunk cur, nxt;
+  fetch(0, cur);
+  for (int i = 0; i < slots; ++i) {
+    fetch(i + 1, nxt);
+    float v[8];
+    rotate(cur, v);
+    if (lane + 64 * i < nch) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) pv[i] = *reinterpret_cast<const uint4*>(pinv + 8 * min(lane + 64 * i, nch - 1));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      float v[8];
-      rotate(i, v);
-      if (lane + 64 * i < nch) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (position(pv[i], e) < dl)
-            ml = fmaxf(ml, fabsf(v[e]));
-          else
-            mh = fmaxf(mh, fabsf(v[e]));
-        }
+      for (int e = 0; e < 8; ++e) {
+        if (position(cur.pv, e) < dl)
+          ml = fmaxf(ml, fabsf(v[e]));
+        else
+          mh = fmaxf(mh, fabsf(v[e]));
       }
     }
+    cur = nxt;
   }
   ml = wave_max(ml);
   mh = wave_max(mh);
@@ -137,27 +142,25 @@ __global__ __launch_bounds__(kRhtWaves * 64) void k_quant_rows_rht(const T* __re
     if (dl > 0) sxl[row] = rl.s;
     if (dh > 0) sxh[row] = rh.s;
   }
-  // pass 2: the same rotation again, codes to their positions in LDS
+  // pass 2: the same rotation again (the row now comes from L2), codes to
+  // their positions in LDS
   uint8_t* rb = rowb[w];
-  {
-    uint4 pv[CH];
+  fetch(0, cur);
+  for (int i = 0; i < slots; ++i) {
+    fetch(i + 1, nxt);
+    float v[8];
+    rotate(cur, v);
+    if (lane + 64 * i < nch) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) pv[i] = *reinterpret_cast<const uint4*>(pinv + 8 * min(lane + 64 * i, nch - 1));
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      float v[8];
-      rotate(i, v);
-      if (lane + 64 * i < nch) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = position(pv[i], e);
-          if (j < dl)  // 4-bit subspace: per 8 positions, the 4 even then the 4 odd
-            rb[(j & ~7) + 4 * (j & 1) + ((j & 7) >> 1)] = (uint8_t)code_one<4>(v[e], rl);
-          else
-            rb[j] = (uint8_t)code_one<8>(v[e], rh);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int j = position(cur.pv, e);
+        if (j < dl)  // 4-bit subspace: per 8 positions, the 4 even then the 4 odd
+          rb[(j & ~7) + 4 * (j & 1) + ((j & 7) >> 1)] = (uint8_t)code_one<4>(v[e], rl);
+        else
+          rb[j] = (uint8_t)code_one<8>(v[e], rh);
       }
     }
+    cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS bytes are written
   __builtin_amdgcn_wave_barrier();
@@ -190,22 +193,9 @@ hipError_t launch_rht_t(const void* X, int n, int d, int dl, const void* rot, vo
   const uint8_t* sb = (const uint8_t*)rot;
   const uint16_t* pinv = (const uint16_t*)((const uint8_t*)rot + rht_signs_bytes(d));
   const dim3 grid((unsigned)((n + kRhtWaves - 1) / kRhtWaves)), block(kRhtWaves * 64);
-  const int nch = d / 8;
   const T* x = (const T*)X;
-#define TQ_RHT(C)                                                                                                \
-  hipLaunchKernelGGL((k_quant_rows_rht<T, C>), grid, block, 0, st, x, n, d, dl, sb, pinv, (uint8_t*)xl, sxl, \
-                     (uint8_t*)xh, sxh)
-  if (nch <= 64)
-    TQ_RHT(1);
-  else if (nch <= 128)
-    TQ_RHT(2);
-  else if (nch <= 256)
-    TQ_RHT(4);
-  else if (nch <= 512)
-    TQ_RHT(8);
-  else
-    TQ_RHT(16);
-#undef TQ_RHT
+  hipLaunchKernelGGL((k_quant_rows_rht<T>), grid, block, 0, st, x, n, d, dl, sb, pinv, (uint8_t*)xl, sxl, (uint8_t*)xh,
+                     sxh);
   return hipGetLastError();
 }
 

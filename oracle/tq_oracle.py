@@ -20,7 +20,11 @@ It evaluates the plain definition of the layer, step by step, in numpy:
   section 02 (note on INT32 accumulation) and section 04.C, Figure 4;
 * the two-subspace mixed-precision output -- CoQuant Eq. 3-9;
 * layers that share one input, grouped -- CoQuant, the grouping paragraph
-  around Eq. 14.
+  around Eq. 14;
+* the fully quantised low-rank branch Q(X)[Q(U)Q(V) + Q(R)] with the first
+  stage's integer result re-quantised per token -- TwinQuant notes, the
+  error expression of section 04.A and the fused two-stage low-rank pipeline
+  of section 04.C.
 
 Readings of points the pages leave open (each one is also listed in the
 design notes): q_max = 7 / 127; "round" is round-half-to-even; the scale is
@@ -55,6 +59,8 @@ __all__ = [
     "block_rotation",
     "rotate",
     "subspace_split",
+    "requantize_lowrank",
+    "tq_linear_qlr_ref",
 ]
 
 
@@ -213,6 +219,67 @@ def tq_linear_group_ref(x, rs, l1s=None, l2s=None, rows=None, bits: int = 4):
     y = np.concatenate([o["Y"] for o in outs], axis=1)
     t = None if outs[0]["T"] is None else np.concatenate([o["T"] for o in outs], axis=1)
     return {"codes_x": outs[0]["codes_x"], "s_x": outs[0]["s_x"], "layers": outs, "T": t, "Y": y}
+
+
+def requantize_lowrank(acc1, s_u, bits: int = 4):
+    """Per-token re-quantisation of the first low-rank stage (TwinQuant notes,
+    section 04.C: the integer result of Q(X) Q(U) is brought back to ``bits``
+    before it meets Q(V)).
+
+    acc1 is the exact integer product C_x C_u^T (tokens x r).  The real-valued
+    stage is s_x[i] * s_u[j] * acc1[i, j]; the token's own factor s_x[i] is
+    common to its whole row, so it is kept outside and the row that is
+    quantised is t[i, j] = fl32(fl32(acc1[i, j]) * s_u[j]) (acc1 is exact in
+    fp32 below 2^24 in magnitude, which is asserted).  t is quantised per
+    token by ``quantize_rows``, so the stage's scale is s_x * s_t.
+
+    Returns (t fp32, codes int16, s_t fp32).
+    """
+    acc1 = np.asarray(acc1)
+    if acc1.size and int(np.max(np.abs(acc1))) >= 2 ** 24:
+        raise ValueError("first-stage sum not exact in fp32")
+    t = (acc1.astype(np.float32) * np.asarray(s_u, dtype=np.float32)[None, :]).astype(np.float32)
+    ct, s_t = quantize_rows(t, bits)
+    return t, ct, s_t
+
+
+def tq_linear_qlr_ref(x, r, u, v, rows=None, cols=None, bits: int = 4):
+    """Layer with both branches quantised (TwinQuant notes, section 04.A error
+    expression Q(X)[Q(U)Q(V) + Q(R)], kernel of section 04.C, Figure 4):
+
+        acc  = C_x C_w^T                     residual product, exact
+        acc1 = C_x C_u^T                     first low-rank stage, exact
+        (t, C_t, s_t) = requantize_lowrank(acc1, s_u)
+        acc2 = C_t C_v^T                     second low-rank stage, exact
+        Y = s_x s_w^T (.) acc + (s_x s_t) s_v^T (.) acc2     (fp64)
+
+    X (n x d) per token, R (d x m), U (d x r) and V (r x m) per output
+    channel (column), all symmetric at ``bits``.  ``rows`` / ``cols`` restrict
+    the evaluation to some tokens / output channels (every step is row- or
+    column-local, so the sampled values equal the full computation's).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    r = np.asarray(r, dtype=np.float32)
+    u = np.asarray(u, dtype=np.float32)
+    v = np.asarray(v, dtype=np.float32)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    if cols is not None:
+        r = r[:, np.asarray(cols)]
+        v = v[:, np.asarray(cols)]
+    cx, s_x = quantize_rows(x, bits)
+    cw, s_w = quantize_weight(r, bits)
+    acc = int_matmul(cx, cw)
+    cu, s_u = quantize_weight(u, bits)
+    acc1 = int_matmul(cx, cu)
+    t, ct, s_t = requantize_lowrank(acc1, s_u, bits)
+    cv, s_v = quantize_weight(v, bits)
+    acc2 = int_matmul(ct, cv)
+    sx = s_x.astype(np.float64)[:, None]
+    y = sx * s_w.astype(np.float64)[None, :] * acc.astype(np.float64)
+    y = y + (sx * s_t.astype(np.float64)[:, None]) * s_v.astype(np.float64)[None, :] * acc2.astype(np.float64)
+    return {"codes_x": cx, "s_x": s_x, "acc": acc, "codes_u": cu, "s_u": s_u, "acc1": acc1, "t": t,
+            "codes_t": ct, "s_t": s_t, "codes_v": cv, "s_v": s_v, "acc2": acc2, "Y": y}
 
 
 def tq_linear_mp_ref(xrot, wrot, d_hi: int, rows=None, cols=None, bits_lo: int = 4, bits_hi: int = 8):

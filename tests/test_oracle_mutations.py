@@ -17,7 +17,7 @@ import test_oracle_pins as pins
 _orig = {name: getattr(tqo, name) for name in (
     "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
     "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
-    "subspace_split", "tq_linear_group_ref", "rht_rows")}
+    "subspace_split", "tq_linear_group_ref", "rht_rows", "requantize_lowrank", "tq_linear_qlr_ref")}
 
 
 def _q_reciprocal(a, bits=4):
@@ -223,6 +223,54 @@ def _rht_signs_after(x, signs, perm, block=128):
     return _rht_generic(x, signs, perm, block, signs_after=True)
 
 
+def _requant_no_su(acc1, s_u, bits=4):  # the column scales of U left out of the first stage
+    return _orig["requantize_lowrank"](acc1, np.ones_like(np.asarray(s_u, np.float32)), bits)
+
+
+def _requant_per_column(acc1, s_u, bits=4):  # re-quantised per rank column instead of per token
+    t = (np.asarray(acc1).astype(np.float32) * np.asarray(s_u, np.float32)[None, :]).astype(np.float32)
+    c, s = _orig["quantize_rows"](t.T, bits)
+    return t, c.T, s
+
+
+def _requant_trunc(acc1, s_u, bits=4):  # codes truncated toward zero
+    t, c, s = _orig["requantize_lowrank"](acc1, s_u, bits)
+    live = s > 0
+    c[live] = np.clip(np.trunc((t[live] / s[live][:, None]).astype(np.float32)), -8, 7)
+    return t, c, s
+
+
+def _requant_8bit(acc1, s_u, bits=4):  # the intermediate kept at 8 bits
+    return _orig["requantize_lowrank"](acc1, s_u, 8)
+
+
+def _qlr_generic(x, r, u, v, rows=None, cols=None, bits=4, lr_sx=True, lr_st=True, unrequantised=False):
+    out = _orig["tq_linear_qlr_ref"](x, r, u, v, rows, cols, bits)
+    xs = np.asarray(x) if rows is None else np.asarray(x)[np.asarray(rows)]
+    rs = np.asarray(r) if cols is None else np.asarray(r)[:, np.asarray(cols)]
+    y0 = _orig["tq_linear_ref"](xs, rs, bits=bits)["Y"]
+    sx = out["s_x"].astype(np.float64)[:, None] if lr_sx else 1.0
+    st = out["s_t"].astype(np.float64)[:, None] if lr_st else 1.0
+    tt = out["codes_t"].astype(np.float64) * st
+    if unrequantised:
+        tt = out["t"].astype(np.float64)
+    vv = out["codes_v"].astype(np.float64) * out["s_v"].astype(np.float64)[:, None]
+    out["Y"] = y0 + sx * (tt @ vv.T)
+    return out
+
+
+def _qlr_lr_no_sx(x, r, u, v, rows=None, cols=None, bits=4):  # the token scale missing from the low-rank term
+    return _qlr_generic(x, r, u, v, rows, cols, bits, lr_sx=False)
+
+
+def _qlr_lr_no_st(x, r, u, v, rows=None, cols=None, bits=4):  # the stage scale missing
+    return _qlr_generic(x, r, u, v, rows, cols, bits, lr_st=False)
+
+
+def _qlr_unrequantised(x, r, u, v, rows=None, cols=None, bits=4):  # the fp32 first stage fed on, not its codes
+    return _qlr_generic(x, r, u, v, rows, cols, bits, unrequantised=True)
+
+
 MUTANTS = {
     "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
     "quantize_weight": [_w_per_input_channel],
@@ -237,6 +285,8 @@ MUTANTS = {
     "subspace_split": [_split_swapped],
     "tq_linear_group_ref": [_group_first_l2, _group_reversed, _group_l1_shared],
     "rht_rows": [_rht_sub_swapped, _rht_inverse_perm, _rht_scale_by_block, _rht_signs_after],
+    "requantize_lowrank": [_requant_no_su, _requant_per_column, _requant_trunc, _requant_8bit],
+    "tq_linear_qlr_ref": [_qlr_lr_no_sx, _qlr_lr_no_st, _qlr_unrequantised],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]

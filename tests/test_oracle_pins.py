@@ -428,6 +428,135 @@ def pin_rht_layer_rotation_invariance(seed=19):
     assert np.array_equal(out["codes_xl"], pre["codes_xl"]) and np.array_equal(out["codes_xh"], pre["codes_xh"])
 
 
+# ----------------------------------------------------------------------------
+# fully quantised low-rank branch
+# ----------------------------------------------------------------------------
+
+def _qlr_lossless_case(rng, n, d, m, rk, a=-3):
+    """X, R, V that quantise without loss, and U whose columns are one-hot
+    (entry +-7 2^a at input channel k_j, k_0 = 0) with column 0 of every token's
+    codes at +-7: then X U V is reproduced exactly by the two quantised stages."""
+    x, r, cx, sx, cw, sw = _lossless_case(rng, n, d, m)
+    cx[:, 0] = np.where(rng.integers(0, 2, size=n) == 1, 7, -7)
+    x = (cx * sx[:, None]).astype(np.float32)
+    ks = np.concatenate([[0], rng.choice(np.arange(1, d), size=rk - 1, replace=False)])
+    sg = np.where(rng.integers(0, 2, size=rk) == 1, 7, -7)
+    u = np.zeros((d, rk), np.float32)
+    u[ks, np.arange(rk)] = sg * 2.0 ** a
+    cv = lossless_codes(rng, m, rk, 7)
+    sv = (2.0 ** rng.integers(-8, -3, size=m)).astype(np.float32)
+    v = (cv * sv[:, None]).T.astype(np.float32)
+    return x, r, u, v, cx, sx, ks, sg, cv, sv
+
+
+def pin_qlr_lossless(seed=20):
+    """Both branches quantised: with lossless inputs the first stage's integer
+    sums, its per-token re-quantisation and the output are known in closed
+    form, and Y equals X R + (X U) V exactly."""
+    rng = np.random.default_rng(seed)
+    n, d, m, rk, a = 5, 48, 7, 4, -3
+    x, r, u, v, cx, sx, ks, sg, cv, sv = _qlr_lossless_case(rng, n, d, m, rk, a)
+    out = tqo.tq_linear_qlr_ref(x, r, u, v)
+    assert np.array_equal(out["codes_u"], np.diag(sg) @ np.eye(d, dtype=np.int64)[ks])
+    assert np.array_equal(out["s_u"], np.full(rk, 2.0 ** a, np.float32))
+    acc1 = cx[:, ks] * sg[None, :]
+    assert np.array_equal(out["acc1"], acc1)
+    # t = acc1 2^a, every token's max |t| = 49 2^a: s_t = 7 2^a, codes = acc1 / 7
+    assert np.array_equal(out["s_t"], np.full(n, 7 * 2.0 ** a, np.float32))
+    assert np.array_equal(out["codes_t"], acc1 // 7)
+    x64, r64, u64, v64 = (t.astype(np.float64) for t in (x, r, u, v))
+    assert np.array_equal(out["Y"], x64 @ r64 + (x64 @ u64) @ v64)
+    # V = 0 leaves the plain W4A4 layer
+    assert np.array_equal(tqo.tq_linear_qlr_ref(x, r, u, np.zeros_like(v))["Y"], tqo.tq_linear_ref(x, r)["Y"])
+    # a lossy re-quantisation known in closed form: both rank columns read
+    # input channel 0, the second at half the first (7 2^a and 3.5 2^a), so
+    # every token's first stage is (t0, t0 / 2) with |t0| = 49 2^a: s_t = 7 2^a
+    # and the codes are +-7 and +-4 (3.5 rounds half to even), i.e. the second
+    # column comes back as 4/7 of the first instead of 1/2
+    u2 = np.zeros((d, 2), np.float32)
+    u2[0] = [7 * 2.0 ** a, 3.5 * 2.0 ** a]
+    v2 = (lossless_codes(rng, m, 2, 7) * sv[:, None]).T.astype(np.float32)
+    o2 = tqo.tq_linear_qlr_ref(x, r, u2, v2)
+    sgn = np.sign(cx[:, 0])
+    assert np.array_equal(o2["codes_t"], np.stack([7 * sgn, 4 * sgn], axis=1))
+    that = np.stack([sgn * 49.0, sgn * 28.0], axis=1) * (sx.astype(np.float64) * 2.0 ** a)[:, None]
+    want = x64 @ r64 + that @ v2.astype(np.float64)
+    assert np.allclose(o2["Y"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def pin_qlr_invariants(seed=21):
+    """Power-of-two rescalings that the definition passes through exactly:
+    a token row of X scales its row of Y; U -> 2^k U scales the low-rank term
+    by 2^k; a column of U keeps its codes and scales only its own s_u (U is
+    quantised per column); a column of V scales its column of the low-rank
+    term and keeps its codes (V per column); a permutation of the rank
+    columns (U's columns with V's rows) changes nothing; U = 0 removes the
+    branch."""
+    rng = np.random.default_rng(seed)
+    n, d, m, rk = 6, 64, 9, 5
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    r = (0.02 * rng.standard_normal((d, m))).astype(np.float32)
+    u = rng.standard_normal((d, rk)).astype(np.float32) * (2.0 ** rng.integers(-3, 3, size=rk)).astype(np.float32)
+    v = (0.05 * rng.standard_normal((rk, m))).astype(np.float32)
+    out = tqo.tq_linear_qlr_ref(x, r, u, v)
+    base = out["Y"]
+    zr = np.zeros_like(r)
+    lr = tqo.tq_linear_qlr_ref(x, zr, u, v)["Y"]
+    assert np.abs(lr).max() > 0
+    xs = x.copy()
+    xs[2] *= 8.0
+    xs[4] *= 0.25
+    want = base.copy()
+    want[2] *= 8.0
+    want[4] *= 0.25
+    assert np.array_equal(tqo.tq_linear_qlr_ref(xs, r, u, v)["Y"], want)
+    assert np.array_equal(tqo.tq_linear_qlr_ref(x, zr, 4.0 * u, v)["Y"], 4.0 * lr)
+    us = u.copy()
+    us[:, 1] *= 16.0
+    o2 = tqo.tq_linear_qlr_ref(x, r, us, v)
+    assert np.array_equal(o2["codes_u"], out["codes_u"])
+    want_su = out["s_u"].copy()
+    want_su[1] *= 16.0
+    assert np.array_equal(o2["s_u"], want_su)
+    vs = v.copy()
+    vs[:, 2] *= 4.0
+    vs[:, 7] *= 0.125
+    o3 = tqo.tq_linear_qlr_ref(x, zr, u, vs)
+    assert np.array_equal(o3["codes_v"], out["codes_v"])
+    want = lr.copy()
+    want[:, 2] *= 4.0
+    want[:, 7] *= 0.125
+    assert np.array_equal(o3["Y"], want)
+    p = rng.permutation(rk)
+    assert np.allclose(tqo.tq_linear_qlr_ref(x, r, u[:, p], v[p])["Y"], base, rtol=0, atol=1e-12 * np.abs(base).max())
+    assert np.array_equal(tqo.tq_linear_qlr_ref(x, r, np.zeros_like(u), v)["Y"], tqo.tq_linear_ref(x, r)["Y"])
+    # sampled rows / columns equal the full evaluation
+    rows, cols = np.array([5, 0, 3]), np.array([8, 1, 2])
+    sub = tqo.tq_linear_qlr_ref(x, r, u, v, rows=rows, cols=cols)["Y"]
+    assert np.array_equal(sub, base[np.ix_(rows, cols)])
+
+
+def pin_qlr_requant_step(seed=22):
+    """The re-quantised first stage is a per-token symmetric 4-bit grid: every
+    code in [-8, 7], some code at +-7 in each token, and |c_t s_t - t| at most
+    half a step (round to nearest), on generic data with an outlier channel."""
+    rng = np.random.default_rng(seed)
+    n, d, m, rk = 40, 96, 11, 16
+    x = rng.standard_normal((n, d))
+    x[:, 5] *= 20.0
+    x = x.astype(np.float32)
+    u = (rng.standard_normal((d, rk)) * np.linspace(0.2, 3.0, rk)).astype(np.float32)
+    v = (0.1 * rng.standard_normal((rk, m))).astype(np.float32)
+    out = tqo.tq_linear_qlr_ref(x, np.zeros((d, m), np.float32), u, v)
+    ct, st, t = out["codes_t"].astype(np.int64), out["s_t"].astype(np.float64), out["t"].astype(np.float64)
+    assert ct.min() >= -8 and ct.max() <= 7
+    assert np.all(np.abs(ct).max(axis=1) == 7)
+    err = np.abs(ct * st[:, None] - t)
+    assert np.all(err <= 0.5 * st[:, None] * (1 + 1e-6))
+    # the rounding is to nearest: most codes sit well inside half a step
+    assert np.mean(err <= 0.25 * st[:, None]) > 0.45
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -446,6 +575,9 @@ ALL_PINS = [
     pin_group_stacking,
     pin_rht_rows,
     pin_rht_layer_rotation_invariance,
+    pin_qlr_lossless,
+    pin_qlr_invariants,
+    pin_qlr_requant_step,
 ]
 
 

@@ -279,6 +279,61 @@ tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, i
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Fully quantised low-rank branch (TwinQuant notes, "TwinQuant: Learnable
+ * Subspace Decomposition for W4A4 LLM Quantization", section 04.A error
+ * expression Q(X)[Q(U)Q(V) + Q(R)] and section 04.C, Figure 4: the low-rank
+ * product is taken on integer codes in two stages, the first stage's int32
+ * result re-quantised per token on-chip, and both branches meet in one
+ * epilogue):
+ *
+ *   acc  = C_x C_w^T,  acc1 = C_x C_u^T                       (exact, int32)
+ *   t    = fl32(fl32(acc1) * s_u)   per token; C_t, s_t = 4-bit absmax codes of t
+ *   Y    = s_x s_w (.) acc + (s_x s_t) s_v (.) (C_t C_v^T)
+ *
+ * U (d x r) and V (r x m) are quantised per column at 4 bits (symmetric, as
+ * the weight R); the token scale s_x is common to a row of t and is kept
+ * outside it.
+ *
+ * tq_lowrank_q_bytes -- size of the packed factors (0 for invalid shapes):
+ * r_pad = r rounded up to 32, 64, 128 or 256; U's codes as r_pad rows of
+ * d / 2 bytes (nibble-packed like tq_pack_weight, rows r .. r_pad - 1 zero),
+ * its r_pad scales, V's codes as m rows of r_pad / 2 bytes (ranks past r
+ * zero) and its m scales, each part 256-byte aligned.
+ */
+size_t tq_lowrank_q_bytes(int64_t d, int64_t m, int64_t r);
+
+/*
+ * tq_pack_lowrank_q -- quantises and packs U (d x r) and V (r x m), row-major
+ * device arrays of dtype dt, into lowrank_q (tq_lowrank_q_bytes bytes, caller
+ * owned, 16-byte aligned).  1 <= r <= 256, d % 32 == 0.  Offline.
+ */
+tq_status tq_pack_lowrank_q(const void* U, const void* V, tq_dtype dt, int64_t d, int64_t m, int64_t r,
+                            void* lowrank_q, hipStream_t stream);
+
+/*
+ * tq_linear_qlr -- the layer above on X (n x d, x_dt) with R packed by
+ * tq_pack_weight (4 bits) and the factors by tq_pack_lowrank_q; Y (n x m,
+ * y_dt).  Three launches on `stream`: the per-token quantiser (codes as int8
+ * in the tile GEMM's order), the first low-rank stage with its
+ * re-quantisation (writes only the r_pad code bytes and s_t of each token),
+ * and the tile GEMM whose epilogue adds the second stage on the int8 MFMA.
+ * ws: tq_linear_qlr_workspace_bytes(n, d, r) bytes of device memory.  Errors
+ * as tq_linear (r < 1 is TQ_ERR_SHAPE).
+ */
+size_t tq_linear_qlr_workspace_bytes(int64_t n, int64_t d, int64_t r);
+tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                        const void* w_codes, const float* s_w, const void* lowrank_q, void* Y,
+                        tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Byte offsets inside the tq_linear_qlr workspace: off[0] s_x (n fp32),
+ * off[1] activation codes (n x d int8, per 8 k the 4 even-k codes then the 4
+ * odd-k codes), off[2] s_t (n fp32), off[3] first-stage codes (n x r_pad int8
+ * in the same order over the ranks).  For tests.
+ */
+tq_status tq_linear_qlr_workspace_offsets(int64_t n, int64_t d, int64_t r, size_t off[4]);
+
+/*
  * tq_debug_accumulate -- exact integer product of two code matrices, exported.
  *   x_codes  n x k codes, w_codes m x k codes (both bits wide, K-contiguous).
  *   acc      out: n x m int32, acc[i][j] = sum_t x[i][t] * w[j][t], exactly.

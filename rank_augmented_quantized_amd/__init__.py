@@ -18,11 +18,16 @@ from .tq import (  # noqa: F401
     tq_linear_mp_rht,
     tq_linear_mp_workspace_bytes,
     tq_linear_mp_workspace_offsets,
+    tq_linear_qlr,
+    tq_linear_qlr_workspace_bytes,
+    tq_linear_qlr_workspace_offsets,
     tq_linear_workspace_bytes,
     tq_linear_workspace_offsets,
     tq_lowrank_group_bytes,
+    tq_lowrank_q_bytes,
     tq_pack_lowrank,
     tq_pack_lowrank_group,
+    tq_pack_lowrank_q,
     tq_pack_rht,
     tq_pack_weight,
     tq_profile_enable,

@@ -172,6 +172,46 @@ MpWs mp_ws(int64_t n, int64_t d, int64_t d_hi) {
 
 bool valid_dtype(tq_dtype t) { return t == TQ_F32 || t == TQ_BF16; }
 
+// Packed quantised low-rank factors: U^T codes (r_pad rows of d / 2 bytes),
+// s_u (r_pad), V^T codes (m rows of r_pad / 2 bytes), s_v (m).
+struct QlrPack {
+  size_t uc, su, vc, sv, total;
+};
+QlrPack qlr_pack(int64_t d, int64_t m, int64_t r_pad) {
+  QlrPack p{};
+  size_t o = 0;
+  p.uc = o;
+  o = align256(o + (size_t)r_pad * (size_t)d / 2);
+  p.su = o;
+  o = align256(o + (size_t)r_pad * 4);
+  p.vc = o;
+  o = align256(o + (size_t)m * (size_t)r_pad / 2);
+  p.sv = o;
+  o = align256(o + (size_t)m * 4);
+  p.total = o;
+  return p;
+}
+
+// Workspace of tq_linear_qlr: s_x, the int8-order activation codes, s_t and
+// the first stage's codes (r_pad int8 bytes per token).
+struct QlrWs {
+  size_t sx, xc, st, tc, total;
+};
+QlrWs qlr_ws(int64_t n, int64_t d, int64_t r_pad) {
+  QlrWs w{};
+  size_t o = 0;
+  w.sx = o;
+  o = align256(o + (size_t)n * 4);
+  w.xc = o;
+  o = align256(o + (size_t)n * (size_t)d);
+  w.st = o;
+  o = align256(o + (size_t)n * 4);
+  w.tc = o;
+  o = align256(o + (size_t)n * (size_t)r_pad);
+  w.total = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,7 +230,7 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 102; }
+int tq_version(void) { return 103; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
   if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
@@ -570,6 +610,89 @@ tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, i
          tq::launch_quant_rows_rht(X, x_dt == TQ_BF16, (int)n, (int)d, (int)(d - d_hi), rot, base + W.xl,
                                    (float*)(base + W.sxl), base + W.xh, (float*)(base + W.sxh), stream));
   return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
+}
+
+size_t tq_lowrank_q_bytes(int64_t d, int64_t m, int64_t r) {
+  if (d <= 0 || m <= 0 || r < 1 || r > 256) return 0;
+  return qlr_pack(d, m, r_padded(r)).total;
+}
+
+tq_status tq_pack_lowrank_q(const void* U, const void* V, tq_dtype dt, int64_t d, int64_t m, int64_t r,
+                            void* lowrank_q, hipStream_t stream) {
+  if (!valid_dtype(dt)) return TQ_ERR_DTYPE;
+  if (d <= 0 || m <= 0 || d > kMaxDim || m > kMaxDim || d % 32 || r < 1 || r > 256) return TQ_ERR_SHAPE;
+  if (!U || !V || !lowrank_q) return TQ_ERR_NULL;
+  if (!aligned16(lowrank_q)) return TQ_ERR_ALIGN;
+  const int rp = (int)r_padded(r);
+  const QlrPack P = qlr_pack(d, m, rp);
+  uint8_t* b = (uint8_t*)lowrank_q;
+  const bool bf = dt == TQ_BF16;
+  // U (d x r) per column -> r_pad code rows of d; V (r x m) per column -> m code rows of r_pad
+  TQ_RUN("pack_lowrank_q_u", stream,
+         tq::launch_pack_weight_padded(U, bf, (int)d, rp, (int)r, (int)d, (int)r, 4, b + P.uc, (float*)(b + P.su),
+                                       stream));
+  TQ_RUN("pack_lowrank_q_v", stream,
+         tq::launch_pack_weight_padded(V, bf, rp, (int)m, (int)m, (int)r, (int)m, 4, b + P.vc, (float*)(b + P.sv),
+                                       stream));
+  return TQ_OK;
+}
+
+size_t tq_linear_qlr_workspace_bytes(int64_t n, int64_t d, int64_t r) {
+  if (n < 0 || d <= 0 || r < 1 || r > 256) return 0;
+  return qlr_ws(n, d, r_padded(r)).total;
+}
+
+tq_status tq_linear_qlr_workspace_offsets(int64_t n, int64_t d, int64_t r, size_t off[4]) {
+  if (n < 0 || d <= 0 || r < 1 || r > 256) return TQ_ERR_SHAPE;
+  if (!off) return TQ_ERR_NULL;
+  const QlrWs W = qlr_ws(n, d, r_padded(r));
+  off[0] = W.sx;
+  off[1] = W.xc;
+  off[2] = W.st;
+  off[3] = W.tc;
+  return TQ_OK;
+}
+
+tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                        const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (r < 1) return TQ_ERR_SHAPE;
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank_q, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  const int64_t rp = r_padded(r);
+  const QlrWs W = qlr_ws(n, d, rp);
+  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
+  const QlrPack P = qlr_pack(d, m, rp);
+  uint8_t* base = (uint8_t*)ws;
+  const uint8_t* lq = (const uint8_t*)lowrank_q;
+  float* sx = (float*)(base + W.sx);
+  uint8_t* xc = base + W.xc;
+  float* stt = (float*)(base + W.st);
+  uint8_t* tc = base + W.tc;
+  TQ_RUN("quant_rows_qlr", stream,
+         tq::launch_quant_rows_i8(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, 4, xc, sx, nullptr, nullptr, stream));
+  TQ_RUN("qlr_stage1", stream,
+         tq::launch_qlr_stage1(xc, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, tc, stt, stream));
+  GemmArgs g{};
+  g.A = xc;
+  g.lda = d;
+  g.B = (const uint8_t*)w_codes;
+  g.ldb = d / 2;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(d / 2);
+  g.sx = sx;
+  g.sw = s_w;
+  g.r_pad = (int)rp;
+  g.Vq = lq + P.vc;
+  g.sv = (const float*)(lq + P.sv);
+  g.Tq = tc;
+  g.st = stt;
+  g.Y = Y;
+  g.ldy = m;
+  g.y_bf16 = y_dt == TQ_BF16;
+  TQ_RUN("gemm_qlr", stream, tq::launch_gemm8(g, tq::EPI_QLR, true, 4, stream));
+  return TQ_OK;
 }
 
 tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m, int bits,

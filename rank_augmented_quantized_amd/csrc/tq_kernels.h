@@ -11,7 +11,7 @@
 
 namespace tq {
 
-enum Epilogue { EPI_ACC = 0, EPI_LINEAR = 1, EPI_MP = 2 };
+enum Epilogue { EPI_ACC = 0, EPI_LINEAR = 1, EPI_MP = 2, EPI_QLR = 3 };
 
 // Timing events for the next launch, set by the library's profiler.  A
 // launcher that supports them (hipExtLaunchKernelGGL: timestamps taken by
@@ -104,10 +104,20 @@ struct GemmArgs {
   int64_t ldy;  // elements
   int y_bf16;
   int32_t* acc;  // EPI_ACC output, M x N
+  // EPI_QLR, the quantised low-rank branch: second-stage weight codes
+  // (N rows of r_pad / 2 nibble-packed bytes) and scales, first-stage codes
+  // (M rows of r_pad int8 bytes in the int8 code order) and scales
+  const uint8_t* Vq;
+  const float* sv;
+  const uint8_t* Tq;
+  const float* st;
 };
 
 hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, void* codes, float* sw,
                               hipStream_t st);
+// The same for a dv x mv matrix (row stride ldw elements) zero-padded to d x m.
+hipError_t launch_pack_weight_padded(const void* W, bool bf16, int d, int m, int ldw, int dv, int mv, int bits,
+                                     void* codes, float* sw, hipStream_t st);
 // L1^T (rows1 rows of d, rows r.. zero) to out1 and L2^T (m x r_pad) to out2, bf16.
 hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, int rows1,
                                void* out1, void* out2, hipStream_t st);
@@ -185,6 +195,13 @@ hipError_t launch_pack_rht(const float* signs, const int32_t* perm, int d, void*
 // int8 in the tile GEMM's order (dl bytes per row), [dl, d) at 8 bits.
 hipError_t launch_quant_rows_rht(const void* X, bool bf16, int n, int d, int dl, const void* rot, void* xl,
                                  float* sxl, void* xh, float* sxh, hipStream_t st);
+// First stage of the quantised low-rank branch (tq_qlr.hip): the exact
+// integer product of the int8-order activation codes (n x d) with the packed
+// codes of U^T (r_pad rows of d / 2 bytes), scaled per rank by s_u in fp32 and
+// re-quantised per token at 4 bits: codes to ct (n rows of r_pad int8 bytes,
+// int8 code order), scales to st.  d % 32 == 0, r_pad in {32, 64, 128, 256}.
+hipError_t launch_qlr_stage1(const uint8_t* xc, int n, int d, const uint8_t* uc, const float* su, int r_pad,
+                             uint8_t* ct, float* st, hipStream_t stream);
 bool small_fused_ok(int n, int d, int r_pad);
 SmallPlan plan_small(int n, int d, int r_pad);
 hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);

@@ -24,8 +24,10 @@ __device__ __forceinline__ float ld_f32<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ld_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
 
+// W is dv x mv (row stride ldw), taken as zero-padded to d x m: padded
+// channels get scale 0 and codes 0, padded rows codes 0.
 template <typename T, int BITS>
-__global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, int d, int m,
+__global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, int d, int m, int ldw, int dv, int mv,
                                                      uint8_t* __restrict__ codes, float* __restrict__ sw) {
   __shared__ float red[4][64];
   __shared__ float tile[64][65];
@@ -33,9 +35,11 @@ __global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, in
   __shared__ int s_f[64];
   const int tid = threadIdx.x, tx = tid & 63, ty = tid >> 6;
   const int j0 = blockIdx.x * 64;
-  const int j = min(j0 + tx, m - 1);
+  const int j = min(j0 + tx, mv - 1);
+  const bool jv = j0 + tx < mv;
   float am = 0.0f;
-  for (int k = ty; k < d; k += 4) am = fmaxf(am, fabsf(ld_f32<T>(W + (size_t)k * m + j)));
+  if (jv)
+    for (int k = ty; k < dv; k += 4) am = fmaxf(am, fabsf(ld_f32<T>(W + (size_t)k * ldw + j)));
   red[ty][tx] = am;
   __syncthreads();
   if (ty == 0) {
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, in
   const RowScale rs = {s_s[c], s_r[c], s_f[c] != 0};
   for (int k0 = 0; k0 < d; k0 += 64) {
     for (int kk = ty; kk < 64; kk += 4)
-      tile[kk][tx] = (k0 + kk < d) ? ld_f32<T>(W + (size_t)(k0 + kk) * m + j) : 0.0f;
+      tile[kk][tx] = (jv && k0 + kk < dv) ? ld_f32<T>(W + (size_t)(k0 + kk) * ldw + j) : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -518,20 +522,25 @@ __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 template <typename T>
-static hipError_t launch_pack_weight_t(const void* W, int d, int m, int bits, void* codes, float* sw,
-                                       hipStream_t st) {
+static hipError_t launch_pack_weight_t(const void* W, int d, int m, int ldw, int dv, int mv, int bits, void* codes,
+                                       float* sw, hipStream_t st) {
   dim3 grid((m + 63) / 64), block(256);
   if (bits == 4)
-    hipLaunchKernelGGL((k_pack_weight<T, 4>), grid, block, 0, st, (const T*)W, d, m, (uint8_t*)codes, sw);
+    hipLaunchKernelGGL((k_pack_weight<T, 4>), grid, block, 0, st, (const T*)W, d, m, ldw, dv, mv, (uint8_t*)codes, sw);
   else
-    hipLaunchKernelGGL((k_pack_weight<T, 8>), grid, block, 0, st, (const T*)W, d, m, (uint8_t*)codes, sw);
+    hipLaunchKernelGGL((k_pack_weight<T, 8>), grid, block, 0, st, (const T*)W, d, m, ldw, dv, mv, (uint8_t*)codes, sw);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, void* codes, float* sw,
                               hipStream_t st) {
-  return bf16 ? launch_pack_weight_t<bf16_t>(W, d, m, bits, codes, sw, st)
-              : launch_pack_weight_t<float>(W, d, m, bits, codes, sw, st);
+  return launch_pack_weight_padded(W, bf16, d, m, m, d, m, bits, codes, sw, st);
+}
+
+hipError_t launch_pack_weight_padded(const void* W, bool bf16, int d, int m, int ldw, int dv, int mv, int bits,
+                                     void* codes, float* sw, hipStream_t st) {
+  return bf16 ? launch_pack_weight_t<bf16_t>(W, d, m, ldw, dv, mv, bits, codes, sw, st)
+              : launch_pack_weight_t<float>(W, d, m, ldw, dv, mv, bits, codes, sw, st);
 }
 
 hipError_t launch_pack_lowrank(const void* L1, const void* L2, bool bf16, int d, int m, int r, int r_pad, int rows1,

@@ -28,7 +28,8 @@ EXPORTS = (
     "tq_linear_mp_workspace_bytes", "tq_linear_mp", "tq_debug_accumulate", "tq_profile_enable",
     "tq_profile_read", "tq_profile_reset", "tq_lowrank_group_bytes", "tq_pack_lowrank_group",
     "tq_linear_group_workspace_bytes", "tq_linear_group", "tq_linear_mp_workspace_offsets", "tq_rht_bytes",
-    "tq_pack_rht", "tq_linear_mp_rht",
+    "tq_pack_rht", "tq_linear_mp_rht", "tq_lowrank_q_bytes", "tq_pack_lowrank_q", "tq_linear_qlr_workspace_bytes",
+    "tq_linear_qlr_workspace_offsets", "tq_linear_qlr",
 )
 
 
@@ -82,6 +83,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_pack_rht": (st, [ptr, ptr, i64, ptr, ptr]),
         "tq_linear_mp_rht": (st, [ptr, c_int, i64, i64, i64, ptr, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz,
                                   ptr]),
+        "tq_lowrank_q_bytes": (sz, [i64, i64, i64]),
+        "tq_pack_lowrank_q": (st, [ptr, ptr, c_int, i64, i64, i64, ptr, ptr]),
+        "tq_linear_qlr_workspace_bytes": (sz, [i64, i64, i64]),
+        "tq_linear_qlr_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "tq_linear_qlr": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -288,6 +294,47 @@ def tq_linear_mp_rht(X, d_hi: int, rot, wl_codes, s_wl, wh_codes, s_wh, m: int, 
     _check("tq_linear_mp_rht", lib.tq_linear_mp_rht(_p(X), _dt(X), n, d, d_hi, _p(rot), m, _p(wl_codes), _p(s_wl),
                                                     _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
                                                     _stream(X)))
+    return Y
+
+
+def tq_lowrank_q_bytes(d: int, m: int, r: int) -> int:
+    return load().tq_lowrank_q_bytes(d, m, r)
+
+
+def tq_pack_lowrank_q(U, V, out=None):
+    """Quantise (per column, 4 bits) and lay out the low-rank factors U (d x r), V (r x m) for tq_linear_qlr."""
+    lib = load()
+    _need_cuda(U, V)
+    d, r = U.shape
+    m = V.shape[1]
+    if out is None:
+        out = torch.empty(lib.tq_lowrank_q_bytes(d, m, r), dtype=torch.uint8, device=U.device)
+    _check("tq_pack_lowrank_q", lib.tq_pack_lowrank_q(_p(U), _p(V), _dt(U), d, m, r, _p(out), _stream(U)))
+    return out
+
+
+def tq_linear_qlr_workspace_bytes(n: int, d: int, r: int) -> int:
+    return load().tq_linear_qlr_workspace_bytes(n, d, r)
+
+
+def tq_linear_qlr_workspace_offsets(n: int, d: int, r: int) -> dict:
+    """Byte offsets of s_x, the activation codes, s_t and the first-stage codes inside tq_linear_qlr's workspace."""
+    off = (ctypes.c_size_t * 4)()
+    _check("tq_linear_qlr_workspace_offsets", load().tq_linear_qlr_workspace_offsets(n, d, r, off))
+    return {"s_x": off[0], "x_codes": off[1], "s_t": off[2], "t_codes": off[3]}
+
+
+def tq_linear_qlr(X, w_codes, s_w, lowrank_q, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
+    """Y = s_x s_w (Q4(X) Q4(R)) + (s_x s_t) s_v (Q4(T) Q4(V)), T the per-token re-quantised Q4(X) Q4(U)."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, lowrank_q, Y, ws)
+    n, d = X.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = torch.empty(max(1, tq_linear_qlr_workspace_bytes(n, d, r)), dtype=torch.uint8, device=X.device)
+    _check("tq_linear_qlr", lib.tq_linear_qlr(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank_q),
+                                              _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
     return Y
 
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 102
+    assert lib.tq_version() == 103
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -162,6 +162,29 @@ def test_rht_validation(lib):
     assert lib.tq_linear_mp_rht(A, 1, 0, d, dh, NUL, m, A, B, C, A, B, 1, C, 0, S) == 0
     off = tqb.tq_linear_mp_workspace_offsets(n, d, dh)
     assert off["x_codes_h"] >= off["x_codes_l"] + n * (d - dh) and all(v % 256 == 0 for v in off.values())
+
+
+def test_qlr_validation(lib):
+    # packed factors: U^T codes r_pad x d/2, s_u r_pad, V^T codes m x r_pad/2, s_v m (256-byte aligned parts)
+    assert lib.tq_lowrank_q_bytes(512, 256, 32) == 32 * 256 + 256 + 256 * 16 + 1024
+    assert lib.tq_lowrank_q_bytes(512, 256, 0) == 0 and lib.tq_lowrank_q_bytes(512, 256, 257) == 0
+    assert lib.tq_pack_lowrank_q(A, B, 1, 520, 256, 32, C, S) == -2  # d % 32
+    assert lib.tq_pack_lowrank_q(A, B, 1, 512, 256, 0, C, S) == -2
+    assert lib.tq_pack_lowrank_q(A, NUL, 1, 512, 256, 32, C, S) == -1
+    assert lib.tq_pack_lowrank_q(A, B, 1, 512, 256, 32, MIS, S) == -5
+    assert lib.tq_pack_lowrank_q(A, B, 7, 512, 256, 32, C, S) == -3
+    n, d, m, r = 64, 512, 256, 32
+    need = lib.tq_linear_qlr_workspace_bytes(n, d, r)
+    assert need == 256 + n * d + 256 + n * 32
+    assert lib.tq_linear_qlr(A, 1, n, d, m, 0, B, C, A, B, 1, C, need, S) == -2  # r < 1
+    assert lib.tq_linear_qlr(A, 1, n, 520, m, r, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear_qlr(A, 1, n, d, m, r, B, C, NUL, B, 1, C, need, S) == -1
+    assert lib.tq_linear_qlr(A, 1, n, d, m, r, B, C, A, MIS, 1, C, need, S) == -5
+    assert lib.tq_linear_qlr(A, 1, n, d, m, r, B, C, A, B, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_qlr(A, 1, 0, d, m, r, B, C, A, B, 1, C, 0, S) == 0
+    off = tqb.tq_linear_qlr_workspace_offsets(n, d, r)
+    assert off["x_codes"] >= off["s_x"] + 4 * n and off["t_codes"] >= off["s_t"] + 4 * n
+    assert all(v % 256 == 0 for v in off.values())
 
 
 def test_linear_mp_validation(lib):

@@ -669,10 +669,16 @@ tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int6
   uint8_t* xc = base + W.xc;
   float* stt = (float*)(base + W.st);
   uint8_t* tc = base + W.tc;
-  TQ_RUN("quant_rows_qlr", stream,
-         tq::launch_quant_rows_i8(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, 4, xc, sx, nullptr, nullptr, stream));
-  TQ_RUN("qlr_stage1", stream,
-         tq::launch_qlr_stage1(xc, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, tc, stt, stream));
+  if (tq::qlr_fused_ok((int)d, (int)rp)) {
+    TQ_RUN("qlr_prologue", stream,
+           tq::launch_qlr_prologue(X, x_dt == TQ_BF16, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp,
+                                   xc, sx, tc, stt, stream));
+  } else {
+    TQ_RUN("quant_rows_qlr", stream,
+           tq::launch_quant_rows_i8(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, 4, xc, sx, nullptr, nullptr, stream));
+    TQ_RUN("qlr_stage1", stream,
+           tq::launch_qlr_stage1(xc, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, tc, stt, stream));
+  }
   GemmArgs g{};
   g.A = xc;
   g.lda = d;

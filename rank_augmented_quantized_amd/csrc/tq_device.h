@@ -280,4 +280,41 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(m);
 }
 
+// One token row (nch chunks of 8 values, chunk lane + 64 i in slot i) quantised
+// at 4 bits by one wave with the whole row in registers: the codes go to
+// `codes` as int8 in the tile GEMM's order and, when `copy` is not null, to
+// `copy` as well; returns s_x.
+template <typename T, int CH>
+__device__ __forceinline__ float quant_row_i8_wave(const T* x, int nch, int lane, uint8_t* codes, uint8_t* copy) {
+  Row8<T> r[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ch = lane + 64 * i;
+    if (ch < nch) r[i].load(x + 8 * ch);
+  }
+  float mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (lane + 64 * i < nch) {
+      float v[8];
+      r[i].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
+  }
+  const RowScale rs = row_scale<4>(wave_max(mx));
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int ch = lane + 64 * i;
+    if (ch < nch) {
+      float v[8];
+      r[i].get(v);
+      const uint2 c = quant8_int8(v, rs);
+      *reinterpret_cast<uint2*>(codes + 8 * ch) = c;
+      if (copy) *reinterpret_cast<uint2*>(copy + 8 * ch) = c;
+    }
+  }
+  return rs.s;
+}
+
 }  // namespace tq

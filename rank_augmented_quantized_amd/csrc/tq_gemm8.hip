@@ -407,57 +407,50 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
                                                                 0, 0, 0);
       }
     }
+    // Second stage of the quantised low-rank branch, (s_x s_t) s_v (Q(T) Q(V))
+    // (TwinQuant notes, section 04.C: both stages on integer codes, merged in
+    // the residual GEMM's epilogue), added block by block in the store loop
+    // below: each 32 x 32 block takes its exact int32 product over the r_pad
+    // ranks on v_mfma_i32_32x32x32_i8 and adds it to y in fp32 just before
+    // the block is stored, so the fp32 tile shrinks as the int32 blocks come.
+    // V rows are the channels' nibble-packed codes (r_pad / 2 bytes; step q,
+    // lane group lg: bytes 16 q + 8 lg, 16 codes expanded by unpack16, so the
+    // sum carries a factor 16, taken out exactly with the scale), T rows the
+    // tokens' int8 codes (r_pad bytes; bytes 32 q + 16 lg: the same 16 ranks
+    // in the same order).
+    const uint8_t* vq[FM];
+    const uint8_t* tq8[FN];
+    float stv[FN];
     if constexpr (EPI == EPI_QLR) {
-      // Second stage of the quantised low-rank branch, (s_x s_t) s_v (Q(T) Q(V))
-      // (TwinQuant notes, section 04.C: both stages on integer codes, merged
-      // in the residual GEMM's epilogue): each 32 x 32 block takes its exact
-      // int32 product over the r_pad ranks on v_mfma_i32_32x32x32_i8 and adds
-      // it to y in fp32.  V rows are the channels' nibble-packed codes (r_pad
-      // / 2 bytes; step q, lane group lg: bytes 16 q + 8 lg, 16 codes expanded
-      // by unpack16, so the sum carries a factor 16, taken out exactly with
-      // the scale), T rows the tokens' int8 codes (r_pad bytes; bytes 32 q +
-      // 16 lg: the same 16 ranks in the same order).  The blocks run one after
-      // another (the fence on y), so only one int32 block is live beside y.
-      const int nq = g.r_pad >> 5;
-      const uint8_t* vq[FM];
-      const uint8_t* tq8[FN];
 #pragma unroll
       for (int a = 0; a < FM; ++a)
         vq[a] = g.Vq + (size_t)min(ch0 + wm * WM + 32 * a + l32, g.N - 1) * (g.r_pad / 2) + 8 * lg;
 #pragma unroll
-      for (int b = 0; b < FN; ++b) tq8[b] = g.Tq + (size_t)min(tok(b), g.M - 1) * g.r_pad + 16 * lg;
-      float stv[FN];
-#pragma unroll
       for (int b = 0; b < FN; ++b) {
         const int t = min(tok(b), g.M - 1);
+        tq8[b] = g.Tq + (size_t)t * g.r_pad + 16 * lg;
         stv[b] = g.sx[t] * g.st[t] * (1.0f / 16);
       }
-#pragma unroll
-      for (int a = 0; a < FM; ++a) {
-        float4 svv[4];
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) svv[e4] = load4(g.sv, chan(a, e4));
-#pragma unroll
-        for (int b = 0; b < FN; ++b) {
-          i32x16 acc2;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc2[i] = 0;
-          for (int q = 0; q < nq; ++q) {
-            const uint2 va = *reinterpret_cast<const uint2*>(vq[a] + 16 * q);
-            const i32x4 tb = *reinterpret_cast<const i32x4*>(tq8[b] + 32 * q);
-            acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(va.x, va.y), tb, acc2, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            y[a][b][4 * e4 + 0] += (float)acc2[4 * e4 + 0] * (svv[e4].x * stv[b]);
-            y[a][b][4 * e4 + 1] += (float)acc2[4 * e4 + 1] * (svv[e4].y * stv[b]);
-            y[a][b][4 * e4 + 2] += (float)acc2[4 * e4 + 2] * (svv[e4].z * stv[b]);
-            y[a][b][4 * e4 + 3] += (float)acc2[4 * e4 + 3] * (svv[e4].w * stv[b]);
-          }
-          asm volatile("" : "+v"(y[a][b]));
-        }
-      }
     }
+    auto qlr_add = [&](int a, int b, const uint2& v0, const float4 (&svv)[4]) {
+      i32x16 acc2;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc2[i] = 0;
+      acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(v0.x, v0.y), *reinterpret_cast<const i32x4*>(tq8[b]),
+                                                   acc2, 0, 0, 0);
+      for (int q = 1; q < (g.r_pad >> 5); ++q) {
+        const uint2 va = *reinterpret_cast<const uint2*>(vq[a] + 16 * q);
+        const i32x4 tb = *reinterpret_cast<const i32x4*>(tq8[b] + 32 * q);
+        acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(va.x, va.y), tb, acc2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        y[a][b][4 * e4 + 0] += (float)acc2[4 * e4 + 0] * (svv[e4].x * stv[b]);
+        y[a][b][4 * e4 + 1] += (float)acc2[4 * e4 + 1] * (svv[e4].y * stv[b]);
+        y[a][b][4 * e4 + 2] += (float)acc2[4 * e4 + 2] * (svv[e4].z * stv[b]);
+        y[a][b][4 * e4 + 3] += (float)acc2[4 * e4 + 3] * (svv[e4].w * stv[b]);
+      }
+    };
     if constexpr (EPI == EPI_MP) {
       // Two-subspace layer: add the 8-bit subspace, s_x2 s_w2 (Q8(X_h) Q8(W_h))
       // (CoQuant notes, "CoQuant: Joint Weight-Activation Subspace Projection
@@ -544,8 +537,16 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     auto yslot = [&](int row, int j, int half) -> int { return ychunk(row, j) + 8 * (half ^ ((row >> 4) & 1)); };
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
+      uint2 v0;
+      float4 svv[4];
+      if constexpr (EPI == EPI_QLR) {
+        v0 = *reinterpret_cast<const uint2*>(vq[a]);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) svv[e4] = load4(g.sv, chan(a, e4));
+      }
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
+        if constexpr (EPI == EPI_QLR) qlr_add(a, b, v0, svv);
         if (g.y_bf16) {
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {

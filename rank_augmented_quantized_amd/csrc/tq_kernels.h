@@ -202,6 +202,11 @@ hipError_t launch_quant_rows_rht(const void* X, bool bf16, int n, int d, int dl,
 // int8 code order), scales to st.  d % 32 == 0, r_pad in {32, 64, 128, 256}.
 hipError_t launch_qlr_stage1(const uint8_t* xc, int n, int d, const uint8_t* uc, const float* su, int r_pad,
                              uint8_t* ct, float* st, hipStream_t stream);
+// The quantiser and the first stage in one launch (d <= 4096, r_pad <= 128):
+// X (n x d) -> s_x, int8-order codes (n x d), first-stage codes and s_t as above.
+bool qlr_fused_ok(int d, int r_pad);
+hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uint8_t* uc, const float* su, int r_pad,
+                               uint8_t* xc, float* sx, uint8_t* ct, float* st, hipStream_t stream);
 bool small_fused_ok(int n, int d, int r_pad);
 SmallPlan plan_small(int n, int d, int r_pad);
 hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);

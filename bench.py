@@ -191,6 +191,33 @@ class GroupCase:
                               Y=self.Ys[g], ws=self.ws1)
 
 
+class QlrCase:
+    """The layer with its low-rank branch quantised too (tq_linear_qlr): Q(U), Q(V) packed from the workload's
+    L1, L2; `copies` weight sets cycled."""
+
+    def __init__(self, wl, n, copies, torch, tq, dev):
+        from workloads import draw_linear
+
+        c = draw_linear(wl, n=n)
+        self.n, self.d, self.m, self.r = n, wl.d, wl.m, wl.r
+        self.X = torch.from_numpy(c["X"]).to(dev).bfloat16()
+        R = torch.from_numpy(c["R"]).to(dev)
+        U = torch.from_numpy(c["L1"]).to(dev)
+        V = torch.from_numpy(c["L2"]).to(dev)
+        self.w = []
+        for _ in range(copies):
+            wc, sw = tq.tq_pack_weight(R, 4)
+            self.w.append((wc, sw, tq.tq_pack_lowrank_q(U, V)))
+        del R, U, V
+        self.Y = torch.empty((n, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(tq.tq_linear_qlr_workspace_bytes(n, self.d, self.r), dtype=torch.uint8, device=dev)
+        self.tq = tq
+
+    def __call__(self, i):
+        wc, sw, lq = self.w[i % len(self.w)]
+        self.tq.tq_linear_qlr(self.X, wc, sw, lq, self.m, self.r, Y=self.Y, ws=self.ws)
+
+
 class MpCase:
     """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
     applied online inside the quantiser (tq_linear_mp_rht)."""
@@ -349,6 +376,26 @@ def main():
             log(f"[bench] sweep {row}")
             del c
             torch.cuda.empty_cache()
+        for name, ns in (("attn_proj", (4096,)), ("mlp_gate_up", (1, 4096))):
+            w = WORKLOADS[name]
+            for nn in ns:
+                c = QlrCase(w, nn, args.copies if nn <= 256 else 2, torch, tq, dev)
+                t = time_calls(c, max(20, args.steps // 2), 10, torch)
+                km = kernel_ms(c, 20, torch, tq)
+                o = 2.0 * nn * w.d * w.m
+                # X, the weight codes and scales, Q(U) and Q(V) with their scales (r padded to 32), Y
+                rp = max(32, w.r)
+                b = nn * w.d * 2 + w.d * w.m // 2 + 4 * w.m + rp * w.d // 2 + 4 * rp + w.m * rp // 2 + 4 * w.m + \
+                    2 * nn * w.m
+                row = {"workload": f"{w.title}: low-rank branch quantised too", "n": nn, "us": round(t * 1e3, 2),
+                       "TOPS": round(o / (t * 1e-3) / 1e12, 2), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                       "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                       "pct_hbm": round(100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                       "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+                sweep.append(row)
+                log(f"[bench] sweep {row}")
+                del c
+                torch.cuda.empty_cache()
         w = WORKLOADS["two_subspace"]
         for rht in (False, True):
             log(f"[bench] {w.title}{' (rotation online)' if rht else ''}: building inputs")

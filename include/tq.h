@@ -313,12 +313,13 @@ tq_status tq_pack_lowrank_q(const void* U, const void* V, tq_dtype dt, int64_t d
 /*
  * tq_linear_qlr -- the layer above on X (n x d, x_dt) with R packed by
  * tq_pack_weight (4 bits) and the factors by tq_pack_lowrank_q; Y (n x m,
- * y_dt).  Three launches on `stream`: the per-token quantiser (codes as int8
- * in the tile GEMM's order), the first low-rank stage with its
- * re-quantisation (writes only the r_pad code bytes and s_t of each token),
- * and the tile GEMM whose epilogue adds the second stage on the int8 MFMA.
- * ws: tq_linear_qlr_workspace_bytes(n, d, r) bytes of device memory.  Errors
- * as tq_linear (r < 1 is TQ_ERR_SHAPE).
+ * y_dt).  Launches on `stream`: the per-token quantiser together with the
+ * first low-rank stage and its re-quantisation (one launch for d <= 4096 and
+ * r <= 128, else two; only the r_pad code bytes and s_t of each token are
+ * written), then the integer GEMM -- the tile GEMM, or for n <= 32 the
+ * weight-streaming small-n GEMM -- whose epilogue adds the second stage on
+ * the int8 MFMA.  ws: tq_linear_qlr_workspace_bytes(n, d, r) bytes of device
+ * memory.  Errors as tq_linear (r < 1 is TQ_ERR_SHAPE).
  */
 size_t tq_linear_qlr_workspace_bytes(int64_t n, int64_t d, int64_t r);
 tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
@@ -328,8 +329,9 @@ tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int6
 /*
  * Byte offsets inside the tq_linear_qlr workspace: off[0] s_x (n fp32),
  * off[1] activation codes (n x d int8, per 8 k the 4 even-k codes then the 4
- * odd-k codes), off[2] s_t (n fp32), off[3] first-stage codes (n x r_pad int8
- * in the same order over the ranks).  For tests.
+ * odd-k codes; for n <= 32 nibble-packed, n x d / 2 bytes), off[2] s_t
+ * (n fp32), off[3] first-stage codes (n x r_pad int8 in the int8 order over
+ * the ranks).  For tests.
  */
 tq_status tq_linear_qlr_workspace_offsets(int64_t n, int64_t d, int64_t r, size_t off[4]);
 

@@ -669,19 +669,28 @@ tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int6
   uint8_t* xc = base + W.xc;
   float* stt = (float*)(base + W.st);
   uint8_t* tc = base + W.tc;
+  // few tokens: nibble-packed activation codes for the weight-streaming
+  // small-n GEMM; otherwise int8 codes for the tile GEMM
+  const bool small = n <= kSmallN;
+  const bool xb = x_dt == TQ_BF16;
   if (tq::qlr_fused_ok((int)d, (int)rp)) {
     TQ_RUN("qlr_prologue", stream,
-           tq::launch_qlr_prologue(X, x_dt == TQ_BF16, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp,
-                                   xc, sx, tc, stt, stream));
+           tq::launch_qlr_prologue(X, xb, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, xc, sx, tc,
+                                   stt, small, stream));
   } else {
-    TQ_RUN("quant_rows_qlr", stream,
-           tq::launch_quant_rows_i8(X, x_dt == TQ_BF16, (int)n, (int)d, (int)d, 4, xc, sx, nullptr, nullptr, stream));
+    if (small)
+      TQ_RUN("quant_rows_qlr", stream,
+             tq::launch_quant_rows_fast(X, xb, (int)n, (int)d, (int)d, 4, 4, xc, sx, nullptr, nullptr, stream));
+    else
+      TQ_RUN("quant_rows_qlr", stream,
+             tq::launch_quant_rows_i8(X, xb, (int)n, (int)d, (int)d, 4, xc, sx, nullptr, nullptr, stream));
     TQ_RUN("qlr_stage1", stream,
-           tq::launch_qlr_stage1(xc, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, tc, stt, stream));
+           tq::launch_qlr_stage1(xc, (int)n, (int)d, lq + P.uc, (const float*)(lq + P.su), (int)rp, tc, stt, small,
+                                 stream));
   }
   GemmArgs g{};
   g.A = xc;
-  g.lda = d;
+  g.lda = small ? d / 2 : d;
   g.B = (const uint8_t*)w_codes;
   g.ldb = d / 2;
   g.M = (int)n;
@@ -697,7 +706,10 @@ tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int6
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
-  TQ_RUN("gemm_qlr", stream, tq::launch_gemm8(g, tq::EPI_QLR, true, 4, stream));
+  if (small)
+    TQ_RUN("gemm_small_n_qlr", stream, tq::launch_gemv(g, 4, tq::EPI_QLR, stream));
+  else
+    TQ_RUN("gemm_qlr", stream, tq::launch_gemm8(g, tq::EPI_QLR, true, 4, stream));
   return TQ_OK;
 }
 

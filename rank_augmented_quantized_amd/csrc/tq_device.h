@@ -282,9 +282,10 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // One token row (nch chunks of 8 values, chunk lane + 64 i in slot i) quantised
 // at 4 bits by one wave with the whole row in registers: the codes go to
-// `codes` as int8 in the tile GEMM's order and, when `copy` is not null, to
-// `copy` as well; returns s_x.
-template <typename T, int CH>
+// `codes` as int8 in the tile GEMM's order (PK: nibble-packed, even k in the
+// low nibble, d / 2 bytes) and, when `copy` is not null, to `copy` as int8
+// in the tile GEMM's order; returns s_x.
+template <typename T, int CH, bool PK = false>
 __device__ __forceinline__ float quant_row_i8_wave(const T* x, int nch, int lane, uint8_t* codes, uint8_t* copy) {
   Row8<T> r[CH];
 #pragma unroll
@@ -310,7 +311,10 @@ __device__ __forceinline__ float quant_row_i8_wave(const T* x, int nch, int lane
       float v[8];
       r[i].get(v);
       const uint2 c = quant8_int8(v, rs);
-      *reinterpret_cast<uint2*>(codes + 8 * ch) = c;
+      if constexpr (PK)  // byte j: code 2 j (even k, low nibble) and code 2 j + 1
+        *reinterpret_cast<uint32_t*>(codes + 4 * ch) = (c.x & 0x0F0F0F0Fu) | ((c.y & 0x0F0F0F0Fu) << 4);
+      else
+        *reinterpret_cast<uint2*>(codes + 8 * ch) = c;
       if (copy) *reinterpret_cast<uint2*>(copy + 8 * ch) = c;
     }
   }

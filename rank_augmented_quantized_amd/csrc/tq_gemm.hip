@@ -47,6 +47,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   constexpr int NT = WAVES * 64;
   constexpr int MT = TWO ? 32 : 16;  // token rows held for the low-rank stage
   constexpr bool LR = EPI == EPI_LINEAR;
+  constexpr bool QL = EPI == EPI_QLR;  // quantised low-rank branch: second stage on the int8 MFMA
   __shared__ int red[WAVES][TWO ? 2 : 1][4][64];
   __shared__ __attribute__((aligned(16))) bf16_t sT[LR ? MT * 256 : 1];
   __shared__ __attribute__((aligned(16))) bf16_t sL[LR ? 16 * 256 : 1];
@@ -136,10 +137,29 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 
   // ---- issue every load of the first batch before any wait ----
   float sxv[4], swv = 0.0f;  // epilogue scales
-  if (LR) {
+  if (LR || QL) {
     swv = g.sw[min(n0 + l16, g.N - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
+  }
+  // QL: the first 64 ranks of the second stage's operands and its scales
+  // (lane: token or channel l % 16, the 16 ranks 16 (l / 16) ..; ranks past
+  // r_pad are zero), loaded with the first batch
+  i32x4 qa = {0, 0, 0, 0};
+  uint2 qb = {0u, 0u};
+  float qs[4], qsv = 0.0f;
+  const uint8_t* qtp = nullptr;
+  const uint8_t* qvp = nullptr;
+  if constexpr (QL) {
+    qtp = g.Tq + (size_t)min(16 * (wave & 1) + l16, g.M - 1) * g.r_pad + 16 * lg;
+    qvp = g.Vq + (size_t)min(n0 + l16, g.N - 1) * (g.r_pad / 2) + 8 * lg;
+    if (16 * lg < g.r_pad) {
+      qa = *reinterpret_cast<const i32x4*>(qtp);
+      qb = *reinterpret_cast<const uint2*>(qvp);
+    }
+    qsv = g.sv[min(n0 + l16, g.N - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qs[i] = g.st[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)] * (1.0f / 16);
   }
   load_batch(sbeg);
   // Low-rank operands, with clamped (always valid) indices, masked where used,
@@ -257,6 +277,21 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     }
   } else {
     f32x4 lr = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (QL) {
+      // (s_x s_t) s_v (Q(T) Q(V)) for the tile's 16 tokens and the block's 16
+      // channels: exact int32 over the ranks (V expanded by unpack16: a factor
+      // 16, taken out with s_t), 64 ranks per v_mfma_i32_16x16x64_i8
+      i32x4 q2 = {0, 0, 0, 0};
+      q2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa, unpack16(qb.x, qb.y), q2, 0, 0, 0);
+      for (int q0 = 64; q0 < g.r_pad; q0 += 64) {
+        const bool ok = q0 + 16 * lg < g.r_pad;
+        const i32x4 a = ok ? *reinterpret_cast<const i32x4*>(qtp + q0) : i32x4{0, 0, 0, 0};
+        const uint2 b = ok ? *reinterpret_cast<const uint2*>(qvp + q0 / 2) : uint2{0u, 0u};
+        q2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack16(b.x, b.y), q2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lr[i] = (float)q2[i] * (sxv[i] * qs[i] * qsv);
+    }
     for (int t0 = 0; t0 < rp; t0 += 32) {
       // A: T rows (tokens), B: L2^T rows (channels); 8 consecutive t per lane
       const uint4 a8 = *reinterpret_cast<const uint4*>(sT + (16 * tile + l16) * rp + t0 + 8 * lg);
@@ -314,6 +349,7 @@ hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st
   if (bits == 4) {
     if (epi == EPI_ACC) return gemv_cols<4, EPI_ACC>(g, st);
     if (epi == EPI_LINEAR) return gemv_cols<4, EPI_LINEAR>(g, st);
+    if (epi == EPI_QLR) return gemv_cols<4, EPI_QLR>(g, st);
   } else if (bits == 8 && epi == EPI_ACC) {
     return gemv_cols<8, EPI_ACC>(g, st);
   }

@@ -196,17 +196,19 @@ hipError_t launch_pack_rht(const float* signs, const int32_t* perm, int d, void*
 hipError_t launch_quant_rows_rht(const void* X, bool bf16, int n, int d, int dl, const void* rot, void* xl,
                                  float* sxl, void* xh, float* sxh, hipStream_t st);
 // First stage of the quantised low-rank branch (tq_qlr.hip): the exact
-// integer product of the int8-order activation codes (n x d) with the packed
-// codes of U^T (r_pad rows of d / 2 bytes), scaled per rank by s_u in fp32 and
-// re-quantised per token at 4 bits: codes to ct (n rows of r_pad int8 bytes,
-// int8 code order), scales to st.  d % 32 == 0, r_pad in {32, 64, 128, 256}.
+// integer product of the activation codes (n x d: int8 in the tile GEMM's
+// order, or nibble-packed when `packed`) with the packed codes of U^T (r_pad
+// rows of d / 2 bytes), scaled per rank by s_u in fp32 and re-quantised per
+// token at 4 bits: codes to ct (n rows of r_pad int8 bytes, int8 code order),
+// scales to st.  d % 32 == 0, r_pad in {32, 64, 128, 256}.
 hipError_t launch_qlr_stage1(const uint8_t* xc, int n, int d, const uint8_t* uc, const float* su, int r_pad,
-                             uint8_t* ct, float* st, hipStream_t stream);
+                             uint8_t* ct, float* st, bool packed, hipStream_t stream);
 // The quantiser and the first stage in one launch (d <= 4096, r_pad <= 128):
-// X (n x d) -> s_x, int8-order codes (n x d), first-stage codes and s_t as above.
+// X (n x d) -> s_x, activation codes (int8 order, or nibble-packed when
+// `packed`), first-stage codes and s_t as above.
 bool qlr_fused_ok(int d, int r_pad);
 hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uint8_t* uc, const float* su, int r_pad,
-                               uint8_t* xc, float* sx, uint8_t* ct, float* st, hipStream_t stream);
+                               uint8_t* xc, float* sx, uint8_t* ct, float* st, bool packed, hipStream_t stream);
 bool small_fused_ok(int n, int d, int r_pad);
 SmallPlan plan_small(int n, int d, int r_pad);
 hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);

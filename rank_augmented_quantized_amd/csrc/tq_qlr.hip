@@ -25,7 +25,7 @@ namespace {
 constexpr int kQlrTok = 32;   // tokens per block
 constexpr int kQlrWaves = 8;  // waves per block, splitting the k steps
 
-template <int NB>  // NB 32-rank blocks
+template <int NB, bool XPK>  // NB 32-rank blocks; XPK: nibble-packed activation codes (d / 2 bytes per row)
 __global__ __launch_bounds__(kQlrWaves * 64) void k_qlr_stage1(const uint8_t* __restrict__ xc, int n, int d,
                                                                  const uint8_t* __restrict__ uc,
                                                                  const float* __restrict__ su,
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kQlrWaves * 64) void k_qlr_stage1(const uint8_t* __
 
   const int steps = (d + 127) / 128;
   if (wave < steps) {
-    const uint8_t* xr = xc + (size_t)min(tok0 + l32, n - 1) * d;  // rows past n: any valid row, results unused
+    const uint8_t* xr = xc + (size_t)min(tok0 + l32, n - 1) * (XPK ? d / 2 : d);  // rows past n: results unused
     const size_t ub = (size_t)d / 2;                               // packed bytes per rank row
     const uint8_t* ur = uc + (size_t)l32 * ub + 32 * lg;
     i32x16 acc[NB];
@@ -51,31 +51,43 @@ __global__ __launch_bounds__(kQlrWaves * 64) void k_qlr_stage1(const uint8_t* __
       for (int i = 0; i < 16; ++i) acc[b][i] = 0;
     for (int s = wave; s < steps; s += kQlrWaves) {
       const int o = 128 * s + 64 * lg;  // this lane's first k of the step (d % 32 == 0: chunks are whole)
-      uint4 xv[4];
+      i32x4 xv[4];
+      if constexpr (XPK) {  // 32 packed bytes, expanded like U's (16 x code)
+        const uint4 p0 = o < d ? *reinterpret_cast<const uint4*>(xr + o / 2) : uint4{0u, 0u, 0u, 0u};
+        const uint4 p1 = o + 32 < d ? *reinterpret_cast<const uint4*>(xr + o / 2 + 16) : uint4{0u, 0u, 0u, 0u};
+        xv[0] = unpack16(p0.x, p0.y);
+        xv[1] = unpack16(p0.z, p0.w);
+        xv[2] = unpack16(p1.x, p1.y);
+        xv[3] = unpack16(p1.z, p1.w);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xv[q] = o + 16 * q < d ? *reinterpret_cast<const uint4*>(xr + o + 16 * q) : uint4{0u, 0u, 0u, 0u};
+        for (int q = 0; q < 4; ++q)
+          xv[q] = __builtin_bit_cast(i32x4, o + 16 * q < d ? *reinterpret_cast<const uint4*>(xr + o + 16 * q)
+                                                           : uint4{0u, 0u, 0u, 0u});
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const uint8_t* up = ur + (size_t)32 * b * ub + 64 * s;
         const uint4 u0 = o < d ? *reinterpret_cast<const uint4*>(up) : uint4{0u, 0u, 0u, 0u};
         const uint4 u1 = o + 32 < d ? *reinterpret_cast<const uint4*>(up + 16) : uint4{0u, 0u, 0u, 0u};
-        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u0.x, u0.y), __builtin_bit_cast(i32x4, xv[0]), acc[b],
+        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u0.x, u0.y), xv[0], acc[b],
                                                        0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u0.z, u0.w), __builtin_bit_cast(i32x4, xv[1]), acc[b],
+        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u0.z, u0.w), xv[1], acc[b],
                                                        0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u1.x, u1.y), __builtin_bit_cast(i32x4, xv[2]), acc[b],
+        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u1.x, u1.y), xv[2], acc[b],
                                                        0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u1.z, u1.w), __builtin_bit_cast(i32x4, xv[3]), acc[b],
+        acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(u1.z, u1.w), xv[3], acc[b],
                                                        0, 0, 0);
       }
     }
     // result layout: lane l, element e -> rank 8 (e / 4) + 4 (l / 32) + e % 4
     // of the block, token l % 32; the sums carry the factor 16 of unpack16
+    // (256 with packed activations, expanded the same way)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) atomicAdd(&red[32 * b + 8 * (e >> 2) + 4 * lg + (e & 3)][l32], acc[b][e] >> 4);
+      for (int e = 0; e < 16; ++e)
+        atomicAdd(&red[32 * b + 8 * (e >> 2) + 4 * lg + (e & 3)][l32], acc[b][e] >> (XPK ? 8 : 4));
   }
   __syncthreads();
 
@@ -130,7 +142,7 @@ __host__ __device__ constexpr int qlr_fused_lds(int d, int r_pad) {
   return 16 * (d + 16) + 16 * r_pad * 4 + (r_pad / 8) * 16 * 4;
 }
 
-template <typename T, int CH, int NQ>  // NQ 16-rank groups
+template <typename T, int CH, int NQ, bool PK>  // NQ 16-rank groups; PK: activation codes to memory nibble-packed
 __global__ __launch_bounds__(kQlrFusedWaves * 64) void k_qlr_prologue(const T* __restrict__ X, int n, int d,
                                                                      const uint8_t* __restrict__ uc,
                                                                      const float* __restrict__ su,
@@ -153,7 +165,8 @@ __global__ __launch_bounds__(kQlrFusedWaves * 64) void k_qlr_prologue(const T* _
     const int row = row0 + w;
     uint8_t* lrow = lds + w * XS;
     if (row < n) {
-      const float s = quant_row_i8_wave<T, CH>(X + (size_t)row * d, nch, lane, xc + (size_t)row * d, lrow);
+      const float s =
+          quant_row_i8_wave<T, CH, PK>(X + (size_t)row * d, nch, lane, xc + (size_t)row * (PK ? d / 2 : d), lrow);
       if (lane == 0) sx[row] = s;
     } else {
       for (int ch = lane; ch < nch; ch += 64) *reinterpret_cast<uint2*>(lrow + 8 * ch) = uint2{0u, 0u};
@@ -235,40 +248,51 @@ __global__ __launch_bounds__(kQlrFusedWaves * 64) void k_qlr_prologue(const T* _
   }
 }
 
-template <typename T, int CH>
-hipError_t launch_fused_ch(const void* X, int n, int d, const uint8_t* uc, const float* su, int r_pad, uint8_t* xc,
+template <typename T, int CH, bool PK>
+hipError_t launch_fused_pk(const void* X, int n, int d, const uint8_t* uc, const float* su, int r_pad, uint8_t* xc,
                            float* sx, uint8_t* ct, float* st, hipStream_t stream) {
   const dim3 grid((unsigned)((n + 15) / 16)), block(kQlrFusedWaves * 64);
   const unsigned lds = (unsigned)qlr_fused_lds(d, r_pad);
   const T* x = (const T*)X;
   switch (r_pad) {
-    case 32: launch_kernel(k_qlr_prologue<T, CH, 2>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
-    case 64: launch_kernel(k_qlr_prologue<T, CH, 4>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
-    case 128: launch_kernel(k_qlr_prologue<T, CH, 8>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
+    case 32: launch_kernel(k_qlr_prologue<T, CH, 2, PK>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
+    case 64: launch_kernel(k_qlr_prologue<T, CH, 4, PK>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
+    case 128: launch_kernel(k_qlr_prologue<T, CH, 8, PK>, grid, block, lds, stream, x, n, d, uc, su, xc, sx, ct, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// few tokens (the small-n GEMM takes packed codes): packed; else int8
+template <typename T, int CH>
+hipError_t launch_fused_ch(const void* X, int n, int d, const uint8_t* uc, const float* su, int r_pad, uint8_t* xc,
+                           float* sx, uint8_t* ct, float* st, bool packed, hipStream_t stream) {
+  return packed ? launch_fused_pk<T, CH, true>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream)
+                : launch_fused_pk<T, CH, false>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
+}
+
 template <typename T>
 hipError_t launch_fused_t(const void* X, int n, int d, const uint8_t* uc, const float* su, int r_pad, uint8_t* xc,
-                          float* sx, uint8_t* ct, float* st, hipStream_t stream) {
+                          float* sx, uint8_t* ct, float* st, bool packed, hipStream_t stream) {
   int ch = 1;
   while (ch * 512 < d) ch <<= 1;  // chunks of 8 values per lane for the whole row
   switch (ch) {
-    case 1: return launch_fused_ch<T, 1>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
-    case 2: return launch_fused_ch<T, 2>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
-    case 4: return launch_fused_ch<T, 4>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
-    case 8: return launch_fused_ch<T, 8>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
+    case 1: return launch_fused_ch<T, 1>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream);
+    case 2: return launch_fused_ch<T, 2>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream);
+    case 4: return launch_fused_ch<T, 4>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream);
+    case 8: return launch_fused_ch<T, 8>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int NB>
 hipError_t launch_nb(const uint8_t* xc, int n, int d, const uint8_t* uc, const float* su, uint8_t* ct, float* st,
-                     hipStream_t stream) {
-  launch_kernel(k_qlr_stage1<NB>, dim3((unsigned)((n + kQlrTok - 1) / kQlrTok)), dim3(kQlrWaves * 64), 0, stream, xc,
-                n, d, uc, su, ct, st);
+                     bool packed, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + kQlrTok - 1) / kQlrTok)), block(kQlrWaves * 64);
+  if (packed)
+    launch_kernel(k_qlr_stage1<NB, true>, grid, block, 0, stream, xc, n, d, uc, su, ct, st);
+  else
+    launch_kernel(k_qlr_stage1<NB, false>, grid, block, 0, stream, xc, n, d, uc, su, ct, st);
   return hipGetLastError();
 }
 
@@ -279,24 +303,24 @@ bool qlr_fused_ok(int d, int r_pad) {
 }
 
 hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uint8_t* uc, const float* su, int r_pad,
-                               uint8_t* xc, float* sx, uint8_t* ct, float* st, hipStream_t stream) {
+                               uint8_t* xc, float* sx, uint8_t* ct, float* st, bool packed, hipStream_t stream) {
   if (n <= 0 || !qlr_fused_ok(d, r_pad)) return hipErrorInvalidValue;
-  return bf16 ? launch_fused_t<bf16_t>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream)
-              : launch_fused_t<float>(X, n, d, uc, su, r_pad, xc, sx, ct, st, stream);
+  return bf16 ? launch_fused_t<bf16_t>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream)
+              : launch_fused_t<float>(X, n, d, uc, su, r_pad, xc, sx, ct, st, packed, stream);
 }
 
 hipError_t launch_qlr_stage1(const uint8_t* xc, int n, int d, const uint8_t* uc, const float* su, int r_pad,
-                             uint8_t* ct, float* st, hipStream_t stream) {
+                             uint8_t* ct, float* st, bool packed, hipStream_t stream) {
   if (n <= 0 || d <= 0 || d % 32) return hipErrorInvalidValue;
   switch (r_pad) {
     case 32:
-      return launch_nb<1>(xc, n, d, uc, su, ct, st, stream);
+      return launch_nb<1>(xc, n, d, uc, su, ct, st, packed, stream);
     case 64:
-      return launch_nb<2>(xc, n, d, uc, su, ct, st, stream);
+      return launch_nb<2>(xc, n, d, uc, su, ct, st, packed, stream);
     case 128:
-      return launch_nb<4>(xc, n, d, uc, su, ct, st, stream);
+      return launch_nb<4>(xc, n, d, uc, su, ct, st, packed, stream);
     case 256:
-      return launch_nb<8>(xc, n, d, uc, su, ct, st, stream);
+      return launch_nb<8>(xc, n, d, uc, su, ct, st, packed, stream);
     default:
       return hipErrorInvalidValue;
   }

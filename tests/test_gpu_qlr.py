@@ -85,7 +85,10 @@ def _ws_parts(ws, n, d, rk):
     rp = _r_pad(rk)
     b = ws.cpu().numpy()
     sx = b[off["s_x"]: off["s_x"] + 4 * n].view(np.float32)
-    xc = _int8_codes(b[off["x_codes"]: off["x_codes"] + n * d].reshape(n, d))
+    if n <= 32:  # few tokens: nibble-packed codes for the small-n GEMM
+        xc = tqo.unpack_int4(b[off["x_codes"]: off["x_codes"] + n * d // 2].reshape(n, d // 2))
+    else:
+        xc = _int8_codes(b[off["x_codes"]: off["x_codes"] + n * d].reshape(n, d))
     st = b[off["s_t"]: off["s_t"] + 4 * n].view(np.float32)
     tc = _int8_codes(b[off["t_codes"]: off["t_codes"] + n * rp].reshape(n, rp))
     return sx, xc, st, tc
@@ -101,6 +104,11 @@ CASES = [
     ("n33_r256", 33, 512, 256, 256, "normal", "f32", 0),
     ("n1030_r32_d4096", 1030, 4096, 1024, 32, "normal", "bf16", 4),
     ("n64_r16_no_outliers", 64, 768, 256, 16, "normal", "bf16", 0),
+    ("n70_r32_d5120_two_launch", 70, 5120, 256, 32, "normal", "bf16", 2),
+    ("n5_r64_d14336_two_launch", 5, 14336, 128, 64, "student_t", "f32", 0),
+    ("n32_r32_small_n", 32, 2048, 520, 32, "normal", "bf16", 2),
+    ("n17_r256_small_n_two_launch", 17, 1024, 272, 256, "normal", "bf16", 0),
+    ("n2_r64_d4096", 2, 4096, 1024, 64, "normal", "bf16", 2),
 ]
 
 
@@ -165,7 +173,7 @@ def test_linear_qlr_attn_proj_sampled():
 
 
 def test_linear_qlr_graph_replay_matches_eager():
-    """The three launches captured in a HIP graph and replayed give the eager output on every replay."""
+    """The layer's launches captured in a HIP graph and replayed give the eager output on every replay."""
     n, d, m, rk = 300, 1024, 512, 32
     c = draw_custom(n, d, m, rk, seed=79)
     wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)

@@ -24,7 +24,10 @@ It evaluates the plain definition of the layer, step by step, in numpy:
 * the fully quantised low-rank branch Q(X)[Q(U)Q(V) + Q(R)] with the first
   stage's integer result re-quantised per token -- TwinQuant notes, the
   error expression of section 04.A and the fused two-stage low-rank pipeline
-  of section 04.C.
+  of section 04.C;
+* per-token asymmetric activations (a zero-point per token) for the
+  two-subspace layer -- CoQuant Eq. 1 with z != 0 and the experimental
+  protocol (per-token asymmetric activations, per-channel symmetric weights).
 
 Readings of points the pages leave open (each one is also listed in the
 design notes): q_max = 7 / 127; "round" is round-half-to-even; the scale is
@@ -61,6 +64,8 @@ __all__ = [
     "subspace_split",
     "requantize_lowrank",
     "tq_linear_qlr_ref",
+    "quantize_rows_asym",
+    "tq_linear_mp_asym_ref",
 ]
 
 
@@ -309,6 +314,76 @@ def tq_linear_mp_ref(xrot, wrot, d_hi: int, rows=None, cols=None, bits_lo: int =
         acc = int_matmul(cx, cw)
         y = y + (s_x.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]) * acc.astype(np.float64)
         out.update({f"codes_x{tag}": cx, f"s_x{tag}": s_x, f"codes_w{tag}": cw, f"s_w{tag}": s_w, f"acc_{tag}": acc})
+    out["Y"] = y
+    return out
+
+
+def quantize_rows_asym(a, bits: int = 4):
+    """Per-row asymmetric quantisation (CoQuant Eq. 1 with a zero-point: the
+    dequantised value is u s + z, u the rounded and clipped (x - z) / s).
+
+    The scale and zero-point follow the row's range: z = min(row) and
+    s = fl32(fl32(max - min) / (2^N - 1)); each code is
+    u = clip(rint(fl32(fl32(x - z) / s)), 0, 2^N - 1) with IEEE fp32
+    subtraction and division and round half to even.  A constant row has
+    s = 0 and codes 0 (it dequantises to z exactly).
+
+    Returns (u int16 [rows, K] in [0, 2^N - 1], s float32 [rows], z float32 [rows]).
+    """
+    a = np.asarray(a, dtype=np.float32)
+    if a.ndim != 2:
+        raise ValueError("quantize_rows_asym expects a 2-D array")
+    if not np.all(np.isfinite(a)):
+        raise ValueError("non-finite input is outside the quantiser's contract")
+    qm = (1 << bits) - 1
+    if a.shape[1] == 0:
+        z = np.zeros(a.shape[0], np.float32)
+        return np.zeros(a.shape, np.int16), z.copy(), z
+    mn = a.min(axis=1)
+    mx = a.max(axis=1)
+    s = ((mx - mn).astype(np.float32) / np.float32(qm)).astype(np.float32)
+    u = np.zeros(a.shape, dtype=np.int16)
+    live = s > 0
+    if np.any(live):
+        dlt = (a[live] - mn[live][:, None]).astype(np.float32)  # fl32(x - z)
+        q = (dlt / s[live][:, None]).astype(np.float32)          # IEEE fp32 division
+        u[live] = np.clip(np.rint(q), 0, qm).astype(np.int16)
+    return u, s, mn.astype(np.float32)
+
+
+def tq_linear_mp_asym_ref(xrot, wrot, d_hi: int, rows=None, cols=None, bits_lo: int = 4, bits_hi: int = 8):
+    """The two-subspace output (CoQuant Eq. 9) with each subspace of each
+    token quantised asymmetrically (``quantize_rows_asym``) and the weights
+    per output channel symmetrically, as in the CoQuant protocol.  With
+    x^ = u s_x + z_x and w^ = c_w s_w, each subspace contributes
+
+        sum_k x^_k w^_k = s_x s_w (u . c_w) + z_x s_w (sum_k c_w)
+
+    so Y = sum over the two subspaces of s_x s_w^T (.) (U C_w^T)
+    + z_x (s_w (.) colsum(C_w))^T, in fp64.
+    """
+    xrot = np.asarray(xrot, dtype=np.float32)
+    wrot = np.asarray(wrot, dtype=np.float32)
+    d = xrot.shape[1]
+    if not 0 <= d_hi <= d:
+        raise ValueError("d_hi out of range")
+    if rows is not None:
+        xrot = xrot[np.asarray(rows)]
+    if cols is not None:
+        wrot = wrot[:, np.asarray(cols)]
+    dl = d - d_hi
+    out = {}
+    y = np.zeros((xrot.shape[0], wrot.shape[1]), dtype=np.float64)
+    for tag, xs, ws, bits in (("l", xrot[:, :dl], wrot[:dl], bits_lo), ("h", xrot[:, dl:], wrot[dl:], bits_hi)):
+        u, s_x, z_x = quantize_rows_asym(xs, bits)
+        cw, s_w = quantize_weight(ws, bits)
+        acc = int_matmul(u, cw)
+        colsum = cw.astype(np.int64).sum(axis=1)
+        sw = s_w.astype(np.float64)
+        y = y + (s_x.astype(np.float64)[:, None] * sw[None, :]) * acc.astype(np.float64)
+        y = y + z_x.astype(np.float64)[:, None] * (sw * colsum.astype(np.float64))[None, :]
+        out.update({f"codes_x{tag}": u, f"s_x{tag}": s_x, f"z_x{tag}": z_x, f"codes_w{tag}": cw, f"s_w{tag}": s_w,
+                    f"colsum_{tag}": colsum, f"acc_{tag}": acc})
     out["Y"] = y
     return out
 

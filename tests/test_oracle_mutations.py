@@ -17,7 +17,7 @@ import test_oracle_pins as pins
 _orig = {name: getattr(tqo, name) for name in (
     "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
     "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
-    "subspace_split", "tq_linear_group_ref", "rht_rows", "requantize_lowrank", "tq_linear_qlr_ref")}
+    "subspace_split", "tq_linear_group_ref", "rht_rows", "requantize_lowrank", "tq_linear_qlr_ref", "quantize_rows_asym", "tq_linear_mp_asym_ref")}
 
 
 def _q_reciprocal(a, bits=4):
@@ -271,6 +271,61 @@ def _qlr_unrequantised(x, r, u, v, rows=None, cols=None, bits=4):  # the fp32 fi
     return _qlr_generic(x, r, u, v, rows, cols, bits, unrequantised=True)
 
 
+def _asym_generic(a, bits=4, qm_used=None, clip_lo=0, clip_hi=None, z_from="min", sub_after=False):
+    a = np.asarray(a, dtype=np.float32)
+    qm = (1 << bits) - 1
+    qmu = qm if qm_used is None else qm_used
+    hi = qm if clip_hi is None else clip_hi
+    mn, mx = a.min(axis=1), a.max(axis=1)
+    z = mn if z_from == "min" else (mx if z_from == "max" else np.zeros_like(mn))
+    s = ((mx - mn).astype(np.float32) / np.float32(qmu)).astype(np.float32)
+    u = np.zeros(a.shape, np.int16)
+    live = s > 0
+    if sub_after:  # x / s - z / s instead of (x - z) / s
+        q = (a[live] / s[live][:, None]).astype(np.float32) - (z[live] / s[live]).astype(np.float32)[:, None]
+    else:
+        q = ((a[live] - z[live][:, None]).astype(np.float32) / s[live][:, None]).astype(np.float32)
+    u[live] = np.clip(np.rint(q), clip_lo, hi)
+    return u, s, z.astype(np.float32)
+
+
+def _asym_qmax_signed(a, bits=4):  # the symmetric q_max 2^(N-1) - 1 as the step count
+    return _asym_generic(a, bits, qm_used=(1 << (bits - 1)) - 1)
+
+
+def _asym_signed_clip(a, bits=4):  # codes clipped to the signed range
+    return _asym_generic(a, bits, clip_lo=-(1 << (bits - 1)), clip_hi=(1 << (bits - 1)) - 1)
+
+
+def _asym_z_max(a, bits=4):  # zero-point at the maximum
+    return _asym_generic(a, bits, z_from="max")
+
+
+def _asym_sub_after(a, bits=4):  # the zero-point subtracted after the division
+    return _asym_generic(a, bits, sub_after=True)
+
+
+def _mp_asym_no_zero_term(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi=8):  # z s_w colsum dropped
+    out = _orig["tq_linear_mp_asym_ref"](xrot, wrot, d_hi, rows, cols, bits_lo, bits_hi)
+    y = 0.0
+    for t in ("l", "h"):
+        y = y + (out[f"s_x{t}"].astype(np.float64)[:, None] * out[f"s_w{t}"].astype(np.float64)[None, :]) * \
+            out[f"acc_{t}"].astype(np.float64)
+    out["Y"] = y
+    return out
+
+
+def _mp_asym_shared_z(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi=8):  # the 4-bit z used for both
+    out = _orig["tq_linear_mp_asym_ref"](xrot, wrot, d_hi, rows, cols, bits_lo, bits_hi)
+    y = 0.0
+    for t in ("l", "h"):
+        sw = out[f"s_w{t}"].astype(np.float64)
+        y = y + (out[f"s_x{t}"].astype(np.float64)[:, None] * sw[None, :]) * out[f"acc_{t}"].astype(np.float64)
+        y = y + out["z_xl"].astype(np.float64)[:, None] * (sw * out[f"colsum_{t}"].astype(np.float64))[None, :]
+    out["Y"] = y
+    return out
+
+
 MUTANTS = {
     "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
     "quantize_weight": [_w_per_input_channel],
@@ -287,6 +342,8 @@ MUTANTS = {
     "rht_rows": [_rht_sub_swapped, _rht_inverse_perm, _rht_scale_by_block, _rht_signs_after],
     "requantize_lowrank": [_requant_no_su, _requant_per_column, _requant_trunc, _requant_8bit],
     "tq_linear_qlr_ref": [_qlr_lr_no_sx, _qlr_lr_no_st, _qlr_unrequantised],
+    "quantize_rows_asym": [_asym_qmax_signed, _asym_signed_clip, _asym_z_max, _asym_sub_after],
+    "tq_linear_mp_asym_ref": [_mp_asym_no_zero_term, _mp_asym_shared_z],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]

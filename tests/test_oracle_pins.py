@@ -557,6 +557,97 @@ def pin_qlr_requant_step(seed=22):
     assert np.mean(err <= 0.25 * st[:, None]) > 0.45
 
 
+# ----------------------------------------------------------------------------
+# asymmetric per-token activations (two-subspace layer)
+# ----------------------------------------------------------------------------
+
+def pin_asym_quantizer_bruteforce(seed=23):
+    """Rows with a given min and max: s = rn32(rn32(max - min) / (2^N - 1)),
+    z = min, and each code rne(rn32(rn32(x - z) / s)) clipped to [0, 2^N - 1],
+    evaluated in exact rational arithmetic with IEEE rounding (rn32)."""
+    rng = np.random.default_rng(seed)
+    for bits in (4, 8):
+        qm = (1 << bits) - 1
+        for mn, mx in ((-3.0, 5.0), (0.25, 0.75), (-1.0e-3, 7.0e-3), (-12.375, -0.5), (2.0 ** -100, 3 * 2.0 ** -99)):
+            vals = np.concatenate([[mn, mx], rng.uniform(mn, mx, size=200)]).astype(np.float32)
+            # ties: values exactly half-way between grid points
+            f_mn, f_mx = Fraction(float(np.float32(mn))), Fraction(float(np.float32(mx)))
+            srange = rn32(f_mx - f_mn)
+            s = rn32(srange / qm)
+            halfs = [float(np.float32(float(f_mn + (Fraction(2 * j + 1, 2)) * s))) for j in range(0, qm, max(1, qm // 7))]
+            row = np.concatenate([vals, np.asarray(halfs, np.float32)]).astype(np.float32)[None, :]
+            u, s_got, z_got = tqo.quantize_rows_asym(row, bits)
+            assert Fraction(float(s_got[0])) == s and Fraction(float(z_got[0])) == f_mn
+            for x, c in zip(row[0], u[0]):
+                want = min(max(rne_int(rn32(rn32(Fraction(float(x)) - f_mn) / s)), 0), qm)
+                assert int(c) == want, (bits, mn, mx, float(x), int(c), want)
+
+
+def _asym_lossless(rng, n, k, qm, e_lo, e_hi):
+    u = rng.integers(0, qm + 1, size=(n, k)).astype(np.int64)
+    u[:, 0], u[:, 1] = 0, qm  # every row spans the whole grid
+    s = 2.0 ** rng.integers(e_lo, e_hi, size=n)
+    z = s * rng.integers(-3 * qm, 2 * qm, size=n)  # a multiple of the step: x - z is exact
+    return u, s, z, (u * s[:, None] + z[:, None])
+
+
+def pin_asym_two_subspace_lossless(seed=24):
+    """Inputs that quantise without loss (each row z + u s with u spanning
+    [0, 2^N - 1], s a power of two, z a multiple of s): codes, scales and
+    zero-points are known and Y = X_l W_l + X_h W_h exactly; a per-row shift
+    by a multiple of the step moves only z and adds shift * s_w * colsum(C_w);
+    a constant row has s = 0, codes 0 and dequantises to its value."""
+    rng = np.random.default_rng(seed)
+    n, dl, dh, m = 5, 64, 32, 7
+    ul, sl, zl, xl = _asym_lossless(rng, n, dl, 15, -5, 1)
+    uh, sh, zh, xh = _asym_lossless(rng, n, dh, 255, -9, -4)
+    cwl = lossless_codes(rng, m, dl, 7)
+    cwh = lossless_codes(rng, m, dh, 127)
+    swl = 2.0 ** rng.integers(-8, -3, size=m)
+    swh = 2.0 ** rng.integers(-12, -8, size=m)
+    wl, wh = (cwl * swl[:, None]).T, (cwh * swh[:, None]).T
+    xrot = np.hstack([xl, xh]).astype(np.float32)
+    wrot = np.vstack([wl, wh]).astype(np.float32)
+    out = tqo.tq_linear_mp_asym_ref(xrot, wrot, dh)
+    assert np.array_equal(out["codes_xl"], ul) and np.array_equal(out["codes_xh"], uh)
+    assert np.array_equal(out["s_xl"], sl.astype(np.float32)) and np.array_equal(out["z_xl"], zl.astype(np.float32))
+    assert np.array_equal(out["s_xh"], sh.astype(np.float32)) and np.array_equal(out["z_xh"], zh.astype(np.float32))
+    assert np.array_equal(out["colsum_l"], cwl.sum(axis=1)) and np.array_equal(out["colsum_h"], cwh.sum(axis=1))
+    assert np.array_equal(out["Y"], xl @ wl + xh @ wh)
+    # shift row 2 of the 4-bit subspace by 5 steps
+    xs = xrot.copy()
+    xs[2, :dl] += np.float32(5 * sl[2])
+    o2 = tqo.tq_linear_mp_asym_ref(xs, wrot, dh)
+    assert np.array_equal(o2["codes_xl"], ul)
+    want = out["Y"].copy()
+    want[2] += 5 * sl[2] * (swl * cwl.sum(axis=1))
+    assert np.array_equal(o2["Y"], want)
+    # a constant row
+    xc = xrot.copy()
+    xc[1] = np.float32(0.375)
+    o3 = tqo.tq_linear_mp_asym_ref(xc, wrot, dh)
+    assert o3["s_xl"][1] == 0 and o3["s_xh"][1] == 0 and not o3["codes_xl"][1].any() and not o3["codes_xh"][1].any()
+    assert np.array_equal(o3["Y"][1], 0.375 * (wl.sum(axis=0) + wh.sum(axis=0)))
+
+
+def pin_asym_half_step(seed=25):
+    """Generic rows (an outlier channel, all-positive rows): every code in
+    [0, 2^N - 1], the row's minimum at code 0 and maximum at 2^N - 1, and the
+    dequantised u s + z within half a step of x."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((30, 96))
+    x[:, 7] *= 25.0
+    x[::3] = np.abs(x[::3]) + 3.0
+    x = x.astype(np.float32)
+    for bits in (4, 8):
+        qm = (1 << bits) - 1
+        u, s, z = tqo.quantize_rows_asym(x, bits)
+        assert u.min() >= 0 and u.max() <= qm
+        assert np.all(u[np.arange(30), x.argmin(axis=1)] == 0) and np.all(u[np.arange(30), x.argmax(axis=1)] == qm)
+        deq = u.astype(np.float64) * s.astype(np.float64)[:, None] + z.astype(np.float64)[:, None]
+        assert np.all(np.abs(deq - x) <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-5) + 1e-6 * np.abs(x))
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -578,6 +669,9 @@ ALL_PINS = [
     pin_qlr_lossless,
     pin_qlr_invariants,
     pin_qlr_requant_step,
+    pin_asym_quantizer_bruteforce,
+    pin_asym_two_subspace_lossless,
+    pin_asym_half_step,
 ]
 
 

@@ -279,6 +279,46 @@ tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, i
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Per-token asymmetric activations for the two-subspace layer (CoQuant notes,
+ * "CoQuant: Joint Weight-Activation Subspace Projection for Mixed-Precision
+ * LLMs", Eq. 1 with a zero-point, and the experimental protocol: per-token
+ * asymmetric activations, per-channel symmetric weights).  Each subspace of
+ * each token row gets z = min and s = fl32(fl32(max - min) / (2^N - 1)), and
+ * each value the code u = rne(fl32(fl32(x - z) / s)) in [0, 2^N - 1] (a
+ * constant row: s = 0, u = 0); the subspace contributes
+ * s_x s_w (U C_w^T) + z_x s_w colsum(C_w).
+ *
+ * tq_weight_colsum -- colsum[j] = sum over k of the codes of row j (m rows of
+ * k codes, bits 4 or 8, as written by tq_pack_weight); int32, exact.  Offline.
+ */
+tq_status tq_weight_colsum(const void* w_codes, int64_t m, int64_t k, int bits, int32_t* colsum,
+                           hipStream_t stream);
+
+/*
+ * tq_linear_mp_asym -- tq_linear_mp with asymmetric activations; colsum_l /
+ * colsum_h: tq_weight_colsum of wl_codes / wh_codes (m int32 each, needed when
+ * that subspace is not empty).  d <= 8192.  ws:
+ * tq_linear_mp_asym_workspace_bytes(n, d, d_hi) bytes.  Two launches: the
+ * quantiser (one wave per token row, the row read once) and the two-subspace
+ * GEMM, whose epilogue adds each subspace's zero-point term.  Errors as
+ * tq_linear_mp, plus TQ_ERR_SHAPE for d > 8192.
+ */
+size_t tq_linear_mp_asym_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
+tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                            const void* wl_codes, const float* s_wl, const int32_t* colsum_l,
+                            const void* wh_codes, const float* s_wh, const int32_t* colsum_h, void* Y,
+                            tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Byte offsets inside the tq_linear_mp_asym workspace: off[0..3] as
+ * tq_linear_mp_workspace_offsets, but the stored codes are u - 8 (4-bit
+ * subspace, int8 in the tile GEMM's order) and u - 128 (8-bit subspace, int8,
+ * natural order); off[4] z of the 4-bit subspace, off[5] z of the 8-bit
+ * subspace (n fp32 each).  For tests.
+ */
+tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[6]);
+
+/*
  * Fully quantised low-rank branch (TwinQuant notes, "TwinQuant: Learnable
  * Subspace Decomposition for W4A4 LLM Quantization", section 04.A error
  * expression Q(X)[Q(U)Q(V) + Q(R)] and section 04.C, Figure 4: the low-rank

@@ -15,6 +15,9 @@ from .tq import (  # noqa: F401
     tq_linear_group,
     tq_linear_group_workspace_bytes,
     tq_linear_mp,
+    tq_linear_mp_asym,
+    tq_linear_mp_asym_workspace_bytes,
+    tq_linear_mp_asym_workspace_offsets,
     tq_linear_mp_rht,
     tq_linear_mp_workspace_bytes,
     tq_linear_mp_workspace_offsets,
@@ -34,4 +37,5 @@ from .tq import (  # noqa: F401
     tq_profile_read,
     tq_profile_reset,
     tq_quantize_act,
+    tq_weight_colsum,
 )

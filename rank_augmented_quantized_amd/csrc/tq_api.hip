@@ -172,6 +172,24 @@ MpWs mp_ws(int64_t n, int64_t d, int64_t d_hi) {
 
 bool valid_dtype(tq_dtype t) { return t == TQ_F32 || t == TQ_BF16; }
 
+// Workspace of tq_linear_mp_asym: the two-subspace workspace, then the two
+// zero-point vectors.
+struct MpAsymWs {
+  MpWs mp;
+  size_t zl, zh, total;
+};
+MpAsymWs mp_asym_ws(int64_t n, int64_t d, int64_t d_hi) {
+  MpAsymWs w{};
+  w.mp = mp_ws(n, d, d_hi);
+  size_t o = w.mp.total;
+  w.zl = o;
+  o = align256(o + (size_t)n * 4);
+  w.zh = o;
+  o = align256(o + (size_t)n * 4);
+  w.total = o;
+  return w;
+}
+
 // Packed quantised low-rank factors: U^T codes (r_pad rows of d / 2 bytes),
 // s_u (r_pad), V^T codes (m rows of r_pad / 2 bytes), s_v (m).
 struct QlrPack {
@@ -230,7 +248,7 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 103; }
+int tq_version(void) { return 104; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
   if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
@@ -505,10 +523,13 @@ tq_status mp_check(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d
   return TQ_OK;
 }
 
-// The two-subspace GEMM on the codes and scales in the workspace.
+// The two-subspace GEMM on the codes and scales in the workspace (with the
+// zero-points and weight code sums of asymmetric activations when zl / zh
+// are not null).
 tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_codes, const float* s_wl,
                   const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, const MpWs& W, uint8_t* base,
-                  hipStream_t stream) {
+                  hipStream_t stream, const float* zl = nullptr, const float* zh = nullptr,
+                  const int32_t* csl = nullptr, const int32_t* csh = nullptr) {
   const int64_t dl = d - d_hi;
   float* sxl = (float*)(base + W.sxl);
   float* sxh = (float*)(base + W.sxh);
@@ -535,6 +556,10 @@ tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_
   g.Kb2 = (int)d_hi;
   g.sx2 = sxh;
   g.sw2 = s_wh;
+  g.zx = dl > 0 ? zl : nullptr;
+  g.csw = csl;
+  g.zx2 = d_hi > 0 ? zh : nullptr;
+  g.csw2 = csh;
   TQ_RUN("gemm_mp", stream, tq::launch_gemm8(g, tq::EPI_MP, true, 4, stream));
   return TQ_OK;
 }
@@ -579,6 +604,57 @@ tq_status tq_linear_mp_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, siz
   off[2] = W.xl;
   off[3] = W.xh;
   return TQ_OK;
+}
+
+tq_status tq_weight_colsum(const void* w_codes, int64_t m, int64_t k, int bits, int32_t* colsum, hipStream_t stream) {
+  if (bits != 4 && bits != 8) return TQ_ERR_BITS;
+  if (m <= 0 || k <= 0 || m > kMaxDim || k > kMaxK || k % (bits == 4 ? 32 : 16)) return TQ_ERR_SHAPE;
+  if (!w_codes || !colsum) return TQ_ERR_NULL;
+  if (!aligned16(w_codes) || !aligned16(colsum)) return TQ_ERR_ALIGN;
+  TQ_RUN("weight_colsum", stream, tq::launch_weight_colsum(w_codes, bits, (int)m, (int)k, colsum, stream));
+  return TQ_OK;
+}
+
+size_t tq_linear_mp_asym_workspace_bytes(int64_t n, int64_t d, int64_t d_hi) {
+  if (n < 0 || d <= 0 || d_hi < 0 || d_hi > d) return 0;
+  return mp_asym_ws(n, d, d_hi).total;
+}
+
+tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[6]) {
+  if (n < 0 || d <= 0 || d_hi < 0 || d_hi > d) return TQ_ERR_SHAPE;
+  if (!off) return TQ_ERR_NULL;
+  const MpAsymWs W = mp_asym_ws(n, d, d_hi);
+  off[0] = W.mp.sxl;
+  off[1] = W.mp.sxh;
+  off[2] = W.mp.xl;
+  off[3] = W.mp.xh;
+  off[4] = W.zl;
+  off[5] = W.zh;
+  return TQ_OK;
+}
+
+tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                            const void* wl_codes, const float* s_wl, const int32_t* colsum_l, const void* wh_codes,
+                            const float* s_wh, const int32_t* colsum_h, void* Y, tq_dtype y_dt, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
+  if (st != TQ_OK) return st;
+  if (d > tq::kAsymMaxD) return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  const int64_t dl = d - d_hi;
+  if ((dl > 0 && !colsum_l) || (d_hi > 0 && !colsum_h)) return TQ_ERR_NULL;
+  if ((dl > 0 && !aligned16(colsum_l)) || (d_hi > 0 && !aligned16(colsum_h))) return TQ_ERR_ALIGN;
+  const MpAsymWs W = mp_asym_ws(n, d, d_hi);
+  if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  float* zl = (float*)(base + W.zl);
+  float* zh = (float*)(base + W.zh);
+  TQ_RUN("quant_rows_asym", stream,
+         tq::launch_quant_rows_asym(Xrot, x_dt == TQ_BF16, (int)n, (int)d, (int)dl, base + W.mp.xl,
+                                    (float*)(base + W.mp.sxl), zl, base + W.mp.xh, (float*)(base + W.mp.sxh), zh,
+                                    stream));
+  return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W.mp, base, stream, zl, zh, colsum_l,
+                 colsum_h);
 }
 
 size_t tq_rht_bytes(int64_t d) {

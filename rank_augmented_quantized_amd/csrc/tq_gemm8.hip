@@ -321,14 +321,14 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
       if (c + 3 < g.N) return *reinterpret_cast<const float4*>(p + c);
       return float4{p[min(c, g.N - 1)], p[min(c + 1, g.N - 1)], p[min(c + 2, g.N - 1)], p[min(c + 3, g.N - 1)]};
     };
+    f32x16 y[FM][FN];
     // bf16 Y is staged per wave in LDS (WN token rows of WM channels, 128-byte
     // rows: chunk j of row r at slot j ^ ((r >> 1) & 7), and rows with bit 4
     // set swap the 8-byte halves of each chunk, so the 32 rows a store
     // instruction touches land on distinct banks) and written as whole
     // 128-byte row pieces; fp32 Y is stored directly.
     // Dequantisation: the int32 sums carry the factor 2^SH, folded exactly
-    // into s_x; acc is converted in place to the fp32 tile y.
-    f32x16 y[FM][FN];
+    // into s_x; acc is converted in place to the fp32 tile y (declared above).
     // The low-rank operands of the first TQ 16-t steps are loaded with the
     // scales, before the dequantisation, so the epilogue pays one L2 round
     // trip for both instead of one per step.
@@ -362,6 +362,37 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
         for (int e4 = 0; e4 < 4; ++e4) swv[a][e4] = load4(g.sw, chan(a, e4));
 #pragma unroll
       for (int b = 0; b < FN; ++b) sxv[b] = g.sx[min(tok(b), g.M - 1)] * (1.0f / (1 << SH));
+      // asymmetric two-subspace layer: per token z + 2^(N-1) s_x of each
+      // subspace, per channel its s_w and weight code sum (an empty subspace
+      // contributes zeros)
+      const bool zp_on = EPI == EPI_MP && (g.zx != nullptr || g.zx2 != nullptr);
+      float zzl[FN], zzh[FN];
+      float4 swh[FM][4];
+      int4 csl[FM][4], csh[FM][4];
+      if constexpr (EPI == EPI_MP) {
+        if (zp_on) {
+          auto ld4i = [&](const int32_t* p, int c) -> int4 {
+            if (c + 3 < g.N) return *reinterpret_cast<const int4*>(p + c);
+            return int4{p[min(c, g.N - 1)], p[min(c + 1, g.N - 1)], p[min(c + 2, g.N - 1)], p[min(c + 3, g.N - 1)]};
+          };
+          const bool lo = g.zx && g.Kb > 0, hi = g.zx2 && g.Kb2 > 0;
+#pragma unroll
+          for (int b = 0; b < FN; ++b) {
+            const int t = min(tok(b), g.M - 1);
+            zzl[b] = lo ? g.zx[t] + 8.0f * g.sx[t] : 0.0f;
+            zzh[b] = hi ? g.zx2[t] + 128.0f * g.sx2[t] : 0.0f;
+          }
+#pragma unroll
+          for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const int c = chan(a, e4);
+              csl[a][e4] = lo ? ld4i(g.csw, c) : int4{0, 0, 0, 0};
+              csh[a][e4] = hi ? ld4i(g.csw2, c) : int4{0, 0, 0, 0};
+              swh[a][e4] = hi ? load4(g.sw2, c) : float4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+      }
       if (EPI == EPI_MP && g.Kb == 0) {  // no 4-bit subspace (its scales are never written)
 #pragma unroll
         for (int a = 0; a < FM; ++a)
@@ -381,6 +412,31 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
             y[a][b][4 * e4 + 2] = (float)acc[a][b][4 * e4 + 2] * (swv[a][e4].z * sxv[b]);
             y[a][b][4 * e4 + 3] = (float)acc[a][b][4 * e4 + 3] * (swv[a][e4].w * sxv[b]);
           }
+      if constexpr (EPI == EPI_MP) {
+        // asymmetric activations: the codes are u - 8 (4-bit subspace) and
+        // u - 128 (8-bit subspace), so each subspace adds its zero-point
+        // term (z + 2^(N-1) s_x) s_w colsum(C_w) (CoQuant Eq. 1 with a
+        // zero-point).  Both are added here, before the 8-bit product's
+        // registers are live; their operands were loaded with the scales.
+        if (zp_on) {
+#pragma unroll
+          for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+              const float w0 = swv[a][e4].x * (float)csl[a][e4].x, w1 = swv[a][e4].y * (float)csl[a][e4].y;
+              const float w2 = swv[a][e4].z * (float)csl[a][e4].z, w3 = swv[a][e4].w * (float)csl[a][e4].w;
+              const float h0 = swh[a][e4].x * (float)csh[a][e4].x, h1 = swh[a][e4].y * (float)csh[a][e4].y;
+              const float h2 = swh[a][e4].z * (float)csh[a][e4].z, h3 = swh[a][e4].w * (float)csh[a][e4].w;
+#pragma unroll
+              for (int b = 0; b < FN; ++b) {
+                y[a][b][4 * e4 + 0] += zzl[b] * w0 + zzh[b] * h0;
+                y[a][b][4 * e4 + 1] += zzl[b] * w1 + zzh[b] * h1;
+                y[a][b][4 * e4 + 2] += zzl[b] * w2 + zzh[b] * h2;
+                y[a][b][4 * e4 + 3] += zzl[b] * w3 + zzh[b] * h3;
+              }
+            }
+        }
+      }
     }
     if (lr_on) {
       // D[channel][token] += sum_t L2^T[channel][t] T[token][t] on the bf16

@@ -111,6 +111,12 @@ struct GemmArgs {
   const float* sv;
   const uint8_t* Tq;
   const float* st;
+  // EPI_MP with asymmetric activations: per-token zero-points of the two
+  // segments and the weight code sums per channel (null: symmetric)
+  const float* zx;
+  const float* zx2;
+  const int32_t* csw;
+  const int32_t* csw2;
 };
 
 hipError_t launch_pack_weight(const void* W, bool bf16, int d, int m, int bits, void* codes, float* sw,
@@ -209,6 +215,15 @@ hipError_t launch_qlr_stage1(const uint8_t* xc, int n, int d, const uint8_t* uc,
 bool qlr_fused_ok(int d, int r_pad);
 hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uint8_t* uc, const float* su, int r_pad,
                                uint8_t* xc, float* sx, uint8_t* ct, float* st, bool packed, hipStream_t stream);
+// Per-token asymmetric quantiser of the two-subspace layer (tq_asym.hip):
+// columns [0, dl) at 4 bits (u - 8 as int8 in the tile GEMM's order, dl bytes
+// per row), [dl, d) at 8 bits (u - 128, natural order); per row and segment
+// the scale and the zero-point.  d <= kAsymMaxD.
+constexpr int kAsymMaxD = 8192;
+hipError_t launch_quant_rows_asym(const void* X, bool bf16, int n, int d, int dl, void* xl, float* sl, float* zl,
+                                  void* xh, float* sh, float* zh, hipStream_t st);
+// colsum[j] = sum over k of code row j (m rows of k codes, 4 or 8 bits).
+hipError_t launch_weight_colsum(const void* codes, int bits, int m, int k, int32_t* colsum, hipStream_t st);
 bool small_fused_ok(int n, int d, int r_pad);
 SmallPlan plan_small(int n, int d, int r_pad);
 hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);

@@ -29,7 +29,8 @@ EXPORTS = (
     "tq_profile_read", "tq_profile_reset", "tq_lowrank_group_bytes", "tq_pack_lowrank_group",
     "tq_linear_group_workspace_bytes", "tq_linear_group", "tq_linear_mp_workspace_offsets", "tq_rht_bytes",
     "tq_pack_rht", "tq_linear_mp_rht", "tq_lowrank_q_bytes", "tq_pack_lowrank_q", "tq_linear_qlr_workspace_bytes",
-    "tq_linear_qlr_workspace_offsets", "tq_linear_qlr",
+    "tq_linear_qlr_workspace_offsets", "tq_linear_qlr", "tq_weight_colsum", "tq_linear_mp_asym_workspace_bytes",
+    "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym",
 )
 
 
@@ -88,6 +89,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_qlr_workspace_bytes": (sz, [i64, i64, i64]),
         "tq_linear_qlr_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_linear_qlr": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
+        "tq_weight_colsum": (st, [ptr, i64, i64, c_int, ptr, ptr]),
+        "tq_linear_mp_asym_workspace_bytes": (sz, [i64, i64, i64]),
+        "tq_linear_mp_asym_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "tq_linear_mp_asym": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, ptr, ptr, c_int, ptr,
+                                   sz, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -335,6 +341,44 @@ def tq_linear_qlr(X, w_codes, s_w, lowrank_q, m: int, r: int, y_dtype=torch.bflo
         ws = torch.empty(max(1, tq_linear_qlr_workspace_bytes(n, d, r)), dtype=torch.uint8, device=X.device)
     _check("tq_linear_qlr", lib.tq_linear_qlr(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank_q),
                                               _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    return Y
+
+
+def tq_weight_colsum(w_codes, k: int, bits: int = 4, colsum=None):
+    """Sum of each code row of a packed weight (m rows of k codes) -> int32 m."""
+    lib = load()
+    _need_cuda(w_codes, colsum)
+    m = w_codes.shape[0]
+    if colsum is None:
+        colsum = torch.empty(m, dtype=torch.int32, device=w_codes.device)
+    _check("tq_weight_colsum", lib.tq_weight_colsum(_p(w_codes), m, k, bits, _p(colsum), _stream(w_codes)))
+    return colsum
+
+
+def tq_linear_mp_asym_workspace_bytes(n: int, d: int, d_hi: int) -> int:
+    return load().tq_linear_mp_asym_workspace_bytes(n, d, d_hi)
+
+
+def tq_linear_mp_asym_workspace_offsets(n: int, d: int, d_hi: int) -> dict:
+    off = (ctypes.c_size_t * 6)()
+    _check("tq_linear_mp_asym_workspace_offsets", load().tq_linear_mp_asym_workspace_offsets(n, d, d_hi, off))
+    return {"s_xl": off[0], "s_xh": off[1], "x_codes_l": off[2], "x_codes_h": off[3], "z_xl": off[4], "z_xh": off[5]}
+
+
+def tq_linear_mp_asym(Xrot, d_hi: int, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, m: int,
+                      y_dtype=torch.bfloat16, Y=None, ws=None):
+    """tq_linear_mp with per-token asymmetric activations (zero-points), weights symmetric per channel."""
+    lib = load()
+    _need_cuda(Xrot, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, Y, ws)
+    n, d = Xrot.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=Xrot.device)
+    if ws is None:
+        ws = torch.empty(max(1, tq_linear_mp_asym_workspace_bytes(n, d, d_hi)), dtype=torch.uint8,
+                         device=Xrot.device)
+    _check("tq_linear_mp_asym", lib.tq_linear_mp_asym(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
+                                                      _p(colsum_l), _p(wh_codes), _p(s_wh), _p(colsum_h), _p(Y),
+                                                      _dt(Y), _p(ws), ws.numel(), _stream(Xrot)))
     return Y
 
 

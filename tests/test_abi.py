@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 103
+    assert lib.tq_version() == 104
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -184,6 +184,26 @@ def test_qlr_validation(lib):
     assert lib.tq_linear_qlr(A, 1, 0, d, m, r, B, C, A, B, 1, C, 0, S) == 0
     off = tqb.tq_linear_qlr_workspace_offsets(n, d, r)
     assert off["x_codes"] >= off["s_x"] + 4 * n and off["t_codes"] >= off["s_t"] + 4 * n
+    assert all(v % 256 == 0 for v in off.values())
+
+
+def test_mp_asym_validation(lib):
+    assert lib.tq_weight_colsum(A, 8, 48, 4, C, S) == -2  # k % 32
+    assert lib.tq_weight_colsum(A, 8, 64, 6, C, S) == -4
+    assert lib.tq_weight_colsum(NUL, 8, 64, 4, C, S) == -1
+    assert lib.tq_weight_colsum(A, 8, 64, 4, MIS, S) == -5
+    n, d, dh, m = 64, 512, 64, 256
+    need = lib.tq_linear_mp_asym_workspace_bytes(n, d, dh)
+    assert need == lib.tq_linear_mp_workspace_bytes(n, d, dh) + 2 * 256
+    assert lib.tq_linear_mp_asym(A, 1, n, d, 40, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d_hi % 16
+    assert lib.tq_linear_mp_asym(A, 1, n, 16384, 128, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d > 8192
+    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, NUL, A, B, C, A, 1, C, need, S) == -1  # colsum_l
+    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, A, A, B, NUL, A, 1, C, need, S) == -1  # colsum_h
+    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, MIS, A, B, C, A, 1, C, need, S) == -5
+    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, A, A, B, C, A, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_mp_asym(A, 1, 0, d, dh, m, B, C, A, A, B, C, A, 1, C, 0, S) == 0
+    off = tqb.tq_linear_mp_asym_workspace_offsets(n, d, dh)
+    assert off["z_xl"] >= off["x_codes_h"] + n * dh and off["z_xh"] >= off["z_xl"] + 4 * n
     assert all(v % 256 == 0 for v in off.values())
 
 

@@ -222,13 +222,13 @@ class MpCase:
     """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
     applied online inside the quantiser (tq_linear_mp_rht)."""
 
-    def __init__(self, wl, torch, tq, dev, rht=False):
+    def __init__(self, wl, torch, tq, dev, rht=False, asym=False):
         from workloads import draw_two_subspace
 
         c = draw_two_subspace(wl)
         self.n, self.d, self.m, self.dh = wl.n, wl.d, wl.m, wl.d_hi
         dl = self.d - self.dh
-        self.rht = rht
+        self.rht, self.asym = rht, asym
         self.X = torch.from_numpy(c["X" if rht else "Xrot"]).to(dev).bfloat16()
         if rht:
             self.rot = tq.tq_pack_rht(torch.from_numpy(c["signs"].astype("float32")).to(dev),
@@ -237,12 +237,19 @@ class MpCase:
         self.wl = tq.tq_pack_weight(W[:dl].contiguous().to(dev), 4)
         self.wh = tq.tq_pack_weight(W[dl:].contiguous().to(dev), 8)
         del W, c
+        if asym:
+            self.csl = tq.tq_weight_colsum(self.wl[0], dl, 4)
+            self.csh = tq.tq_weight_colsum(self.wh[0], self.dh, 8)
         self.Y = torch.empty((self.n, self.m), dtype=torch.bfloat16, device=dev)
-        self.ws = torch.empty(tq.tq_linear_mp_workspace_bytes(self.n, self.d, self.dh), dtype=torch.uint8, device=dev)
+        wsb = (tq.tq_linear_mp_asym_workspace_bytes if asym else tq.tq_linear_mp_workspace_bytes)(self.n, self.d, self.dh)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         self.tq = tq
 
     def __call__(self, i):
-        if self.rht:
+        if self.asym:
+            self.tq.tq_linear_mp_asym(self.X, self.dh, self.wl[0], self.wl[1], self.csl, self.wh[0], self.wh[1],
+                                      self.csh, self.m, Y=self.Y, ws=self.ws)
+        elif self.rht:
             self.tq.tq_linear_mp_rht(self.X, self.dh, self.rot, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m,
                                      Y=self.Y, ws=self.ws)
         else:
@@ -397,14 +404,17 @@ def main():
                 del c
                 torch.cuda.empty_cache()
         w = WORKLOADS["two_subspace"]
-        for rht in (False, True):
-            log(f"[bench] {w.title}{' (rotation online)' if rht else ''}: building inputs")
-            c = MpCase(w, torch, tq, dev, rht=rht)
+        for rht, asym in ((False, False), (True, False), (False, True)):
+            log(f"[bench] {w.title}{' (rotation online)' if rht else ''}{' (asymmetric)' if asym else ''}: "
+                "building inputs")
+            c = MpCase(w, torch, tq, dev, rht=rht, asym=asym)
             t = time_calls(c, 20, 3, torch)
             km = kernel_ms(c, 10, torch, tq)
             o = 2.0 * w.n * w.d * w.m
             b = w.n * w.d * 2 + (w.d - w.d_hi) * w.m // 2 + w.d_hi * w.m + 8 * w.m + 2 * w.n * w.m
-            row = {"workload": w.title + (": unrotated X, rotation inside the quantiser" if rht else ""), "n": w.n,
+            tag = ": unrotated X, rotation inside the quantiser" if rht else ""
+            tag = ": per-token asymmetric activations" if asym else tag
+            row = {"workload": w.title + tag, "n": w.n,
                    "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
                    "GBps": round(b / (t * 1e-3) / 1e9, 1),
                    "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),

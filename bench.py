@@ -222,10 +222,10 @@ class MpCase:
     """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
     applied online inside the quantiser (tq_linear_mp_rht)."""
 
-    def __init__(self, wl, torch, tq, dev, rht=False, asym=False):
+    def __init__(self, wl, torch, tq, dev, rht=False, asym=False, case=None):
         from workloads import draw_two_subspace
 
-        c = draw_two_subspace(wl)
+        c = case if case is not None else draw_two_subspace(wl)
         self.n, self.d, self.m, self.dh = wl.n, wl.d, wl.m, wl.d_hi
         dl = self.d - self.dh
         self.rht, self.asym = rht, asym
@@ -404,10 +404,13 @@ def main():
                 del c
                 torch.cuda.empty_cache()
         w = WORKLOADS["two_subspace"]
+        from workloads import draw_two_subspace
+
+        mp_inputs = draw_two_subspace(w)  # drawn once for the three lines
         for rht, asym in ((False, False), (True, False), (False, True)):
             log(f"[bench] {w.title}{' (rotation online)' if rht else ''}{' (asymmetric)' if asym else ''}: "
                 "building inputs")
-            c = MpCase(w, torch, tq, dev, rht=rht, asym=asym)
+            c = MpCase(w, torch, tq, dev, rht=rht, asym=asym, case=mp_inputs)
             t = time_calls(c, 20, 3, torch)
             km = kernel_ms(c, 10, torch, tq)
             o = 2.0 * w.n * w.d * w.m

@@ -648,6 +648,36 @@ def pin_asym_half_step(seed=25):
         assert np.all(np.abs(deq - x) <= 0.5 * s.astype(np.float64)[:, None] * (1 + 1e-5) + 1e-6 * np.abs(x))
 
 
+# ----------------------------------------------------------------------------
+# 6/3-bit two-subspace layer
+# ----------------------------------------------------------------------------
+
+def pin_two_subspace_6_3_lossless(seed=26):
+    """CoQuant's other bit pair: the two-subspace output at 3 bits (low) and 6
+    bits (high), q_max 3 and 31, with inputs that quantise without loss, is
+    exactly X_l W_l + X_h W_h; codes at 4/8 bits of the same data differ."""
+    rng = np.random.default_rng(seed)
+    n, dl, dh, m = 5, 64, 16, 6
+    cxl = lossless_codes(rng, n, dl, 3)
+    cxh = lossless_codes(rng, n, dh, 31)
+    cwl = lossless_codes(rng, m, dl, 3)
+    cwh = lossless_codes(rng, m, dh, 31)
+    sxl = 2.0 ** rng.integers(-4, 2, size=n)
+    sxh = 2.0 ** rng.integers(-9, -5, size=n)
+    swl = 2.0 ** rng.integers(-8, -3, size=m)
+    swh = 2.0 ** rng.integers(-12, -8, size=m)
+    xl, xh = cxl * sxl[:, None], cxh * sxh[:, None]
+    wl, wh = (cwl * swl[:, None]).T, (cwh * swh[:, None]).T
+    xrot = np.hstack([xl, xh]).astype(np.float32)
+    wrot = np.vstack([wl, wh]).astype(np.float32)
+    out = tqo.tq_linear_mp_ref(xrot, wrot, dh, bits_lo=3, bits_hi=6)
+    assert np.array_equal(out["codes_xl"], cxl) and np.array_equal(out["codes_xh"], cxh)
+    assert np.array_equal(out["codes_wl"], cwl) and np.array_equal(out["codes_wh"], cwh)
+    assert np.array_equal(out["s_xl"], (sxl * 1.0).astype(np.float32))
+    assert np.array_equal(out["Y"], xl @ wl + xh @ wh)
+    assert not np.array_equal(tqo.tq_linear_mp_ref(xrot, wrot, dh)["codes_xl"], cxl)
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -672,6 +702,7 @@ ALL_PINS = [
     pin_asym_quantizer_bruteforce,
     pin_asym_two_subspace_lossless,
     pin_asym_half_step,
+    pin_two_subspace_6_3_lossless,
 ]
 
 
@@ -683,6 +714,13 @@ def test_pin(pin):
 @pytest.mark.slow
 def test_pin_quantizer_bruteforce_int4():
     pin_quantizer_bruteforce()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("bits", [3, 6])
+def test_pin_quantizer_bruteforce_3_6(bits):
+    """The 3- and 6-bit grids of the 6/3-bit two-subspace layer, against exact rational arithmetic."""
+    pin_quantizer_bruteforce(amaxes=(3.0, 0.69921875, 1.5 * 2.0 ** -100), bits=bits)
 
 
 @pytest.mark.slow

@@ -78,15 +78,17 @@ const char* tq_status_string(tq_status s);
 /* ABI version of this header (major * 100 + minor). */
 int tq_version(void);
 
-/* Bytes of a code matrix: rows * k * bits / 8 (0 for invalid arguments). */
+/* Bytes of a code matrix: rows * k * bits / 8, with 3- and 6-bit codes stored
+ * like 4- and 8-bit ones (0 for invalid arguments). */
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits);
 
 /*
  * tq_pack_weight -- offline per-output-channel symmetric quantisation.
  *   W       d x m weight (Y = X W), element type w_dt (TQ_F32 or TQ_BF16).
- *   bits    4 or 8.
- *   w_codes out: m x (d*bits/8) bytes; row j holds output channel j (column j
- *           of W) with k contiguous.
+ *   bits    4 or 8; or 3 or 6 (the 6/3-bit two-subspace layer: q_max 3 or
+ *           31, stored like 4 or 8 bits).
+ *   w_codes out: m x tq_codes_bytes(1, d, bits) bytes; row j holds output
+ *           channel j (column j of W) with k contiguous.
  *   s_w     out: m fp32 scales.
  * Per-channel symmetric weights follow CoQuant's experimental protocol (the
  * ResQ setting: per-channel symmetric weight quantisation).
@@ -216,7 +218,7 @@ tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r
 size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
 
 /*
- * tq_linear_mp -- the two-subspace mixed-precision layer, equation (2).
+ * tq_linear_mp -- the two-subspace mixed-precision layer.
  *   Xrot     n x d rotated activations (x_dt).  The first d - d_hi columns
  *            are the low-precision subspace (4 bits), the last d_hi columns
  *            the high-precision subspace (8 bits); each subspace has its own
@@ -234,6 +236,18 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
                        const void* wl_codes, const float* s_wl, const void* wh_codes,
                        const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/*
+ * tq_linear_mp_bits -- tq_linear_mp at other bit widths: (bits_lo, bits_hi) =
+ * (4, 8), or (3, 6), the other pair of CoQuant's experimental protocol (1/8 of
+ * the channels at 6 bits, the rest at 3); the weights packed by
+ * tq_pack_weight at those widths.  Codes keep the 4- and 8-bit storage, so the
+ * same kernels run.  TQ_ERR_BITS for other pairs; otherwise as tq_linear_mp.
+ */
+tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                            int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl,
+                            const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /*
  * Byte offsets inside the tq_linear_mp (and tq_linear_mp_rht) workspace:

@@ -248,18 +248,18 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 104; }
+int tq_version(void) { return 105; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
-  if (rows < 0 || k < 0 || (bits != 4 && bits != 8) || (bits == 4 && (k & 1))) return 0;
-  return (size_t)rows * (size_t)k * (size_t)bits / 8;
+  if (rows < 0 || k < 0 || (bits != 3 && bits != 4 && bits != 6 && bits != 8) || (bits <= 4 && (k & 1))) return 0;
+  return (size_t)rows * (size_t)k * (size_t)(bits <= 4 ? 4 : 8) / 8;  // 3 / 6 bits stored like 4 / 8
 }
 
 tq_status tq_pack_weight(const void* W, tq_dtype w_dt, int64_t d, int64_t m, int bits, void* w_codes, float* s_w,
                          hipStream_t stream) {
-  if (bits != 4 && bits != 8) return TQ_ERR_BITS;
+  if (bits != 3 && bits != 4 && bits != 6 && bits != 8) return TQ_ERR_BITS;
   if (!valid_dtype(w_dt)) return TQ_ERR_DTYPE;
-  if (d <= 0 || m <= 0 || d > kMaxDim || m > kMaxDim || d % (bits == 4 ? 32 : 16)) return TQ_ERR_SHAPE;
+  if (d <= 0 || m <= 0 || d > kMaxDim || m > kMaxDim || d % (bits <= 4 ? 32 : 16)) return TQ_ERR_SHAPE;
   if (!W || !w_codes || !s_w) return TQ_ERR_NULL;
   if (!aligned16(W) || !aligned16(w_codes) || !aligned16(s_w)) return TQ_ERR_ALIGN;
   TQ_RUN("pack_weight", stream, tq::launch_pack_weight(W, w_dt == TQ_BF16, (int)d, (int)m, bits, w_codes, s_w, stream));
@@ -568,9 +568,11 @@ tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_
 
 extern "C" {
 
-tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
-                       const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
-                       tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                            int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl, const void* wh_codes,
+                            const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!((bits_lo == 4 && bits_hi == 8) || (bits_lo == 3 && bits_hi == 6))) return TQ_ERR_BITS;
   const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
   if (st != TQ_OK || n == 0) return st;
   const int64_t dl = d - d_hi;
@@ -584,15 +586,25 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
   const bool xb = x_dt == TQ_BF16;
   if (dl > 0 && d_hi > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)dl, 8, xl, sxl, xh, sxh, stream));
+           tq::launch_quant_rows_i8_bits(Xrot, xb, (int)n, (int)d, (int)dl, bits_lo, bits_hi, xl, sxl, xh, sxh,
+                                         stream));
   } else if (dl > 0) {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_i8(Xrot, xb, (int)n, (int)d, (int)d, 4, xl, sxl, nullptr, nullptr, stream));
+           tq::launch_quant_rows_i8_bits(Xrot, xb, (int)n, (int)d, (int)d, bits_lo, bits_lo, xl, sxl, nullptr,
+                                         nullptr, stream));
   } else {
     TQ_RUN("quant_rows_mp", stream,
-           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, 8, 8, xh, sxh, nullptr, nullptr, stream));
+           tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, bits_hi, bits_hi, xh, sxh, nullptr, nullptr,
+                                      stream));
   }
   return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
+}
+
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+                       const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
+                       tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return tq_linear_mp_bits(Xrot, x_dt, n, d, d_hi, m, 4, 8, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws, ws_bytes,
+                           stream);
 }
 
 tq_status tq_linear_mp_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[4]) {

@@ -127,6 +127,17 @@ struct QTraits<8> {
   static constexpr int QMAX = 127;
   static constexpr float NEAR = 0x1p-14f;
 };
+// 3 and 6 bits (the 6/3-bit two-subspace layer), stored like 4 and 8 bits
+template <>
+struct QTraits<3> {
+  static constexpr int QMAX = 3;
+  static constexpr float NEAR = 0x1p-18f;
+};
+template <>
+struct QTraits<6> {
+  static constexpr int QMAX = 31;
+  static constexpr float NEAR = 0x1p-14f;
+};
 
 struct RowScale {
   float s;
@@ -211,7 +222,9 @@ __device__ __forceinline__ void store_codes_int8(uint8_t* row, int ch, const int
 // and each code's byte is the low byte of t = fma(x, y, 1.5 * 2^23), whose
 // bits are bits(1.5 * 2^23) + code with zero low mantissa bits in the
 // constant; v_perm_b32 gathers the 4 bytes of a dword.
+template <int BITS = 4>
 __device__ __forceinline__ uint2 quant8_int8(const float (&x)[8], const RowScale& rs) {
+  static_assert(BITS <= 4, "codes of at most 4 bits");
   if (rs.fast) {
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
     uint32_t t[8];
@@ -223,7 +236,7 @@ __device__ __forceinline__ uint2 quant8_int8(const float (&x)[8], const RowScale
       em = fminf(em, fabsf(fabsf(d) - 0.5f));
       t[i] = __float_as_uint(tf);
     }
-    if (__builtin_expect(!(em < QTraits<4>::NEAR), 1)) {
+    if (__builtin_expect(!(em < QTraits<BITS>::NEAR), 1)) {
       // bytes [b0 of t0, t2, t4, t6] and [b0 of t1, t3, t5, t7]
       const uint32_t e = __builtin_amdgcn_perm(t[2], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[6], t[4], 0x04000c0cu);
       const uint32_t o = __builtin_amdgcn_perm(t[3], t[1], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[5], 0x04000c0cu);
@@ -231,7 +244,7 @@ __device__ __forceinline__ uint2 quant8_int8(const float (&x)[8], const RowScale
     }
   }
   int c[8];
-  quant8_exact<4>(x, rs.s, c);
+  quant8_exact<BITS>(x, rs.s, c);
   return codes_int8(c);
 }
 // 8 codes -> 8 int8 bytes.

@@ -149,6 +149,10 @@ hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L
 // int8 tile GEMM (dl bytes per row); columns [dl, d) take bits_b bits.
 hipError_t launch_quant_rows_i8(const void* X, bool bf16, int n, int d, int dl, int bits_b, void* ca, float* sa,
                                 void* cb, float* sb, hipStream_t st);
+// The same for the two-subspace layer at bits_a / bits_b = 4 / 8 or 3 / 6
+// (3-bit codes stored like 4-bit ones, 6-bit like 8-bit).
+hipError_t launch_quant_rows_i8_bits(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
+                                     float* sa, void* cb, float* sb, hipStream_t st);
 // Per-token quantiser with one wave per row (falls back to a block per row for very long rows).
 hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
                                   float* sa, void* cb, float* sb, hipStream_t st);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, in
     if (j0 + tx < m) sw[j0 + tx] = rs.s;
   }
   __syncthreads();
-  const size_t row_bytes = (size_t)d * BITS / 8;
+  const size_t row_bytes = (size_t)d * (BITS <= 4 ? 4 : 8) / 8;  // 3 / 6 bits stored like 4 / 8
   const int c = tid >> 2, kg = tid & 3;
   const RowScale rs = {s_s[c], s_r[c], s_f[c] != 0};
   for (int k0 = 0; k0 < d; k0 += 64) {
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(256) void k_pack_weight(const T* __restrict__ W, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = tile[kb + i][c];
         quant8<BITS>(v, rs, q);
-        uint8_t* dst = codes + (size_t)(j0 + c) * row_bytes + (size_t)(k0 + kb) * BITS / 8;
-        if (BITS == 4)
+        uint8_t* dst = codes + (size_t)(j0 + c) * row_bytes + (size_t)(k0 + kb) * (BITS <= 4 ? 4 : 8) / 8;
+        if (BITS <= 4)
           *reinterpret_cast<uint32_t*>(dst) = pack_nibbles(q);
         else
           *reinterpret_cast<uint2*>(dst) = pack_bytes(q);
@@ -161,15 +161,15 @@ __device__ __forceinline__ void quant_row_block(const T* __restrict__ x, int d, 
     Load8<T>::load(x + 8 * ch, v, raw);
     if (ch < nchl) {
       quant8<BA>(v, ra, q);
-      if (BA == 4 && X8)
+      if (BA <= 4 && X8)
         store_codes_int8(ca, ch, q);
-      else if (BA == 4)
+      else if (BA <= 4)
         *reinterpret_cast<uint32_t*>(ca + (size_t)ch * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(ca + (size_t)ch * 8) = pack_bytes(q);
     } else {
       quant8<BB>(v, rb, q);
-      if (BB == 4)
+      if (BB <= 4)
         *reinterpret_cast<uint32_t*>(cb + (size_t)(ch - nchl) * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(cb + (size_t)(ch - nchl) * 8) = pack_bytes(q);
@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const T* __restrict__ X, int
                                                     uint8_t* __restrict__ cb, float* __restrict__ sb) {
   __shared__ float red[16];
   const int row = blockIdx.x;
-  const size_t lda = X8 ? (size_t)dl : (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
+  const size_t lda = X8 ? (size_t)dl : (size_t)dl * (BA <= 4 ? 4 : 8) / 8,
+               ldb = (size_t)(d - dl) * (BB <= 4 ? 4 : 8) / 8;
   quant_row_block<T, BA, BB, X8>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row, cb ? cb + row * ldb : nullptr,
                                  sb ? sb + row : nullptr, red);
 }
@@ -234,14 +235,14 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
   // division path, so neither is evaluated speculatively for the other.
   auto store = [&](int ch, const int (&q)[8]) {
     if (ch < nchl) {
-      if (BA == 4 && X8)
+      if (BA <= 4 && X8)
         store_codes_int8(ca, ch, q);
-      else if (BA == 4)
+      else if (BA <= 4)
         *reinterpret_cast<uint32_t*>(ca + (size_t)ch * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(ca + (size_t)ch * 8) = pack_bytes(q);
     } else {
-      if (BB == 4)
+      if (BB <= 4)
         *reinterpret_cast<uint32_t*>(cb + (size_t)(ch - nchl) * 4) = pack_nibbles(q);
       else
         *reinterpret_cast<uint2*>(cb + (size_t)(ch - nchl) * 8) = pack_bytes(q);
@@ -256,8 +257,8 @@ __device__ __forceinline__ void quant_row_wave(const T* __restrict__ x, int d, i
         float v[8];
         int q[8];
         c[i].get(v);
-        if (BA == 4 && X8 && ch < nchl) {
-          *reinterpret_cast<uint2*>(ca + 8 * ch) = quant8_int8(v, ra);
+        if (BA <= 4 && X8 && ch < nchl) {
+          *reinterpret_cast<uint2*>(ca + 8 * ch) = quant8_int8<BA <= 4 ? BA : 4>(v, ra);
           continue;
         }
         if (ch < nchl)
@@ -292,7 +293,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_wave(const T* __restrict__ X
                                                          uint8_t* __restrict__ cb, float* __restrict__ sb) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  const size_t lda = X8 ? (size_t)dl : (size_t)dl * BA / 8, ldb = (size_t)(d - dl) * BB / 8;
+  const size_t lda = X8 ? (size_t)dl : (size_t)dl * (BA <= 4 ? 4 : 8) / 8,
+               ldb = (size_t)(d - dl) * (BB <= 4 ? 4 : 8) / 8;
   quant_row_wave<T, BA, BB, CH, X8>(X + (size_t)row * d, d, dl, ca + row * lda, sa + row,
                                     cb ? cb + row * ldb : nullptr, sb ? sb + row : nullptr);
 }
@@ -525,10 +527,15 @@ template <typename T>
 static hipError_t launch_pack_weight_t(const void* W, int d, int m, int ldw, int dv, int mv, int bits, void* codes,
                                        float* sw, hipStream_t st) {
   dim3 grid((m + 63) / 64), block(256);
-  if (bits == 4)
-    hipLaunchKernelGGL((k_pack_weight<T, 4>), grid, block, 0, st, (const T*)W, d, m, ldw, dv, mv, (uint8_t*)codes, sw);
-  else
-    hipLaunchKernelGGL((k_pack_weight<T, 8>), grid, block, 0, st, (const T*)W, d, m, ldw, dv, mv, (uint8_t*)codes, sw);
+  const T* w = (const T*)W;
+  uint8_t* c = (uint8_t*)codes;
+  switch (bits) {
+    case 3: hipLaunchKernelGGL((k_pack_weight<T, 3>), grid, block, 0, st, w, d, m, ldw, dv, mv, c, sw); break;
+    case 4: hipLaunchKernelGGL((k_pack_weight<T, 4>), grid, block, 0, st, w, d, m, ldw, dv, mv, c, sw); break;
+    case 6: hipLaunchKernelGGL((k_pack_weight<T, 6>), grid, block, 0, st, w, d, m, ldw, dv, mv, c, sw); break;
+    case 8: hipLaunchKernelGGL((k_pack_weight<T, 8>), grid, block, 0, st, w, d, m, ldw, dv, mv, c, sw); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -601,8 +608,10 @@ static hipError_t launch_quant_rows_wave_t(const void* X, int n, int d, int dl, 
     default:  // rows beyond 16384 values: a block per row
       if constexpr (X8)
         hipLaunchKernelGGL((k_quant_rows<T, BA, BB, true>), dim3(n), dim3(256), 0, st, x, n, d, dl, a, sa, b, sb);
-      else
+      else if constexpr ((BA == 4 || BA == 8) && (BB == 4 || BB == 8))
         return launch_quant_rows_t<T>(X, n, d, dl, BA, BB, ca, sa, cb, sb, st);
+      else
+        hipLaunchKernelGGL((k_quant_rows<T, BA, BB>), dim3(n), dim3(256), 0, st, x, n, d, dl, a, sa, b, sb);
   }
   return hipGetLastError();
 }
@@ -616,11 +625,28 @@ hipError_t launch_quant_rows_i8(const void* X, bool bf16, int n, int d, int dl, 
                      : launch_quant_rows_wave_t<float, 4, 4, true>(X, n, d, dl, ca, sa, cb, sb, st);
 }
 
+hipError_t launch_quant_rows_i8_bits(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
+                                     float* sa, void* cb, float* sb, hipStream_t st) {
+#define TQ_QB(T)                                                                                                   \
+  if (bits_a == 4) return bits_b == 8 ? launch_quant_rows_wave_t<T, 4, 8, true>(X, n, d, dl, ca, sa, cb, sb, st)    \
+                                      : launch_quant_rows_wave_t<T, 4, 4, true>(X, n, d, dl, ca, sa, cb, sb, st);   \
+  if (bits_a == 3) return bits_b == 6 ? launch_quant_rows_wave_t<T, 3, 6, true>(X, n, d, dl, ca, sa, cb, sb, st)    \
+                                      : launch_quant_rows_wave_t<T, 3, 3, true>(X, n, d, dl, ca, sa, cb, sb, st);   \
+  return hipErrorInvalidValue;
+  if (bf16) {
+    TQ_QB(bf16_t)
+  } else {
+    TQ_QB(float)
+  }
+#undef TQ_QB
+}
+
 hipError_t launch_quant_rows_fast(const void* X, bool bf16, int n, int d, int dl, int bits_a, int bits_b, void* ca,
                                   float* sa, void* cb, float* sb, hipStream_t st) {
 #define TQ_QR(T)                                                                                          \
   if (bits_a == 4 && bits_b == 8) return launch_quant_rows_wave_t<T, 4, 8>(X, n, d, dl, ca, sa, cb, sb, st); \
   if (bits_a == 4) return launch_quant_rows_wave_t<T, 4, 4>(X, n, d, dl, ca, sa, cb, sb, st);               \
+  if (bits_a == 6) return launch_quant_rows_wave_t<T, 6, 6>(X, n, d, dl, ca, sa, cb, sb, st);               \
   return launch_quant_rows_wave_t<T, 8, 8>(X, n, d, dl, ca, sa, cb, sb, st);
   if (bf16) {
     TQ_QR(bf16_t)

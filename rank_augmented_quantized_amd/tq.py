@@ -30,7 +30,7 @@ EXPORTS = (
     "tq_linear_group_workspace_bytes", "tq_linear_group", "tq_linear_mp_workspace_offsets", "tq_rht_bytes",
     "tq_pack_rht", "tq_linear_mp_rht", "tq_lowrank_q_bytes", "tq_pack_lowrank_q", "tq_linear_qlr_workspace_bytes",
     "tq_linear_qlr_workspace_offsets", "tq_linear_qlr", "tq_weight_colsum", "tq_linear_mp_asym_workspace_bytes",
-    "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym",
+    "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits",
 )
 
 
@@ -90,6 +90,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_qlr_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_linear_qlr": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
         "tq_weight_colsum": (st, [ptr, i64, i64, c_int, ptr, ptr]),
+        "tq_linear_mp_bits": (st, [ptr, c_int, i64, i64, i64, i64, c_int, c_int, ptr, ptr, ptr, ptr, ptr, c_int, ptr,
+                                   sz, ptr]),
         "tq_linear_mp_asym_workspace_bytes": (sz, [i64, i64, i64]),
         "tq_linear_mp_asym_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_linear_mp_asym": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, ptr, ptr, c_int, ptr,
@@ -140,7 +142,7 @@ def tq_pack_weight(W, bits: int = 4, w_codes=None, s_w=None):
     _need_cuda(W)
     d, m = W.shape
     if w_codes is None:
-        w_codes = torch.empty((m, d * bits // 8), dtype=torch.uint8, device=W.device)
+        w_codes = torch.empty((m, d * (4 if bits <= 4 else 8) // 8), dtype=torch.uint8, device=W.device)
     if s_w is None:
         s_w = torch.empty(m, dtype=torch.float32, device=W.device)
     _check("tq_pack_weight", lib.tq_pack_weight(_p(W), _dt(W), d, m, bits, _p(w_codes), _p(s_w), _stream(W)))
@@ -206,8 +208,9 @@ def tq_linear_mp_workspace_bytes(n: int, d: int, d_hi: int) -> int:
     return load().tq_linear_mp_workspace_bytes(n, d, d_hi)
 
 
-def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtype=torch.bfloat16, Y=None, ws=None):
-    """Y = Q4(X_l) Q4(W_l) + Q8(X_h) Q8(W_h), X_h = the last d_hi columns of Xrot."""
+def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtype=torch.bfloat16, Y=None, ws=None,
+                 bits=(4, 8)):
+    """Y = Q4(X_l) Q4(W_l) + Q8(X_h) Q8(W_h), X_h = the last d_hi columns of Xrot (bits=(3, 6): Q3 and Q6)."""
     lib = load()
     _need_cuda(Xrot, wl_codes, s_wl, wh_codes, s_wh, Y, ws)
     n, d = Xrot.shape
@@ -215,9 +218,14 @@ def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtyp
         Y = torch.empty((n, m), dtype=y_dtype, device=Xrot.device)
     if ws is None:
         ws = torch.empty(max(1, tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=Xrot.device)
-    _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
-                                            _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
-                                            _stream(Xrot)))
+    if tuple(bits) == (4, 8):
+        _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
+                                                _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                                _stream(Xrot)))
+    else:
+        _check("tq_linear_mp_bits", lib.tq_linear_mp_bits(_p(Xrot), _dt(Xrot), n, d, d_hi, m, bits[0], bits[1],
+                                                          _p(wl_codes), _p(s_wl), _p(wh_codes), _p(s_wh), _p(Y),
+                                                          _dt(Y), _p(ws), ws.numel(), _stream(Xrot)))
     return Y
 
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 104
+    assert lib.tq_version() == 105
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -185,6 +185,20 @@ def test_qlr_validation(lib):
     off = tqb.tq_linear_qlr_workspace_offsets(n, d, r)
     assert off["x_codes"] >= off["s_x"] + 4 * n and off["t_codes"] >= off["s_t"] + 4 * n
     assert all(v % 256 == 0 for v in off.values())
+
+
+def test_mp_bits_validation(lib):
+    assert lib.tq_codes_bytes(4, 64, 3) == 4 * 32 and lib.tq_codes_bytes(4, 64, 6) == 4 * 64
+    assert lib.tq_codes_bytes(4, 64, 5) == 0
+    assert lib.tq_pack_weight(A, 1, 512, 64, 5, B, C, S) == -4
+    assert lib.tq_pack_weight(A, 1, 48, 64, 3, B, C, S) == -2  # 3-bit rows: d % 32
+    n, d, dh, m = 64, 512, 64, 256
+    need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 4, 6, B, C, A, B, C, 1, A, need, S) == -4
+    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 3, 8, B, C, A, B, C, 1, A, need, S) == -4
+    assert lib.tq_linear_mp_bits(A, 1, n, d, 40, m, 3, 6, B, C, A, B, C, 1, A, need, S) == -2
+    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 3, 6, B, C, A, B, C, 1, A, need - 1, S) == -6
+    assert lib.tq_linear_mp_bits(A, 1, 0, d, dh, m, 3, 6, B, C, A, B, C, 1, A, 0, S) == 0
 
 
 def test_mp_asym_validation(lib):

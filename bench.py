@@ -222,20 +222,20 @@ class MpCase:
     """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
     applied online inside the quantiser (tq_linear_mp_rht)."""
 
-    def __init__(self, wl, torch, tq, dev, rht=False, asym=False, case=None):
+    def __init__(self, wl, torch, tq, dev, rht=False, asym=False, case=None, bits=(4, 8)):
         from workloads import draw_two_subspace
 
         c = case if case is not None else draw_two_subspace(wl)
         self.n, self.d, self.m, self.dh = wl.n, wl.d, wl.m, wl.d_hi
         dl = self.d - self.dh
-        self.rht, self.asym = rht, asym
+        self.rht, self.asym, self.bits = rht, asym, tuple(bits)
         self.X = torch.from_numpy(c["X" if rht else "Xrot"]).to(dev).bfloat16()
         if rht:
             self.rot = tq.tq_pack_rht(torch.from_numpy(c["signs"].astype("float32")).to(dev),
                                       torch.from_numpy(c["perm"].astype("int32")).to(dev))
         W = torch.from_numpy(c["Wrot"])
-        self.wl = tq.tq_pack_weight(W[:dl].contiguous().to(dev), 4)
-        self.wh = tq.tq_pack_weight(W[dl:].contiguous().to(dev), 8)
+        self.wl = tq.tq_pack_weight(W[:dl].contiguous().to(dev), self.bits[0])
+        self.wh = tq.tq_pack_weight(W[dl:].contiguous().to(dev), self.bits[1])
         del W, c
         if asym:
             self.csl = tq.tq_weight_colsum(self.wl[0], dl, 4)
@@ -254,7 +254,7 @@ class MpCase:
                                      Y=self.Y, ws=self.ws)
         else:
             self.tq.tq_linear_mp(self.X, self.dh, self.wl[0], self.wl[1], self.wh[0], self.wh[1], self.m, Y=self.Y,
-                                 ws=self.ws)
+                                 ws=self.ws, bits=self.bits)
 
 
 def cpu_baseline(wl, rows, seconds):
@@ -407,16 +407,18 @@ def main():
         from workloads import draw_two_subspace
 
         mp_inputs = draw_two_subspace(w)  # drawn once for the three lines
-        for rht, asym in ((False, False), (True, False), (False, True)):
-            log(f"[bench] {w.title}{' (rotation online)' if rht else ''}{' (asymmetric)' if asym else ''}: "
-                "building inputs")
-            c = MpCase(w, torch, tq, dev, rht=rht, asym=asym, case=mp_inputs)
+        for rht, asym, bits in ((False, False, (4, 8)), (True, False, (4, 8)), (False, True, (4, 8)),
+                                (False, False, (3, 6))):
+            log(f"[bench] {w.title}{' (rotation online)' if rht else ''}{' (asymmetric)' if asym else ''}"
+                f"{' (6/3 bits)' if bits != (4, 8) else ''}: building inputs")
+            c = MpCase(w, torch, tq, dev, rht=rht, asym=asym, case=mp_inputs, bits=bits)
             t = time_calls(c, 20, 3, torch)
             km = kernel_ms(c, 10, torch, tq)
             o = 2.0 * w.n * w.d * w.m
             b = w.n * w.d * 2 + (w.d - w.d_hi) * w.m // 2 + w.d_hi * w.m + 8 * w.m + 2 * w.n * w.m
             tag = ": unrotated X, rotation inside the quantiser" if rht else ""
             tag = ": per-token asymmetric activations" if asym else tag
+            tag = ": 6-bit and 3-bit subspaces" if bits != (4, 8) else tag
             row = {"workload": w.title + tag, "n": w.n,
                    "us": round(t * 1e3, 2), "TOPS": round(o / (t * 1e-3) / 1e12, 2),
                    "GBps": round(b / (t * 1e-3) / 1e9, 1),

@@ -26,8 +26,9 @@ It evaluates the plain definition of the layer, step by step, in numpy:
   error expression of section 04.A and the fused two-stage low-rank pipeline
   of section 04.C;
 * per-token asymmetric activations (a zero-point per token) for the
-  two-subspace layer -- CoQuant Eq. 1 with z != 0 and the experimental
-  protocol (per-token asymmetric activations, per-channel symmetric weights).
+  two-subspace layer and for the rank-augmented layer -- CoQuant Eq. 1 with
+  z != 0 and the experimental protocol (per-token asymmetric activations,
+  per-channel symmetric weights).
 
 Readings of points the pages leave open (each one is also listed in the
 design notes): q_max = 7 / 127; "round" is round-half-to-even; the scale is
@@ -66,6 +67,7 @@ __all__ = [
     "tq_linear_qlr_ref",
     "quantize_rows_asym",
     "tq_linear_mp_asym_ref",
+    "tq_linear_asym_ref",
 ]
 
 
@@ -386,6 +388,38 @@ def tq_linear_mp_asym_ref(xrot, wrot, d_hi: int, rows=None, cols=None, bits_lo: 
                     f"colsum_{tag}": colsum, f"acc_{tag}": acc})
     out["Y"] = y
     return out
+
+
+def tq_linear_asym_ref(x, r, l1=None, l2=None, rows=None, cols=None):
+    """The rank-augmented layer with per-token asymmetric 4-bit activations:
+
+        Y = s_x s_w^T (.) (U C_w^T) + z_x (s_w (.) colsum(C_w))^T + (X L1) L2      (fp64)
+
+    U, s_x, z_x from ``quantize_rows_asym`` (4 bits), C_w, s_w per output
+    channel as in ``tq_linear_ref``; the low-rank branch from the unquantised
+    activations as there.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    r = np.asarray(r, dtype=np.float32)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    if cols is not None:
+        r = r[:, np.asarray(cols)]
+        if l2 is not None:
+            l2 = np.asarray(l2)[:, np.asarray(cols)]
+    u, s_x, z_x = quantize_rows_asym(x, 4)
+    cw, s_w = quantize_weight(r, 4)
+    acc = int_matmul(u, cw)
+    colsum = cw.astype(np.int64).sum(axis=1)
+    sw = s_w.astype(np.float64)
+    y = (s_x.astype(np.float64)[:, None] * sw[None, :]) * acc.astype(np.float64)
+    y = y + z_x.astype(np.float64)[:, None] * (sw * colsum.astype(np.float64))[None, :]
+    t = None
+    if l1 is not None and np.asarray(l1).shape[1] > 0:
+        t, ylr = lowrank_branch(x, l1, l2)
+        y = y + ylr
+    return {"codes_x": u, "s_x": s_x, "z_x": z_x, "codes_w": cw, "s_w": s_w, "colsum": colsum, "acc": acc, "T": t,
+            "Y": y}
 
 
 def hadamard(k: int) -> np.ndarray:

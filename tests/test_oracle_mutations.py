@@ -17,7 +17,7 @@ import test_oracle_pins as pins
 _orig = {name: getattr(tqo, name) for name in (
     "quantize_rows", "quantize_weight", "pack_int4", "unpack_int4", "int_matmul",
     "lowrank_branch", "tq_linear_ref", "tq_linear_mp_ref", "hadamard", "block_rotation",
-    "subspace_split", "tq_linear_group_ref", "rht_rows", "requantize_lowrank", "tq_linear_qlr_ref", "quantize_rows_asym", "tq_linear_mp_asym_ref")}
+    "subspace_split", "tq_linear_group_ref", "rht_rows", "requantize_lowrank", "tq_linear_qlr_ref", "quantize_rows_asym", "tq_linear_mp_asym_ref", "tq_linear_asym_ref")}
 
 
 def _q_reciprocal(a, bits=4):
@@ -326,6 +326,26 @@ def _mp_asym_shared_z(xrot, wrot, d_hi, rows=None, cols=None, bits_lo=4, bits_hi
     return out
 
 
+def _linear_asym_no_zero_term(x, r, l1=None, l2=None, rows=None, cols=None):  # z s_w colsum dropped
+    out = _orig["tq_linear_asym_ref"](x, r, l1, l2, rows, cols)
+    y = (out["s_x"].astype(np.float64)[:, None] * out["s_w"].astype(np.float64)[None, :]) * out["acc"]
+    if out["T"] is not None:
+        y = y + out["T"] @ np.asarray(l2 if cols is None else np.asarray(l2)[:, cols], np.float64)
+    out["Y"] = y
+    return out
+
+
+def _linear_asym_offset_codes(x, r, l1=None, l2=None, rows=None, cols=None):  # codes u - 8 without the 8 s term
+    out = _orig["tq_linear_asym_ref"](x, r, l1, l2, rows, cols)
+    sw = out["s_w"].astype(np.float64)
+    y = (out["s_x"].astype(np.float64)[:, None] * sw[None, :]) * _orig["int_matmul"](out["codes_x"] - 8, out["codes_w"])
+    y = y + out["z_x"].astype(np.float64)[:, None] * (sw * out["colsum"])[None, :]
+    if out["T"] is not None:
+        y = y + out["T"] @ np.asarray(l2 if cols is None else np.asarray(l2)[:, cols], np.float64)
+    out["Y"] = y
+    return out
+
+
 MUTANTS = {
     "quantize_rows": [_q_reciprocal, _q_half_away, _q_qmax_pow2, _q_per_tensor, _q_no_clamp_low],
     "quantize_weight": [_w_per_input_channel],
@@ -344,6 +364,7 @@ MUTANTS = {
     "tq_linear_qlr_ref": [_qlr_lr_no_sx, _qlr_lr_no_st, _qlr_unrequantised],
     "quantize_rows_asym": [_asym_qmax_signed, _asym_signed_clip, _asym_z_max, _asym_sub_after],
     "tq_linear_mp_asym_ref": [_mp_asym_no_zero_term, _mp_asym_shared_z],
+    "tq_linear_asym_ref": [_linear_asym_no_zero_term, _linear_asym_offset_codes],
 }
 
 CASES = [(name, f) for name, fs in MUTANTS.items() for f in fs]

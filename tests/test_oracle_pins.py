@@ -678,6 +678,39 @@ def pin_two_subspace_6_3_lossless(seed=26):
     assert not np.array_equal(tqo.tq_linear_mp_ref(xrot, wrot, dh)["codes_xl"], cxl)
 
 
+def pin_asym_linear(seed=27):
+    """The rank-augmented layer with asymmetric activations: with lossless
+    inputs (rows z + u s spanning the 4-bit grid, R from codes) Y equals
+    X R + (X L1) L2 up to the fp64 rounding of the low-rank branch, and
+    exactly X R without it; its residual term is the one-subspace case of the
+    asymmetric two-subspace layer; a shifted row adds shift * s_w * colsum."""
+    rng = np.random.default_rng(seed)
+    n, d, m, rk = 6, 64, 9, 4
+    u, s, z, x = _asym_lossless(rng, n, d, 15, -5, 1)
+    cw = lossless_codes(rng, m, d, 7)
+    sw = 2.0 ** rng.integers(-8, -3, size=m)
+    w = (cw * sw[:, None]).T
+    x32, w32 = x.astype(np.float32), w.astype(np.float32)
+    out = tqo.tq_linear_asym_ref(x32, w32)
+    assert np.array_equal(out["codes_x"], u) and np.array_equal(out["z_x"], z.astype(np.float32))
+    assert np.array_equal(out["s_x"], s.astype(np.float32)) and np.array_equal(out["colsum"], cw.sum(axis=1))
+    assert np.array_equal(out["Y"], x @ w)
+    l1 = rng.standard_normal((d, rk)).astype(np.float32)
+    l2 = rng.standard_normal((rk, m)).astype(np.float32)
+    full = tqo.tq_linear_asym_ref(x32, w32, l1, l2)["Y"]
+    ref = x @ w + (x @ l1.astype(np.float64)) @ l2.astype(np.float64)
+    assert np.allclose(full, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    xg = rng.standard_normal((n, d)).astype(np.float32)
+    wg = (0.02 * rng.standard_normal((d, m))).astype(np.float32)
+    assert np.array_equal(tqo.tq_linear_asym_ref(xg, wg)["Y"], tqo.tq_linear_mp_asym_ref(xg, wg, 0)["Y"])
+    xs = x32.copy()
+    xs[3] += np.float32(2 * s[3])
+    o2 = tqo.tq_linear_asym_ref(xs, w32)
+    want = out["Y"].copy()
+    want[3] += 2 * s[3] * (sw * cw.sum(axis=1))
+    assert np.array_equal(o2["codes_x"], u) and np.array_equal(o2["Y"], want)
+
+
 ALL_PINS = [
     pin_quantizer_golden,
     pin_quantizer_invariants,
@@ -703,6 +736,7 @@ ALL_PINS = [
     pin_asym_two_subspace_lossless,
     pin_asym_half_step,
     pin_two_subspace_6_3_lossless,
+    pin_asym_linear,
 ]
 
 

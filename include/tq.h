@@ -311,11 +311,11 @@ tq_status tq_weight_colsum(const void* w_codes, int64_t m, int64_t k, int bits, 
 /*
  * tq_linear_mp_asym -- tq_linear_mp with asymmetric activations; colsum_l /
  * colsum_h: tq_weight_colsum of wl_codes / wh_codes (m int32 each, needed when
- * that subspace is not empty).  d <= 8192.  ws:
+ * that subspace is not empty).  d <= 16384.  ws:
  * tq_linear_mp_asym_workspace_bytes(n, d, d_hi) bytes.  Two launches: the
  * quantiser (one wave per token row, the row read once) and the two-subspace
  * GEMM, whose epilogue adds each subspace's zero-point term.  Errors as
- * tq_linear_mp, plus TQ_ERR_SHAPE for d > 8192.
+ * tq_linear_mp, plus TQ_ERR_SHAPE for d > 16384.
  */
 size_t tq_linear_mp_asym_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
 tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
@@ -331,6 +331,29 @@ tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t 
  * subspace (n fp32 each).  For tests.
  */
 tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi, size_t off[6]);
+
+/*
+ * tq_linear_asym -- tq_linear with per-token asymmetric 4-bit activations
+ * (same z, s and codes as tq_linear_mp_asym's 4-bit subspace):
+ *   Y = s_x s_w (.) (U C_w^T) + z_x (s_w (.) colsum(C_w)) + (X L1) L2,
+ * colsum = tq_weight_colsum(w_codes, m, d, 4) (m int32).  d <= 16384.  Every
+ * n takes the tile GEMM (two launches: the quantiser with T = X L1, then the
+ * GEMM whose epilogue adds the zero-point term).  ws:
+ * tq_linear_asym_workspace_bytes(n, d, m, r) bytes, zero-filled once before
+ * its first use (as tq_linear's).  Errors as tq_linear, plus TQ_ERR_SHAPE for
+ * d > 16384.
+ */
+size_t tq_linear_asym_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
+tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                         const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank,
+                         void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Byte offsets inside the tq_linear_asym workspace: off[0] s_x (n fp32),
+ * off[1] activation codes (n x d int8, u - 8, in the tile GEMM's order),
+ * off[2] z_x (n fp32), off[3] T (n x r_pad bf16).  For tests.
+ */
+tq_status tq_linear_asym_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]);
 
 /*
  * Fully quantised low-rank branch (TwinQuant notes, "TwinQuant: Learnable

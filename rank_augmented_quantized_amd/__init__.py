@@ -12,6 +12,8 @@ from .tq import (  # noqa: F401
     tq_codes_bytes,
     tq_debug_accumulate,
     tq_linear,
+    tq_linear_asym,
+    tq_linear_asym_workspace_offsets,
     tq_linear_group,
     tq_linear_group_workspace_bytes,
     tq_linear_mp,

@@ -115,10 +115,11 @@ struct LinearWs {
 
 // tcols: columns of T (r_pad of one layer; a power of two covering all the
 // layers of a group)
-LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols) {
+// tile: the tile-GEMM layout for every n (the asymmetric layer)
+LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool tile = false) {
   (void)m;
   LinearWs w{};
-  w.small = n <= kSmallN;
+  w.small = !tile && n <= kSmallN;
   w.r_pad = (int)tcols;
   w.fused = w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
   size_t psize = 0;
@@ -248,7 +249,7 @@ const char* tq_status_string(tq_status s) {
   return "unknown tq_status";
 }
 
-int tq_version(void) { return 105; }
+int tq_version(void) { return 106; }
 
 size_t tq_codes_bytes(int64_t rows, int64_t k, int bits) {
   if (rows < 0 || k < 0 || (bits != 3 && bits != 4 && bits != 6 && bits != 8) || (bits <= 4 && (k & 1))) return 0;
@@ -698,6 +699,72 @@ tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, i
          tq::launch_quant_rows_rht(X, x_dt == TQ_BF16, (int)n, (int)d, (int)(d - d_hi), rot, base + W.xl,
                                    (float*)(base + W.sxl), base + W.xh, (float*)(base + W.sxh), stream));
   return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
+}
+
+// Workspace of tq_linear_asym: the tile-GEMM layout of tq_linear, then the
+// zero-points.
+size_t asym_zx_offset(const LinearWs& L) { return L.total; }
+size_t asym_total(const LinearWs& L, int64_t n) { return align256(L.total + (size_t)n * 4); }
+
+size_t tq_linear_asym_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r) {
+  if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
+  return asym_total(linear_ws(n, d, m, r_padded(r), true), n);
+}
+
+tq_status tq_linear_asym_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]) {
+  if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return TQ_ERR_SHAPE;
+  if (!off) return TQ_ERR_NULL;
+  const LinearWs L = linear_ws(n, d, m, r_padded(r), true);
+  off[0] = L.sx;
+  off[1] = L.xc;
+  off[2] = asym_zx_offset(L);
+  off[3] = L.t;
+  return TQ_OK;
+}
+
+tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                         const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank, void* Y,
+                         tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  if (d > tq::kAsymMaxD) return TQ_ERR_SHAPE;
+  if (!colsum) return TQ_ERR_NULL;
+  if (!aligned16(colsum)) return TQ_ERR_ALIGN;
+  const int rp = (int)r_padded(r);
+  const LinearWs L = linear_ws(n, d, m, rp, true);
+  if (ws_bytes < asym_total(L, n)) return TQ_ERR_WORKSPACE;
+  uint8_t* base = (uint8_t*)ws;
+  float* sx = (float*)(base + L.sx);
+  float* zx = (float*)(base + asym_zx_offset(L));
+  uint8_t* xc = base + L.xc;
+  tq::bf16_t* T = (tq::bf16_t*)(base + L.t);
+  const tq::bf16_t* L1t = (const tq::bf16_t*)lowrank;
+  TQ_RUN("prologue_asym", stream,
+         tq::launch_prologue_asym(X, x_dt == TQ_BF16, (int)n, (int)d, L1t, rp, L.plan, xc, sx, zx,
+                                  (float*)(base + L.p), rp ? T : nullptr, (unsigned*)(base + L.ctr), stream));
+  GemmArgs g{};
+  g.A = xc;
+  g.lda = d;  // int8 codes u - 8
+  g.B = (const uint8_t*)w_codes;
+  g.ldb = d / 2;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(d / 2);
+  g.sx = sx;
+  g.sw = s_w;
+  g.T = rp ? T : nullptr;
+  g.L2t = lowrank ? L1t + (size_t)rp * d : nullptr;
+  g.r_pad = rp;
+  g.ldt = rp;
+  g.groups.n = 1;
+  g.groups.start[1] = (int)m;
+  g.zx = zx;
+  g.csw = colsum;
+  g.Y = Y;
+  g.ldy = m;
+  g.y_bf16 = y_dt == TQ_BF16;
+  TQ_RUN("gemm_asym", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, 4, stream));
+  return TQ_OK;
 }
 
 size_t tq_lowrank_q_bytes(int64_t d, int64_t m, int64_t r) {

@@ -22,58 +22,6 @@
 namespace tq {
 namespace {
 
-// Maximum of any floats over the 64 lanes (DPP inside rows, then the four
-// row results as scalars).
-template <int CTRL>
-__device__ __forceinline__ float dpp_fmax(float x) {
-  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false);
-  return fmaxf(x, __int_as_float(y));
-}
-__device__ __forceinline__ float wave_fmax(float v) {
-  v = dpp_fmax<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_fmax<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_fmax<0x141>(v);  // row_half_mirror
-  v = dpp_fmax<0x140>(v);  // row_mirror
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, e));
-}
-
-struct AsymScale {
-  float s, z, rcp;
-  bool fast;
-};
-
-template <int BITS>
-__device__ __forceinline__ AsymScale asym_scale(float mn, float mx) {
-  AsymScale a;
-  a.z = mn;
-  a.s = (mx - mn) / (float)((1 << BITS) - 1);  // correctly rounded fp32 subtraction and division
-  a.fast = (a.s >= 0x1p-125f) && (a.s <= 0x1p+125f);
-  a.rcp = a.fast ? 1.0f / a.s : 0.0f;
-  return a;
-}
-
-// u - 2^(N-1) for v = fl32(x - z): the fast path rounds v * fl32(1 / s) with
-// the magic-number add and falls back to the IEEE division when the
-// product lies within NEAR of a half-integer (|v / s| <= 2^N - 1, so the
-// product's error stays far below NEAR: the same decision as the division).
-template <int BITS>
-__device__ __forceinline__ int code_asym(float v, const AsymScale& a) {
-  constexpr int QM = (1 << BITS) - 1, OFF = 1 << (BITS - 1);
-  if (a.fast) {
-    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-    const float t = __builtin_fmaf(v, a.rcp, MAGIC);
-    const float dd = __builtin_fmaf(v, a.rcp, -(t - MAGIC));
-    if (!(fabsf(fabsf(dd) - 0.5f) < QTraits<BITS>::NEAR))
-      return min((int)(__float_as_uint(t) - 0x4B400000u), QM) - OFF;
-  }
-  if (!(a.s > 0.0f)) return -OFF;
-  return min(max((int)rintf(v / a.s), 0), QM) - OFF;
-}
-
 template <typename T, int CH>
 __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X, int n, int d, int dl,
                                                          uint8_t* __restrict__ xl, float* __restrict__ sl,
@@ -84,11 +32,25 @@ __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X
   const int lane = threadIdx.x & 63;
   const int nch = d >> 3, nchl = dl >> 3, dh = d - dl;
   const T* x = X + (size_t)row * d;
-  Row8<T> c[CH];
+  // rows up to 8192 values stay in registers; longer rows are read twice
+  // (the second pass from L2)
+  constexpr bool KEEP = CH <= 16;
+  Row8<T> c[KEEP ? CH : 1];
+  auto get = [&](int i, float (&v)[8]) {
+    if constexpr (KEEP) {
+      c[i].get(v);
+    } else {
+      Row8<T> t;
+      t.load(x + 8 * (lane + 64 * i));
+      t.get(v);
+    }
+  };
+  if constexpr (KEEP) {
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int ch = lane + 64 * i;
-    if (ch < nch) c[i].load(x + 8 * ch);
+    for (int i = 0; i < CH; ++i) {
+      const int ch = lane + 64 * i;
+      if (ch < nch) c[i].load(x + 8 * ch);
+    }
   }
   // max and -min of each segment (lanes without values keep -inf)
   float mxl = -INFINITY, nml = -INFINITY, mxh = -INFINITY, nmh = -INFINITY;
@@ -97,7 +59,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X
     const int ch = lane + 64 * i;
     if (ch < nch) {
       float v[8];
-      c[i].get(v);
+      get(i, v);
       float hi = v[0], lo = v[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) {
@@ -134,7 +96,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X
     if (ch < nch) {
       float v[8];
       int q[8];
-      c[i].get(v);
+      get(i, v);
       if (ch < nchl) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = code_asym<4>(v[e] - al.z, al);
@@ -192,6 +154,7 @@ hipError_t launch_asym_t(const void* X, int n, int d, int dl, void* xl, float* s
     TQ_ASYM(4)
     TQ_ASYM(8)
     TQ_ASYM(16)
+    TQ_ASYM(32)
     default:
       return hipErrorInvalidValue;
   }

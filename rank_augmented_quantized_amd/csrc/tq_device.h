@@ -334,4 +334,61 @@ __device__ __forceinline__ float quant_row_i8_wave(const T* x, int nch, int lane
   return rs.s;
 }
 
+// ---------------------------------------------------------------------------
+// Per-token asymmetric quantisation (CoQuant Eq. 1 with a zero-point): the
+// row's z = min and s = fl32(fl32(max - min) / (2^N - 1)); the code of x is
+// u = rne(fl32(fl32(x - z) / s)) in [0, 2^N - 1], returned as u - 2^(N-1).
+// ---------------------------------------------------------------------------
+// Maximum of any floats over the 64 lanes (DPP inside rows, then the four
+// row results as scalars).
+template <int CTRL>
+__device__ __forceinline__ float dpp_fmax(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xF, 0xF, false);
+  return fmaxf(x, __int_as_float(y));
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+  v = dpp_fmax<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_fmax<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_fmax<0x141>(v);  // row_half_mirror
+  v = dpp_fmax<0x140>(v);  // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, e));
+}
+
+struct AsymScale {
+  float s, z, rcp;
+  bool fast;
+};
+
+template <int BITS>
+__device__ __forceinline__ AsymScale asym_scale(float mn, float mx) {
+  AsymScale a;
+  a.z = mn;
+  a.s = (mx - mn) / (float)((1 << BITS) - 1);  // correctly rounded fp32 subtraction and division
+  a.fast = (a.s >= 0x1p-125f) && (a.s <= 0x1p+125f);
+  a.rcp = a.fast ? 1.0f / a.s : 0.0f;
+  return a;
+}
+
+// u - 2^(N-1) for v = fl32(x - z): the fast path rounds v * fl32(1 / s) with
+// the magic-number add and falls back to the IEEE division when the
+// product lies within NEAR of a half-integer (|v / s| <= 2^N - 1, so the
+// product's error stays far below NEAR: the same decision as the division).
+template <int BITS>
+__device__ __forceinline__ int code_asym(float v, const AsymScale& a) {
+  constexpr int QM = (1 << BITS) - 1, OFF = 1 << (BITS - 1);
+  if (a.fast) {
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    const float t = __builtin_fmaf(v, a.rcp, MAGIC);
+    const float dd = __builtin_fmaf(v, a.rcp, -(t - MAGIC));
+    if (!(fabsf(fabsf(dd) - 0.5f) < QTraits<BITS>::NEAR))
+      return min((int)(__float_as_uint(t) - 0x4B400000u), QM) - OFF;
+  }
+  if (!(a.s > 0.0f)) return -OFF;
+  return min(max((int)rintf(v / a.s), 0), QM) - OFF;
+}
+
 }  // namespace tq

@@ -591,6 +591,18 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
     uint8_t* sYw = smem + wave * (WN * WM * 2);
     auto ychunk = [&](int row, int j) -> int { return row * (WM * 2) + 16 * (j ^ ((row >> 1) & 7)); };
     auto yslot = [&](int row, int j, int half) -> int { return ychunk(row, j) + 8 * (half ^ ((row >> 4) & 1)); };
+    // asymmetric activations of the rank-augmented layer (codes u - 8): the
+    // zero-point term (z + 8 s_x) s_w colsum(C_w) (CoQuant Eq. 1 with a
+    // zero-point), added block by block like the quantised branch
+    const bool zp_lin = EPI == EPI_LINEAR && g.zx != nullptr;
+    float zzv[FN];
+    if (EPI == EPI_LINEAR && zp_lin) {
+#pragma unroll
+      for (int b = 0; b < FN; ++b) {
+        const int t = min(tok(b), g.M - 1);
+        zzv[b] = g.zx[t] + 8.0f * g.sx[t];
+      }
+    }
 #pragma unroll
     for (int a = 0; a < FM; ++a) {
       uint2 v0;
@@ -600,9 +612,29 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) svv[e4] = load4(g.sv, chan(a, e4));
       }
+      if (EPI == EPI_LINEAR && zp_lin) {  // svv: s_w colsum of the block's channels
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = chan(a, e4);
+          const float4 s4 = load4(g.sw, c);
+          const int4 c4 = c + 3 < g.N ? *reinterpret_cast<const int4*>(g.csw + c)
+                                      : int4{g.csw[min(c, g.N - 1)], g.csw[min(c + 1, g.N - 1)],
+                                             g.csw[min(c + 2, g.N - 1)], g.csw[min(c + 3, g.N - 1)]};
+          svv[e4] = float4{s4.x * (float)c4.x, s4.y * (float)c4.y, s4.z * (float)c4.z, s4.w * (float)c4.w};
+        }
+      }
 #pragma unroll
       for (int b = 0; b < FN; ++b) {
         if constexpr (EPI == EPI_QLR) qlr_add(a, b, v0, svv);
+        if (EPI == EPI_LINEAR && zp_lin) {
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            y[a][b][4 * e4 + 0] += zzv[b] * svv[e4].x;
+            y[a][b][4 * e4 + 1] += zzv[b] * svv[e4].y;
+            y[a][b][4 * e4 + 2] += zzv[b] * svv[e4].z;
+            y[a][b][4 * e4 + 3] += zzv[b] * svv[e4].w;
+          }
+        }
         if (g.y_bf16) {
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {

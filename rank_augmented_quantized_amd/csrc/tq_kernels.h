@@ -145,6 +145,12 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks);
 int gemv_max_chunks(int M, int Kb, int r_pad);
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st);
+// The prologue of the asymmetric layer: per-token asymmetric codes (u - 8,
+// int8 for the tile GEMM), scales and zero-points (zx), and T as above; p from
+// plan_prologue(n, d, r_pad, false, 1).
+hipError_t launch_prologue_asym(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad,
+                                const ProloguePlan& p, void* xc, float* sx, float* zx, float* P, void* Tout,
+                                unsigned* counters, hipStream_t st);
 // The same with the 4-bit codes of columns [0, dl) as int8 in the order of the
 // int8 tile GEMM (dl bytes per row); columns [dl, d) take bits_b bits.
 hipError_t launch_quant_rows_i8(const void* X, bool bf16, int n, int d, int dl, int bits_b, void* ca, float* sa,
@@ -223,7 +229,7 @@ hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uin
 // columns [0, dl) at 4 bits (u - 8 as int8 in the tile GEMM's order, dl bytes
 // per row), [dl, d) at 8 bits (u - 128, natural order); per row and segment
 // the scale and the zero-point.  d <= kAsymMaxD.
-constexpr int kAsymMaxD = 8192;
+constexpr int kAsymMaxD = 16384;
 hipError_t launch_quant_rows_asym(const void* X, bool bf16, int n, int d, int dl, void* xl, float* sl, float* zl,
                                   void* xh, float* sh, float* zh, hipStream_t st);
 // colsum[j] = sum over k of code row j (m rows of k codes, 4 or 8 bits).

@@ -682,6 +682,7 @@ struct FusedArgs {
   uint8_t* xc;
   float* sx;
   bf16_t* T;
+  float* zx;  // ASYM: per-token zero-points
 };
 constexpr int kFusedWaves = 16;
 constexpr int kFusedMaxD = 4096;  // the 16 bf16 rows fill at most 128 KiB of LDS
@@ -692,7 +693,9 @@ __host__ __device__ constexpr int fused_lds_bytes(int d, int qs) {
   return x > p ? x : p;
 }
 
-template <typename T, int CH, int QS>
+// ASYM: per-token asymmetric codes (u - 8, z = min, s = range / 15) and the
+// zero-points, for the asymmetric layer.
+template <typename T, int CH, int QS, bool ASYM = false>
 __global__ __launch_bounds__(1024) void k_prologue_rows(FusedArgs a) {
   constexpr int WAVES = kFusedWaves, COLS = 16 * QS;
   constexpr int U = QS <= 2 ? 8 : (QS <= 4 ? 4 : 1);  // L1 steps fetched ahead
@@ -713,27 +716,61 @@ __global__ __launch_bounds__(1024) void k_prologue_rows(FusedArgs a) {
         const int ch = lane + 64 * i;
         if (ch < nch) r[i].load(x + 8 * ch);
       }
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (lane + 64 * i < nch) {
-          float v[8];
-          r[i].get(v);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
-        }
-      }
-      const RowScale rs = row_scale<4>(wave_max(mx));
-      if (lane == 0) a.sx[row] = rs.s;
       uint8_t* cr = a.xc + (size_t)row * d;
+      if constexpr (ASYM) {
+        float hi = -INFINITY, nlo = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int ch = lane + 64 * i;
-        if (ch < nch) {
-          float v[8];
-          r[i].get(v);
-          *reinterpret_cast<uint2*>(cr + 8 * ch) = quant8_int8(v, rs);
-          if constexpr (QS > 0) *reinterpret_cast<uint4*>(sx_row + 16 * ch) = r[i].bf16();
+        for (int i = 0; i < CH; ++i) {
+          if (lane + 64 * i < nch) {
+            float v[8];
+            r[i].get(v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              hi = fmaxf(hi, v[e]);
+              nlo = fmaxf(nlo, -v[e]);
+            }
+          }
+        }
+        const AsymScale as = asym_scale<4>(-wave_fmax(nlo), wave_fmax(hi));
+        if (lane == 0) {
+          a.sx[row] = as.s;
+          a.zx[row] = as.z;
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const int ch = lane + 64 * i;
+          if (ch < nch) {
+            float v[8];
+            int q[8];
+            r[i].get(v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = code_asym<4>(v[e] - as.z, as);
+            store_codes_int8(cr, ch, q);
+            if constexpr (QS > 0) *reinterpret_cast<uint4*>(sx_row + 16 * ch) = r[i].bf16();
+          }
+        }
+      } else {
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          if (lane + 64 * i < nch) {
+            float v[8];
+            r[i].get(v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+          }
+        }
+        const RowScale rs = row_scale<4>(wave_max(mx));
+        if (lane == 0) a.sx[row] = rs.s;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const int ch = lane + 64 * i;
+          if (ch < nch) {
+            float v[8];
+            r[i].get(v);
+            *reinterpret_cast<uint2*>(cr + 8 * ch) = quant8_int8(v, rs);
+            if constexpr (QS > 0) *reinterpret_cast<uint4*>(sx_row + 16 * ch) = r[i].bf16();
+          }
         }
       }
     } else if constexpr (QS > 0) {
@@ -798,37 +835,38 @@ static bool fused_fits(int d, int qs) {
   return d <= kFusedMaxD && (qs == 0 || qs == 2 || qs == 4 || qs == 8) && fused_lds_bytes(d, qs) <= 160 * 1024;
 }
 
-template <typename T, int CH>
+template <typename T, int CH, bool ASYM>
 static hipError_t launch_rows_ch(const FusedArgs& a, int qs, hipStream_t st) {
   const dim3 grid((unsigned)((a.n + 15) / 16)), block(64 * kFusedWaves);
   const unsigned lds = (unsigned)fused_lds_bytes(a.d, qs);
   switch (qs) {
-    case 0: launch_kernel(k_prologue_rows<T, CH, 0>, grid, block, lds, st, a); break;
-    case 2: launch_kernel(k_prologue_rows<T, CH, 2>, grid, block, lds, st, a); break;
-    case 4: launch_kernel(k_prologue_rows<T, CH, 4>, grid, block, lds, st, a); break;
-    case 8: launch_kernel(k_prologue_rows<T, CH, 8>, grid, block, lds, st, a); break;
+    case 0: launch_kernel(k_prologue_rows<T, CH, 0, ASYM>, grid, block, lds, st, a); break;
+    case 2: launch_kernel(k_prologue_rows<T, CH, 2, ASYM>, grid, block, lds, st, a); break;
+    case 4: launch_kernel(k_prologue_rows<T, CH, 4, ASYM>, grid, block, lds, st, a); break;
+    case 8: launch_kernel(k_prologue_rows<T, CH, 8, ASYM>, grid, block, lds, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool ASYM>
 static hipError_t launch_rows_t(const FusedArgs& a, int qs, hipStream_t st) {
   switch (chunks_for(a.d)) {
-    case 1: return launch_rows_ch<T, 1>(a, qs, st);
-    case 2: return launch_rows_ch<T, 2>(a, qs, st);
-    case 4: return launch_rows_ch<T, 4>(a, qs, st);
-    case 8: return launch_rows_ch<T, 8>(a, qs, st);
+    case 1: return launch_rows_ch<T, 1, ASYM>(a, qs, st);
+    case 2: return launch_rows_ch<T, 2, ASYM>(a, qs, st);
+    case 4: return launch_rows_ch<T, 4, ASYM>(a, qs, st);
+    case 8: return launch_rows_ch<T, 8, ASYM>(a, qs, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 static hipError_t launch_prologue_fused(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad,
-                                        void* xc, float* sx, void* Tout, hipStream_t st) {
-  const FusedArgs a{X, n, d, (const bf16_t*)L1t, r_pad, (uint8_t*)xc, sx, (bf16_t*)Tout};
+                                        void* xc, float* sx, void* Tout, hipStream_t st, float* zx = nullptr) {
+  const FusedArgs a{X, n, d, (const bf16_t*)L1t, r_pad, (uint8_t*)xc, sx, (bf16_t*)Tout, zx};
   const int qs = r_pad / 16;
   if (!fused_fits(d, qs)) return hipErrorInvalidValue;
-  return bf16 ? launch_rows_t<bf16_t>(a, qs, st) : launch_rows_t<float>(a, qs, st);
+  if (zx) return bf16 ? launch_rows_t<bf16_t, true>(a, qs, st) : launch_rows_t<float, true>(a, qs, st);
+  return bf16 ? launch_rows_t<bf16_t, false>(a, qs, st) : launch_rows_t<float, false>(a, qs, st);
 }
 
 // Fewest tokens for the fused prologue.
@@ -925,6 +963,19 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, int waves, int ch, hi
     case 2: return launch_prologue_q<T, 2, 4, 4, true>(a, ch, st);
     default: return launch_prologue_q<T, 4, 4, 2, true>(a, ch, st);
   }
+}
+
+hipError_t launch_prologue_asym(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad,
+                                const ProloguePlan& p, void* xc, float* sx, float* zx, float* P, void* Tout,
+                                unsigned* counters, hipStream_t st) {
+  if (p.fused) return launch_prologue_fused(X, bf16, n, d, L1t, r_pad, xc, sx, Tout, st, zx);
+  // the asymmetric quantiser (int8 codes for the tile GEMM), then the T blocks alone
+  hipError_t e = launch_quant_rows_asym(X, bf16, n, d, d, xc, sx, zx, nullptr, nullptr, nullptr, st);
+  if (e != hipSuccess || p.ntb == 0) return e;
+  PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, 0, p.partial ? 1 : 0,
+                 p.row_blocks ? 1 : 0, p.sum_to_p0 ? 1 : 0, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters};
+  const int ch = std::min(chunks_for(d), 32);
+  return bf16 ? launch_prologue_t<bf16_t>(a, p.waves, ch, st) : launch_prologue_t<float>(a, p.waves, ch, st);
 }
 
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,

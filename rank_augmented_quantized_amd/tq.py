@@ -30,7 +30,8 @@ EXPORTS = (
     "tq_linear_group_workspace_bytes", "tq_linear_group", "tq_linear_mp_workspace_offsets", "tq_rht_bytes",
     "tq_pack_rht", "tq_linear_mp_rht", "tq_lowrank_q_bytes", "tq_pack_lowrank_q", "tq_linear_qlr_workspace_bytes",
     "tq_linear_qlr_workspace_offsets", "tq_linear_qlr", "tq_weight_colsum", "tq_linear_mp_asym_workspace_bytes",
-    "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits",
+    "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits", "tq_linear_asym_workspace_bytes",
+    "tq_linear_asym_workspace_offsets", "tq_linear_asym",
 )
 
 
@@ -90,6 +91,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_qlr_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_linear_qlr": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
         "tq_weight_colsum": (st, [ptr, i64, i64, c_int, ptr, ptr]),
+        "tq_linear_asym_workspace_bytes": (sz, [i64, i64, i64, i64]),
+        "tq_linear_asym_workspace_offsets": (st, [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "tq_linear_asym": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
         "tq_linear_mp_bits": (st, [ptr, c_int, i64, i64, i64, i64, c_int, c_int, ptr, ptr, ptr, ptr, ptr, c_int, ptr,
                                    sz, ptr]),
         "tq_linear_mp_asym_workspace_bytes": (sz, [i64, i64, i64]),
@@ -387,6 +391,26 @@ def tq_linear_mp_asym(Xrot, d_hi: int, wl_codes, s_wl, colsum_l, wh_codes, s_wh,
     _check("tq_linear_mp_asym", lib.tq_linear_mp_asym(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
                                                       _p(colsum_l), _p(wh_codes), _p(s_wh), _p(colsum_h), _p(Y),
                                                       _dt(Y), _p(ws), ws.numel(), _stream(Xrot)))
+    return Y
+
+
+def tq_linear_asym_workspace_offsets(n: int, d: int, m: int, r: int) -> dict:
+    off = (ctypes.c_size_t * 4)()
+    _check("tq_linear_asym_workspace_offsets", load().tq_linear_asym_workspace_offsets(n, d, m, r, off))
+    return {"s_x": off[0], "x_codes": off[1], "z_x": off[2], "T": off[3]}
+
+
+def tq_linear_asym(X, w_codes, s_w, colsum, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
+    """tq_linear with per-token asymmetric activations; colsum = tq_weight_colsum(w_codes, d, 4)."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, colsum, lowrank, Y, ws)
+    n, d = X.shape
+    if Y is None:
+        Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
+    if ws is None:
+        ws = torch.zeros(max(1, lib.tq_linear_asym_workspace_bytes(n, d, m, r)), dtype=torch.uint8, device=X.device)
+    _check("tq_linear_asym", lib.tq_linear_asym(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(colsum),
+                                                _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
     return Y
 
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.tq_version() == 105
+    assert lib.tq_version() == 106
     for code in range(-7, 1):
         assert lib.tq_status_string(code)
     assert b"unknown" in lib.tq_status_string(-99)
@@ -187,6 +187,20 @@ def test_qlr_validation(lib):
     assert all(v % 256 == 0 for v in off.values())
 
 
+def test_linear_asym_validation(lib):
+    n, d, m, r = 64, 512, 256, 32
+    need = lib.tq_linear_asym_workspace_bytes(n, d, m, r)
+    assert need > lib.tq_linear_workspace_bytes(n, d, m, r)
+    assert lib.tq_linear_asym(A, 1, n, 520, m, r, B, C, A, B, A, 1, C, need, S) == -2
+    assert lib.tq_linear_asym(A, 1, n, 32768, m, r, B, C, A, B, A, 1, C, need, S) == -2  # d > 16384
+    assert lib.tq_linear_asym(A, 1, n, d, m, r, B, C, NUL, B, A, 1, C, need, S) == -1  # colsum
+    assert lib.tq_linear_asym(A, 1, n, d, m, r, B, C, MIS, B, A, 1, C, need, S) == -5
+    assert lib.tq_linear_asym(A, 1, n, d, m, r, B, C, A, B, A, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_asym(A, 1, 0, d, m, r, B, C, A, B, A, 1, C, 0, S) == 0
+    off = tqb.tq_linear_asym_workspace_offsets(n, d, m, r)
+    assert off["x_codes"] >= off["s_x"] + 4 * n and off["z_x"] >= off["T"] and all(v % 256 == 0 for v in off.values())
+
+
 def test_mp_bits_validation(lib):
     assert lib.tq_codes_bytes(4, 64, 3) == 4 * 32 and lib.tq_codes_bytes(4, 64, 6) == 4 * 64
     assert lib.tq_codes_bytes(4, 64, 5) == 0
@@ -210,7 +224,7 @@ def test_mp_asym_validation(lib):
     need = lib.tq_linear_mp_asym_workspace_bytes(n, d, dh)
     assert need == lib.tq_linear_mp_workspace_bytes(n, d, dh) + 2 * 256
     assert lib.tq_linear_mp_asym(A, 1, n, d, 40, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d_hi % 16
-    assert lib.tq_linear_mp_asym(A, 1, n, 16384, 128, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d > 8192
+    assert lib.tq_linear_mp_asym(A, 1, n, 32768, 128, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d > 16384
     assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, NUL, A, B, C, A, 1, C, need, S) == -1  # colsum_l
     assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, A, A, B, NUL, A, 1, C, need, S) == -1  # colsum_h
     assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, MIS, A, B, C, A, 1, C, need, S) == -5

@@ -218,6 +218,33 @@ class QlrCase:
         self.tq.tq_linear_qlr(self.X, wc, sw, lq, self.m, self.r, Y=self.Y, ws=self.ws)
 
 
+class AsymCase:
+    """The rank-augmented layer with per-token asymmetric activations (tq_linear_asym); `copies` weight sets."""
+
+    def __init__(self, wl, n, copies, torch, tq, dev):
+        from workloads import draw_linear
+
+        c = draw_linear(wl, n=n)
+        self.n, self.d, self.m, self.r = n, wl.d, wl.m, wl.r
+        self.X = torch.from_numpy(c["X"]).to(dev).bfloat16()
+        R = torch.from_numpy(c["R"]).to(dev)
+        L1 = torch.from_numpy(c["L1"]).to(dev).bfloat16()
+        L2 = torch.from_numpy(c["L2"]).to(dev).bfloat16()
+        self.w = []
+        for _ in range(copies):
+            wc, sw = tq.tq_pack_weight(R, 4)
+            self.w.append((wc, sw, tq.tq_weight_colsum(wc, wl.d, 4), tq.tq_pack_lowrank(L1, L2)))
+        del R
+        self.Y = torch.empty((n, self.m), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.zeros(tq.load().tq_linear_asym_workspace_bytes(n, self.d, self.m, self.r), dtype=torch.uint8,
+                              device=dev)
+        self.tq = tq
+
+    def __call__(self, i):
+        wc, sw, cs, lr = self.w[i % len(self.w)]
+        self.tq.tq_linear_asym(self.X, wc, sw, cs, lr, self.m, self.r, Y=self.Y, ws=self.ws)
+
+
 class MpCase:
     """The two-subspace layer on pre-rotated X' (tq_linear_mp) or, with rht, on unrotated X with the rotation
     applied online inside the quantiser (tq_linear_mp_rht)."""
@@ -398,6 +425,22 @@ def main():
                        "TOPS": round(o / (t * 1e-3) / 1e12, 2), "GBps": round(b / (t * 1e-3) / 1e9, 1),
                        "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
                        "pct_hbm": round(100 * b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                       "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
+                sweep.append(row)
+                log(f"[bench] sweep {row}")
+                del c
+                torch.cuda.empty_cache()
+        for name, ns in (("attn_proj", (4096,)), ("mlp_gate_up", (16,))):
+            w = WORKLOADS[name]
+            for nn in ns:
+                c = AsymCase(w, nn, args.copies if nn <= 256 else 2, torch, tq, dev)
+                t = time_calls(c, max(20, args.steps // 2), 10, torch)
+                km = kernel_ms(c, 20, torch, tq)
+                o = 2.0 * nn * w.d * w.m
+                b = alg_bytes(nn, w.d, w.m, w.r) + 4 * w.m
+                row = {"workload": f"{w.title}: per-token asymmetric activations", "n": nn, "us": round(t * 1e3, 2),
+                       "TOPS": round(o / (t * 1e-3) / 1e12, 2), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                       "pct_mfma": round(100 * o / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
                        "kernels_us": {k: round(v * 1e3, 2) for k, v in km.items()}}
                 sweep.append(row)
                 log(f"[bench] sweep {row}")

@@ -126,3 +126,33 @@ def test_linear_asym_attn_proj_sampled():
     rows = np.sort(rng.choice(4096, 48, replace=False))
     cols = np.sort(rng.choice(4096, 64, replace=False))
     _check(c["X"], c["R"], c["L1"], c["L2"], y, ws, cs, rows=rows, cols=cols)
+
+
+def test_linear_asym_graph_replay_matches_eager():
+    """The asymmetric layer (quantiser, T blocks with their cross-block counters, GEMM) captured in a HIP graph
+    and replayed gives the eager output on every replay."""
+    n, d, m, rk = 300, 2048, 512, 32
+    c = draw_custom(n, d, m, rk, seed=81)
+    wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+    cs = tq.tq_weight_colsum(wc, d, 4)
+    lr = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+    x = _t(c["X"], torch.bfloat16)
+    ws = torch.zeros(tq.load().tq_linear_asym_workspace_bytes(n, d, m, rk), dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, m), dtype=torch.bfloat16, device=DEV)
+    tq.tq_linear_asym(x, wc, sw, cs, lr, m, rk, Y=y, ws=ws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tq.tq_linear_asym(x, wc, sw, cs, lr, m, rk, Y=y, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tq.tq_linear_asym(x, wc, sw, cs, lr, m, rk, Y=y, ws=ws)
+    for _ in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)

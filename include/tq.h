@@ -336,9 +336,10 @@ tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi
  * tq_linear_asym -- tq_linear with per-token asymmetric 4-bit activations
  * (same z, s and codes as tq_linear_mp_asym's 4-bit subspace):
  *   Y = s_x s_w (.) (U C_w^T) + z_x (s_w (.) colsum(C_w)) + (X L1) L2,
- * colsum = tq_weight_colsum(w_codes, m, d, 4) (m int32).  d <= 16384.  Every
- * n takes the tile GEMM (two launches: the quantiser with T = X L1, then the
- * GEMM whose epilogue adds the zero-point term).  ws:
+ * colsum = tq_weight_colsum(w_codes, m, d, 4) (m int32).  d <= 16384.  Two
+ * launches: the quantiser with T = X L1, then the GEMM (the tile GEMM, or for
+ * n <= 32 the weight-streaming small-n GEMM) whose epilogue adds the
+ * zero-point term.  ws:
  * tq_linear_asym_workspace_bytes(n, d, m, r) bytes, zero-filled once before
  * its first use (as tq_linear's).  Errors as tq_linear, plus TQ_ERR_SHAPE for
  * d > 16384.
@@ -350,8 +351,9 @@ tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int
 
 /*
  * Byte offsets inside the tq_linear_asym workspace: off[0] s_x (n fp32),
- * off[1] activation codes (n x d int8, u - 8, in the tile GEMM's order),
- * off[2] z_x (n fp32), off[3] T (n x r_pad bf16).  For tests.
+ * off[1] activation codes (u - 8: n x d int8 in the tile GEMM's order, or
+ * for n <= 32 nibble-packed, n x d / 2 bytes), off[2] z_x (n fp32), off[3] T
+ * (n x r_pad bf16).  For tests.
  */
 tq_status tq_linear_asym_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]);
 

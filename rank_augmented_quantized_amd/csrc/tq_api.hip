@@ -115,13 +115,13 @@ struct LinearWs {
 
 // tcols: columns of T (r_pad of one layer; a power of two covering all the
 // layers of a group)
-// tile: the tile-GEMM layout for every n (the asymmetric layer)
-LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool tile = false) {
+// two_launch: never the one-launch few-token kernel (the asymmetric layer)
+LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_launch = false) {
   (void)m;
   LinearWs w{};
-  w.small = !tile && n <= kSmallN;
+  w.small = n <= kSmallN;
   w.r_pad = (int)tcols;
-  w.fused = w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
+  w.fused = !two_launch && w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
   size_t psize = 0;
   int counters = 0;
   if (w.fused) {
@@ -701,14 +701,14 @@ tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, i
   return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
 }
 
-// Workspace of tq_linear_asym: the tile-GEMM layout of tq_linear, then the
+// Workspace of tq_linear_asym: the two-launch layout of tq_linear, then the
 // zero-points.
 size_t asym_zx_offset(const LinearWs& L) { return L.total; }
 size_t asym_total(const LinearWs& L, int64_t n) { return align256(L.total + (size_t)n * 4); }
 
 size_t tq_linear_asym_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r) {
   if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
-  return asym_total(linear_ws(n, d, m, r_padded(r), true), n);
+  return asym_total(linear_ws(n, d, m, r_padded(r), true), n);  // two-launch layout
 }
 
 tq_status tq_linear_asym_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]) {
@@ -739,12 +739,13 @@ tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int
   uint8_t* xc = base + L.xc;
   tq::bf16_t* T = (tq::bf16_t*)(base + L.t);
   const tq::bf16_t* L1t = (const tq::bf16_t*)lowrank;
+  float* P = (float*)(base + L.p);
   TQ_RUN("prologue_asym", stream,
-         tq::launch_prologue_asym(X, x_dt == TQ_BF16, (int)n, (int)d, L1t, rp, L.plan, xc, sx, zx,
-                                  (float*)(base + L.p), rp ? T : nullptr, (unsigned*)(base + L.ctr), stream));
+         tq::launch_prologue_asym(X, x_dt == TQ_BF16, (int)n, (int)d, L1t, rp, L.plan, xc, sx, zx, P,
+                                  rp ? T : nullptr, (unsigned*)(base + L.ctr), stream));
   GemmArgs g{};
   g.A = xc;
-  g.lda = d;  // int8 codes u - 8
+  g.lda = L.small ? d / 2 : d;  // codes u - 8: nibble-packed for the small-n GEMM, else int8
   g.B = (const uint8_t*)w_codes;
   g.ldb = d / 2;
   g.M = (int)n;
@@ -763,7 +764,16 @@ tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
-  TQ_RUN("gemm_asym", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, 4, stream));
+  if (L.small) {
+    if (rp && (L.plan.partial || L.plan.sum_to_p0)) {
+      g.P = P;
+      g.nchunk = L.plan.partial ? L.plan.nchunk : 1;
+      g.Tout = T;
+    }
+    TQ_RUN("gemm_small_n_asym", stream, tq::launch_gemv(g, 4, tq::EPI_LINEAR, stream));
+  } else {
+    TQ_RUN("gemm_asym", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, 4, stream));
+  }
   return TQ_OK;
 }
 

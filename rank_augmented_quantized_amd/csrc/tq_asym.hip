@@ -22,7 +22,9 @@
 namespace tq {
 namespace {
 
-template <typename T, int CH>
+// PK: the 4-bit segment nibble-packed (dl / 2 bytes per row, even k in the
+// low nibble) for the small-n GEMM, else int8 in the tile GEMM's order.
+template <typename T, int CH, bool PK = false>
 __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X, int n, int d, int dl,
                                                          uint8_t* __restrict__ xl, float* __restrict__ sl,
                                                          float* __restrict__ zl, uint8_t* __restrict__ xh,
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X
       zh[row] = ah.z;
     }
   }
-  uint8_t* rl = xl + (size_t)row * dl;
+  uint8_t* rl = xl + (size_t)row * (PK ? dl / 2 : dl);
   uint8_t* rh = xh + (size_t)row * dh;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -100,7 +102,10 @@ __global__ __launch_bounds__(256) void k_quant_rows_asym(const T* __restrict__ X
       if (ch < nchl) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = code_asym<4>(v[e] - al.z, al);
-        store_codes_int8(rl, ch, q);
+        if constexpr (PK)
+          *reinterpret_cast<uint32_t*>(rl + 4 * ch) = pack_nibbles(q);
+        else
+          store_codes_int8(rl, ch, q);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = code_asym<8>(v[e] - ah.z, ah);
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(256) void k_weight_colsum(const uint8_t* __restrict
   if (lane == 0) colsum[row] = acc;
 }
 
-template <typename T>
+template <typename T, bool PK>
 hipError_t launch_asym_t(const void* X, int n, int d, int dl, void* xl, float* sl, float* zl, void* xh, float* sh,
                          float* zh, hipStream_t st) {
   const dim3 grid((unsigned)((n + 3) / 4)), block(256);
@@ -145,7 +150,7 @@ hipError_t launch_asym_t(const void* X, int n, int d, int dl, void* xl, float* s
   while (ch * 512 < d) ch <<= 1;
 #define TQ_ASYM(C)                                                                                            \
   case C:                                                                                                     \
-    launch_kernel(k_quant_rows_asym<T, C>, grid, block, 0, st, x, n, d, dl, (uint8_t*)xl, sl, zl, (uint8_t*)xh, \
+    launch_kernel(k_quant_rows_asym<T, C, PK>, grid, block, 0, st, x, n, d, dl, (uint8_t*)xl, sl, zl, (uint8_t*)xh, \
                   sh, zh);                                                                                    \
     break;
   switch (ch) {
@@ -165,10 +170,13 @@ hipError_t launch_asym_t(const void* X, int n, int d, int dl, void* xl, float* s
 }  // namespace
 
 hipError_t launch_quant_rows_asym(const void* X, bool bf16, int n, int d, int dl, void* xl, float* sl, float* zl,
-                                  void* xh, float* sh, float* zh, hipStream_t st) {
+                                  void* xh, float* sh, float* zh, hipStream_t st, bool packed) {
   if (n <= 0 || d <= 0 || d > kAsymMaxD || dl < 0 || dl > d || dl % 32 || (d - dl) % 16) return hipErrorInvalidValue;
-  return bf16 ? launch_asym_t<bf16_t>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st)
-              : launch_asym_t<float>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st);
+  if (packed)
+    return bf16 ? launch_asym_t<bf16_t, true>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st)
+                : launch_asym_t<float, true>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st);
+  return bf16 ? launch_asym_t<bf16_t, false>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st)
+              : launch_asym_t<float, false>(X, n, d, dl, xl, sl, zl, xh, sh, zh, st);
 }
 
 hipError_t launch_weight_colsum(const void* codes, int bits, int m, int k, int32_t* colsum, hipStream_t st) {

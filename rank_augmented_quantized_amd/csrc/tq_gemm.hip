@@ -137,10 +137,21 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 
   // ---- issue every load of the first batch before any wait ----
   float sxv[4], swv = 0.0f;  // epilogue scales
+  // asymmetric activations (codes u - 8): per row z + 8 s_x, per channel
+  // s_w colsum(C_w) (CoQuant Eq. 1 with a zero-point)
+  float zzv[4] = {0.f, 0.f, 0.f, 0.f}, wzv = 0.0f;
   if (LR || QL) {
     swv = g.sw[min(n0 + l16, g.N - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
+    if (LR && g.zx) {
+      wzv = swv * (float)g.csw[min(n0 + l16, g.N - 1)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = min(16 * (wave & 1) + 4 * lg + i, g.M - 1);
+        zzv[i] = g.zx[rr] + 8.0f * g.sx[rr];
+      }
+    }
   }
   // QL: the first 64 ranks of the second stage's operands and its scales
   // (lane: token or channel l % 16, the 16 ranks 16 (l / 16) ..; ranks past
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * tile + 4 * lg + i;
       if (row >= g.M || col >= g.N) continue;
-      const float y = (float)sacc[i] * (sxv[i] * swv) + lr[i];
+      const float y = (float)sacc[i] * (sxv[i] * swv) + lr[i] + zzv[i] * wzv;
       if (g.y_bf16)
         reinterpret_cast<bf16_t*>(g.Y)[(size_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_bits(y);
       else

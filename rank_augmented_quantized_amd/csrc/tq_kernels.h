@@ -145,9 +145,10 @@ ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks);
 int gemv_max_chunks(int M, int Kb, int r_pad);
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,
                            void* xc, float* sx, float* P, void* Tout, unsigned* counters, hipStream_t st);
-// The prologue of the asymmetric layer: per-token asymmetric codes (u - 8,
-// int8 for the tile GEMM), scales and zero-points (zx), and T as above; p from
-// plan_prologue(n, d, r_pad, false, 1).
+// The prologue of the asymmetric layer: per-token asymmetric codes (u - 8;
+// int8 for the tile GEMM, nibble-packed for the small-n GEMM when p is a
+// small plan), scales and zero-points (zx), and T (or its k-chunk partials)
+// as above.
 hipError_t launch_prologue_asym(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad,
                                 const ProloguePlan& p, void* xc, float* sx, float* zx, float* P, void* Tout,
                                 unsigned* counters, hipStream_t st);
@@ -231,7 +232,7 @@ hipError_t launch_qlr_prologue(const void* X, bool bf16, int n, int d, const uin
 // the scale and the zero-point.  d <= kAsymMaxD.
 constexpr int kAsymMaxD = 16384;
 hipError_t launch_quant_rows_asym(const void* X, bool bf16, int n, int d, int dl, void* xl, float* sl, float* zl,
-                                  void* xh, float* sh, float* zh, hipStream_t st);
+                                  void* xh, float* sh, float* zh, hipStream_t st, bool packed = false);
 // colsum[j] = sum over k of code row j (m rows of k codes, 4 or 8 bits).
 hipError_t launch_weight_colsum(const void* codes, int bits, int m, int k, int32_t* colsum, hipStream_t st);
 bool small_fused_ok(int n, int d, int r_pad);

@@ -970,7 +970,7 @@ hipError_t launch_prologue_asym(const void* X, bool bf16, int n, int d, const vo
                                 unsigned* counters, hipStream_t st) {
   if (p.fused) return launch_prologue_fused(X, bf16, n, d, L1t, r_pad, xc, sx, Tout, st, zx);
   // the asymmetric quantiser (int8 codes for the tile GEMM), then the T blocks alone
-  hipError_t e = launch_quant_rows_asym(X, bf16, n, d, d, xc, sx, zx, nullptr, nullptr, nullptr, st);
+  hipError_t e = launch_quant_rows_asym(X, bf16, n, d, d, xc, sx, zx, nullptr, nullptr, nullptr, st, p.row_blocks);
   if (e != hipSuccess || p.ntb == 0) return e;
   PrologueArgs a{X, n, d, (const bf16_t*)L1t, r_pad, p.kc, p.nchunk, p.qs, p.nqg, 0, p.partial ? 1 : 0,
                  p.row_blocks ? 1 : 0, p.sum_to_p0 ? 1 : 0, (uint8_t*)xc, sx, P, (bf16_t*)Tout, counters};

@@ -72,7 +72,10 @@ def _check(x, r_w, l1, l2, y, ws, cs, rows=None, cols=None):
     r = slice(None) if rows is None else rows
     assert np.array_equal(b[off["s_x"]: off["s_x"] + 4 * n].view(np.float32)[r], ref["s_x"])
     assert np.array_equal(b[off["z_x"]: off["z_x"] + 4 * n].view(np.float32)[r], ref["z_x"])
-    codes = _int8_codes(b[off["x_codes"]: off["x_codes"] + n * d].reshape(n, d)) + 8
+    if n <= 32:  # few tokens: nibble-packed codes for the small-n GEMM
+        codes = tqo.unpack_int4(b[off["x_codes"]: off["x_codes"] + n * d // 2].reshape(n, d // 2)) + 8
+    else:
+        codes = _int8_codes(b[off["x_codes"]: off["x_codes"] + n * d].reshape(n, d)) + 8
     assert np.array_equal(codes[r], ref["codes_x"])
     if cols is None:
         assert np.array_equal(cs.cpu().numpy(), ref["colsum"])
@@ -100,6 +103,9 @@ CASES = [
     ("n1100_r0_fused_f32", 1100, 512, 256, 0, "normal", "f32", 0),
     ("n33_r64_d14336_streamed", 33, 14336, 256, 64, "student_t", "bf16", 0),
     ("n64_r32_d8192", 64, 8192, 128, 32, "normal", "f32", 2),
+    ("n2_r64_small_n", 2, 4096, 1024, 64, "normal", "bf16", 2),
+    ("n32_r32_small_n", 32, 2048, 520, 32, "normal", "bf16", 0),
+    ("n16_r0_small_n_f32", 16, 1024, 256, 0, "normal", "f32", 2),
 ]
 
 

@@ -263,3 +263,35 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(tqb, "_lib", None)
     with pytest.raises(ImportError, match="missing"):
         tqb.load(str(tmp_path / "nope.so"))
+
+
+@pytest.mark.parametrize("n,d,m,r", [(1, 512, 256, 32), (17, 4096, 1024, 64), (33, 14336, 4096, 100),
+                                     (1030, 2048, 512, 0), (4096, 4096, 4096, 256)])
+def test_workspace_regions_fit_and_do_not_overlap(lib, n, d, m, r):
+    """Every region the offset queries report lies inside the reported workspace size, 256-byte aligned, and the
+    regions do not overlap (sizes from the layouts documented in include/tq.h)."""
+    rp = 0 if r == 0 else max(32, 1 << (r - 1).bit_length())
+    small = n <= 32
+
+    def check(total, regions):
+        regions = sorted(regions)
+        for (o, sz), (o2, _) in zip(regions, regions[1:]):
+            assert o % 256 == 0 and o + sz <= o2, (regions,)
+        assert regions[-1][0] + regions[-1][1] <= total
+
+    off = tqb.tq_linear_workspace_offsets(n, d, m, r)
+    check(lib.tq_linear_workspace_bytes(n, d, m, r),
+          [(off["s_x"], 4 * n), (off["x_codes"], n * (d // 2 if small else d)), (off["T"], n * rp * 2)])
+    if r:
+        off = tqb.tq_linear_qlr_workspace_offsets(n, d, r)
+        check(lib.tq_linear_qlr_workspace_bytes(n, d, r),
+              [(off["s_x"], 4 * n), (off["x_codes"], n * d), (off["s_t"], 4 * n), (off["t_codes"], n * rp)])
+    off = tqb.tq_linear_asym_workspace_offsets(n, d, m, r)
+    check(lib.tq_linear_asym_workspace_bytes(n, d, m, r),
+          [(off["s_x"], 4 * n), (off["x_codes"], n * (d // 2 if small else d)), (off["z_x"], 4 * n),
+           (off["T"], n * rp * 2)])
+    dh = 128 if d >= 256 else 0
+    off = tqb.tq_linear_mp_asym_workspace_offsets(n, d, dh)
+    check(lib.tq_linear_mp_asym_workspace_bytes(n, d, dh),
+          [(off["s_xl"], 4 * n), (off["s_xh"], 4 * n), (off["x_codes_l"], n * (d - dh)), (off["x_codes_h"], n * dh),
+           (off["z_xl"], 4 * n), (off["z_xh"], 4 * n)])

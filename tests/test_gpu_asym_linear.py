@@ -106,6 +106,8 @@ CASES = [
     ("n2_r64_small_n", 2, 4096, 1024, 64, "normal", "bf16", 2),
     ("n32_r32_small_n", 32, 2048, 520, 32, "normal", "bf16", 0),
     ("n16_r0_small_n_f32", 16, 1024, 256, 0, "normal", "f32", 2),
+    ("n3_r32_d16384_max_small_n", 3, 16384, 256, 32, "student_t", "bf16", 0),
+    ("n40_r16_d16384_max", 40, 16384, 128, 16, "normal", "f32", 2),
 ]
 
 

@@ -232,7 +232,7 @@ size_t tq_linear_mp_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
  * CoQuant Eq. 9 with 8-bit high-precision and 4-bit low-precision subspaces
  * (CoQuant experimental protocol).
  */
-tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
                        const void* wl_codes, const float* s_wl, const void* wh_codes,
                        const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
                        hipStream_t stream);
@@ -244,7 +244,7 @@ tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, in
  * tq_pack_weight at those widths.  Codes keep the 4- and 8-bit storage, so the
  * same kernels run.  TQ_ERR_BITS for other pairs; otherwise as tq_linear_mp.
  */
-tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
                             int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl,
                             const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
                             size_t ws_bytes, hipStream_t stream);
@@ -287,10 +287,10 @@ tq_status tq_pack_rht(const float* signs, const int32_t* perm, int64_t d, void* 
  * those of tq_linear_mp for the rotated weight U^T W.  Workspace and errors as
  * tq_linear_mp, plus TQ_ERR_SHAPE for d outside the rotation's range.
  */
-tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi,
-                           const void* rot, int64_t m, const void* wl_codes, const float* s_wl,
-                           const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
-                           size_t ws_bytes, hipStream_t stream);
+tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                           const void* rot, const void* wl_codes, const float* s_wl, const void* wh_codes,
+                           const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /*
  * Per-token asymmetric activations for the two-subspace layer (CoQuant notes,
@@ -318,7 +318,7 @@ tq_status tq_weight_colsum(const void* w_codes, int64_t m, int64_t k, int bits, 
  * tq_linear_mp, plus TQ_ERR_SHAPE for d > 16384.
  */
 size_t tq_linear_mp_asym_workspace_bytes(int64_t n, int64_t d, int64_t d_hi);
-tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
                             const void* wl_codes, const float* s_wl, const int32_t* colsum_l,
                             const void* wh_codes, const float* s_wh, const int32_t* colsum_h, void* Y,
                             tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -418,13 +418,46 @@ tq_status tq_linear_qlr_workspace_offsets(int64_t n, int64_t d, int64_t r, size_
  * tq_debug_accumulate -- exact integer product of two code matrices, exported.
  *   x_codes  n x k codes, w_codes m x k codes (both bits wide, K-contiguous).
  *   acc      out: n x m int32, acc[i][j] = sum_t x[i][t] * w[j][t], exactly.
- * Runs the same integer main loops as tq_linear / tq_linear_mp (the prefill
- * loop for n > 32, the small-n loop otherwise) so the accumulators of the
- * product path can be checked bit for bit.  k must be a multiple of 32
- * (bits = 4) or 16 (bits = 8).
+ * The integer GEMM on caller codes (the tile GEMM's main loop for n > 32 on
+ * nibble-packed or int8 codes, the small-n loop otherwise).  The layers'
+ * own kernels export their sums through the *_debug entry points below.
+ * k must be a multiple of 32 (bits = 4) or 16 (bits = 8).
  */
 tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k,
                               int64_t m, int bits, int32_t* acc, hipStream_t stream);
+
+/*
+ * Accumulator export (test hooks).  Each runs the layer exactly as the entry
+ * point it is named after -- same checks, workspace, launches, kernel
+ * templates and Y -- through the kernels' export instance, which also stores
+ * the exact int32 sums of its integer products before they are dequantised:
+ *   acc    n x m int32, acc[i][j] = sum_k C_x[i][k] C_w[j][k] (the residual,
+ *          or the 4-bit subspace; asymmetric layers: the stored codes u - 8);
+ *   acc_h  n x m int32, the 8-bit subspace's sums (u - 128 when asymmetric);
+ *          may be NULL when d_hi == 0;
+ *   acc2   n x m int32, the quantised branch's second stage sum_t C_t C_v.
+ * Caller-owned device buffers, 16-byte aligned; TQ_ERR_NULL / TQ_ERR_ALIGN
+ * otherwise.  Slower than the plain entry points (extra stores); meant for
+ * checking the accumulators bit for bit, not for production use.
+ */
+tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                          const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
+                          size_t ws_bytes, int32_t* acc, hipStream_t stream);
+tq_status tq_linear_mp_bits_debug(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                                  int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl,
+                                  const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
+                                  size_t ws_bytes, int32_t* acc_l, int32_t* acc_h, hipStream_t stream);
+tq_status tq_linear_asym_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                               const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank,
+                               void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, int32_t* acc, hipStream_t stream);
+tq_status tq_linear_mp_asym_debug(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                                  const void* wl_codes, const float* s_wl, const int32_t* colsum_l,
+                                  const void* wh_codes, const float* s_wh, const int32_t* colsum_h, void* Y,
+                                  tq_dtype y_dt, void* ws, size_t ws_bytes, int32_t* acc_l, int32_t* acc_h,
+                                  hipStream_t stream);
+tq_status tq_linear_qlr_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                              const void* w_codes, const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt,
+                              void* ws, size_t ws_bytes, int32_t* acc, int32_t* acc2, hipStream_t stream);
 
 /*
  * Kernel timing.  While enabled, every kernel the library launches is

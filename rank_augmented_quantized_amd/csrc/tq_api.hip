@@ -78,7 +78,11 @@ namespace {
 template <typename F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   Profiler& p = prof();
-  if (!p.on) return launch();
+  std::unique_lock<std::mutex> lk(p.mu);
+  if (!p.on) {
+    lk.unlock();
+    return launch();
+  }
   hipEvent_t e0 = p.get(), e1 = p.get(), x0 = p.get(), x1 = p.get();
   tq::LaunchEvents& ev = tq::launch_events();
   ev = tq::LaunchEvents{x0, x1, false};
@@ -314,9 +318,11 @@ namespace {
 
 // The layer (or G layers stacked along the channels, sharing X) once the
 // arguments are checked: ms[g] channels per layer, m = their sum.
+// acc: when not null, the kernels' exact int32 residual sums (n x m) are
+// also stored there (test hook).
 tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, int G,
                      const int64_t* ms, const void* w_codes, const float* s_w, const void* lowrank, void* Y,
-                     tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+                     tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream, int32_t* acc = nullptr) {
   const int rp = (int)r_padded(r);
   const LinearWs L = linear_ws(n, d, m, group_tcols(G, r));
   if (ws_bytes < L.total) return TQ_ERR_WORKSPACE;
@@ -359,6 +365,7 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
     a.sync = (unsigned*)(base + L.sync);
     a.Y = Y;
     a.y_bf16 = y_dt == TQ_BF16;
+    a.acc = acc;
     TQ_RUN("linear_small", stream, tq::launch_linear_small(a, xb, stream));
     return TQ_OK;
   }
@@ -386,6 +393,7 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
+  g.acc = acc;
 
   TQ_RUN("prologue", stream,
          tq::launch_prologue(X, xb, (int)n, (int)d, L1t, L.r_pad, L.plan, xc, sx, P, T, ctr, stream));
@@ -438,6 +446,17 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   if (st != TQ_OK || n == 0) return st;
   const int64_t ms[1] = {m};
   return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream);
+}
+
+tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                          const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
+                          size_t ws_bytes, int32_t* acc, hipStream_t stream) {
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  if (!acc) return TQ_ERR_NULL;
+  if (!aligned16(acc)) return TQ_ERR_ALIGN;
+  const int64_t ms[1] = {m};
+  return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream, acc);
 }
 
 size_t tq_lowrank_group_bytes(int64_t d, const int64_t* m, int64_t G, int64_t r) {
@@ -524,13 +543,22 @@ tq_status mp_check(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d
   return TQ_OK;
 }
 
+// Accumulator-export buffers of the test-hook entry points: the residual (or
+// 4-bit) product always, the second product when it is not empty.
+tq_status debug_check(const int32_t* acc, const int32_t* acc2, bool need2) {
+  if (!acc || (need2 && !acc2)) return TQ_ERR_NULL;
+  if (!aligned16(acc) || (need2 && !aligned16(acc2))) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
 // The two-subspace GEMM on the codes and scales in the workspace (with the
 // zero-points and weight code sums of asymmetric activations when zl / zh
 // are not null).
 tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_codes, const float* s_wl,
                   const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, const MpWs& W, uint8_t* base,
                   hipStream_t stream, const float* zl = nullptr, const float* zh = nullptr,
-                  const int32_t* csl = nullptr, const int32_t* csh = nullptr) {
+                  const int32_t* csl = nullptr, const int32_t* csh = nullptr, int32_t* acc_l = nullptr,
+                  int32_t* acc_h = nullptr) {
   const int64_t dl = d - d_hi;
   float* sxl = (float*)(base + W.sxl);
   float* sxh = (float*)(base + W.sxh);
@@ -561,21 +589,16 @@ tq_status mp_gemm(int64_t n, int64_t d, int64_t d_hi, int64_t m, const void* wl_
   g.csw = csl;
   g.zx2 = d_hi > 0 ? zh : nullptr;
   g.csw2 = csh;
+  g.acc = acc_l;
+  g.acc2 = acc_h;
   TQ_RUN("gemm_mp", stream, tq::launch_gemm8(g, tq::EPI_MP, true, 4, stream));
   return TQ_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
-                            int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl, const void* wh_codes,
-                            const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
-  if (!((bits_lo == 4 && bits_hi == 8) || (bits_lo == 3 && bits_hi == 6))) return TQ_ERR_BITS;
-  const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
-  if (st != TQ_OK || n == 0) return st;
+tq_status mp_bits_run(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi, int bits_lo,
+                      int bits_hi, const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh,
+                      void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream, int32_t* acc_l,
+                      int32_t* acc_h) {
   const int64_t dl = d - d_hi;
   const MpWs W = mp_ws(n, d, d_hi);
   if (ws_bytes < W.total) return TQ_ERR_WORKSPACE;
@@ -598,13 +621,42 @@ tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t 
            tq::launch_quant_rows_fast(Xrot, xb, (int)n, (int)d, (int)d, bits_hi, bits_hi, xh, sxh, nullptr, nullptr,
                                       stream));
   }
-  return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream);
+  return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W, base, stream, nullptr, nullptr, nullptr,
+                 nullptr, acc_l, acc_h);
 }
 
-tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_mp_bits(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                            int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl, const void* wh_codes,
+                            const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!((bits_lo == 4 && bits_hi == 8) || (bits_lo == 3 && bits_hi == 6))) return TQ_ERR_BITS;
+  const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  return mp_bits_run(Xrot, x_dt, n, d, m, d_hi, bits_lo, bits_hi, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws,
+                     ws_bytes, stream, nullptr, nullptr);
+}
+
+tq_status tq_linear_mp_bits_debug(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                                  int bits_lo, int bits_hi, const void* wl_codes, const float* s_wl,
+                                  const void* wh_codes, const float* s_wh, void* Y, tq_dtype y_dt, void* ws,
+                                  size_t ws_bytes, int32_t* acc_l, int32_t* acc_h, hipStream_t stream) {
+  if (!((bits_lo == 4 && bits_hi == 8) || (bits_lo == 3 && bits_hi == 6))) return TQ_ERR_BITS;
+  const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  const tq_status sd = debug_check(acc_l, acc_h, d_hi > 0);
+  if (sd != TQ_OK) return sd;
+  return mp_bits_run(Xrot, x_dt, n, d, m, d_hi, bits_lo, bits_hi, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws,
+                     ws_bytes, stream, acc_l, acc_h);
+}
+
+tq_status tq_linear_mp(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
                        const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh, void* Y,
                        tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return tq_linear_mp_bits(Xrot, x_dt, n, d, d_hi, m, 4, 8, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws, ws_bytes,
+  return tq_linear_mp_bits(Xrot, x_dt, n, d, m, d_hi, 4, 8, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws, ws_bytes,
                            stream);
 }
 
@@ -646,10 +698,14 @@ tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi
   return TQ_OK;
 }
 
-tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, int64_t m,
-                            const void* wl_codes, const float* s_wl, const int32_t* colsum_l, const void* wh_codes,
-                            const float* s_wh, const int32_t* colsum_h, void* Y, tq_dtype y_dt, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+tq_status mp_asym_run(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                      const void* wl_codes, const float* s_wl, const int32_t* colsum_l, const void* wh_codes,
+                      const float* s_wh, const int32_t* colsum_h, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                      hipStream_t stream, int32_t* acc_l, int32_t* acc_h) {
   const tq_status st = mp_check(Xrot, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
   if (st != TQ_OK) return st;
   if (d > tq::kAsymMaxD) return TQ_ERR_SHAPE;
@@ -667,7 +723,32 @@ tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t 
                                     (float*)(base + W.mp.sxl), zl, base + W.mp.xh, (float*)(base + W.mp.sxh), zh,
                                     stream));
   return mp_gemm(n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, W.mp, base, stream, zl, zh, colsum_l,
-                 colsum_h);
+                 colsum_h, acc_l, acc_h);
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_mp_asym(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                            const void* wl_codes, const float* s_wl, const int32_t* colsum_l, const void* wh_codes,
+                            const float* s_wh, const int32_t* colsum_h, void* Y, tq_dtype y_dt, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  return mp_asym_run(Xrot, x_dt, n, d, m, d_hi, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, Y, y_dt, ws,
+                     ws_bytes, stream, nullptr, nullptr);
+}
+
+tq_status tq_linear_mp_asym_debug(const void* Xrot, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                                  const void* wl_codes, const float* s_wl, const int32_t* colsum_l,
+                                  const void* wh_codes, const float* s_wh, const int32_t* colsum_h, void* Y,
+                                  tq_dtype y_dt, void* ws, size_t ws_bytes, int32_t* acc_l, int32_t* acc_h,
+                                  hipStream_t stream) {
+  if (n > 0) {
+    const tq_status sd = debug_check(acc_l, acc_h, d_hi > 0);
+    if (sd != TQ_OK) return sd;
+  }
+  return mp_asym_run(Xrot, x_dt, n, d, m, d_hi, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, Y, y_dt, ws,
+                     ws_bytes, stream, acc_l, acc_h);
 }
 
 size_t tq_rht_bytes(int64_t d) {
@@ -683,9 +764,9 @@ tq_status tq_pack_rht(const float* signs, const int32_t* perm, int64_t d, void* 
   return TQ_OK;
 }
 
-tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t d_hi, const void* rot,
-                           int64_t m, const void* wl_codes, const float* s_wl, const void* wh_codes, const float* s_wh,
-                           void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+tq_status tq_linear_mp_rht(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t d_hi,
+                           const void* rot, const void* wl_codes, const float* s_wl, const void* wh_codes,
+                           const float* s_wh, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
   const tq_status st = mp_check(X, x_dt, n, d, d_hi, m, wl_codes, s_wl, wh_codes, s_wh, Y, y_dt, ws);
   if (st != TQ_OK) return st;
   if (d % 128 || d > tq::kRhtMaxD) return TQ_ERR_SHAPE;
@@ -722,9 +803,13 @@ tq_status tq_linear_asym_workspace_offsets(int64_t n, int64_t d, int64_t m, int6
   return TQ_OK;
 }
 
-tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
-                         const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank, void* Y,
-                         tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+tq_status asym_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                   const float* s_w, const int32_t* colsum, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
+                   size_t ws_bytes, hipStream_t stream, int32_t* acc) {
   const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
   if (st != TQ_OK || n == 0) return st;
   if (d > tq::kAsymMaxD) return TQ_ERR_SHAPE;
@@ -764,6 +849,7 @@ tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
+  g.acc = acc;
   if (L.small) {
     if (rp && (L.plan.partial || L.plan.sum_to_p0)) {
       g.P = P;
@@ -775,6 +861,26 @@ tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int
     TQ_RUN("gemm_asym", stream, tq::launch_gemm8(g, tq::EPI_LINEAR, true, 4, stream));
   }
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_asym(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                         const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank, void* Y,
+                         tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return asym_run(X, x_dt, n, d, m, r, w_codes, s_w, colsum, lowrank, Y, y_dt, ws, ws_bytes, stream, nullptr);
+}
+
+tq_status tq_linear_asym_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                               const void* w_codes, const float* s_w, const int32_t* colsum, const void* lowrank,
+                               void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, int32_t* acc, hipStream_t stream) {
+  if (n > 0) {
+    const tq_status sd = debug_check(acc, nullptr, false);
+    if (sd != TQ_OK) return sd;
+  }
+  return asym_run(X, x_dt, n, d, m, r, w_codes, s_w, colsum, lowrank, Y, y_dt, ws, ws_bytes, stream, acc);
 }
 
 size_t tq_lowrank_q_bytes(int64_t d, int64_t m, int64_t r) {
@@ -818,9 +924,13 @@ tq_status tq_linear_qlr_workspace_offsets(int64_t n, int64_t d, int64_t r, size_
   return TQ_OK;
 }
 
-tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
-                        const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+tq_status qlr_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                  const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                  hipStream_t stream, int32_t* acc, int32_t* acc2) {
   if (r < 1) return TQ_ERR_SHAPE;
   const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank_q, Y, y_dt, ws);
   if (st != TQ_OK || n == 0) return st;
@@ -871,11 +981,33 @@ tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int6
   g.Y = Y;
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
+  g.acc = acc;
+  g.acc2 = acc2;
   if (small)
     TQ_RUN("gemm_small_n_qlr", stream, tq::launch_gemv(g, 4, tq::EPI_QLR, stream));
   else
     TQ_RUN("gemm_qlr", stream, tq::launch_gemm8(g, tq::EPI_QLR, true, 4, stream));
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_qlr(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, const void* w_codes,
+                        const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return qlr_run(X, x_dt, n, d, m, r, w_codes, s_w, lowrank_q, Y, y_dt, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+tq_status tq_linear_qlr_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                              const void* w_codes, const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt,
+                              void* ws, size_t ws_bytes, int32_t* acc, int32_t* acc2, hipStream_t stream) {
+  if (n > 0) {
+    const tq_status sd = debug_check(acc, acc2, true);
+    if (sd != TQ_OK) return sd;
+  }
+  return qlr_run(X, x_dt, n, d, m, r, w_codes, s_w, lowrank_q, Y, y_dt, ws, ws_bytes, stream, acc, acc2);
 }
 
 tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m, int bits,

@@ -41,7 +41,10 @@ namespace tq {
 // within the 160 KB of LDS next to the static arrays.
 __host__ __device__ constexpr int gemv_xl_bytes(int waves) { return waves == 8 ? 24576 : 12288; }
 
-template <int BITS, int EPI, int WAVES, bool TWO, bool XL>
+// DBG: the test-hook instance, which also stores the exact int32 sums of the
+// residual product (g.acc) and, for the quantised low-rank branch, of its
+// second stage (g.acc2); its code is this template's, with those stores added.
+template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g) {
   constexpr int U = (WAVES == 4 && TWO && !XL) ? 4 : ((WAVES == 4 || TWO) ? 8 : 16);  // 64-byte steps per wave per batch
   constexpr int NT = WAVES * 64;
@@ -280,6 +283,13 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     sacc[i] = (BITS == 4) ? (v >> 8) : v;
   }
   const int col = n0 + l16;
+  if constexpr (DBG && EPI != EPI_ACC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * tile + 4 * lg + i;
+      if (row < g.M && col < g.N) g.acc[(size_t)row * g.N + col] = sacc[i];
+    }
+  }
   if constexpr (EPI == EPI_ACC) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -302,6 +312,13 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) lr[i] = (float)q2[i] * (sxv[i] * qs[i] * qsv);
+      if constexpr (DBG) {  // C_t C_v^T exactly (the expanded V carries 16 x code)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * tile + 4 * lg + i;
+          if (row < g.M && col < g.N) g.acc2[(size_t)row * g.N + col] = q2[i] >> 4;
+        }
+      }
     }
     for (int t0 = 0; t0 < rp; t0 += 32) {
       // A: T rows (tokens), B: L2^T rows (channels); 8 consecutive t per lane
@@ -331,21 +348,21 @@ int gemv_max_chunks(int M, int Kb, int r_pad) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int BITS, int EPI, bool TWO>
+template <int BITS, int EPI, bool TWO, bool DBG>
 static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
   const unsigned blocks = (unsigned)((g.N + 15) / 16);
   const size_t xl = (size_t)g.M * (size_t)(g.Kb + 16);  // activation codes in LDS
   const bool use_xl = xl <= (size_t)gemv_xl_bytes(g.Kb > 2048 ? 8 : 4) && g.Kb % 16 == 0;
   if (g.Kb > 2048) {
     if (use_xl)
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, true>), dim3(blocks), dim3(512), xl, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, true, DBG>), dim3(blocks), dim3(512), xl, st, g);
     else
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, false>), dim3(blocks), dim3(512), 0, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, false, DBG>), dim3(blocks), dim3(512), 0, st, g);
   } else {
     if (use_xl)
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, true>), dim3(blocks), dim3(256), xl, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, true, DBG>), dim3(blocks), dim3(256), xl, st, g);
     else
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, false>), dim3(blocks), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, false, DBG>), dim3(blocks), dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }
@@ -353,7 +370,10 @@ static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
 template <int BITS, int EPI>
 static hipError_t gemv_cols(const GemmArgs& g, hipStream_t st) {
   if (EPI == EPI_LINEAR && (g.r_pad > 256 || (g.r_pad > 0 && (!g.P || g.nchunk < 1)))) return hipErrorInvalidValue;
-  return g.M > 16 ? gemv_cols_t<BITS, EPI, true>(g, st) : gemv_cols_t<BITS, EPI, false>(g, st);
+  // the accumulator-export instance (test hook) when an export buffer is set
+  if (EPI != EPI_ACC && g.acc)
+    return g.M > 16 ? gemv_cols_t<BITS, EPI, true, true>(g, st) : gemv_cols_t<BITS, EPI, false, true>(g, st);
+  return g.M > 16 ? gemv_cols_t<BITS, EPI, true, false>(g, st) : gemv_cols_t<BITS, EPI, false, false>(g, st);
 }
 
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st) {

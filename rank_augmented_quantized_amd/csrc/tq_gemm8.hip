@@ -88,7 +88,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // KF: every row's code bytes are a whole number of stages, so no direct load
 // needs the per-lane end-of-row test (which costs VALU slots next to the MFMAs)
-template <int EPI, bool XP, int BN, bool W8 = false, bool KF = false>
+// DBG: the test-hook instance, which also stores the exact int32 sums of the
+// residual product (g.acc) and of the second integer product (g.acc2); its
+// code is this template's, with those stores added.
+template <int EPI, bool XP, int BN, bool W8 = false, bool KF = false, bool DBG = false>
 __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   static_assert(!W8 || (EPI == EPI_ACC && !XP), "8-bit weights: the integer check only");
   constexpr int BM = 256;                        // channels per tile
@@ -294,29 +297,36 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   constexpr int SH = W8 ? 0 : (XP ? 8 : 4);
   auto chan = [&](int a, int e4) { return ch0 + wm * WM + 32 * a + 8 * e4 + 4 * lg; };
   auto tok = [&](int b) { return tk0 + wn * WN + 32 * b + l32; };
-  if constexpr (EPI == EPI_ACC) {
+  // the 4 int32 sums v of block (a, b), group e4, to dst (M x N), shifted
+  // right by sh (exact: the sums are multiples of 2^sh); add: on top of what
+  // the same lane stored there before (8-bit chunks)
+  auto store_i32 = [&](int32_t* dst, int a, int b, int e4, i32x4 v, int sh, bool add) {
+    const int t = tok(b), c = chan(a, e4);
+    if (t >= g.M) return;
+    int32_t* op = dst + (size_t)t * g.N + c;
+    v = v >> sh;
+    if (c + 3 < g.N && (g.N & 3) == 0) {
+      if (add) v += *reinterpret_cast<const i32x4*>(op);
+      *reinterpret_cast<i32x4*>(op) = v;
+    } else {
+      for (int q = 0; q < 4; ++q)
+        if (c + q < g.N) op[q] = add ? op[q] + v[q] : v[q];
+    }
+  };
+  auto quad = [](const i32x16& x, int e4) { return i32x4{x[4 * e4], x[4 * e4 + 1], x[4 * e4 + 2], x[4 * e4 + 3]}; };
+  // the main loop's exact sums (EPI_ACC, or the test hook of the other epilogues)
+  auto export_acc = [&]() {
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        const int t = tok(b);
-        if (t >= g.M) continue;
+      for (int b = 0; b < FN; ++b)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int c = chan(a, e4);
-          int32_t* op = g.acc + (size_t)t * g.N + c;
-          const int v0 = acc[a][b][4 * e4] >> SH, v1 = acc[a][b][4 * e4 + 1] >> SH;
-          const int v2 = acc[a][b][4 * e4 + 2] >> SH, v3 = acc[a][b][4 * e4 + 3] >> SH;
-          if (c + 3 < g.N && (g.N & 3) == 0) {
-            *reinterpret_cast<int4*>(op) = int4{v0, v1, v2, v3};
-          } else {
-            const int v[4] = {v0, v1, v2, v3};
-            for (int q = 0; q < 4; ++q)
-              if (c + q < g.N) op[q] = v[q];
-          }
-        }
-      }
+        for (int e4 = 0; e4 < 4; ++e4) store_i32(g.acc, a, b, e4, quad(acc[a][b], e4), SH, false);
+  };
+  if constexpr (EPI == EPI_ACC) {
+    export_acc();
   } else {
+    if constexpr (DBG) export_acc();
     auto load4 = [&](const float* p, int c) -> float4 {  // p[c..c+3], clamped at the channel tail
       if (c + 3 < g.N) return *reinterpret_cast<const float4*>(p + c);
       return float4{p[min(c, g.N - 1)], p[min(c + 1, g.N - 1)], p[min(c + 2, g.N - 1)], p[min(c + 3, g.N - 1)]};
@@ -499,6 +509,10 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
         const i32x4 tb = *reinterpret_cast<const i32x4*>(tq8[b] + 32 * q);
         acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(va.x, va.y), tb, acc2, 0, 0, 0);
       }
+      if (DBG) {  // test hook: C_t C_v^T exactly (the expanded V carries 16 x code)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) store_i32(g.acc2, a, b, e4, quad(acc2, e4), 4, false);
+      }
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         y[a][b][4 * e4 + 0] += (float)acc2[4 * e4 + 0] * (svv[e4].x * stv[b]);
@@ -573,6 +587,10 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
                   const i32x4 bv = *reinterpret_cast<const i32x4*>(smem + BM * 128 + (fb[st] - WPL) + 4096 * b);
                   acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc2, 0, 0, 0);
                 }
+              }
+              if (DBG) {  // test hook: the 8-bit segment's exact sums, chunks added in int32
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) store_i32(g.acc2, a, b, e4, quad(acc2, e4), 0, k0 > 0);
               }
 #pragma unroll
               for (int e4 = 0; e4 < 4; ++e4) {
@@ -689,20 +707,20 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   }
 }
 
-template <int EPI, bool XP, bool W8, bool KF>
+template <int EPI, bool XP, bool W8, bool KF, bool DBG>
 hipError_t launch_kf(const GemmArgs& g, hipStream_t st) {
   const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
   // the two-subspace epilogue keeps a 64 x 64 fp32 tile per wave (256 x 128
   // tiles): with 64 x 128 it would not fit the registers beside the 8-bit product
   if constexpr (EPI != EPI_MP) {
     if (big >= 224) {
-      launch_kernel(k_gemm8<EPI, XP, 256, W8, KF>, dim3((unsigned)big), dim3(512), 0, st, g);
+      launch_kernel(k_gemm8<EPI, XP, 256, W8, KF, DBG>, dim3((unsigned)big), dim3(512), 0, st, g);
       return hipGetLastError();
     }
   }
   {
     const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
-    launch_kernel(k_gemm8<EPI, XP, 128, W8, KF>, dim3(blocks), dim3(512), 0, st, g);
+    launch_kernel(k_gemm8<EPI, XP, 128, W8, KF, DBG>, dim3(blocks), dim3(512), 0, st, g);
   }
   return hipGetLastError();
 }
@@ -711,7 +729,11 @@ template <int EPI, bool XP, bool W8 = false>
 hipError_t launch_t(const GemmArgs& g, hipStream_t st) {
   // whole stages: WROW weight bytes per row per stage, and then also whole
   // activation stages (XROW = 2 WROW for int8 activations, WROW otherwise)
-  return g.Kb % (W8 ? 128 : 64) == 0 ? launch_kf<EPI, XP, W8, true>(g, st) : launch_kf<EPI, XP, W8, false>(g, st);
+  const bool kf = g.Kb % (W8 ? 128 : 64) == 0;
+  // the accumulator-export instance (test hook) when an export buffer is set
+  if (EPI != EPI_ACC && g.acc)
+    return kf ? launch_kf<EPI, XP, W8, true, true>(g, st) : launch_kf<EPI, XP, W8, false, true>(g, st);
+  return kf ? launch_kf<EPI, XP, W8, true, false>(g, st) : launch_kf<EPI, XP, W8, false, false>(g, st);
 }
 
 }  // namespace

@@ -103,7 +103,15 @@ struct GemmArgs {
   void* Y;
   int64_t ldy;  // elements
   int y_bf16;
-  int32_t* acc;  // EPI_ACC output, M x N
+  // EPI_ACC output, M x N.  With the other epilogues, when not null, the
+  // kernel also stores there the exact int32 sums of its main loop (the
+  // residual product C_x C_w^T) before dequantising them: a test hook that
+  // exports the accumulators of the very kernel that produces Y.
+  int32_t* acc;
+  // Test hook of the second integer product, M x N, when not null: the 8-bit
+  // segment's sums (EPI_MP) or the quantised low-rank branch's second stage
+  // C_t C_v^T (EPI_QLR).
+  int32_t* acc2;
   // EPI_QLR, the quantised low-rank branch: second-stage weight codes
   // (N rows of r_pad / 2 nibble-packed bytes) and scales, first-stage codes
   // (M rows of r_pad int8 bytes in the int8 code order) and scales
@@ -197,6 +205,7 @@ struct SmallArgs {
   unsigned* sync;  // hand-off words, kSyncBytes: [0] producers done, [2] wait-limit flag, consumer shard counters
   void* Y;
   int y_bf16;
+  int32_t* acc;  // test hook: when not null, the exact int32 sums of the residual product (n x m)
 };
 constexpr int kSyncBytes = 4096;  // workspace bytes of the hand-off words
 

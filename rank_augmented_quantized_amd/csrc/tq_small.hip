@@ -63,7 +63,10 @@ __device__ __forceinline__ void signal_done(unsigned* ctr) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T, int WAVES, int NR>
+// DBG: the test-hook instance, which also stores the exact int32 sums of the
+// residual product to a.acc (n x m); its code is this template's, with those
+// stores added.
+template <typename T, int WAVES, int NR, bool DBG = false>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_small(SmallArgs a) {
   constexpr int NT = WAVES * 64;
   constexpr int U = (WAVES == 4) ? 8 : 16;  // 64-byte weight steps per wave per batch
@@ -357,6 +360,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_linear_sma
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * lg + i;
       if (row >= n || col >= m) continue;
+      if constexpr (DBG) a.acc[(size_t)row * m + col] = s[i];
       const float y = (float)s[i] * (sRed[WAVES + row] * swv) + lrv[i];
       if (a.y_bf16)
         reinterpret_cast<bf16_t*>(a.Y)[(size_t)row * m + col] = (bf16_t)f32_to_bf16_bits(y);
@@ -432,10 +436,16 @@ template <typename T>
 static hipError_t launch_small_t(const SmallArgs& a, hipStream_t st) {
   if (!small_fused_ok(a.n, a.d, a.r_pad)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(a.nt + (a.m + 15) / 16));
-  if (a.n == 1)
+  if (a.acc) {  // the accumulator-export instance (test hook)
+    if (a.n == 1)
+      hipLaunchKernelGGL((k_linear_small<T, 4, 1, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_linear_small<T, 4, 2, true>), grid, dim3(256), 0, st, a);
+  } else if (a.n == 1) {
     hipLaunchKernelGGL((k_linear_small<T, 4, 1>), grid, dim3(256), 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((k_linear_small<T, 4, 2>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ EXPORTS = (
     "tq_pack_rht", "tq_linear_mp_rht", "tq_lowrank_q_bytes", "tq_pack_lowrank_q", "tq_linear_qlr_workspace_bytes",
     "tq_linear_qlr_workspace_offsets", "tq_linear_qlr", "tq_weight_colsum", "tq_linear_mp_asym_workspace_bytes",
     "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits", "tq_linear_asym_workspace_bytes",
-    "tq_linear_asym_workspace_offsets", "tq_linear_asym",
+    "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
+    "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug",
 )
 
 
@@ -83,7 +84,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_mp_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_rht_bytes": (sz, [i64]),
         "tq_pack_rht": (st, [ptr, ptr, i64, ptr, ptr]),
-        "tq_linear_mp_rht": (st, [ptr, c_int, i64, i64, i64, ptr, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz,
+        "tq_linear_mp_rht": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz,
                                   ptr]),
         "tq_lowrank_q_bytes": (sz, [i64, i64, i64]),
         "tq_pack_lowrank_q": (st, [ptr, ptr, c_int, i64, i64, i64, ptr, ptr]),
@@ -100,6 +101,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_mp_asym_workspace_offsets": (st, [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "tq_linear_mp_asym": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, ptr, ptr, c_int, ptr,
                                    sz, ptr]),
+        "tq_linear_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr, ptr]),
+        "tq_linear_mp_bits_debug": (st, [ptr, c_int, i64, i64, i64, i64, c_int, c_int, ptr, ptr, ptr, ptr, ptr,
+                                         c_int, ptr, sz, ptr, ptr, ptr]),
+        "tq_linear_asym_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr,
+                                      ptr]),
+        "tq_linear_mp_asym_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, ptr, ptr, c_int,
+                                         ptr, sz, ptr, ptr, ptr]),
+        "tq_linear_qlr_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr, ptr,
+                                     ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -194,17 +204,22 @@ def linear_workspace(n: int, d: int, m: int, r: int, device) -> torch.Tensor:
     return torch.zeros(max(1, tq_linear_workspace_bytes(n, d, m, r)), dtype=torch.uint8, device=device)
 
 
-def tq_linear(X, w_codes, s_w, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
-    """Y = s_x s_w (Q4(X) Q4(R)) + (X L1) L2 for X n x d."""
+def tq_linear(X, w_codes, s_w, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None, acc=None):
+    """Y = s_x s_w (Q4(X) Q4(R)) + (X L1) L2 for X n x d.  acc (n x m int32, optional): the kernels' exact
+    residual sums, through tq_linear_debug."""
     lib = load()
-    _need_cuda(X, w_codes, s_w, lowrank, Y, ws)
+    _need_cuda(X, w_codes, s_w, lowrank, Y, ws, acc)
     n, d = X.shape
     if Y is None:
         Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
     if ws is None:
         ws = linear_workspace(n, d, m, r, X.device)
-    _check("tq_linear", lib.tq_linear(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
-                                      _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    if acc is None:
+        _check("tq_linear", lib.tq_linear(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
+                                          _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    else:
+        _check("tq_linear_debug", lib.tq_linear_debug(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
+                                                      _p(Y), _dt(Y), _p(ws), ws.numel(), _p(acc), _stream(X)))
     return Y
 
 
@@ -213,21 +228,27 @@ def tq_linear_mp_workspace_bytes(n: int, d: int, d_hi: int) -> int:
 
 
 def tq_linear_mp(Xrot, d_hi: int, wl_codes, s_wl, wh_codes, s_wh, m: int, y_dtype=torch.bfloat16, Y=None, ws=None,
-                 bits=(4, 8)):
-    """Y = Q4(X_l) Q4(W_l) + Q8(X_h) Q8(W_h), X_h = the last d_hi columns of Xrot (bits=(3, 6): Q3 and Q6)."""
+                 bits=(4, 8), acc_l=None, acc_h=None):
+    """Y = Q4(X_l) Q4(W_l) + Q8(X_h) Q8(W_h), X_h = the last d_hi columns of Xrot (bits=(3, 6): Q3 and Q6).
+    acc_l / acc_h (n x m int32, optional): the kernel's exact sums of both subspaces, through
+    tq_linear_mp_bits_debug."""
     lib = load()
-    _need_cuda(Xrot, wl_codes, s_wl, wh_codes, s_wh, Y, ws)
+    _need_cuda(Xrot, wl_codes, s_wl, wh_codes, s_wh, Y, ws, acc_l, acc_h)
     n, d = Xrot.shape
     if Y is None:
         Y = torch.empty((n, m), dtype=y_dtype, device=Xrot.device)
     if ws is None:
         ws = torch.empty(max(1, tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=Xrot.device)
-    if tuple(bits) == (4, 8):
-        _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
+    if acc_l is not None:
+        _check("tq_linear_mp_bits_debug", lib.tq_linear_mp_bits_debug(
+            _p(Xrot), _dt(Xrot), n, d, m, d_hi, bits[0], bits[1], _p(wl_codes), _p(s_wl), _p(wh_codes), _p(s_wh),
+            _p(Y), _dt(Y), _p(ws), ws.numel(), _p(acc_l), _p(acc_h), _stream(Xrot)))
+    elif tuple(bits) == (4, 8):
+        _check("tq_linear_mp", lib.tq_linear_mp(_p(Xrot), _dt(Xrot), n, d, m, d_hi, _p(wl_codes), _p(s_wl),
                                                 _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
                                                 _stream(Xrot)))
     else:
-        _check("tq_linear_mp_bits", lib.tq_linear_mp_bits(_p(Xrot), _dt(Xrot), n, d, d_hi, m, bits[0], bits[1],
+        _check("tq_linear_mp_bits", lib.tq_linear_mp_bits(_p(Xrot), _dt(Xrot), n, d, m, d_hi, bits[0], bits[1],
                                                           _p(wl_codes), _p(s_wl), _p(wh_codes), _p(s_wh), _p(Y),
                                                           _dt(Y), _p(ws), ws.numel(), _stream(Xrot)))
     return Y
@@ -309,7 +330,7 @@ def tq_linear_mp_rht(X, d_hi: int, rot, wl_codes, s_wl, wh_codes, s_wh, m: int, 
         Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
     if ws is None:
         ws = torch.empty(max(1, tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=X.device)
-    _check("tq_linear_mp_rht", lib.tq_linear_mp_rht(_p(X), _dt(X), n, d, d_hi, _p(rot), m, _p(wl_codes), _p(s_wl),
+    _check("tq_linear_mp_rht", lib.tq_linear_mp_rht(_p(X), _dt(X), n, d, m, d_hi, _p(rot), _p(wl_codes), _p(s_wl),
                                                     _p(wh_codes), _p(s_wh), _p(Y), _dt(Y), _p(ws), ws.numel(),
                                                     _stream(X)))
     return Y
@@ -342,17 +363,25 @@ def tq_linear_qlr_workspace_offsets(n: int, d: int, r: int) -> dict:
     return {"s_x": off[0], "x_codes": off[1], "s_t": off[2], "t_codes": off[3]}
 
 
-def tq_linear_qlr(X, w_codes, s_w, lowrank_q, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
-    """Y = s_x s_w (Q4(X) Q4(R)) + (s_x s_t) s_v (Q4(T) Q4(V)), T the per-token re-quantised Q4(X) Q4(U)."""
+def tq_linear_qlr(X, w_codes, s_w, lowrank_q, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None, acc=None,
+                  acc2=None):
+    """Y = s_x s_w (Q4(X) Q4(R)) + (s_x s_t) s_v (Q4(T) Q4(V)), T the per-token re-quantised Q4(X) Q4(U).
+    acc / acc2 (n x m int32, optional): the kernel's exact residual and second-stage sums, through
+    tq_linear_qlr_debug."""
     lib = load()
-    _need_cuda(X, w_codes, s_w, lowrank_q, Y, ws)
+    _need_cuda(X, w_codes, s_w, lowrank_q, Y, ws, acc, acc2)
     n, d = X.shape
     if Y is None:
         Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
     if ws is None:
         ws = torch.empty(max(1, tq_linear_qlr_workspace_bytes(n, d, r)), dtype=torch.uint8, device=X.device)
-    _check("tq_linear_qlr", lib.tq_linear_qlr(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank_q),
-                                              _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    if acc is not None:
+        _check("tq_linear_qlr_debug", lib.tq_linear_qlr_debug(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w),
+                                                              _p(lowrank_q), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                                              _p(acc), _p(acc2), _stream(X)))
+    else:
+        _check("tq_linear_qlr", lib.tq_linear_qlr(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank_q),
+                                                  _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
     return Y
 
 
@@ -378,19 +407,26 @@ def tq_linear_mp_asym_workspace_offsets(n: int, d: int, d_hi: int) -> dict:
 
 
 def tq_linear_mp_asym(Xrot, d_hi: int, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, m: int,
-                      y_dtype=torch.bfloat16, Y=None, ws=None):
-    """tq_linear_mp with per-token asymmetric activations (zero-points), weights symmetric per channel."""
+                      y_dtype=torch.bfloat16, Y=None, ws=None, acc_l=None, acc_h=None):
+    """tq_linear_mp with per-token asymmetric activations (zero-points), weights symmetric per channel.
+    acc_l / acc_h (optional): the kernel's exact sums of the stored codes, through tq_linear_mp_asym_debug."""
     lib = load()
-    _need_cuda(Xrot, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, Y, ws)
+    _need_cuda(Xrot, wl_codes, s_wl, colsum_l, wh_codes, s_wh, colsum_h, Y, ws, acc_l, acc_h)
     n, d = Xrot.shape
     if Y is None:
         Y = torch.empty((n, m), dtype=y_dtype, device=Xrot.device)
     if ws is None:
         ws = torch.empty(max(1, tq_linear_mp_asym_workspace_bytes(n, d, d_hi)), dtype=torch.uint8,
                          device=Xrot.device)
-    _check("tq_linear_mp_asym", lib.tq_linear_mp_asym(_p(Xrot), _dt(Xrot), n, d, d_hi, m, _p(wl_codes), _p(s_wl),
-                                                      _p(colsum_l), _p(wh_codes), _p(s_wh), _p(colsum_h), _p(Y),
-                                                      _dt(Y), _p(ws), ws.numel(), _stream(Xrot)))
+    if acc_l is not None:
+        _check("tq_linear_mp_asym_debug", lib.tq_linear_mp_asym_debug(
+            _p(Xrot), _dt(Xrot), n, d, m, d_hi, _p(wl_codes), _p(s_wl), _p(colsum_l), _p(wh_codes), _p(s_wh),
+            _p(colsum_h), _p(Y), _dt(Y), _p(ws), ws.numel(), _p(acc_l), _p(acc_h), _stream(Xrot)))
+    else:
+        _check("tq_linear_mp_asym", lib.tq_linear_mp_asym(_p(Xrot), _dt(Xrot), n, d, m, d_hi, _p(wl_codes),
+                                                          _p(s_wl), _p(colsum_l), _p(wh_codes), _p(s_wh),
+                                                          _p(colsum_h), _p(Y), _dt(Y), _p(ws), ws.numel(),
+                                                          _stream(Xrot)))
     return Y
 
 
@@ -400,17 +436,24 @@ def tq_linear_asym_workspace_offsets(n: int, d: int, m: int, r: int) -> dict:
     return {"s_x": off[0], "x_codes": off[1], "z_x": off[2], "T": off[3]}
 
 
-def tq_linear_asym(X, w_codes, s_w, colsum, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None):
-    """tq_linear with per-token asymmetric activations; colsum = tq_weight_colsum(w_codes, d, 4)."""
+def tq_linear_asym(X, w_codes, s_w, colsum, lowrank, m: int, r: int, y_dtype=torch.bfloat16, Y=None, ws=None,
+                   acc=None):
+    """tq_linear with per-token asymmetric activations; colsum = tq_weight_colsum(w_codes, d, 4).
+    acc (optional): the kernel's exact sums of the stored codes (u - 8), through tq_linear_asym_debug."""
     lib = load()
-    _need_cuda(X, w_codes, s_w, colsum, lowrank, Y, ws)
+    _need_cuda(X, w_codes, s_w, colsum, lowrank, Y, ws, acc)
     n, d = X.shape
     if Y is None:
         Y = torch.empty((n, m), dtype=y_dtype, device=X.device)
     if ws is None:
         ws = torch.zeros(max(1, lib.tq_linear_asym_workspace_bytes(n, d, m, r)), dtype=torch.uint8, device=X.device)
-    _check("tq_linear_asym", lib.tq_linear_asym(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(colsum),
-                                                _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
+    if acc is not None:
+        _check("tq_linear_asym_debug", lib.tq_linear_asym_debug(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w),
+                                                                _p(colsum), _p(lowrank), _p(Y), _dt(Y), _p(ws),
+                                                                ws.numel(), _p(acc), _stream(X)))
+    else:
+        _check("tq_linear_asym", lib.tq_linear_asym(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(colsum),
+                                                    _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(), _stream(X)))
     return Y
 
 

@@ -154,12 +154,12 @@ def test_rht_validation(lib):
     assert lib.tq_pack_rht(A, B, 256, MIS, S) == -5
     n, d, dh, m = 8, 512, 128, 64
     need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
-    assert lib.tq_linear_mp_rht(A, 1, n, 544, 160, B, m, A, B, C, A, B, 1, C, need, S) == -2  # d % 128
-    assert lib.tq_linear_mp_rht(A, 1, n, 16384, 128, B, m, A, B, C, A, B, 1, C, need, S) == -2
-    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, NUL, m, A, B, C, A, B, 1, C, need, S) == -1
-    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, MIS, m, A, B, C, A, B, 1, C, need, S) == -5
-    assert lib.tq_linear_mp_rht(A, 1, n, d, dh, B, m, A, B, C, A, B, 1, C, need - 1, S) == -6
-    assert lib.tq_linear_mp_rht(A, 1, 0, d, dh, NUL, m, A, B, C, A, B, 1, C, 0, S) == 0
+    assert lib.tq_linear_mp_rht(A, 1, n, 544, m, 160, B, A, B, C, A, B, 1, C, need, S) == -2  # d % 128
+    assert lib.tq_linear_mp_rht(A, 1, n, 16384, m, 128, B, A, B, C, A, B, 1, C, need, S) == -2
+    assert lib.tq_linear_mp_rht(A, 1, n, d, m, dh, NUL, A, B, C, A, B, 1, C, need, S) == -1
+    assert lib.tq_linear_mp_rht(A, 1, n, d, m, dh, MIS, A, B, C, A, B, 1, C, need, S) == -5
+    assert lib.tq_linear_mp_rht(A, 1, n, d, m, dh, B, A, B, C, A, B, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_mp_rht(A, 1, 0, d, m, dh, NUL, A, B, C, A, B, 1, C, 0, S) == 0
     off = tqb.tq_linear_mp_workspace_offsets(n, d, dh)
     assert off["x_codes_h"] >= off["x_codes_l"] + n * (d - dh) and all(v % 256 == 0 for v in off.values())
 
@@ -208,11 +208,11 @@ def test_mp_bits_validation(lib):
     assert lib.tq_pack_weight(A, 1, 48, 64, 3, B, C, S) == -2  # 3-bit rows: d % 32
     n, d, dh, m = 64, 512, 64, 256
     need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
-    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 4, 6, B, C, A, B, C, 1, A, need, S) == -4
-    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 3, 8, B, C, A, B, C, 1, A, need, S) == -4
-    assert lib.tq_linear_mp_bits(A, 1, n, d, 40, m, 3, 6, B, C, A, B, C, 1, A, need, S) == -2
-    assert lib.tq_linear_mp_bits(A, 1, n, d, dh, m, 3, 6, B, C, A, B, C, 1, A, need - 1, S) == -6
-    assert lib.tq_linear_mp_bits(A, 1, 0, d, dh, m, 3, 6, B, C, A, B, C, 1, A, 0, S) == 0
+    assert lib.tq_linear_mp_bits(A, 1, n, d, m, dh, 4, 6, B, C, A, B, C, 1, A, need, S) == -4
+    assert lib.tq_linear_mp_bits(A, 1, n, d, m, dh, 3, 8, B, C, A, B, C, 1, A, need, S) == -4
+    assert lib.tq_linear_mp_bits(A, 1, n, d, m, 40, 3, 6, B, C, A, B, C, 1, A, need, S) == -2
+    assert lib.tq_linear_mp_bits(A, 1, n, d, m, dh, 3, 6, B, C, A, B, C, 1, A, need - 1, S) == -6
+    assert lib.tq_linear_mp_bits(A, 1, 0, d, m, dh, 3, 6, B, C, A, B, C, 1, A, 0, S) == 0
 
 
 def test_mp_asym_validation(lib):
@@ -223,13 +223,13 @@ def test_mp_asym_validation(lib):
     n, d, dh, m = 64, 512, 64, 256
     need = lib.tq_linear_mp_asym_workspace_bytes(n, d, dh)
     assert need == lib.tq_linear_mp_workspace_bytes(n, d, dh) + 2 * 256
-    assert lib.tq_linear_mp_asym(A, 1, n, d, 40, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d_hi % 16
-    assert lib.tq_linear_mp_asym(A, 1, n, 32768, 128, m, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d > 16384
-    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, NUL, A, B, C, A, 1, C, need, S) == -1  # colsum_l
-    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, A, A, B, NUL, A, 1, C, need, S) == -1  # colsum_h
-    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, MIS, A, B, C, A, 1, C, need, S) == -5
-    assert lib.tq_linear_mp_asym(A, 1, n, d, dh, m, B, C, A, A, B, C, A, 1, C, need - 1, S) == -6
-    assert lib.tq_linear_mp_asym(A, 1, 0, d, dh, m, B, C, A, A, B, C, A, 1, C, 0, S) == 0
+    assert lib.tq_linear_mp_asym(A, 1, n, d, m, 40, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d_hi % 16
+    assert lib.tq_linear_mp_asym(A, 1, n, 32768, m, 128, B, C, A, A, B, C, A, 1, C, need, S) == -2  # d > 16384
+    assert lib.tq_linear_mp_asym(A, 1, n, d, m, dh, B, C, NUL, A, B, C, A, 1, C, need, S) == -1  # colsum_l
+    assert lib.tq_linear_mp_asym(A, 1, n, d, m, dh, B, C, A, A, B, NUL, A, 1, C, need, S) == -1  # colsum_h
+    assert lib.tq_linear_mp_asym(A, 1, n, d, m, dh, B, C, MIS, A, B, C, A, 1, C, need, S) == -5
+    assert lib.tq_linear_mp_asym(A, 1, n, d, m, dh, B, C, A, A, B, C, A, 1, C, need - 1, S) == -6
+    assert lib.tq_linear_mp_asym(A, 1, 0, d, m, dh, B, C, A, A, B, C, A, 1, C, 0, S) == 0
     off = tqb.tq_linear_mp_asym_workspace_offsets(n, d, dh)
     assert off["z_xl"] >= off["x_codes_h"] + n * dh and off["z_xh"] >= off["z_xl"] + 4 * n
     assert all(v % 256 == 0 for v in off.values())
@@ -238,11 +238,34 @@ def test_mp_asym_validation(lib):
 def test_linear_mp_validation(lib):
     n, d, dh, m = 64, 512, 64, 256
     need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
-    assert lib.tq_linear_mp(A, 1, n, d, 40, m, B, C, A, B, C, 1, A, need, S) == -2  # d_hi % 16
-    assert lib.tq_linear_mp(A, 1, n, 520, 64, m, B, C, A, B, C, 1, A, need, S) == -2  # (d - d_hi) % 32
-    assert lib.tq_linear_mp(A, 1, n, d, d + 16, m, B, C, A, B, C, 1, A, need, S) == -2
-    assert lib.tq_linear_mp(A, 1, n, d, dh, m, B, C, NUL, B, C, 1, A, need, S) == -1
-    assert lib.tq_linear_mp(A, 1, n, d, dh, m, B, C, A, B, C, 1, A, need - 1, S) == -6
+    assert lib.tq_linear_mp(A, 1, n, d, m, 40, B, C, A, B, C, 1, A, need, S) == -2  # d_hi % 16
+    assert lib.tq_linear_mp(A, 1, n, 520, m, 64, B, C, A, B, C, 1, A, need, S) == -2  # (d - d_hi) % 32
+    assert lib.tq_linear_mp(A, 1, n, d, m, d + 16, B, C, A, B, C, 1, A, need, S) == -2
+    assert lib.tq_linear_mp(A, 1, n, d, m, dh, B, C, NUL, B, C, 1, A, need, S) == -1
+    assert lib.tq_linear_mp(A, 1, n, d, m, dh, B, C, A, B, C, 1, A, need - 1, S) == -6
+
+
+def test_debug_entry_points_validation(lib):
+    """The accumulator-export variants check their export buffers after the layer's own checks."""
+    n, d, m, r = 64, 512, 256, 16
+    need = lib.tq_linear_workspace_bytes(n, d, m, r)
+    assert lib.tq_linear_debug(A, 1, n, d, m, r, B, C, A, B, 1, C, need, NUL, S) == -1
+    assert lib.tq_linear_debug(A, 1, n, d, m, r, B, C, A, B, 1, C, need, MIS, S) == -5
+    assert lib.tq_linear_debug(A, 1, n, 500, m, r, B, C, A, B, 1, C, need, A, S) == -2
+    assert lib.tq_linear_debug(A, 1, 0, d, m, r, NUL, NUL, NUL, NUL, 1, NUL, 0, NUL, S) == 0
+    dh = 64
+    need = lib.tq_linear_mp_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp_bits_debug(A, 1, n, d, m, dh, 4, 8, B, C, A, B, C, 1, A, need, A, NUL, S) == -1
+    assert lib.tq_linear_mp_bits_debug(A, 1, n, d, m, 0, 4, 8, B, C, NUL, NUL, C, 1, A, need, NUL, NUL, S) == -1
+    assert lib.tq_linear_mp_bits_debug(A, 1, n, d, m, dh, 4, 8, B, C, A, B, C, 1, A, need, A, MIS, S) == -5
+    assert lib.tq_linear_mp_bits_debug(A, 1, n, d, m, dh, 4, 6, B, C, A, B, C, 1, A, need, A, B, S) == -4
+    need = lib.tq_linear_mp_asym_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp_asym_debug(A, 1, n, d, m, dh, B, C, A, A, B, C, A, 1, C, need, NUL, B, S) == -1
+    need = lib.tq_linear_asym_workspace_bytes(n, d, m, r)
+    assert lib.tq_linear_asym_debug(A, 1, n, d, m, r, B, C, A, B, A, 1, C, need, MIS, S) == -5
+    need = lib.tq_linear_qlr_workspace_bytes(n, d, r)
+    assert lib.tq_linear_qlr_debug(A, 1, n, d, m, r, B, C, A, B, 1, C, need, A, NUL, S) == -1
+    assert lib.tq_linear_qlr_debug(A, 1, n, d, m, 0, B, C, A, B, 1, C, need, A, B, S) == -2
 
 
 def test_debug_accumulate_validation(lib):

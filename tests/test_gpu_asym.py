@@ -51,9 +51,19 @@ def _run(xrot, wrot, d_hi, x_dtype=torch.bfloat16, y_dtype=torch.bfloat16):
     csl = tq.tq_weight_colsum(wl[0], dl, 4) if dl else None
     csh = tq.tq_weight_colsum(wh[0], d_hi, 8) if d_hi else None
     ws = torch.empty(max(1, tq.tq_linear_mp_asym_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=DEV)
-    y = tq.tq_linear_mp_asym(_t(xrot, x_dtype), d_hi, wl[0], wl[1], csl, wh[0], wh[1], csh, m, y_dtype=y_dtype,
-                             ws=ws)
+    xt = _t(xrot, x_dtype)
+    y = tq.tq_linear_mp_asym(xt, d_hi, wl[0], wl[1], csl, wh[0], wh[1], csh, m, y_dtype=y_dtype, ws=ws)
     torch.cuda.synchronize()
+    # the same call through tq_linear_mp_asym_debug: the kernel's int32 sums of the stored codes of both subspaces
+    acc_l = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    acc_h = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV) if d_hi else None
+    ws2 = torch.empty_like(ws)
+    y2 = tq.tq_linear_mp_asym(xt, d_hi, wl[0], wl[1], csl, wh[0], wh[1], csh, m, y_dtype=y_dtype, ws=ws2,
+                              acc_l=acc_l, acc_h=acc_h)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    _run.acc = (acc_l.cpu().numpy().astype(np.int64),
+                acc_h.cpu().numpy().astype(np.int64) if d_hi else np.zeros((n, m), np.int64))
     return y, ws, csl, csh
 
 
@@ -84,6 +94,14 @@ def _check(xrot, wrot, d_hi, y, ws, csl, csh, rows=None, cols=None):
         assert np.array_equal(uh[r], ref["codes_xh"])
         if cols is None:
             assert np.array_equal(csh.cpu().numpy(), ref["colsum_h"])
+    # sums of the stored codes u - 2^(N-1): U C_w^T - 2^(N-1) colsum of each subspace, exactly
+    acc_l, acc_h = _run.acc
+    if rows is not None:
+        acc_l, acc_h = acc_l[np.ix_(rows, cols)], acc_h[np.ix_(rows, cols)]
+    if dl:
+        assert np.array_equal(acc_l, ref["acc_l"] - 8 * ref["colsum_l"][None, :])
+    if d_hi:
+        assert np.array_equal(acc_h, ref["acc_h"] - 128 * ref["colsum_h"][None, :])
     yg = y.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         yg = yg[np.ix_(rows, cols)]

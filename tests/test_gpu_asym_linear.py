@@ -57,8 +57,17 @@ def _run(x, xdt, r_w, l1, l2):
     cs = tq.tq_weight_colsum(wc, d, 4)
     lr = tq.tq_pack_lowrank(_t(l1, torch.bfloat16), _t(l2, torch.bfloat16)) if rk else None
     ws = torch.zeros(tq.load().tq_linear_asym_workspace_bytes(n, d, m, rk), dtype=torch.uint8, device=DEV)
-    y = tq.tq_linear_asym(_t(x, torch.bfloat16 if xdt == "bf16" else torch.float32), wc, sw, cs, lr, m, rk, ws=ws)
+    xt = _t(x, torch.bfloat16 if xdt == "bf16" else torch.float32)
+    y = tq.tq_linear_asym(xt, wc, sw, cs, lr, m, rk, ws=ws)
     torch.cuda.synchronize()
+    # the same call through tq_linear_asym_debug: the kernels' int32 sums of the stored codes u - 8
+    acc = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    y2 = torch.empty_like(y)
+    ws2 = torch.zeros(tq.load().tq_linear_asym_workspace_bytes(n, d, m, rk), dtype=torch.uint8, device=DEV)
+    tq.tq_linear_asym(xt, wc, sw, cs, lr, m, rk, Y=y2, ws=ws2, acc=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    _run.acc = acc.cpu().numpy().astype(np.int64)
     return y, ws, cs
 
 
@@ -79,6 +88,9 @@ def _check(x, r_w, l1, l2, y, ws, cs, rows=None, cols=None):
     assert np.array_equal(codes[r], ref["codes_x"])
     if cols is None:
         assert np.array_equal(cs.cpu().numpy(), ref["colsum"])
+    # the kernels' sums over the stored codes u - 8: U C_w^T - 8 colsum, exactly
+    acc = _run.acc if rows is None else _run.acc[np.ix_(rows, cols)]
+    assert np.array_equal(acc, ref["acc"] - 8 * ref["colsum"][None, :])
     if rk:
         rp = _r_pad(rk)
         t = ws[off["T"]: off["T"] + n * rp * 2].view(torch.bfloat16).view(n, rp).float().cpu().numpy()[r, :rk]

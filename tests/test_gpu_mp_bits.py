@@ -48,8 +48,18 @@ def _run(xrot, wrot, d_hi, x_dtype=torch.bfloat16):
     wl = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[:dl])), 3) if dl else (None, None)
     wh = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[dl:])), 6) if d_hi else (None, None)
     ws = torch.empty(max(1, tq.tq_linear_mp_workspace_bytes(n, d, d_hi)), dtype=torch.uint8, device=DEV)
-    y = tq.tq_linear_mp(_t(xrot, x_dtype), d_hi, wl[0], wl[1], wh[0], wh[1], m, ws=ws, bits=(3, 6))
+    xt = _t(xrot, x_dtype)
+    y = tq.tq_linear_mp(xt, d_hi, wl[0], wl[1], wh[0], wh[1], m, ws=ws, bits=(3, 6))
     torch.cuda.synchronize()
+    # the same call through tq_linear_mp_bits_debug: the kernel's int32 sums of both subspaces
+    acc_l = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    acc_h = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV) if d_hi else None
+    y2 = tq.tq_linear_mp(xt, d_hi, wl[0], wl[1], wh[0], wh[1], m, ws=torch.empty_like(ws), bits=(3, 6),
+                         acc_l=acc_l, acc_h=acc_h)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    _run.acc = (acc_l.cpu().numpy().astype(np.int64),
+                acc_h.cpu().numpy().astype(np.int64) if d_hi else np.zeros((n, m), np.int64))
     return y, ws, wl, wh
 
 
@@ -74,6 +84,10 @@ def _check(xrot, wrot, d_hi, y, ws, wl, wh, rows=None, cols=None):
         if cols is None:
             assert np.array_equal(wh[0].cpu().numpy().view(np.int8).astype(np.int16), ref["codes_wh"])
             assert np.array_equal(wh[1].cpu().numpy(), ref["s_wh"])
+    acc_l, acc_h = _run.acc
+    if rows is not None:
+        acc_l, acc_h = acc_l[np.ix_(rows, cols)], acc_h[np.ix_(rows, cols)]
+    assert np.array_equal(acc_l, ref["acc_l"]) and np.array_equal(acc_h, ref["acc_h"])
     yg = y.float().cpu().numpy().astype(np.float64)
     if rows is not None:
         yg = yg[np.ix_(rows, cols)]

@@ -1,8 +1,12 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
 Bar: codes, scales and int32 accumulators bit-exact; Y within
-max|Y - Y_ref| <= 1e-2 * max|Y_ref| (fp64 oracle).  Inputs come from the
-seeded generators; expected values only from ``oracle``.
+max|Y - Y_ref| <= 1e-2 * max|Y_ref| (fp64 oracle); T = X L1 within one bf16
+ulp plus the fp32 summation bound (tq_testutil).  The accumulators are those
+of the kernels that produce Y: each layer call is repeated through its
+accumulator-export entry point (tq_linear_debug, tq_linear_mp_bits_debug),
+whose Y must equal the plain call's bit for bit.  Inputs come from the seeded
+generators; expected values only from ``oracle``.
 """
 
 from __future__ import annotations
@@ -14,6 +18,7 @@ torch = pytest.importorskip("torch")
 
 import oracle.tq_oracle as tqo  # noqa: E402
 import rank_augmented_quantized_amd as tq  # noqa: E402
+from tq_testutil import assert_t_tight  # noqa: E402
 from workloads import WORKLOADS, draw_custom, draw_linear, draw_two_subspace, draw_two_subspace_custom  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -178,16 +183,32 @@ def test_accumulate_bitexact(n, k, m, bits):
 # the layer on small shapes (several tiles, ragged tails)
 # ----------------------------------------------------------------------------
 
-def _run_linear(x, xdt, r_w, l1, l2, y_dtype=torch.bfloat16):
+def _run_linear(x, xdt, r_w, l1, l2, y_dtype=torch.bfloat16, want_acc=False):
     n, d = x.shape
     m = r_w.shape[1]
     r = 0 if l1 is None else l1.shape[1]
     wc, sw = tq.tq_pack_weight(_t(r_w), 4)
     lowrank = tq.tq_pack_lowrank(_t(l1, torch.bfloat16), _t(l2, torch.bfloat16)) if r else None
     ws = tq.linear_workspace(n, d, m, r, DEV)
-    y = tq.tq_linear(_x_tensor(x, xdt), wc, sw, lowrank, m, r, y_dtype=y_dtype, ws=ws)
+    xt = _x_tensor(x, xdt)
+    y = tq.tq_linear(xt, wc, sw, lowrank, m, r, y_dtype=y_dtype, ws=ws)
     torch.cuda.synchronize()
-    return y, ws, wc, sw
+    if not want_acc:
+        return y, ws, wc, sw
+    acc = _linear_acc(xt, wc, sw, lowrank, m, r, y)
+    return y, ws, wc, sw, acc
+
+
+def _linear_acc(xt, wc, sw, lowrank, m, r, y):
+    """The same call through tq_linear_debug: the kernels' int32 residual sums (n x m); its Y must be the plain
+    call's, bit for bit."""
+    n, d = xt.shape
+    acc = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    y2 = torch.empty_like(y)
+    tq.tq_linear(xt, wc, sw, lowrank, m, r, Y=y2, ws=tq.linear_workspace(n, d, m, r, DEV), acc=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    return acc.cpu().numpy().astype(np.int64)
 
 
 def _int8_codes(b):
@@ -226,18 +247,14 @@ def _r_pad(r):
 
 
 def _assert_t(ws, x, l1, n, d, m, r, rows=None):
-    """T = X L1 from the workspace against the fp64 oracle branch (bf16 rounding of X and T)."""
+    """T = X L1 from the workspace against the fp64 product of the bf16-rounded X (tq_testutil bound)."""
     if not r:
         return
     rp = _r_pad(r)
     off = tq.tq_linear_workspace_offsets(n, d, m, r)["T"]
     t = ws[off: off + n * rp * 2].view(torch.bfloat16).view(n, rp).float().cpu().numpy()[:, :r]
     rows = np.arange(n) if rows is None else rows
-    t_ref, _ = tqo.lowrank_branch(x[rows], l1, np.zeros((r, 1)))
-    scale = np.abs(t_ref).max(axis=1, keepdims=True) + 1e-30
-    err = np.abs(t[rows] - t_ref) / scale
-    print(f"  T max rel err {err.max():.3e}", flush=True)
-    assert err.max() <= 2e-2, err.max()
+    assert_t_tight(t[rows], np.asarray(x)[rows], l1)
 
 
 LCASES = [
@@ -271,12 +288,14 @@ def test_linear_small(case):
     l1 = c["L1"] if r else None
     l2 = c["L2"] if r else None
     ydt = torch.float32 if name.endswith("f32_out") else torch.bfloat16
-    y, ws, wc, sw = _run_linear(c["X"], xdt, c["R"], l1, l2, ydt)
+    y, ws, wc, sw, acc_k = _run_linear(c["X"], xdt, c["R"], l1, l2, ydt, want_acc=True)
     ref = tqo.tq_linear_ref(c["X"], c["R"], l1, l2)
     sx, codes = _ws_codes(ws, n, d, m, r)
     assert np.array_equal(sx, ref["s_x"])
     assert np.array_equal(codes, ref["codes_x"])
-    # the product path's accumulators, exported from the same codes
+    # the accumulators of the kernels that produced Y
+    assert np.array_equal(acc_k, ref["acc"])
+    # and the standalone integer GEMM on the same codes
     xc = _ws_packed_codes(ws, n, d, m, r)
     acc = tq.tq_debug_accumulate(xc, wc, d, 4)
     torch.cuda.synchronize()
@@ -388,27 +407,23 @@ WCASES = [("attn_proj", 4096, True), ("attn_proj", 4096, False), ("mlp_gate_up",
 
 @pytest.mark.parametrize("wl,n,outl", WCASES, ids=[f"{w}-n{n}-{'outliers' if o else 'plain'}" for w, n, o in WCASES])
 def test_linear_workload(wl, n, outl):
+    """The workloads at full size, compared in full: every code and scale, every int32 accumulator of the kernels
+    that produced Y, T, and every element of Y."""
     w = WORKLOADS[wl]
     print(f"case {w.title} n={n} outliers={outl}", flush=True)
     c = draw_linear(w, n=n, outliers=outl)
     d, m, r = w.d, w.m, w.r
-    y, ws, wc, sw = _run_linear(c["X"], w.x_dtype, c["R"], c["L1"], c["L2"])
-    rng = np.random.default_rng(n)
-    rows, cols = _sample(n, m, rng)
-    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"], rows=rows, cols=cols)
-    # scales and codes of every token, bit-exact
-    cx_all, sx_all = tqo.quantize_rows(c["X"], 4)
+    y, ws, wc, sw, acc_k = _run_linear(c["X"], w.x_dtype, c["R"], c["L1"], c["L2"], want_acc=True)
+    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
     sx, codes = _ws_codes(ws, n, d, m, r)
-    assert np.array_equal(sx, sx_all)
-    assert np.array_equal(codes, cx_all)
-    # weight scales / codes of the sampled channels
-    assert np.array_equal(sw.cpu().numpy()[cols], ref["s_w"])
-    # accumulators of the sampled outputs, bit-exact
-    acc = tq.tq_debug_accumulate(_ws_packed_codes(ws, n, d, m, r), wc, d, 4)
-    torch.cuda.synchronize()
-    assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), ref["acc"])
-    _assert_t(ws, c["X"], c["L1"], n, d, m, r, rows)
-    _assert_y(y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)], ref["Y"], f"{wl} n={n}")
+    assert np.array_equal(sx, ref["s_x"])
+    assert np.array_equal(codes, ref["codes_x"])
+    assert np.array_equal(sw.cpu().numpy(), ref["s_w"])
+    assert np.array_equal(wc.cpu().numpy(), tqo.pack_int4(ref["codes_w"]))
+    bad = np.argwhere(acc_k != ref["acc"])
+    assert bad.size == 0, f"{len(bad)} accumulators differ, first {bad[:5].tolist()}"
+    _assert_t(ws, c["X"], c["L1"], n, d, m, r)
+    _assert_y(y, ref["Y"], f"{wl} n={n}")
 
 
 # ----------------------------------------------------------------------------
@@ -416,14 +431,30 @@ def test_linear_workload(wl, n, outl):
 # ----------------------------------------------------------------------------
 
 def _run_mp(xrot, wrot, d_hi):
+    """The two-subspace layer, then the same call through tq_linear_mp_bits_debug: returns Y and the kernel's
+    int32 sums of both subspaces (Y of the export call must equal Y bit for bit)."""
     n, d = xrot.shape
     m = wrot.shape[1]
     dl = d - d_hi
     wlc, swl = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[:dl])), 4) if dl else (None, None)
     whc, swh = tq.tq_pack_weight(_t(np.ascontiguousarray(wrot[dl:])), 8) if d_hi else (None, None)
-    y = tq.tq_linear_mp(_t(xrot, torch.bfloat16), d_hi, wlc, swl, whc, swh, m)
+    xt = _t(xrot, torch.bfloat16)
+    y = tq.tq_linear_mp(xt, d_hi, wlc, swl, whc, swh, m)
+    acc_l = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    acc_h = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV) if d_hi else None
+    y2 = tq.tq_linear_mp(xt, d_hi, wlc, swl, whc, swh, m, acc_l=acc_l, acc_h=acc_h)
     torch.cuda.synchronize()
-    return y
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    acc_l = acc_l.cpu().numpy().astype(np.int64)
+    acc_h = acc_h.cpu().numpy().astype(np.int64) if d_hi else np.zeros((n, m), np.int64)
+    return y, acc_l, acc_h
+
+
+def _assert_mp_acc(acc_l, acc_h, ref, rows=None, cols=None):
+    if rows is not None:
+        acc_l, acc_h = acc_l[np.ix_(rows, cols)], acc_h[np.ix_(rows, cols)]
+    assert np.array_equal(acc_l, ref["acc_l"])
+    assert np.array_equal(acc_h, ref["acc_h"])
 
 
 @pytest.mark.parametrize("n,d,m,dh", [(40, 512, 96, 64), (130, 1024, 272, 128), (16, 256, 64, 0),
@@ -435,19 +466,23 @@ def test_linear_mp_small(n, d, m, dh):
     256 x 256 tile (n = 512, m = 28672)."""
     print(f"case mp n={n} d={d} m={m} d_hi={dh}", flush=True)
     c = draw_two_subspace_custom(n, d, m, dh, seed=n + d + m, outlier_count=2, block=128 if d % 128 == 0 else 16)
-    y = _run_mp(c["Xrot"], c["Wrot"], dh)
+    y, acc_l, acc_h = _run_mp(c["Xrot"], c["Wrot"], dh)
     rows, cols = (None, None) if m < 4096 else _sample(n, m, np.random.default_rng(n), 64, 512)
     ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], dh, rows=rows, cols=cols)
+    _assert_mp_acc(acc_l, acc_h, ref, rows, cols)
     if rows is not None:
         y = y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)]
     _assert_y(y, ref["Y"], f"mp n={n} d={d} dh={dh}")
 
 
 def test_linear_mp_workload():
+    """The 70B MLP two-subspace shape (8192 x 8192 x 28672, 128-dim 8-bit subspace), compared in full: every
+    int32 sum of both subspaces and every element of Y."""
     w = WORKLOADS["two_subspace"]
     print(f"case {w.title}", flush=True)
     c = draw_two_subspace(w)
-    y = _run_mp(c["Xrot"], c["Wrot"], w.d_hi)
-    rows, cols = _sample(w.n, w.m, np.random.default_rng(4))
-    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], w.d_hi, rows=rows, cols=cols)
-    _assert_y(y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)], ref["Y"], "two_subspace")
+    y, acc_l, acc_h = _run_mp(c["Xrot"], c["Wrot"], w.d_hi)
+    ref = tqo.tq_linear_mp_ref(c["Xrot"], c["Wrot"], w.d_hi)
+    _assert_mp_acc(acc_l, acc_h, ref)
+    del acc_l, acc_h
+    _assert_y(y, ref["Y"], "two_subspace")

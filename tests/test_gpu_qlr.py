@@ -3,7 +3,10 @@
 Layer: Y = s_x s_w (C_x C_w^T) + (s_x s_t) s_v (C_t C_v^T), C_t / s_t the
 per-token 4-bit re-quantisation of t = fl32(C_x C_u^T) * s_u.  Bar: packed
 codes and scales of U and V, activation codes, s_x, the first stage's codes
-and s_t bit-exact; Y within max|Y - Y_ref| <= 1e-2 * max|Y_ref| (fp64 oracle).
+and s_t bit-exact; the int32 sums of the residual product and of the second
+stage, exported by the kernels that produce Y (tq_linear_qlr_debug, whose Y
+must equal the plain call's bit for bit), bit-exact; Y within
+max|Y - Y_ref| <= 1e-2 * max|Y_ref| (fp64 oracle).
 """
 
 from __future__ import annotations
@@ -74,10 +77,27 @@ def _run(x, xdt, r_w, u, v, y_dtype=torch.bfloat16):
     wc, sw = tq.tq_pack_weight(_t(r_w), 4)
     lq = tq.tq_pack_lowrank_q(_t(u), _t(v))
     ws = torch.zeros(max(1, tq.tq_linear_qlr_workspace_bytes(n, d, rk)), dtype=torch.uint8, device=DEV)
-    y = tq.tq_linear_qlr(_t(x, torch.bfloat16 if xdt == "bf16" else torch.float32), wc, sw, lq, m, rk,
-                         y_dtype=y_dtype, ws=ws)
+    xt = _t(x, torch.bfloat16 if xdt == "bf16" else torch.float32)
+    y = tq.tq_linear_qlr(xt, wc, sw, lq, m, rk, y_dtype=y_dtype, ws=ws)
     torch.cuda.synchronize()
     return y, ws, lq
+
+
+def _acc(x, xdt, r_w, u, v, y):
+    """The same layer through tq_linear_qlr_debug: (residual sums, second-stage sums), int64 n x m."""
+    n, d = x.shape
+    m, rk = r_w.shape[1], u.shape[1]
+    wc, sw = tq.tq_pack_weight(_t(r_w), 4)
+    lq = tq.tq_pack_lowrank_q(_t(u), _t(v))
+    ws = torch.zeros(max(1, tq.tq_linear_qlr_workspace_bytes(n, d, rk)), dtype=torch.uint8, device=DEV)
+    acc = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    acc2 = torch.full((n, m), -(2 ** 31), dtype=torch.int32, device=DEV)
+    y2 = torch.empty_like(y)
+    tq.tq_linear_qlr(_t(x, torch.bfloat16 if xdt == "bf16" else torch.float32), wc, sw, lq, m, rk, Y=y2, ws=ws,
+                     acc=acc, acc2=acc2)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y), "the accumulator-export call changed Y"
+    return acc.cpu().numpy().astype(np.int64), acc2.cpu().numpy().astype(np.int64)
 
 
 def _ws_parts(ws, n, d, rk):
@@ -133,6 +153,9 @@ def test_linear_qlr(case):
     assert np.array_equal(xc, ref["codes_x"])
     assert np.array_equal(st, ref["s_t"])
     assert np.array_equal(tc[:, :rk], ref["codes_t"]) and not tc[:, rk:].any()
+    acc, acc2 = _acc(c["X"], xdt, c["R"], u, v, y)
+    assert np.array_equal(acc, ref["acc"])
+    assert np.array_equal(acc2, ref["acc2"])
     err = np.abs(y.float().cpu().numpy().astype(np.float64) - ref["Y"]).max()
     scale = np.abs(ref["Y"]).max()
     print(f"  max|Y-Yref|/max|Yref| = {err / scale:.3e}", flush=True)

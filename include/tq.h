@@ -200,6 +200,26 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
                     void* Y, tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * tq_linear_noalloc -- tq_linear for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same Y, bit for bit.  The workspace is a file-scope device
+ * array of TQ_NOALLOC_SCRATCH_BYTES, one per device, which the library keeps
+ * until the process ends; its first use on a device looks up its address and
+ * clears its counters with one small kernel on `stream`.  No call allocates
+ * or frees memory.  Returns TQ_ERR_WORKSPACE when
+ * tq_linear_workspace_bytes(n, d, m, r) exceeds TQ_NOALLOC_SCRATCH_BYTES
+ * (nothing enqueued); other errors as tq_linear.  Every call on a device
+ * shares that device's array: calls that overlap in time on one device
+ * (different streams without ordering, or several host threads) race and
+ * give undefined results.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+tq_status tq_linear_noalloc(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                            const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,
+                            hipStream_t stream);
+
+/*
  * tq_linear_workspace_offsets -- where tq_linear keeps its intermediate
  * results inside the workspace, for inspection after a call:
  *   off[0] s_x (n fp32), off[1] activation codes: nibble-packed (n x d/2

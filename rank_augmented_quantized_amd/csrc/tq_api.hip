@@ -448,6 +448,81 @@ tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t 
   return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of tq_linear: its workspace is a file-scope device
+// array, so a caller that cannot allocate (code under graph capture, a tight
+// serving loop) passes only inputs and outputs.
+// ---------------------------------------------------------------------------
+namespace {
+
+// One array per device (each device that the library runs on holds its own
+// copy until the process ends).  In host code `noalloc_scratch` names a
+// host-side stand-in, not the device memory: the kernels are given the
+// address hipGetSymbolAddress returns for the current device, never the name.
+__device__ __attribute__((aligned(256))) uint8_t noalloc_scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+// Leading bytes of the scratch that hold the hand-off words and counters of
+// the layer's kernels (they must be zero before a call; every call leaves
+// them zero again).
+constexpr size_t kNoallocZeroBytes = 64 * 1024;
+constexpr int kMaxDevices = 64;
+
+__global__ void k_zero16(uint4* p, int n16) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = uint4{0, 0, 0, 0};
+}
+
+struct NoallocTable {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+NoallocTable& noalloc_table() {
+  static NoallocTable t;
+  return t;
+}
+
+// The scratch of the current device; on its first use on that device, its
+// address (hipGetSymbolAddress, with the device current) and one clear of its
+// counter bytes by a fill kernel on `stream` (a kernel, not a memset node,
+// so that a first call under graph capture records a plain kernel node).
+tq_status noalloc_scratch_ptr(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_ERR_HIP;
+  NoallocTable& t = noalloc_table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (!t.ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !p) return TQ_ERR_HIP;
+    const int n16 = (int)(kNoallocZeroBytes / 16);
+    hipLaunchKernelGGL(k_zero16, dim3((n16 + 255) / 256), dim3(256), 0, stream, (uint4*)p, n16);
+    if (hipGetLastError() != hipSuccess) return TQ_ERR_HIP;
+    t.ptr[dev] = p;
+  }
+  *out = t.ptr[dev];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_linear_noalloc(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                            const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,
+                            hipStream_t stream) {
+  // the checks of tq_linear, with a stand-in workspace pointer (never used)
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, (void*)X);
+  if (st != TQ_OK || n == 0) return st;
+  const size_t need = linear_ws(n, d, m, r_padded(r)).total;
+  if (need > (size_t)TQ_NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const tq_status sp = noalloc_scratch_ptr(stream, &ws);
+  if (sp != TQ_OK) return sp;
+  const int64_t ms[1] = {m};
+  return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, need, stream);
+}
+
 tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                           const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
                           size_t ws_bytes, int32_t* acc, hipStream_t stream) {

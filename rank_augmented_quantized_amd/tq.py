@@ -32,8 +32,10 @@ EXPORTS = (
     "tq_linear_qlr_workspace_offsets", "tq_linear_qlr", "tq_weight_colsum", "tq_linear_mp_asym_workspace_bytes",
     "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits", "tq_linear_asym_workspace_bytes",
     "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
-    "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug",
+    "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug", "tq_linear_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TQ_NOALLOC_SCRATCH_BYTES of include/tq.h
 
 
 class TQError(RuntimeError):
@@ -110,6 +112,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                          ptr, sz, ptr, ptr, ptr]),
         "tq_linear_qlr_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr, ptr,
                                      ptr]),
+        "tq_linear_noalloc": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -220,6 +223,16 @@ def tq_linear(X, w_codes, s_w, lowrank, m: int, r: int, y_dtype=torch.bfloat16, 
     else:
         _check("tq_linear_debug", lib.tq_linear_debug(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
                                                       _p(Y), _dt(Y), _p(ws), ws.numel(), _p(acc), _stream(X)))
+    return Y
+
+
+def tq_linear_noalloc(X, w_codes, s_w, lowrank, m: int, r: int, Y):
+    """tq_linear with the library's own device scratch instead of a workspace (no allocation: Y is passed in)."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, lowrank, Y)
+    n, d = X.shape
+    _check("tq_linear_noalloc", lib.tq_linear_noalloc(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
+                                                      _p(Y), _dt(Y), _stream(X)))
     return Y
 
 

@@ -188,12 +188,15 @@ size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
  *            zero again, and the rest is scratch whose contents on entry are
  *            ignored.  Calls that share a workspace must be ordered (one
  *            stream, or synchronised streams).
- * For n <= 32 the call runs a memory-bound path (weight codes streamed once;
- * for n <= 2 and d <= 4096 in one launch, whose weight-streaming blocks
- * wait for the blocks that compute T with a bounded wait that sets the third
- * word at off[3] of tq_linear_workspace_offsets instead of hanging);
- * otherwise a tiled MFMA path.  All paths produce bit-identical integer
- * accumulators.
+ * For n <= 32 the call runs a memory-bound path (weight codes streamed once).
+ * For n <= 2, d <= 16384 and n d <= 16384 (and at most 128 partial blocks of
+ * T: ceil(d / 512) r_pad / 16 <= 128) that path is one launch, whose
+ * weight-streaming blocks read partials of T that other blocks of the same
+ * launch store; their waits are bounded: a wait that gives up sets word 32 of
+ * the hand-off words (off[3] of tq_linear_workspace_offsets), writes NaN to
+ * the block's outputs, and every later call on that workspace writes NaN
+ * everywhere until it is zero-filled again.  Otherwise a tiled MFMA path.
+ * All paths produce bit-identical integer accumulators.
  */
 tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                     const void* w_codes, const float* s_w, const void* lowrank,
@@ -227,9 +230,10 @@ tq_status tq_linear_noalloc(const void* X, tq_dtype x_dt, int64_t n, int64_t d, 
  *   bytes listing, for every 8 consecutive k, the 4 even-k codes and then
  *   the 4 odd-k codes (the order in which the tile GEMM consumes them),
  *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
- *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words of
- *   the one-launch path (all zero between calls; the third word is set if a
- *   wait hit its limit).
+ *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words:
+ *   word 0 the call counter of the one-launch path (advanced by one per
+ *   call), word 16 a counter that is zero between calls, word 32 the
+ *   wait-limit flag (zero unless a wait gave up).
  *   Returns TQ_ERR_SHAPE for invalid sizes.
  */
 tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]);
@@ -478,6 +482,19 @@ tq_status tq_linear_mp_asym_debug(const void* Xrot, tq_dtype x_dt, int64_t n, in
 tq_status tq_linear_qlr_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                               const void* w_codes, const float* s_w, const void* lowrank_q, void* Y, tq_dtype y_dt,
                               void* ws, size_t ws_bytes, int32_t* acc, int32_t* acc2, hipStream_t stream);
+
+/*
+ * tq_debug_linear_handoff -- test hook of the one-launch few-token path: runs
+ * tq_linear (same checks and workspace) with its waits limited to `spin`
+ * polls and, when `silent` is non-zero, with the blocks that compute T
+ * tagging their results with the previous call's tag, so that every wait
+ * gives up and the failure path runs (Y all NaN, the flag word set).  Every
+ * kernel still exits.  TQ_ERR_SHAPE when the shape does not take that path
+ * or r == 0.
+ */
+tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                                  const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,
+                                  void* ws, size_t ws_bytes, unsigned spin, int silent, hipStream_t stream);
 
 /*
  * Kernel timing.  While enabled, every kernel the library launches is

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
-SOURCES = ["tq_api.hip", "tq_quant.hip", "tq_gemm.hip", "tq_gemm8.hip", "tq_small.hip", "tq_rht.hip", "tq_qlr.hip", "tq_asym.hip"]
+SOURCES = ["tq_api.hip", "tq_quant.hip", "tq_gemm.hip", "tq_gemm8.hip", "tq_decode.hip", "tq_rht.hip", "tq_qlr.hip", "tq_asym.hip"]
 ARCH = "gfx950"
 
 

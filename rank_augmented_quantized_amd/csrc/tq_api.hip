@@ -112,25 +112,24 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
 struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;  // columns of T
-  bool small, fused;
+  bool small, decode;
   tq::ProloguePlan plan;
-  tq::SmallPlan splan;
+  tq::DecodePlan dplan;
 };
 
 // tcols: columns of T (r_pad of one layer; a power of two covering all the
-// layers of a group)
+// layers of a group); rp: one layer's r_pad (0: tcols)
 // two_launch: never the one-launch few-token kernel (the asymmetric layer)
-LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_launch = false) {
-  (void)m;
+LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_launch = false, int64_t rp = -1) {
   LinearWs w{};
   w.small = n <= kSmallN;
   w.r_pad = (int)tcols;
-  w.fused = !two_launch && w.small && n > 0 && tq::small_fused_ok((int)n, (int)d, w.r_pad);
+  w.decode = !two_launch && n > 0 && tq::decode_ok((int)n, (int)d, w.r_pad);
   size_t psize = 0;
   int counters = 0;
-  if (w.fused) {
-    w.splan = tq::plan_small((int)n, (int)d, w.r_pad);
-    psize = (size_t)w.splan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
+  if (w.decode) {
+    w.dplan = tq::plan_decode((int)n, (int)d, (int)m, (int)(rp < 0 ? tcols : rp), w.r_pad, false);
+    psize = tq::decode_partials_bytes(w.dplan, (int)n, w.r_pad);
   } else {
     w.plan = tq::plan_prologue((int)n, (int)d, w.r_pad, w.small,
                                w.small ? tq::gemv_max_chunks((int)n, (int)(d / 2), w.r_pad) : 1);
@@ -320,11 +319,22 @@ namespace {
 // arguments are checked: ms[g] channels per layer, m = their sum.
 // acc: when not null, the kernels' exact int32 residual sums (n x m) are
 // also stored there (test hook).
+// Test hook of the one-launch few-token path: its polls' limit, and producers
+// that tag their partials with the previous call's epoch.
+struct HandoffDebug {
+  unsigned spin;
+  int silent;
+};
+// Polls of a wait before it gives up: each is a memory round trip, so this
+// is a fraction of a second.
+constexpr unsigned kDecodeSpin = 1u << 18;
+
 tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r, int G,
                      const int64_t* ms, const void* w_codes, const float* s_w, const void* lowrank, void* Y,
-                     tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream, int32_t* acc = nullptr) {
+                     tq_dtype y_dt, void* ws, size_t ws_bytes, hipStream_t stream, int32_t* acc = nullptr,
+                     const HandoffDebug* dbg = nullptr) {
   const int rp = (int)r_padded(r);
-  const LinearWs L = linear_ws(n, d, m, group_tcols(G, r));
+  const LinearWs L = linear_ws(n, d, m, group_tcols(G, r), false, rp);
   if (ws_bytes < L.total) return TQ_ERR_WORKSPACE;
 
   uint8_t* base = (uint8_t*)ws;
@@ -340,8 +350,8 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   groups.n = G;
   for (int g = 0; g < G; ++g) groups.start[g + 1] = groups.start[g] + (int)ms[g];
 
-  if (L.fused) {
-    tq::SmallArgs a{};
+  if (L.decode) {
+    tq::DecodeArgs a{};
     a.X = X;
     a.n = (int)n;
     a.d = (int)d;
@@ -351,13 +361,14 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
     a.L1t = L1t;
     a.L2t = L2t;
     a.r_pad = rp;
+    a.lrp = 0;
+    while ((1 << a.lrp) < rp) ++a.lrp;
     a.ldt = L.r_pad;
     a.groups = groups;
-    a.nt = L.splan.nt;
-    a.nchunk = L.splan.nchunk;
-    a.kc = L.splan.kc;
-    a.qs = L.splan.qs;
-    a.nqg = L.splan.nqg;
+    a.nt = L.dplan.nt;
+    a.nqg = L.dplan.nqg;
+    a.kcs = L.dplan.kcs;
+    a.nchunk = L.dplan.nchunk;
     a.xc = xc;
     a.sx = sx;
     a.P = P;
@@ -366,7 +377,9 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
     a.Y = Y;
     a.y_bf16 = y_dt == TQ_BF16;
     a.acc = acc;
-    TQ_RUN("linear_small", stream, tq::launch_linear_small(a, xb, stream));
+    a.spin = dbg ? dbg->spin : kDecodeSpin;
+    a.silent = dbg ? dbg->silent : 0;
+    TQ_RUN("decode", stream, tq::launch_decode(a, L.dplan, xb, stream));
     return TQ_OK;
   }
 
@@ -521,6 +534,17 @@ tq_status tq_linear_noalloc(const void* X, tq_dtype x_dt, int64_t n, int64_t d, 
   if (sp != TQ_OK) return sp;
   const int64_t ms[1] = {m};
   return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, need, stream);
+}
+
+tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
+                                  const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,
+                                  void* ws, size_t ws_bytes, unsigned spin, int silent, hipStream_t stream) {
+  const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
+  if (st != TQ_OK || n == 0) return st;
+  if (r == 0 || !linear_ws(n, d, m, r_padded(r)).decode) return TQ_ERR_SHAPE;  // no hand-off on this path
+  const int64_t ms[1] = {m};
+  const HandoffDebug dbg{spin, silent};
+  return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream, nullptr, &dbg);
 }
 
 tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,

@@ -258,6 +258,70 @@ __device__ __forceinline__ uint2 pack_bytes(const int (&c)[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct HBM -> LDS loads (gfx950 buffer_load ... lds).
+// ---------------------------------------------------------------------------
+// Raw (stride 0) buffer resource over [base, base + bytes); loads at offsets
+// at or past `bytes` return zeros.  Word 3 is the gfx9-family dword format.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+constexpr int kOutOfRange = (int)0x80000000;  // voffset that no buffer here reaches
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 x lane
+// (buffer_load_dwordx4 ... lds, LDS base in M0).  Written as asm so that the
+// compiler does not track it: its own tracking would wait for every
+// outstanding direct load before any LDS read.  Completion is waited for
+// explicitly (wait_vmcnt); the data goes to LDS, so no VGPR is written.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+// load_lds16 at agent scope (sc1: past the XCD's L2), for words that other
+// blocks write during the launch
+__device__ __forceinline__ void load_lds16_sc1(i32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+// 4 bytes per lane into LDS at lds + 4 x lane; sc1: read at agent scope (past
+// the XCD's L2), for words that other blocks or earlier launches write
+__device__ __forceinline__ void load_lds4_sc1(i32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen sc1 lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
 // INT4 -> INT8 for the int8 MFMA: the nibble of every byte is moved to the
 // byte's high half, so each int8 lane holds 16 * code exactly.  Both operands
 // are scaled the same way, so products carry a factor 256 that the epilogue

@@ -43,32 +43,6 @@
 namespace tq {
 namespace {
 
-// Raw (stride 0) buffer resource over [base, base + bytes); loads at offsets
-// at or past `bytes` return zeros.  Word 3 is the gfx9-family dword format.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  i32x4 r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
-  r[2] = (int)bytes;
-  r[3] = 0x00020000;
-  return r;
-}
-constexpr int kOutOfRange = (int)0x80000000;  // voffset that no buffer here reaches
-
-// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 x lane
-// (buffer_load_dwordx4 ... lds, LDS base in M0).  Written as asm so that the
-// compiler does not track it: its own tracking would wait for every
-// outstanding direct load before any LDS read.  Completion is waited for
-// explicitly (wait_vmcnt); the data goes to LDS, so no VGPR is written.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, int voff, int soff) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %2, %3 offen lds"
-      :
-      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory", "m0");
-}
 // Workgroup barrier without the memory-model fences of __syncthreads (which
 // would wait for all outstanding vector memory operations); the memory
 // clobber keeps the compiler from moving LDS accesses across it.
@@ -78,13 +52,6 @@ __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "
 // slot c ^ psw(r); any 8 or 16 consecutive rows read one chunk each on
 // distinct banks.
 __device__ __forceinline__ int psw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // KF: every row's code bytes are a whole number of stages, so no direct load
 // needs the per-lane end-of-row test (which costs VALU slots next to the MFMAs)

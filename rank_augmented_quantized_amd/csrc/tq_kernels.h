@@ -178,36 +178,8 @@ hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, int w_bits
 // Small-n integer GEMM (M <= 32).
 hipError_t launch_gemv(const GemmArgs& g, int bits, Epilogue epi, hipStream_t st);
 
-// One- or two-token layer in one launch (tq_small.hip): producers (T
-// partials) and consumers (16 output channels each) in one grid.
-struct SmallPlan {
-  int nt;      // T-partial blocks (nchunk x nqg)
-  int nchunk;  // k-chunks of T
-  int kc;      // k values per chunk
-  int qs;      // 16-column slices of T per block
-  int nqg;     // column groups
-};
-struct SmallArgs {
-  const void* X;
-  int n, d, m;
-  const uint8_t* wc;
-  const float* sw;
-  const bf16_t* L1t;   // ldt rows of d (all groups' L1^T)
-  const bf16_t* L2t;   // m x r_pad
-  int r_pad;           // per layer
-  int ldt;             // columns of T (and of the partials) over all groups
-  Groups groups;
-  int nt, nchunk, kc, qs, nqg;
-  uint8_t* xc;     // n x d/2 activation codes (written by the first consumer)
-  float* sx;       // n scales (idem)
-  float* P;        // nchunk x n x ldt fp32 partials of X L1
-  bf16_t* Tout;    // n x ldt: the bf16 T (the first consumer of each group, its columns)
-  unsigned* sync;  // hand-off words, kSyncBytes: [0] producers done, [2] wait-limit flag, consumer shard counters
-  void* Y;
-  int y_bf16;
-  int32_t* acc;  // test hook: when not null, the exact int32 sums of the residual product (n x m)
-};
-constexpr int kSyncBytes = 4096;  // workspace bytes of the hand-off words
+// Workspace bytes of the hand-off words of the one-launch few-token path.
+constexpr int kSyncBytes = 4096;
 
 // Online block-Hadamard rotation of the two-subspace quantiser: the packed
 // rotation holds the signs as bits (d / 8 bytes, padded to 16) and then, for
@@ -244,8 +216,53 @@ hipError_t launch_quant_rows_asym(const void* X, bool bf16, int n, int d, int dl
                                   void* xh, float* sh, float* zh, hipStream_t st, bool packed = false);
 // colsum[j] = sum over k of code row j (m rows of k codes, 4 or 8 bits).
 hipError_t launch_weight_colsum(const void* codes, int bits, int m, int k, int32_t* colsum, hipStream_t st);
-bool small_fused_ok(int n, int d, int r_pad);
-SmallPlan plan_small(int n, int d, int r_pad);
-hipError_t launch_linear_small(const SmallArgs& a, bool x_bf16, hipStream_t st);
+
+
+// Few-token layer (one or two tokens) in one launch (tq_decode.hip): the
+// first nt blocks compute one fp32 partial of T = X L1 each (16 columns, one
+// k-chunk); every other block owns gpb groups of 16 output channels; the
+// partials cross blocks as tagged words.
+constexpr int kDecodeMaxN = 2;
+constexpr int kDecodeMaxD = 16384;
+constexpr int kDecodeSteps = 2;  // 32-k steps per wave in a partial of T (a chunk: 512 k values)
+struct DecodePlan {
+  int gpb;         // 16-channel groups per channel block (1 .. 4)
+  int nqg;         // 16-column groups of T
+  int kcs;         // 32-k steps per chunk of T
+  int nchunk;      // chunks of T
+  int nt;          // blocks that compute a partial (nchunk x nqg)
+  int ncons;       // channel blocks
+  int blocks;      // grid: nt + ncons
+  unsigned lds;    // dynamic LDS bytes
+  unsigned lds_a;  // bytes of the LDS region reused across phases
+};
+struct DecodeArgs {
+  const void* X;
+  int n, d, m;
+  const uint8_t* wc;
+  const float* sw;
+  const bf16_t* L1t;  // ldt rows of d (every layer's L1^T)
+  const bf16_t* L2t;  // m x r_pad
+  int r_pad;          // per layer (a power of two, or 0)
+  int lrp;            // log2(r_pad)
+  int ldt;            // columns of T over all layers
+  Groups groups;
+  int nt, nqg, kcs, nchunk;
+  uint8_t* xc;     // n x d / 2 activation codes (written by the first channel block)
+  float* sx;       // n scales (idem)
+  void* P;         // nchunk x n x ldt tagged 64-bit words {partial of T, epoch}, layer-major
+  bf16_t* Tout;    // n x ldt: T as bf16 (written by the first block of each layer)
+  unsigned* sync;  // hand-off words (kSyncBytes)
+  void* Y;
+  int y_bf16;
+  int32_t* acc;    // test hook: the exact int32 sums of the residual product (n x m)
+  unsigned spin;   // polls before a wait gives up
+  int silent;      // test hook: partials carry the previous call's tag, so every wait gives up
+  int gpb, ncons, lds_a;  // set by launch_decode from the plan
+};
+bool decode_ok(int n, int d, int ldt);
+DecodePlan plan_decode(int n, int d, int m, int r_pad, int ldt, bool x_bf16);
+size_t decode_partials_bytes(const DecodePlan& p, int n, int ldt);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, bool x_bf16, hipStream_t st);
 
 }  // namespace tq

@@ -33,6 +33,7 @@ EXPORTS = (
     "tq_linear_mp_asym_workspace_offsets", "tq_linear_mp_asym", "tq_linear_mp_bits", "tq_linear_asym_workspace_bytes",
     "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
     "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug", "tq_linear_noalloc",
+    "tq_debug_linear_handoff",
 )
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TQ_NOALLOC_SCRATCH_BYTES of include/tq.h
@@ -113,6 +114,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_qlr_debug": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr, ptr,
                                      ptr]),
         "tq_linear_noalloc": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr]),
+        "tq_debug_linear_handoff": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz,
+                                         ctypes.c_uint, c_int, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -233,6 +236,17 @@ def tq_linear_noalloc(X, w_codes, s_w, lowrank, m: int, r: int, Y):
     n, d = X.shape
     _check("tq_linear_noalloc", lib.tq_linear_noalloc(_p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank),
                                                       _p(Y), _dt(Y), _stream(X)))
+    return Y
+
+
+def tq_debug_linear_handoff(X, w_codes, s_w, lowrank, m: int, r: int, Y, ws, spin: int, silent: bool):
+    """tq_linear with the one-launch path's waits limited to ``spin`` polls (and, if ``silent``, never satisfied)."""
+    lib = load()
+    _need_cuda(X, w_codes, s_w, lowrank, Y, ws)
+    n, d = X.shape
+    _check("tq_debug_linear_handoff", lib.tq_debug_linear_handoff(
+        _p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(), spin,
+        1 if silent else 0, _stream(X)))
     return Y
 
 

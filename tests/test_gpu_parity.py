@@ -317,17 +317,26 @@ def test_linear_r0_is_pure_w4a4_and_deterministic():
 
 
 def _sync_words(ws, n, d, m, r):
-    """The hand-off words of the one-launch path (counters and the wait-limit flag; 4 KiB)."""
+    """The hand-off words (4 KiB): word 0 the one-launch path's call counter, word 16 a counter that is zero between
+    calls, word 32 the wait-limit flag."""
     off = tq.tq_linear_workspace_offsets(n, d, m, r)["sync"]
     return ws[off: off + 4096].view(torch.int32).cpu().numpy()
 
 
+def _one_launch(n, d, r):
+    """Shapes of the one-launch few-token path (include/tq.h): one or two tokens, d a multiple of 32 up to 16384,
+    n d <= 16384, and at most 128 blocks computing partials of T (chunks of 512 k times r_pad / 16 column groups)."""
+    nt = -(-d // 512) * (_r_pad(r) // 16)
+    return n <= 2 and n * d <= 16384 and d <= 16384 and d % 32 == 0 and nt <= 128
+
+
 @pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 2048, 200, 64), (1, 4064, 64, 32), (2, 512, 40, 0),
-                                     (2, 1024, 48, 256), (1, 14336, 64, 32), (5, 2048, 200, 64)])
+                                     (2, 1024, 48, 256), (1, 14336, 64, 32), (1, 16384, 40, 32), (1, 16384, 40, 256), (2, 8192, 72, 32),
+                                     (1, 96, 16, 32), (5, 2048, 200, 64)])
 def test_small_n_single_launch_handoff(n, d, m, r):
-    """One or two tokens (d <= 4096) run in one launch whose consumers wait for its producers: every call leaves the
-    hand-off counters at zero, the wait never hits its limit, and calls repeated on one workspace give identical
-    outputs (the d = 14336 and n = 5 cases take the two-launch path and must leave the words untouched)."""
+    """One or two tokens run in one launch whose blocks wait for the partials of T that other blocks compute: every
+    call advances the call counter by one and leaves the other words at zero (no wait gave up), and calls repeated on
+    one workspace give identical outputs (n = 5 takes the two-launch path and leaves the words untouched)."""
     print(f"case n={n} d={d} m={m} r={r}", flush=True)
     c = draw_custom(n, d, m, max(r, 1), seed=90 + n)
     wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
@@ -335,14 +344,45 @@ def test_small_n_single_launch_handoff(n, d, m, r):
     ws = tq.linear_workspace(n, d, m, r, DEV)
     x = _x_tensor(c["X"], "bf16")
     ys = []
-    for _ in range(4):
+    for call in range(4):
         ys.append(tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws))
         torch.cuda.synchronize()
-        assert not _sync_words(ws, n, d, m, r).any()
+        w = _sync_words(ws, n, d, m, r)
+        assert w[0] == (call + 1 if _one_launch(n, d, r) else 0)
+        assert not w[1:].any()
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
     ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"] if r else None, c["L2"] if r else None)
     _assert_y(ys[0], ref["Y"], f"n{n}")
+
+
+@pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 8192, 40, 32)])
+def test_handoff_gives_up_loudly(n, d, m, r):
+    """The one-launch path's failure mode, forced from the host: the blocks computing T tag their partials with the
+    previous call's tag and the waits are limited to a few polls, so every wait gives up (every kernel still exits).
+    Y is then NaN everywhere and the flag word is set; later calls on that workspace keep writing NaN (the flag is
+    sticky), and once the workspace is zero-filled a call gives the correct Y again."""
+    print(f"case n={n} d={d} m={m} r={r}", flush=True)
+    c = draw_custom(n, d, m, r, seed=70 + n)
+    wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+    lowrank = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+    ws = tq.linear_workspace(n, d, m, r, DEV)
+    x = _x_tensor(c["X"], "bf16")
+    y = torch.zeros((n, m), dtype=torch.bfloat16, device=DEV)
+    tq.tq_debug_linear_handoff(x, wc, sw, lowrank, m, r, y, ws, spin=16, silent=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+    w = _sync_words(ws, n, d, m, r)
+    assert w[32] != 0 and w[16] == 0 and w[0] == 1
+    y2 = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y2).all()
+    ws.zero_()
+    y3 = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws)
+    torch.cuda.synchronize()
+    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
+    _assert_y(y3, ref["Y"], "after zero-fill")
+    assert not _sync_words(ws, n, d, m, r)[1:].any()
 
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 2048, 300, 64), (16, 1024, 200, 32), (40, 512, 96, 32),
@@ -374,7 +414,7 @@ def test_graph_replay_matches_eager(n, d, m, r):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_e), f"replay {rep}"
-        assert not _sync_words(ws_g, n, d, m, r).any()
+        assert not _sync_words(ws_g, n, d, m, r)[1:].any()
         y_again = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws_e)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y_again, y_e)

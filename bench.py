@@ -284,6 +284,32 @@ class MpCase:
                                  ws=self.ws, bits=self.bits)
 
 
+def stream_ceiling(torch, tq, dev, copies):
+    """Read bandwidth of tq_debug_stream_read (the decode kernel's loads, nothing else): the weight codes of the
+    Llama-3-8B MLP layers (29.4 MB, `copies` buffers cycled so that the last-level cache cannot serve them) and
+    1 GiB, in GB/s."""
+    out = []
+    for nbytes, ncopy, blocks in ((4096 * 14336 // 2, copies, 1024), (1 << 30, 1, 4096)):
+        bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(i + 1) for i in range(ncopy)]
+        words = torch.empty(blocks, dtype=torch.int32, device=dev)
+        for i in range(5):
+            tq.tq_debug_stream_read(bufs[i % ncopy], words, blocks)
+        torch.cuda.synchronize()
+        steps = 64
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            tq.tq_debug_stream_read(bufs[i % ncopy], words, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out.append({"bytes": nbytes, "copies": ncopy, "blocks": blocks, "us": round(us, 2),
+                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        del bufs, words
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, rows, seconds):
     """The oracle as it stands, timed on the host: the layer on the first `rows` tokens, repeated until about
     `seconds` of CPU work have been timed."""
@@ -321,6 +347,9 @@ def main():
     ap.add_argument("--copies", type=int, default=16, help="weight copies cycled through (defeats the MALL)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="tokens of the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time to accumulate (repetitions)")
+    ap.add_argument("--n", type=int, default=0, help="tokens of the main workload (default: the workload's own)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only measure the streaming-read ceiling (tq_debug_stream_read) and print it")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scales rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -348,22 +377,31 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
         return
     tq.load()
+    if args.stream_ceiling:
+        print(json.dumps({"stream_ceiling": stream_ceiling(torch, tq, dev, args.copies)}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
-    n, d, m, r = wl.n, wl.d, wl.m, wl.r
+    n, d, m, r = args.n or wl.n, wl.d, wl.m, wl.r
 
-    log(f"[bench] {wl.title}: building inputs")
-    case = LinearCase(wl, n, 2, torch, tq, dev)
+    log(f"[bench] {wl.title} n={n}: building inputs")
+    if wl.name == "two_subspace":  # the two-subspace layer (tq_linear_mp) on its own shape
+        case = MpCase(wl, torch, tq, dev)
+        n = wl.n
+    else:
+        case = LinearCase(wl, n, args.copies if n <= 256 else 2, torch, tq, dev)
     ms = time_calls(case, args.steps, args.warmup, torch)
     ops = 2.0 * n * d * m
     value = ops / (ms * 1e-3) / 1e12
     log(f"[bench] {wl.title}: {ms * 1e3:.1f} us/call, {value:.1f} TOPS")
     kms = kernel_ms(case, args.steps, torch, tq)
-    gemm = kms.get("gemm_w4a4") or max(kms.values())
+    gname = "gemm_w4a4" if "gemm_w4a4" in kms else max(kms, key=kms.get)
+    gemm = kms[gname]
     achieved = ops / (gemm * 1e-3) / 1e12
     khash = kernel_source_hash()
     traffic = read_traffic(khash)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic, "kernel": "gemm_w4a4",
+                "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic if (gname == "gemm_w4a4" and wl.name == "attn_proj" and n == wl.n) else None,
+                "kernel": gname,
                 "kernel_us": round(gemm * 1e3, 2),
                 "kernels_us": {k: round(v * 1e3, 2) for k, v in kms.items()}}
     log(f"[bench] kernels: {roofline['kernels_us']}")
@@ -472,6 +510,9 @@ def main():
             del c
             torch.cuda.empty_cache()
 
+    ceiling = None if args.no_sweep else stream_ceiling(torch, tq, dev, args.copies)
+    if ceiling:
+        log(f"[bench] streaming-read ceiling {ceiling}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} tokens")
@@ -484,7 +525,8 @@ def main():
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": wl.title, "n": n, "d": d, "m": m, "r": r, "x_dtype": wl.x_dtype, "y_dtype": "bf16",
                    "pct_int8_mfma_peak": round(100 * value / PEAK_INT8_TOPS, 2)},
-        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "kernel_source_hash": khash,
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "stream_ceiling": ceiling,
+        "kernel_source_hash": khash,
     }
     print(json.dumps(out), flush=True)
 

@@ -497,6 +497,19 @@ tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64
                                   void* ws, size_t ws_bytes, unsigned spin, int silent, hipStream_t stream);
 
 /*
+ * tq_debug_stream_read -- the streaming-read ceiling that bounds the
+ * few-token (decode) kernel (TwinQuant notes, section 04.C: at decode sizes
+ * the layer streams the INT4 weight codes once): reads `bytes` of device
+ * memory at `buf` (16-byte aligned, bytes a multiple of 16) exactly once with
+ * the decode kernel's 16-byte non-temporal loads, `blocks` blocks of 256
+ * threads each reading a contiguous slab, and writes one XOR of what each
+ * block read to out[0 .. blocks - 1] (device, caller-owned).  Kernel timing
+ * names it "stream_read".  TQ_ERR_NULL / TQ_ERR_ALIGN / TQ_ERR_SHAPE (blocks
+ * outside 1 .. 65536) before anything is enqueued.
+ */
+tq_status tq_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t stream);
+
+/*
  * Kernel timing.  While enabled, every kernel the library launches is
  * bracketed by a pair of HIP events recorded on the launch stream.
  * tq_profile_read synchronises on the recorded events and returns, per kernel

@@ -547,6 +547,14 @@ tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64
   return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream, nullptr, &dbg);
 }
 
+tq_status tq_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t stream) {
+  if (!buf || !out) return TQ_ERR_NULL;
+  if (!aligned16(buf) || bytes % 16) return TQ_ERR_ALIGN;
+  if (blocks < 1 || blocks > 65536) return TQ_ERR_SHAPE;
+  TQ_RUN("stream_read", stream, tq::launch_stream_read(buf, bytes, out, blocks, stream));
+  return TQ_OK;
+}
+
 tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                           const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
                           size_t ws_bytes, int32_t* acc, hipStream_t stream) {

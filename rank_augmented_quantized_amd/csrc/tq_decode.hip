@@ -530,4 +530,41 @@ hipError_t launch_decode(const DecodeArgs& args, const DecodePlan& p, bool x_bf1
   return a.n == 1 ? launch_nr<float, 1>(a, q, st) : launch_nr<float, 2>(a, q, st);
 }
 
+// ---------------------------------------------------------------------------
+// The streaming-read ceiling that bounds the decode kernel: `bytes` read once
+// with the same 16-byte non-temporal loads, 8 in flight per lane, each block
+// a contiguous slab; every block XORs what it read and writes one word, so
+// the loads cannot be dropped.
+// ---------------------------------------------------------------------------
+namespace {
+__global__ __launch_bounds__(256) void k_stream_read(const i32x4* __restrict__ p, size_t n16, uint32_t* out) {
+  __shared__ uint32_t acc_s;
+  if (threadIdx.x == 0) acc_s = 0;
+  __syncthreads();
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * per, end = n16 < beg + per ? n16 : beg + per;
+  i32x4 acc = {0, 0, 0, 0};
+  for (size_t i = beg + threadIdx.x; i < end; i += 256 * 8) {
+    i32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t j = i + 256 * (size_t)u;
+      v[u] = j < end ? __builtin_nontemporal_load(p + j) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  atomicXor(&acc_s, (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]));
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = acc_s;
+}
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t st) {
+  if (bytes % 16 || blocks < 1) return hipErrorInvalidValue;
+  launch_kernel(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<const i32x4*>(buf), bytes / 16,
+                out);
+  return hipGetLastError();
+}
+
 }  // namespace tq

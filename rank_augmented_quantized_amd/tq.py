@@ -34,6 +34,7 @@ EXPORTS = (
     "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
     "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug", "tq_linear_noalloc",
     "tq_debug_linear_handoff",
+    "tq_debug_stream_read",
 )
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TQ_NOALLOC_SCRATCH_BYTES of include/tq.h
@@ -116,6 +117,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_noalloc": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr]),
         "tq_debug_linear_handoff": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz,
                                          ctypes.c_uint, c_int, ptr]),
+        "tq_debug_stream_read": (st, [ptr, sz, ptr, c_int, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -248,6 +250,18 @@ def tq_debug_linear_handoff(X, w_codes, s_w, lowrank, m: int, r: int, Y, ws, spi
         _p(X), _dt(X), n, d, m, r, _p(w_codes), _p(s_w), _p(lowrank), _p(Y), _dt(Y), _p(ws), ws.numel(), spin,
         1 if silent else 0, _stream(X)))
     return Y
+
+
+def tq_debug_stream_read(buf, out, blocks: int):
+    """Read all of ``buf`` (a CUDA tensor, whole number of 16-byte units) once with the decode kernel's loads;
+    ``out``: an int32 CUDA tensor of at least ``blocks`` elements (one XOR per block)."""
+    lib = load()
+    _need_cuda(buf, out)
+    nbytes = buf.numel() * buf.element_size()
+    if out.numel() < blocks:
+        raise ValueError("out holds fewer words than blocks")
+    _check("tq_debug_stream_read", lib.tq_debug_stream_read(_p(buf), nbytes, _p(out), blocks, _stream(buf)))
+    return out
 
 
 def tq_linear_mp_workspace_bytes(n: int, d: int, d_hi: int) -> int:

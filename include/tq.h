@@ -30,7 +30,8 @@
  *  - Every pointer is a DEVICE pointer (memory of the current HIP device),
  *    except where stated.  The caller owns all memory; the library never
  *    allocates device memory and keeps no state between calls except the
- *    optional profiling record (tq_profile_*).
+ *    optional profiling record (tq_profile_*, guarded by a lock) and the
+ *    file-scope scratch array of tq_linear_noalloc.
  *  - Every call is asynchronous on `stream` (0 = the null stream).  A status
  *    other than TQ_OK from argument checking means nothing was enqueued.
  *    TQ_ERR_HIP reports a launch failure (hipGetLastError after the launch);
@@ -169,7 +170,7 @@ tq_status tq_linear_group(const void* X, tq_dtype x_dt, int64_t n, int64_t d, co
 tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int bits,
                           void* x_codes, float* s_x, hipStream_t stream);
 
-/* Workspace bytes tq_linear needs for these sizes. */
+/* Workspace bytes tq_linear needs for these sizes (0 for shapes tq_linear rejects). */
 size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
 
 /*
@@ -515,7 +516,9 @@ tq_status tq_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int
  * tq_profile_read synchronises on the recorded events and returns, per kernel
  * name, the number of launches and their summed duration in milliseconds
  * (host arrays of `max` entries; returns the number of kernel names, or a
- * negative tq_status).  tq_profile_reset drops the record.  Not thread-safe.
+ * negative tq_status).  tq_profile_reset drops the record.  The record is
+ * process-wide (one lock guards it); calls from several threads interleave
+ * their entries.
  */
 typedef struct {
   char name[48];

@@ -307,7 +307,7 @@ tq_status tq_quantize_act(const void* X, tq_dtype x_dt, int64_t n, int64_t d, in
 }
 
 size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r) {
-  if (n < 0 || d <= 0 || m <= 0 || r < 0 || r > 256) return 0;
+  if (n < 0 || n > kMaxDim || d <= 0 || d > kMaxK || d % 32 || m <= 0 || m > kMaxDim || r < 0 || r > 256) return 0;
   return linear_ws(n, d, m, r_padded(r)).total;
 }
 

@@ -318,3 +318,48 @@ def test_workspace_regions_fit_and_do_not_overlap(lib, n, d, m, r):
     check(lib.tq_linear_mp_asym_workspace_bytes(n, d, dh),
           [(off["s_xl"], 4 * n), (off["s_xh"], 4 * n), (off["x_codes_l"], n * (d - dh)), (off["x_codes_h"], n * dh),
            (off["z_xl"], 4 * n), (off["z_xh"], 4 * n)])
+
+
+def test_boundary_departures_are_enforced(lib):
+    """Each documented difference from the survey's boundary, checked where it is decided (before any HIP call)."""
+    n, m, r = 8, 256, 16
+    # d: a multiple of 32 (the MFMA k-step), not merely even
+    for d in (34, 48, 100, 4080):
+        need = lib.tq_linear_workspace_bytes(n, 4096, m, r)
+        assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, C, need, S) == -2, d
+    assert lib.tq_linear_workspace_bytes(n, 34, m, r) == 0
+    d = 512
+    need = lib.tq_linear_workspace_bytes(n, d, m, r)
+    # the low-rank factors come as one packed buffer (tq_pack_lowrank), NULL iff r == 0
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, NUL, B, 1, C, need, S) == -1
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, MIS, B, 1, C, need, S) == -5
+    # the workspace is caller-owned and sized by the query; one byte short is refused
+    assert lib.tq_linear(A, 1, n, d, m, r, B, C, A, B, 1, C, need - 1, S) == -6
+    # tq_linear_mp takes (n, d, m, d_hi) in the survey's order: d_hi past d, or not a multiple of 16, is a shape error
+    dh = 64
+    need_mp = lib.tq_linear_mp_workspace_bytes(n, d, dh)
+    assert lib.tq_linear_mp(A, 1, n, d, m, d + 16, B, C, A, B, B, 1, C, need_mp, S) == -2
+    assert lib.tq_linear_mp(A, 1, n, d, m, 40, B, C, A, B, B, 1, C, need_mp, S) == -2
+    assert lib.tq_linear_mp(A, 1, n, d, 0, dh, B, C, A, B, B, 1, C, need_mp, S) == -2
+    assert lib.tq_linear_mp(A, 1, 0, d, m, dh, NUL, NUL, NUL, NUL, NUL, 1, NUL, 0, S) == 0
+
+
+def test_stream_read_validation(lib):
+    out = ctypes.c_void_p(0x40000)
+    assert lib.tq_debug_stream_read(NUL, 1024, out, 4, S) == -1
+    assert lib.tq_debug_stream_read(A, 1024, NUL, 4, S) == -1
+    assert lib.tq_debug_stream_read(MIS, 1024, out, 4, S) == -5
+    assert lib.tq_debug_stream_read(A, 1000, out, 4, S) == -5  # bytes not a multiple of 16
+    assert lib.tq_debug_stream_read(A, 1024, out, 0, S) == -2
+    assert lib.tq_debug_stream_read(A, 1024, out, 70000, S) == -2
+
+
+def test_profiler_is_the_only_switchable_state(lib):
+    """Timing is off unless enabled; with nothing recorded the read returns no entries, and reset clears it."""
+    stats = (tqb.KernelStat * 8)()
+    assert lib.tq_profile_reset() == 0
+    assert lib.tq_profile_read(stats, 8) == 0
+    assert lib.tq_profile_enable(1) == 0
+    assert lib.tq_profile_read(stats, 8) == 0
+    assert lib.tq_profile_enable(0) == 0
+    assert lib.tq_profile_reset() == 0

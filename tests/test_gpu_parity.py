@@ -332,7 +332,9 @@ def _one_launch(n, d, r):
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 2048, 200, 64), (1, 4064, 64, 32), (2, 512, 40, 0),
                                      (2, 1024, 48, 256), (1, 14336, 64, 32), (1, 16384, 40, 32), (1, 16384, 40, 256), (2, 8192, 72, 32),
-                                     (1, 96, 16, 32), (5, 2048, 200, 64)])
+                                     (1, 96, 16, 32), (5, 2048, 200, 64), (3, 96, 16, 32), (16, 4096, 300, 64),
+                                     (8, 14336, 72, 64), (11, 4064, 130, 256), (16, 8192, 64, 32), (9, 16384, 40, 32),
+                                     (24, 2048, 200, 64)])
 def test_small_n_single_launch_handoff(n, d, m, r):
     """One or two tokens run in one launch whose blocks wait for the partials of T that other blocks compute: every
     call advances the call counter by one and leaves the other words at zero (no wait gave up), and calls repeated on

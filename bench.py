@@ -310,6 +310,31 @@ def stream_ceiling(torch, tq, dev, copies):
     return out
 
 
+def mfma_ceiling(torch, tq, dev):
+    """int8 rate of tq_debug_mfma_ceiling (8 independent 32x32x32 MFMA chains per wave on register operands, no
+    memory traffic): one and two blocks of 512 threads per compute unit, in TOP/s."""
+    out = []
+    iters = 256
+    for per_cu in (1, 2):
+        blocks = 256 * per_cu
+        words = torch.empty(512 * blocks, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            tq.tq_debug_mfma_ceiling(words, iters, blocks)
+        torch.cuda.synchronize()
+        steps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            tq.tq_debug_mfma_ceiling(words, iters, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        ops = 2.0 * 32 ** 3 * 8 * iters * blocks * 8  # 8 waves per block
+        out.append({"blocks_per_cu": per_cu, "iters": iters, "us": round(us, 2),
+                    "TOPs": round(ops / (us * 1e-6) / 1e12, 1), "frac_of_5000": round(ops / (us * 1e-6) / 5e15, 4)})
+    return out
+
+
 def cpu_baseline(wl, rows, seconds):
     """The oracle as it stands, timed on the host: the layer on the first `rows` tokens, repeated until about
     `seconds` of CPU work have been timed."""
@@ -350,6 +375,8 @@ def main():
     ap.add_argument("--n", type=int, default=0, help="tokens of the main workload (default: the workload's own)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only measure the streaming-read ceiling (tq_debug_stream_read) and print it")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only the int8 MFMA ceiling (tq_debug_mfma_ceiling), one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scales rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -379,6 +406,9 @@ def main():
     tq.load()
     if args.stream_ceiling:
         print(json.dumps({"stream_ceiling": stream_ceiling(torch, tq, dev, args.copies)}), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(torch, tq, dev)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     n, d, m, r = args.n or wl.n, wl.d, wl.m, wl.r
@@ -513,6 +543,9 @@ def main():
     ceiling = None if args.no_sweep else stream_ceiling(torch, tq, dev, args.copies)
     if ceiling:
         log(f"[bench] streaming-read ceiling {ceiling}")
+    mceiling = None if args.no_sweep else mfma_ceiling(torch, tq, dev)
+    if mceiling:
+        log(f"[bench] int8 MFMA ceiling {mceiling}")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_rows} tokens")
@@ -525,7 +558,7 @@ def main():
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": wl.title, "n": n, "d": d, "m": m, "r": r, "x_dtype": wl.x_dtype, "y_dtype": "bf16",
                    "pct_int8_mfma_peak": round(100 * value / PEAK_INT8_TOPS, 2)},
-        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "stream_ceiling": ceiling,
+        "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "stream_ceiling": ceiling, "mfma_ceiling": mceiling,
         "kernel_source_hash": khash,
     }
     print(json.dumps(out), flush=True)

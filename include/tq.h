@@ -511,6 +511,20 @@ tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64
 tq_status tq_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t stream);
 
 /*
+ * tq_debug_mfma_ceiling -- the int8 matrix-core ceiling that bounds the tile
+ * GEMM (TwinQuant notes, section 04.C and Figure 4: the residual product on
+ * the integer matrix units with int32 accumulation): `blocks` blocks of 512
+ * threads, each wave chaining `iters` rounds of 8 independent
+ * v_mfma_i32_32x32x32_i8 (2 x 32^3 operations each) on register operands,
+ * with no memory traffic inside the loop; every thread then writes one int
+ * to out[0 .. 512 blocks - 1] (device, caller-owned), so the work cannot be
+ * dropped.  Kernel timing names it "mfma_ceiling".  TQ_ERR_NULL /
+ * TQ_ERR_SHAPE (iters outside 1 .. 2^20, blocks outside 1 .. 65536) before
+ * anything is enqueued.
+ */
+tq_status tq_debug_mfma_ceiling(int iters, int blocks, int32_t* out, hipStream_t stream);
+
+/*
  * Kernel timing.  While enabled, every kernel the library launches is
  * bracketed by a pair of HIP events recorded on the launch stream.
  * tq_profile_read synchronises on the recorded events and returns, per kernel

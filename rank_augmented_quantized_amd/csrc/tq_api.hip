@@ -555,6 +555,13 @@ tq_status tq_debug_stream_read(const void* buf, size_t bytes, uint32_t* out, int
   return TQ_OK;
 }
 
+tq_status tq_debug_mfma_ceiling(int iters, int blocks, int32_t* out, hipStream_t stream) {
+  if (!out) return TQ_ERR_NULL;
+  if (iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536) return TQ_ERR_SHAPE;
+  TQ_RUN("mfma_ceiling", stream, tq::launch_mfma_ceiling(iters, blocks, out, stream));
+  return TQ_OK;
+}
+
 tq_status tq_linear_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                           const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt, void* ws,
                           size_t ws_bytes, int32_t* acc, hipStream_t stream) {

@@ -722,4 +722,34 @@ hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, int w_bits
   return hipErrorInvalidValue;
 }
 
+// The int8 MFMA ceiling that bounds the tile GEMM: every wave of `blocks`
+// blocks of 512 threads chains `iters` rounds of 8 independent
+// v_mfma_i32_32x32x32_i8 on register operands (no memory traffic, no LDS, no
+// barrier), then stores the sum of its accumulator lanes, one int per thread,
+// so the products stay live.
+__global__ __launch_bounds__(512) void k_mfma_ceiling(int iters, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const i32x4 a = {lane, lane + 1, lane + 2, lane + 3}, b = {3 * lane, lane, 7, lane ^ 5};
+  i32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[j], 0, 0, 0);
+  }
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += acc[j][i];
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = sum;
+}
+
+hipError_t launch_mfma_ceiling(int iters, int blocks, int32_t* out, hipStream_t st) {
+  launch_kernel(k_mfma_ceiling, dim3((unsigned)blocks), dim3(512), 0, st, iters, out);
+  return hipGetLastError();
+}
+
 }  // namespace tq

@@ -266,5 +266,6 @@ size_t decode_partials_bytes(const DecodePlan& p, int n, int ldt);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, bool x_bf16, hipStream_t st);
 // reads `bytes` (a multiple of 16) once with `blocks` blocks; out: one word per block
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, int blocks, hipStream_t st);
+hipError_t launch_mfma_ceiling(int iters, int blocks, int32_t* out, hipStream_t st);
 
 }  // namespace tq

@@ -34,7 +34,7 @@ EXPORTS = (
     "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
     "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug", "tq_linear_noalloc",
     "tq_debug_linear_handoff",
-    "tq_debug_stream_read",
+    "tq_debug_stream_read", "tq_debug_mfma_ceiling",
 )
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TQ_NOALLOC_SCRATCH_BYTES of include/tq.h
@@ -118,6 +118,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_debug_linear_handoff": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, c_int, ptr, sz,
                                          ctypes.c_uint, c_int, ptr]),
         "tq_debug_stream_read": (st, [ptr, sz, ptr, c_int, ptr]),
+        "tq_debug_mfma_ceiling": (st, [c_int, c_int, ptr, ptr]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -261,6 +262,17 @@ def tq_debug_stream_read(buf, out, blocks: int):
     if out.numel() < blocks:
         raise ValueError("out holds fewer words than blocks")
     _check("tq_debug_stream_read", lib.tq_debug_stream_read(_p(buf), nbytes, _p(out), blocks, _stream(buf)))
+    return out
+
+
+def tq_debug_mfma_ceiling(out, iters: int, blocks: int):
+    """Chain ``iters`` rounds of 8 int8 32x32x32 MFMAs per wave in ``blocks`` blocks of 512 threads;
+    ``out``: an int32 CUDA tensor of at least 512 ``blocks`` elements (one sum per thread)."""
+    lib = load()
+    _need_cuda(out)
+    if out.numel() < 512 * blocks:
+        raise ValueError("out holds fewer words than 512 x blocks")
+    _check("tq_debug_mfma_ceiling", lib.tq_debug_mfma_ceiling(iters, blocks, _p(out), _stream(out)))
     return out
 
 

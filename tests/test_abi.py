@@ -354,6 +354,15 @@ def test_stream_read_validation(lib):
     assert lib.tq_debug_stream_read(A, 1024, out, 70000, S) == -2
 
 
+def test_mfma_ceiling_validation(lib):
+    out = ctypes.c_void_p(0x40000)
+    assert lib.tq_debug_mfma_ceiling(16, 4, NUL, S) == -1
+    assert lib.tq_debug_mfma_ceiling(0, 4, out, S) == -2
+    assert lib.tq_debug_mfma_ceiling((1 << 20) + 1, 4, out, S) == -2
+    assert lib.tq_debug_mfma_ceiling(16, 0, out, S) == -2
+    assert lib.tq_debug_mfma_ceiling(16, 70000, out, S) == -2
+
+
 def test_profiler_is_the_only_switchable_state(lib):
     """Timing is off unless enabled; with nothing recorded the read returns no entries, and reset clears it."""
     stats = (tqb.KernelStat * 8)()

@@ -33,10 +33,11 @@
 // 16 x the code product (256 x when the activations come packed and are
 // expanded the same way) and is shifted back exactly.
 //
-// Tile: 256 channels x BN tokens (BN = 256 or 128) per block of 8 waves, as a
-// 4 x 2 grid of 64 x BN/2 wave tiles.  Stage: 128 k; LDS per stage: packed
-// weights 256 rows x 64 bytes, activations BN rows x 128 bytes (int8) or
-// x 64 bytes (packed, the integer check entry point).
+// Tile: BM = 256 channels x BN tokens (BN = 256 or 128) per block of 8 waves,
+// as a 4 x 2 grid of 64 x BN/2 wave tiles; for grids that would not fill the
+// chip, BM = BN = 128 as a 2 x 4 grid of 64 x 32 wave tiles.  Stage: 128 k;
+// LDS per stage: packed weights BM rows x 64 bytes, activations BN rows x 128
+// bytes (int8) or x 64 bytes (packed, the integer check entry point).
 
 #include "tq_kernels.h"
 
@@ -58,12 +59,14 @@ __device__ __forceinline__ int psw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 // DBG: the test-hook instance, which also stores the exact int32 sums of the
 // residual product (g.acc) and of the second integer product (g.acc2); its
 // code is this template's, with those stores added.
-template <int EPI, bool XP, int BN, bool W8 = false, bool KF = false, bool DBG = false>
+// BM: channels per tile, 256 or 128 (then with BN = 128, the rank-augmented
+// and integer-check epilogues only).
+template <int EPI, bool XP, int BN, bool W8 = false, bool KF = false, bool DBG = false, int BM = 256>
 __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   static_assert(!W8 || (EPI == EPI_ACC && !XP), "8-bit weights: the integer check only");
-  constexpr int BM = 256;                        // channels per tile
-  constexpr int WGM = 4;                         // wave grid: 4 (channels) x 2 (tokens)
-  constexpr int WM = BM / WGM, WN = BN / 2;      // wave tile 64 x BN/2
+  static_assert(BM == 256 || (BM == 128 && BN == 128 && (EPI == EPI_LINEAR || EPI == EPI_ACC)), "tile shapes");
+  constexpr int WGM = BM / 64, WGN = 8 / WGM;    // wave grid: 4 x 2 or 2 x 4 (channels x tokens)
+  constexpr int WM = BM / WGM, WN = BN / WGN;    // wave tile 64 x BN/2, or 64 x 32
   constexpr int FM = WM / 32, FN = WN / 32;      // 32 x 32 blocks per wave tile
   constexpr int XROW = XP ? 64 : 128;            // LDS bytes per activation row per stage
   constexpr int WROW = W8 ? 128 : 64;            // LDS bytes per weight row per stage
@@ -234,8 +237,8 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   };
 
   // ---- main loop: stage kt (128 k) sits in buffer kt % NST.  Each wave
-  // waits for its own loads of stage kt (those of the next stage may stay in
-  // flight); the barrier then publishes stage kt to all waves and frees the
+  // waits for its own loads of stage kt (those of the later stages may stay
+  // in flight); the barrier then publishes stage kt to all waves and frees the
   // buffer of stage kt - 1, which receives stage kt + AHEAD.
   const int KT = (Kb + WROW - 1) / WROW;
 #pragma unroll
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   }
   int buf = 0;
   for (int kt = 0; kt < KT; ++kt) {
-    if (AHEAD >= 2 && kt + 1 < KT)
-      wait_vmcnt<(AHEAD >= 2 ? NL : 0)>();
+    if (AHEAD >= 2 && kt + AHEAD - 1 < KT)
+      wait_vmcnt<(AHEAD - 1) * NL>();
     else
       wait_vmcnt<0>();
     stage_barrier();
@@ -685,10 +688,17 @@ hipError_t launch_kf(const GemmArgs& g, hipStream_t st) {
       return hipGetLastError();
     }
   }
-  {
-    const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 255) / 256));
-    launch_kernel(k_gemm8<EPI, XP, 128, W8, KF, DBG>, dim3(blocks), dim3(512), 0, st, g);
+  const long mid = (long)((g.M + 127) / 128) * ((g.N + 255) / 256);
+  if constexpr ((EPI == EPI_LINEAR || EPI == EPI_ACC) && !W8) {
+    // fewer 256 x 128 tiles than compute units (up to some hundreds of
+    // tokens): 128 x 128 tiles, twice the blocks
+    if (mid < 224) {
+      const unsigned blocks = (unsigned)(((g.M + 127) / 128) * ((g.N + 127) / 128));
+      launch_kernel(k_gemm8<EPI, XP, 128, W8, KF, DBG, 128>, dim3(blocks), dim3(512), 0, st, g);
+      return hipGetLastError();
+    }
   }
+  launch_kernel(k_gemm8<EPI, XP, 128, W8, KF, DBG>, dim3((unsigned)mid), dim3(512), 0, st, g);
   return hipGetLastError();
 }
 

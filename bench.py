@@ -82,6 +82,8 @@ def time_calls(fn, steps, warmup, torch):
 
 
 def kernel_ms(fn, steps, torch, tq):
+    """Per call, the time of each kernel name (dispatch timestamps; a name launched several times per call spans
+    its first start to its last end)."""
     tq.tq_profile_reset()
     tq.tq_profile_enable(True)
     for i in range(steps):
@@ -90,7 +92,7 @@ def kernel_ms(fn, steps, torch, tq):
     stats = tq.tq_profile_read()
     tq.tq_profile_enable(False)
     tq.tq_profile_reset()
-    return {k: v[1] / v[0] for k, v in stats.items()}
+    return {k: v[1] / steps for k, v in stats.items()}
 
 
 class LinearCase:

@@ -526,9 +526,11 @@ tq_status tq_debug_mfma_ceiling(int iters, int blocks, int32_t* out, hipStream_t
 
 /*
  * Kernel timing.  While enabled, every kernel the library launches is
- * bracketed by a pair of HIP events recorded on the launch stream.
- * tq_profile_read synchronises on the recorded events and returns, per kernel
- * name, the number of launches and their summed duration in milliseconds
+ * bracketed by a pair of HIP events recorded on the launch stream (where a
+ * step takes several dispatches under one name, the pair spans the first
+ * one's start to the last one's end).  tq_profile_read synchronises on the
+ * recorded events and returns, per kernel name, the number of launches (one
+ * per step so bracketed) and their summed duration in milliseconds
  * (host arrays of `max` entries; returns the number of kernel names, or a
  * negative tq_status).  tq_profile_reset drops the record.  The record is
  * process-wide (one lock guards it); calls from several threads interleave

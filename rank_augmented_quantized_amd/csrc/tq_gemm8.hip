@@ -84,8 +84,9 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   const int wm = wave % WGM, wn = wave / WGM;
   const int l32 = lane & 31, lg = lane >> 5;
   int tm, tn;
-  tile_of_block(blockIdx.x, (g.N + BM - 1) / BM, (g.M + BN - 1) / BN, tm, tn);
-  const int ch0 = tm * BM, tk0 = tn * BN;
+  const int cend = g.c1 > 0 ? g.c1 : g.N;
+  tile_of_block(blockIdx.x, (cend - g.c0 + BM - 1) / BM, (g.M + BN - 1) / BN, tm, tn);
+  const int ch0 = g.c0 + tm * BM, tk0 = tn * BN;
   const int Kb = g.Kb;                       // weight code bytes per row (K / 2, or K for 8-bit)
   const int Kx = (XP || W8) ? Kb : 2 * Kb;   // activation bytes per row
 
@@ -677,13 +678,30 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   }
 }
 
+// Compute units of the chip: one 256 x 256 tile each per wave.
+constexpr long kTileCUs = 256;
+
 template <int EPI, bool XP, bool W8, bool KF, bool DBG>
 hipError_t launch_kf(const GemmArgs& g, hipStream_t st) {
-  const long big = (long)((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const long tt = (g.M + 255) / 256, big = tt * ((g.N + 255) / 256);
   // the two-subspace epilogue keeps a 64 x 64 fp32 tile per wave (256 x 128
   // tiles): with 64 x 128 it would not fit the registers beside the 8-bit product
   if constexpr (EPI != EPI_MP) {
     if (big >= 224) {
+      // A last wave of 256 x 256 tiles that would fill at most half of the
+      // compute units (rem tiles, whole channel panels): those channels run
+      // as 256 x 128 tiles in a second launch, twice the blocks at half the
+      // work each, instead of a half-empty wave of full tiles.
+      const long rem = big % kTileCUs;
+      if (big > kTileCUs && rem > 0 && 2 * rem <= kTileCUs && rem % tt == 0) {
+        GemmArgs g1 = g, g2 = g;
+        g1.c1 = (int)((g.N + 255) / 256 - rem / tt) * 256;  // whole panels before the last rem / tt
+        g2.c0 = g1.c1;
+        launch_kernel(k_gemm8<EPI, XP, 256, W8, KF, DBG>, dim3((unsigned)(big - rem)), dim3(512), 0, st, g1);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+        launch_kernel(k_gemm8<EPI, XP, 128, W8, KF, DBG>, dim3((unsigned)(2 * rem)), dim3(512), 0, st, g2);
+        return hipGetLastError();
+      }
       launch_kernel(k_gemm8<EPI, XP, 256, W8, KF, DBG>, dim3((unsigned)big), dim3(512), 0, st, g);
       return hipGetLastError();
     }

@@ -23,11 +23,13 @@ struct LaunchEvents {
 };
 LaunchEvents& launch_events();
 
+// Several launches under one name: the start event is taken by the first,
+// the stop event by each in turn, so the record spans first start to last end.
 template <typename K, typename... Args>
 void launch_kernel(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t st, Args... args) {
   LaunchEvents& ev = launch_events();
-  if (ev.start && ev.stop && !ev.used) {
-    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.start, ev.stop, 0, args...);
+  if (ev.start && ev.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, ev.used ? nullptr : ev.start, ev.stop, 0, args...);
     ev.used = true;
   } else {
     hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
@@ -80,6 +82,9 @@ struct GemmArgs {
   const uint8_t* B;  // w codes, N rows
   int64_t lda, ldb;  // bytes per row
   int M, N, Kb;      // Kb: code bytes per row of the main segment
+  // tile GEMM: the launch covers output channels [c0, c1) (c1 = 0: [c0, N));
+  // indexing, bounds and strides stay those of the whole N channels
+  int c0, c1;
   // second (8-bit) segment of the two-subspace layer
   const uint8_t* A2;
   const uint8_t* B2;

@@ -276,6 +276,9 @@ LCASES = [
     ("n1100_f32_fused", 1100, 1024, 80, 32, "student_t", "f32", 0),
     ("n1040_r0_fused", 1040, 256, 64, 0, "normal", "bf16", 1),
     ("n1024_d8192_r32_long_rows", 1024, 8192, 64, 32, "normal", "bf16", 3),
+    # 260 tiles of 256 x 256: the last 4 (two channel panels, the second
+    # ragged) run as 256 x 128 tiles in a second launch
+    ("n512_m33124_split_last_wave", 512, 256, 33124, 32, "normal", "bf16", 2),
 ]
 
 

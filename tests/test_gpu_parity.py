@@ -279,6 +279,9 @@ LCASES = [
     # 260 tiles of 256 x 256: the last 4 (two channel panels, the second
     # ragged) run as 256 x 128 tiles in a second launch
     ("n512_m33124_split_last_wave", 512, 256, 33124, 32, "normal", "bf16", 2),
+    # 224 tiles of 256 x 256 with rows of 144 code bytes: the last 128-k
+    # stage of each row is partial
+    ("n4096_d288_full_tiles_ragged_k", 4096, 288, 3584, 32, "normal", "bf16", 2),
 ]
 
 

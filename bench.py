@@ -337,6 +337,74 @@ def mfma_ceiling(torch, tq, dev):
     return out
 
 
+def activation_format(torch, tq, dev, steps=20):
+    """The tile GEMM on the two activation-code formats, in us and TOP/s: nibble-packed codes (expanded in the loop
+    like the weights) against one int8 byte per code (the layer's format), each with the integer-export epilogue
+    (tq_debug_accumulate / tq_debug_accumulate_i8, int32 stores) and with the layer's dequantising bf16 epilogue
+    without the low-rank term (tq_debug_gemm_w4a4).  Two code sets on 4096^3: the attention-projection workload's
+    own codes (its X through tq_quantize_act, its weights through tq_pack_weight) and uniformly random codes."""
+    from workloads import WORKLOADS, draw_linear
+
+    wl = WORKLOADS["attn_proj"]
+    n, k, m = wl.n, wl.d, wl.m
+    c = draw_linear(wl, n=n)
+    xp_w, sx_w = tq.tq_quantize_act(torch.from_numpy(c["X"]).to(dev).bfloat16(), 4)
+    wp_w, sw_w = tq.tq_pack_weight(torch.from_numpy(c["R"]).to(dev), 4)
+    del c
+    g = torch.Generator(device=dev).manual_seed(5)
+
+    def nibbles(codes):  # byte j: code 2 j in the low nibble, code 2 j + 1 in the high one
+        codes = codes & 0xF
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).to(torch.uint8).contiguous()
+
+    def codes_of(packed):  # nibble-packed -> int32 codes in [-8, 7]
+        b = packed.to(torch.int32)
+        lo, hi = b & 0xF, (b >> 4) & 0xF
+        cds = torch.stack([lo, hi], dim=2).reshape(packed.shape[0], -1)
+        return cds - 16 * (cds >= 8).to(torch.int32)
+
+    def tile_order(codes):  # int8 bytes, within every 8 consecutive k the 4 even-k codes then the 4 odd-k codes
+        g8 = codes.reshape(codes.shape[0], -1, 8)
+        return torch.cat([g8[:, :, 0::2], g8[:, :, 1::2]], dim=2).reshape(codes.shape[0], -1).to(torch.int8).contiguous()
+
+    cx = torch.randint(-8, 8, (n, k), dtype=torch.int32, device=dev, generator=g)
+    cw = torch.randint(-8, 8, (m, k), dtype=torch.int32, device=dev, generator=g)
+    sets = {"workload": (xp_w, tile_order(codes_of(xp_w)), wp_w, sx_w, sw_w),
+            "random": (nibbles(cx), tile_order(cx), nibbles(cw), torch.rand(n, device=dev, generator=g) + 0.5,
+                       torch.rand(m, device=dev, generator=g) * 0.01 + 0.001)}
+    acc = torch.empty((n, m), dtype=torch.int32, device=dev)
+    y = torch.empty((n, m), dtype=torch.bfloat16, device=dev)
+    res = {"n": n, "k": k, "m": m}
+    for sname, (xp, xi8, wp, sx, sw) in sets.items():
+        runs = {"packed_int32": lambda: tq.tq_debug_accumulate(xp, wp, k, 4, acc=acc),
+                "int8_int32": lambda: tq.tq_debug_accumulate_i8(xi8, wp, k, acc=acc),
+                "packed_bf16_y": lambda: tq.tq_debug_gemm_w4a4(xp, True, sx, wp, sw, k, Y=y),
+                "int8_bf16_y": lambda: tq.tq_debug_gemm_w4a4(xi8, False, sx, wp, sw, k, Y=y)}
+        out = {}
+        for name, fn in runs.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            out[name] = {"us": round(us, 2), "TOPs": round(2.0 * n * k * m / (us * 1e-6) / 1e12, 1)}
+            if name == "packed_int32":
+                sums = acc.clone()
+            elif name == "int8_int32":
+                out["same_sums"] = bool(torch.equal(sums, acc))  # both formats give the same int32 sums
+            elif name == "packed_bf16_y":
+                y0 = y.clone()
+            else:
+                out["same_y"] = bool(torch.equal(y0, y))
+        res[sname] = out
+    return res
+
+
 def cpu_baseline(wl, rows, seconds):
     """The oracle as it stands, timed on the host: the layer on the first `rows` tokens, repeated until about
     `seconds` of CPU work have been timed."""
@@ -379,6 +447,8 @@ def main():
                     help="only measure the streaming-read ceiling (tq_debug_stream_read) and print it")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only the int8 MFMA ceiling (tq_debug_mfma_ceiling), one JSON line")
+    ap.add_argument("--activation-format", action="store_true",
+                    help="only the tile GEMM on packed against int8 activation codes at 4096^3, one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (scales rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -411,6 +481,9 @@ def main():
         return
     if args.mfma_ceiling:
         print(json.dumps({"mfma_ceiling": mfma_ceiling(torch, tq, dev)}), flush=True)
+        return
+    if args.activation_format:
+        print(json.dumps({"activation_format": activation_format(torch, tq, dev)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     n, d, m, r = args.n or wl.n, wl.d, wl.m, wl.r

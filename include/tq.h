@@ -452,6 +452,40 @@ tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t 
                               int64_t m, int bits, int32_t* acc, hipStream_t stream);
 
 /*
+ * tq_debug_accumulate_i8 -- the same exact product with the activation codes
+ * as the rank-augmented layer's tile GEMM takes them (TwinQuant notes,
+ * section 04.C and Figure 4: the 4-bit residual product with int32
+ * accumulation): one int8 byte per 4-bit code, and within every 8
+ * consecutive k the 4 codes of even k, then the 4 codes of odd k.
+ *   x_codes  n x k int8 bytes in that order; w_codes m x k nibble-packed
+ *            (as tq_pack_weight writes them); acc out: n x m int32.
+ * Always the tile GEMM (any n), with the integer-export epilogue that
+ * tq_debug_accumulate uses on nibble-packed activations, so the two time
+ * the two activation formats through the same main loop and epilogue.
+ * k a multiple of 32; device buffers, 16-byte aligned, caller-owned.
+ * Kernel timing names it "gemm_acc_i8".
+ */
+tq_status tq_debug_accumulate_i8(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m,
+                                 int32_t* acc, hipStream_t stream);
+
+/*
+ * tq_debug_gemm_w4a4 -- the residual W4A4 product with its dequantising
+ * epilogue and bf16 store, Y[i][j] = s_x[i] s_w[j] sum_t x[i][t] w[j][t]
+ * (TwinQuant notes, section 04.C and Figure 4, without the low-rank term),
+ * on either activation-code format: x_packed = 1, nibble-packed codes as
+ * tq_quantize_act writes them (n x k/2 bytes); 0, one int8 byte per code in
+ * the order of tq_debug_accumulate_i8 (n x k bytes), the format tq_linear's
+ * tile GEMM reads.  w_codes / s_w as tq_pack_weight writes them; s_x n
+ * floats; Y n x m bf16 (device, 16-byte aligned, caller-owned).  Always the
+ * tile GEMM, so the two formats are timed through the same kernel and
+ * epilogue; both give the same Y bit for bit (the scale absorbs the factor
+ * of 16 between the two expanded forms exactly).  k a multiple of 32.
+ * Kernel timing names it "gemm_w4a4_packed_x" or "gemm_w4a4_int8_x".
+ */
+tq_status tq_debug_gemm_w4a4(const void* x_codes, int x_packed, const float* s_x, const void* w_codes,
+                             const float* s_w, int64_t n, int64_t k, int64_t m, void* Y, hipStream_t stream);
+
+/*
  * Accumulator export (test hooks).  Each runs the layer exactly as the entry
  * point it is named after -- same checks, workspace, launches, kernel
  * templates and Y -- through the kernels' export instance, which also stores

@@ -1147,6 +1147,51 @@ tq_status tq_debug_accumulate(const void* x_codes, const void* w_codes, int64_t 
   return TQ_OK;
 }
 
+tq_status tq_debug_accumulate_i8(const void* x_codes, const void* w_codes, int64_t n, int64_t k, int64_t m,
+                                 int32_t* acc, hipStream_t stream) {
+  if (n < 0 || n > kMaxDim || k <= 0 || k > kMaxK || m <= 0 || m > kMaxDim || k % 32) return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!x_codes || !w_codes || !acc) return TQ_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned16(w_codes) || !aligned16(acc)) return TQ_ERR_ALIGN;
+  GemmArgs g{};
+  g.A = (const uint8_t*)x_codes;
+  g.lda = k;  // one int8 byte per code
+  g.B = (const uint8_t*)w_codes;
+  g.ldb = k / 2;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(k / 2);
+  g.acc = acc;
+  TQ_RUN("gemm_acc_i8", stream, tq::launch_gemm8(g, tq::EPI_ACC, true, 4, stream));
+  return TQ_OK;
+}
+
+tq_status tq_debug_gemm_w4a4(const void* x_codes, int x_packed, const float* s_x, const void* w_codes,
+                             const float* s_w, int64_t n, int64_t k, int64_t m, void* Y, hipStream_t stream) {
+  if (n < 0 || n > kMaxDim || k <= 0 || k > kMaxK || m <= 0 || m > kMaxDim || k % 32) return TQ_ERR_SHAPE;
+  if (n == 0) return TQ_OK;
+  if (!x_codes || !s_x || !w_codes || !s_w || !Y) return TQ_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned16(w_codes) || !aligned16(Y)) return TQ_ERR_ALIGN;
+  GemmArgs g{};
+  g.A = (const uint8_t*)x_codes;
+  g.lda = x_packed ? k / 2 : k;
+  g.B = (const uint8_t*)w_codes;
+  g.ldb = k / 2;
+  g.M = (int)n;
+  g.N = (int)m;
+  g.Kb = (int)(k / 2);
+  g.sx = s_x;
+  g.sw = s_w;
+  g.groups.n = 1;
+  g.groups.start[1] = (int)m;
+  g.Y = Y;
+  g.ldy = m;
+  g.y_bf16 = 1;
+  TQ_RUN(x_packed ? "gemm_w4a4_packed_x" : "gemm_w4a4_int8_x", stream,
+         tq::launch_gemm8(g, tq::EPI_LINEAR, !x_packed, 4, stream));
+  return TQ_OK;
+}
+
 tq_status tq_profile_enable(int on) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);

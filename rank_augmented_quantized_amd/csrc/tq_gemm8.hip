@@ -72,7 +72,9 @@ __global__ __launch_bounds__(512) void k_gemm8(GemmArgs g) {
   constexpr int WROW = W8 ? 128 : 64;            // LDS bytes per weight row per stage
   constexpr int WPL = BM * WROW, XPL = BN * XROW;  // stage planes
   constexpr int SPL = WPL + XPL;
-  constexpr int NST = W8 ? 2 : 3;                // stage buffers; NST - 1 stages in flight
+  // stage buffers, NST - 1 stages in flight (packed activations: four, whose
+  // 128 KB also hold the bf16 Y staging)
+  constexpr int NST = W8 ? 2 : (XP ? 4 : 3);
   constexpr int AHEAD = NST - 1;
   constexpr int WI = WPL / 1024 / 8, XI = XPL / 1024 / 8;  // direct loads per wave per stage
   static_assert(WI >= 1 && XI >= 1, "each wave fills whole 1 KB pieces");
@@ -744,7 +746,9 @@ hipError_t launch_gemm8(const GemmArgs& g, Epilogue epi, bool x_int8, int w_bits
   if (w_bits == 8) return (epi == EPI_ACC && x_int8) ? launch_t<EPI_ACC, false, true>(g, st) : hipErrorInvalidValue;
   if (w_bits != 4) return hipErrorInvalidValue;
   if (epi == EPI_LINEAR && x_int8) return launch_t<EPI_LINEAR, false>(g, st);
+  if (epi == EPI_LINEAR && !x_int8) return launch_t<EPI_LINEAR, true>(g, st);
   if (epi == EPI_ACC && !x_int8) return launch_t<EPI_ACC, true>(g, st);
+  if (epi == EPI_ACC && x_int8) return launch_t<EPI_ACC, false>(g, st);
   if (epi == EPI_MP && x_int8) return launch_t<EPI_MP, false>(g, st);
   if (epi == EPI_QLR && x_int8) return launch_t<EPI_QLR, false>(g, st);
   return hipErrorInvalidValue;

@@ -34,7 +34,7 @@ EXPORTS = (
     "tq_linear_asym_workspace_offsets", "tq_linear_asym", "tq_linear_debug", "tq_linear_mp_bits_debug",
     "tq_linear_asym_debug", "tq_linear_mp_asym_debug", "tq_linear_qlr_debug", "tq_linear_noalloc",
     "tq_debug_linear_handoff",
-    "tq_debug_stream_read", "tq_debug_mfma_ceiling",
+    "tq_debug_stream_read", "tq_debug_mfma_ceiling", "tq_debug_accumulate_i8", "tq_debug_gemm_w4a4",
 )
 
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # TQ_NOALLOC_SCRATCH_BYTES of include/tq.h
@@ -78,6 +78,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "tq_linear_mp_workspace_bytes": (sz, [i64, i64, i64]),
         "tq_linear_mp": (st, [ptr, c_int, i64, i64, i64, i64, ptr, ptr, ptr, ptr, ptr, c_int, ptr, sz, ptr]),
         "tq_debug_accumulate": (st, [ptr, ptr, i64, i64, i64, c_int, ptr, ptr]),
+        "tq_debug_accumulate_i8": (st, [ptr, ptr, i64, i64, i64, ptr, ptr]),
+        "tq_debug_gemm_w4a4": (st, [ptr, c_int, ptr, ptr, ptr, i64, i64, i64, ptr, ptr]),
         "tq_profile_enable": (st, [c_int]),
         "tq_profile_read": (c_int, [ctypes.POINTER(KernelStat), c_int]),
         "tq_profile_reset": (st, []),
@@ -520,6 +522,32 @@ def tq_debug_accumulate(x_codes, w_codes, k: int, bits: int = 4, acc=None):
     _check("tq_debug_accumulate", lib.tq_debug_accumulate(_p(x_codes), _p(w_codes), n, k, m, bits, _p(acc),
                                                           _stream(x_codes)))
     return acc
+
+
+def tq_debug_accumulate_i8(x_codes, w_codes, k: int, acc=None):
+    """Exact int32 product -> n x m from int8 activation codes in the tile GEMM's order (x n x k bytes) and
+    nibble-packed weight codes (w m x k/2)."""
+    lib = load()
+    _need_cuda(x_codes, w_codes, acc)
+    n, m = x_codes.shape[0], w_codes.shape[0]
+    if acc is None:
+        acc = torch.empty((n, m), dtype=torch.int32, device=x_codes.device)
+    _check("tq_debug_accumulate_i8", lib.tq_debug_accumulate_i8(_p(x_codes), _p(w_codes), n, k, m, _p(acc),
+                                                                _stream(x_codes)))
+    return acc
+
+
+def tq_debug_gemm_w4a4(x_codes, x_packed: bool, s_x, w_codes, s_w, k: int, Y=None):
+    """bf16 Y = s_x s_w (C_x C_w^T) through the tile GEMM on nibble-packed (x_packed) or int8 (tile order)
+    activation codes."""
+    lib = load()
+    _need_cuda(x_codes, s_x, w_codes, s_w, Y)
+    n, m = x_codes.shape[0], w_codes.shape[0]
+    if Y is None:
+        Y = torch.empty((n, m), dtype=torch.bfloat16, device=x_codes.device)
+    _check("tq_debug_gemm_w4a4", lib.tq_debug_gemm_w4a4(_p(x_codes), 1 if x_packed else 0, _p(s_x), _p(w_codes),
+                                                        _p(s_w), n, k, m, _p(Y), _stream(x_codes)))
+    return Y
 
 
 def tq_profile_enable(on: bool = True):

@@ -354,6 +354,22 @@ def test_stream_read_validation(lib):
     assert lib.tq_debug_stream_read(A, 1024, out, 70000, S) == -2
 
 
+def test_accumulate_i8_validation(lib):
+    assert lib.tq_debug_accumulate_i8(NUL, B, 40, 64, 16, C, S) == -1
+    assert lib.tq_debug_accumulate_i8(A, B, 40, 48, 16, C, S) == -2  # k not a multiple of 32
+    assert lib.tq_debug_accumulate_i8(A, B, 40, 64, 0, C, S) == -2
+    assert lib.tq_debug_accumulate_i8(MIS, B, 40, 64, 16, C, S) == -5
+    assert lib.tq_debug_accumulate_i8(A, B, 0, 64, 16, NUL, S) == 0  # nothing to do
+
+
+def test_gemm_w4a4_debug_validation(lib):
+    assert lib.tq_debug_gemm_w4a4(A, 1, C, B, C, 40, 64, 16, NUL, S) == -1
+    assert lib.tq_debug_gemm_w4a4(A, 0, NUL, B, C, 40, 64, 16, C, S) == -1
+    assert lib.tq_debug_gemm_w4a4(A, 1, C, B, C, 40, 48, 16, C, S) == -2  # k not a multiple of 32
+    assert lib.tq_debug_gemm_w4a4(MIS, 1, C, B, C, 40, 64, 16, C, S) == -5
+    assert lib.tq_debug_gemm_w4a4(NUL, 1, NUL, NUL, NUL, 0, 64, 16, NUL, S) == 0  # nothing to do
+
+
 def test_mfma_ceiling_validation(lib):
     out = ctypes.c_void_p(0x40000)
     assert lib.tq_debug_mfma_ceiling(16, 4, NUL, S) == -1

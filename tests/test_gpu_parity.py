@@ -179,6 +179,51 @@ def test_accumulate_bitexact(n, k, m, bits):
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), tqo.int_matmul(cx, cw))
 
 
+def _tile_order_int8(cx):
+    """Activation codes as the tile GEMM takes them (include/tq.h, tq_debug_accumulate_i8): one int8 byte per code,
+    within every 8 consecutive k the 4 codes of even k, then the 4 codes of odd k."""
+    n, k = cx.shape
+    g = cx.reshape(n, k // 8, 8)
+    return np.concatenate([g[:, :, 0::2], g[:, :, 1::2]], axis=2).reshape(n, k).astype(np.int8)
+
+
+@pytest.mark.parametrize("n,k,m", [(1, 512, 16), (33, 512, 130), (300, 1024, 160), (70, 416, 64), (200, 4064, 300),
+                                   (4096, 256, 3584)])
+def test_accumulate_i8_bitexact(n, k, m):
+    """The tile GEMM's main loop on int8 activation codes (the layer's format), with the integer-export epilogue:
+    every sum equals the exact product; 4096 x 3584 takes 224 tiles of 256 x 256."""
+    print(f"case n={n} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(n * 5 + k + m)
+    cx = rng.integers(-8, 8, size=(n, k))
+    cw = rng.integers(-8, 8, size=(m, k))
+    cx[0, :] = -8
+    cw[0, :] = -8
+    xi8 = torch.from_numpy(_tile_order_int8(cx)).to(DEV)
+    acc = tq.tq_debug_accumulate_i8(xi8, _t(tqo.pack_codes(cw, 4)), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), tqo.int_matmul(cx, cw))
+
+
+@pytest.mark.parametrize("n,k,m", [(33, 512, 130), (300, 1024, 160), (70, 416, 64), (4096, 256, 3584)])
+def test_gemm_w4a4_both_activation_formats(n, k, m):
+    """The residual product with its dequantising epilogue on nibble-packed and on int8 activation codes: the same
+    bf16 Y bit for bit, and each element within the bf16 rounding of s_x s_w (C_x C_w^T) (relative 2^-8)."""
+    print(f"case n={n} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(n * 3 + k + m)
+    cx = rng.integers(-8, 8, size=(n, k))
+    cw = rng.integers(-8, 8, size=(m, k))
+    sx = rng.uniform(0.01, 2.0, size=n).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, size=m).astype(np.float32)
+    wc, sxt, swt = _t(tqo.pack_codes(cw, 4)), _t(sx), _t(sw)
+    y_p = tq.tq_debug_gemm_w4a4(_t(tqo.pack_codes(cx, 4)), True, sxt, wc, swt, k)
+    y_8 = tq.tq_debug_gemm_w4a4(torch.from_numpy(_tile_order_int8(cx)).to(DEV), False, sxt, wc, swt, k)
+    torch.cuda.synchronize()
+    assert torch.equal(y_p, y_8)
+    ref = sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * tqo.int_matmul(cx, cw)
+    y = y_p.float().cpu().numpy().astype(np.float64)
+    assert (np.abs(y - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-30).all()
+
+
 # ----------------------------------------------------------------------------
 # the layer on small shapes (several tiles, ragged tails)
 # ----------------------------------------------------------------------------

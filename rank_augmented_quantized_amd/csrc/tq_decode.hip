@@ -379,7 +379,12 @@ __global__ __launch_bounds__(kNT) void k_decode(DecodeArgs a) {
     return;
   }
 
-  // control wave
+  // control wave.  Its T check, chunk sum and T L2 sit on the path to every
+  // store of Y; with many chunks (long rows: 28 at d = 14336) they take long
+  // enough that its instructions go first (the stream waves mostly wait on
+  // memory meanwhile): 17.2 -> 15.3 us at d = 14336, while at 8 chunks
+  // (d = 4096) the raised priority costs 0.5 us, so it stays at the default.
+  if (a.nchunk >= 16) __builtin_amdgcn_s_setprio(3);
   if (rp > 0) {
     // T rows 0 .. n - 1 of this layer, element e = (row e / rp, column e % rp):
     // the layer's nchunk words per element are contiguous.  One batch of

@@ -90,9 +90,10 @@ __device__ __forceinline__ void lds_done() { __builtin_amdgcn_s_waitcnt(0xC07F);
 
 // ---------------------------------------------------------------------------
 // The kernel.  NR: token rows (1 or 2); DBG: the test-hook instance that also
-// stores the exact int32 sums to a.acc.
+// stores the exact int32 sums to a.acc; HP: the control wave runs at raised
+// priority (chosen by the launcher for T of 16 or more chunks).
 // ---------------------------------------------------------------------------
-template <typename T, int NR, bool DBG>
+template <typename T, int NR, bool DBG, bool HP>
 __global__ __launch_bounds__(kNT) void k_decode(DecodeArgs a) {
   constexpr int SW = kSW, NW = kNW, NT = kNT, U = kU;
   constexpr int CHX = (kDecodeMaxD / 8 + NT - 1) / NT;  // 8-value chunks per thread per row
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(kNT) void k_decode(DecodeArgs a) {
   // enough that its instructions go first (the stream waves mostly wait on
   // memory meanwhile): 17.2 -> 15.3 us at d = 14336, while at 8 chunks
   // (d = 4096) the raised priority costs 0.5 us, so it stays at the default.
-  if (a.nchunk >= 16) __builtin_amdgcn_s_setprio(3);
+  if constexpr (HP) __builtin_amdgcn_s_setprio(3);
   if (rp > 0) {
     // T rows 0 .. n - 1 of this layer, element e = (row e / rp, column e % rp):
     // the layer's nchunk words per element are contiguous.  One batch of
@@ -466,14 +467,22 @@ __global__ __launch_bounds__(kNT) void k_decode(DecodeArgs a) {
   }
 }
 
-template <typename T, int NR>
-hipError_t launch_nr(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+template <typename T, int NR, bool HP>
+hipError_t launch_hp(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
   const dim3 grid((unsigned)p.blocks), block(kNT);
   if (a.acc)
-    hipLaunchKernelGGL((k_decode<T, NR, true>), grid, block, p.lds, st, a);
+    hipLaunchKernelGGL((k_decode<T, NR, true, HP>), grid, block, p.lds, st, a);
   else
-    launch_kernel(k_decode<T, NR, false>, grid, block, p.lds, st, a);
+    launch_kernel(k_decode<T, NR, false, HP>, grid, block, p.lds, st, a);
   return hipGetLastError();
+}
+
+// Chunks of T from which the control wave runs at raised priority.
+constexpr int kDecodeHpChunks = 16;
+
+template <typename T, int NR>
+hipError_t launch_nr(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+  return a.nchunk >= kDecodeHpChunks ? launch_hp<T, NR, true>(a, p, st) : launch_hp<T, NR, false>(a, p, st);
 }
 
 }  // namespace

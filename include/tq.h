@@ -190,14 +190,18 @@ size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
  *            ignored.  Calls that share a workspace must be ordered (one
  *            stream, or synchronised streams).
  * For n <= 32 the call runs a memory-bound path (weight codes streamed once).
- * For n <= 2, d <= 16384 and n d <= 16384 (and at most 128 partial blocks of
- * T: ceil(d / 512) r_pad / 16 <= 128) that path is one launch, whose
- * weight-streaming blocks read partials of T that other blocks of the same
- * launch store; their waits are bounded: a wait that gives up sets word 32 of
- * the hand-off words (off[3] of tq_linear_workspace_offsets), writes NaN to
- * the block's outputs, and every later call on that workspace writes NaN
- * everywhere until it is zero-filled again.  Otherwise a tiled MFMA path.
- * All paths produce bit-identical integer accumulators.
+ * It is one launch for n <= 2, d <= 16384 and n d <= 16384 (and at most 128
+ * partial blocks of T: ceil(d / 512) r_pad / 16 <= 128: the decode kernel),
+ * and for any other n <= 16 with bf16 X and d <= 16384 whose grid is at most a
+ * quarter larger than what the GPU holds at once (the few-token GEMM, whose
+ * first blocks quantise X and compute partials of T; on MI355X 1024 blocks of
+ * 16 output channels for d <= 4096, 256 above); otherwise two launches.  In a one-launch path, weight-streaming blocks read what other
+ * blocks of the same launch store; their waits are bounded: a wait that gives
+ * up sets word 32 of the hand-off words (off[3] of
+ * tq_linear_workspace_offsets), writes NaN to the block's outputs, and every
+ * later call on that workspace writes NaN everywhere until it is zero-filled
+ * again.  For n > 32 a tiled MFMA path.  All paths produce bit-identical
+ * integer accumulators.
  */
 tq_status tq_linear(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                     const void* w_codes, const float* s_w, const void* lowrank,
@@ -232,9 +236,9 @@ tq_status tq_linear_noalloc(const void* X, tq_dtype x_dt, int64_t n, int64_t d, 
  *   the 4 odd-k codes (the order in which the tile GEMM consumes them),
  *   off[2] T = X L1 (n x r_pad bf16, r_pad = r rounded up to a power of two
  *   >= 32; absent when r == 0), off[3] the 4 KiB of uint32 hand-off words:
- *   word 0 the call counter of the one-launch path (advanced by one per
- *   call), word 16 a counter that is zero between calls, word 32 the
- *   wait-limit flag (zero unless a wait gave up).
+ *   word 0 the call counter of the decode kernel (advanced by one per call),
+ *   word 32 the wait-limit flag (zero unless a wait gave up), every other
+ *   word a counter that is zero between calls.
  *   Returns TQ_ERR_SHAPE for invalid sizes.
  */
 tq_status tq_linear_workspace_offsets(int64_t n, int64_t d, int64_t m, int64_t r, size_t off[4]);
@@ -519,13 +523,14 @@ tq_status tq_linear_qlr_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d
                               void* ws, size_t ws_bytes, int32_t* acc, int32_t* acc2, hipStream_t stream);
 
 /*
- * tq_debug_linear_handoff -- test hook of the one-launch few-token path: runs
- * tq_linear (same checks and workspace) with its waits limited to `spin`
- * polls and, when `silent` is non-zero, with the blocks that compute T
- * tagging their results with the previous call's tag, so that every wait
- * gives up and the failure path runs (Y all NaN, the flag word set).  Every
- * kernel still exits.  TQ_ERR_SHAPE when the shape does not take that path
- * or r == 0.
+ * tq_debug_linear_handoff -- test hook of the one-launch few-token paths:
+ * runs tq_linear (same checks and workspace) with its waits limited to
+ * `spin` polls and, when `silent` is non-zero, with the producer blocks never
+ * delivering (the decode kernel's tag their partials of T with the previous
+ * call's tag, the few-token GEMM's never signal), so that every wait gives up
+ * and the failure path runs (Y all NaN, the flag word set).  Every kernel
+ * still exits.  TQ_ERR_SHAPE when the shape and X's type do not take a
+ * one-launch path, or r == 0.
  */
 tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                                   const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,

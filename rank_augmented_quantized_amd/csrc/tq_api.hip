@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "../../include/tq.h"
-#include "tq_kernels.h"
+#include "tq_prologue.h"
 
 namespace {
 
@@ -113,7 +113,8 @@ struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;  // columns of T
   bool small, decode;
-  tq::ProloguePlan plan;
+  bool fused;  // bf16 X takes the one-launch few-token layer (fplan)
+  tq::ProloguePlan plan, fplan;
   tq::DecodePlan dplan;
 };
 
@@ -136,6 +137,14 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_laun
     counters = w.plan.counters;
     if (w.plan.ntb > 0 && (w.plan.nchunk > 1 || w.plan.partial))
       psize = (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
+    // one launch up to 16 tokens; for 17 .. 32 (two 16-token tiles per
+    // block, twice the producers) the two launches measured faster
+    w.fused = !two_launch && n > 0 && n <= 16 && d <= 16384 && w.r_pad % 32 == 0;
+    if (w.fused) {
+      w.fplan = tq::plan_prologue_fused((int)n, (int)d, w.r_pad, tq::gemv_max_chunks((int)n, (int)(d / 2), w.r_pad));
+      if (w.fplan.ntb > 0)
+        psize = std::max(psize, (size_t)w.fplan.nchunk * (size_t)n * (size_t)w.r_pad * 4);
+    }
   }
   size_t o = 0;
   w.sync = o;  // hand-off counters of the few-token launch
@@ -408,6 +417,22 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   g.y_bf16 = y_dt == TQ_BF16;
   g.acc = acc;
 
+  if (L.fused && xb && tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, acc != nullptr)) {
+    // one launch: the quantiser and the partials of T run in the GEMM's grid
+    const tq::ProloguePlan& fp = L.fplan;
+    tq::SmallFuse f{};
+    f.pa = tq::PrologueArgs{X,      (int)n,    (int)d, L1t, L.r_pad, fp.kc, fp.nchunk, fp.qs, fp.nqg,
+                            fp.nqb, 1,         1,      0,   xc,      sx,    P,         T,     ctr};
+    f.nprod = fp.nqb + fp.ntb;
+    f.sync = (unsigned*)(base + L.sync);
+    f.spin = dbg ? dbg->spin : kDecodeSpin;
+    f.silent = dbg ? dbg->silent : 0;
+    g.P = L.r_pad ? P : nullptr;
+    g.nchunk = fp.nchunk;
+    g.Tout = L.r_pad ? T : nullptr;
+    TQ_RUN("small_fused", stream, tq::launch_gemv_fused(g, f, stream));
+    return TQ_OK;
+  }
   TQ_RUN("prologue", stream,
          tq::launch_prologue(X, xb, (int)n, (int)d, L1t, L.r_pad, L.plan, xc, sx, P, T, ctr, stream));
   if (L.small) {
@@ -541,7 +566,10 @@ tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64
                                   void* ws, size_t ws_bytes, unsigned spin, int silent, hipStream_t stream) {
   const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
   if (st != TQ_OK || n == 0) return st;
-  if (r == 0 || !linear_ws(n, d, m, r_padded(r)).decode) return TQ_ERR_SHAPE;  // no hand-off on this path
+  const LinearWs L = linear_ws(n, d, m, r_padded(r));
+  const bool fused = L.fused && x_dt == TQ_BF16 &&
+                     tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, false);
+  if (r == 0 || !(L.decode || fused)) return TQ_ERR_SHAPE;  // no hand-off on this path
   const int64_t ms[1] = {m};
   const HandoffDebug dbg{spin, silent};
   return linear_run(X, x_dt, n, d, m, r, 1, ms, w_codes, s_w, lowrank, Y, y_dt, ws, ws_bytes, stream, nullptr, &dbg);

@@ -14,7 +14,7 @@
 // sums are exact in any order, which leaves the k order inside a fragment
 // free.
 
-#include "tq_kernels.h"
+#include "tq_prologue.h"
 
 namespace tq {
 
@@ -35,6 +35,39 @@ namespace tq {
 //   also writes it to Tout); T L2 for the block's 16 channels
 //   is one 16x16 bf16 MFMA chain whose result layout matches the integer
 //   accumulator's (lane l, element i -> token 4 (l / 16) + i, channel l % 16).
+//
+// FU, the one-launch form (bf16 X, up to 16 tokens): the prologue's work runs in the same grid
+// (TwinQuant notes, section 04.C: the activations are quantised while the
+// residual GEMM runs, and both components meet in one epilogue).  Blocks
+// [0, nqb) quantise one token row each (codes and s_x), blocks [nqb, nprod)
+// compute one fp32 partial of T each (rows 16 rt.., k-chunk c, 32 columns),
+// and the GEMM blocks follow.  A GEMM block issues its first batch of weight
+// loads, which depend on nothing, and only then waits for the producers:
+//  * a producer stores its results at agent scope (written through to the
+//    device's point of coherence, past the XCDs' separate L2s), waits until
+//    every one of them has completed, and after a block barrier adds one to
+//    each copy of the done counter;
+//  * wave 0 of a GEMM block polls one copy (agent-scope loads, which those
+//    L2s cannot serve stale) until it reaches nprod, and releases the
+//    other waves with a barrier that does not wait for their weight loads in
+//    flight.  Codes, scales and partials are then loaded with plain loads.
+//    No L2 can hold a stale copy of them: the dispatch of the kernel
+//    invalidated the caches, no block reads them before the count is
+//    complete, and a line first brought in after that point holds the
+//    stored values.  An acquire at agent scope would invalidate the XCD's
+//    whole L2 in every GEMM block, which costs more than the call itself.
+// The GEMM blocks count themselves out in two levels: each adds one to its
+// group's counter (groups of at least 32 consecutive blocks, at most
+// kFGroups groups), the last of a group resets it and adds one to kFFin, and
+// the last group's last block subtracts nprod from every copy of the done
+// counter and the number of
+// groups from kFFin, so every counter is zero again when the kernel ends,
+// whatever the order in which the blocks ran.  One counter for all the
+// blocks would serialise hundreds of returning atomics on one address at
+// the end of the kernel.  The wait is
+// bounded: a block whose wait gives up sets the sticky flag word kWFlag and
+// writes NaN to its outputs, and GEMM blocks that find the flag set when
+// they start write NaN too, until the workspace is zero-filled again.
 // ---------------------------------------------------------------------------
 // Most bytes of activation codes the small-n GEMM stages in LDS: what
 // leaves the blocks per CU of its launch bounds (2 of 8 waves, 4 of 4 waves)
@@ -44,20 +77,76 @@ __host__ __device__ constexpr int gemv_xl_bytes(int waves) { return waves == 8 ?
 // DBG: the test-hook instance, which also stores the exact int32 sums of the
 // residual product (g.acc) and, for the quantised low-rank branch, of its
 // second stage (g.acc2); its code is this template's, with those stores added.
-template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false>
-__global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g) {
+// hand-off words (uint32 indices into the sync region): the sticky
+// wait-limit flag (shared with the decode kernel), kFCopies copies of the
+// producers-done counter (kFDone + kFStride i: 256 bytes apart, so that the
+// GEMM blocks' polls spread over several memory channels), the counter of
+// finished groups of GEMM blocks, and from kFGroup on one counter per group
+// (4 words apart, at most kFGroups groups)
+constexpr int kWFlag = 32, kFDone = 48, kFStride = 64, kFCopies = 8, kFFin = 80, kFGroup = 512, kFGroups = 128;
+
+__device__ __forceinline__ uint32_t ld_agent(const unsigned* p) {
+  return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A producer block of the one-launch form (bf16 X): one row's codes and s_x,
+// or one fp32 partial of T (QS = 2: 32 columns), then the release and the
+// signal.  smem: the block's LDS.
+template <int WAVES>
+__device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem) {
+  const PrologueArgs& a = f.pa;
+  const int b = blockIdx.x;
+  if (b < a.nqb) {
+    constexpr int CHB = WAVES == 4 ? 2 : 4;  // 8-value chunks per thread: rows up to 8 KB (4 waves), 32 KB (8 waves)
+    quant_row_block_reg<bf16_t, CHB, true>((const bf16_t*)a.X + (size_t)b * a.d, a.d, a.xc + (size_t)b * (a.d >> 1),
+                                           a.sx + b, reinterpret_cast<float*>(smem));
+  } else {
+    auto sP = reinterpret_cast<float (*)[16][33]>(smem);
+    const TBlock t = t_block_products<bf16_t, 2, WAVES, 8>(a, b - a.nqb, sP);
+    __syncthreads();
+    const int rows = min(16, a.n - 16 * t.rt), col0 = 32 * t.qg;
+    for (int e = threadIdx.x; e < rows * 32; e += WAVES * 64) {
+      const int rr = e >> 5, cc = e & 31;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) v += sP[w][rr][cc];  // wave order
+      __hip_atomic_store(&a.P[((size_t)t.c * a.n + 16 * t.rt + rr) * a.r_pad + col0 + cc], v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every store of this thread has completed
+  __syncthreads();
+  if (threadIdx.x < kFCopies && !f.silent)
+    __hip_atomic_fetch_add(f.sync + kFDone + kFStride * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false, bool FU = false>
+__global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g, SmallFuse f) {
   constexpr int U = (WAVES == 4 && TWO && !XL) ? 4 : ((WAVES == 4 || TWO) ? 8 : 16);  // 64-byte steps per wave per batch
   constexpr int NT = WAVES * 64;
   constexpr int MT = TWO ? 32 : 16;  // token rows held for the low-rank stage
   constexpr bool LR = EPI == EPI_LINEAR;
   constexpr bool QL = EPI == EPI_QLR;  // quantised low-rank branch: second stage on the int8 MFMA
-  __shared__ int red[WAVES][TWO ? 2 : 1][4][64];
-  __shared__ __attribute__((aligned(16))) bf16_t sT[LR ? MT * 256 : 1];
-  __shared__ __attribute__((aligned(16))) bf16_t sL[LR ? 16 * 256 : 1];
-  __shared__ __attribute__((aligned(16))) float4 sPart[LR ? NT : 1][2];
+  // LDS: red [WAVES][TWO ? 2 : 1][4][64] int | sT [MT x 256] bf16 | sL [16 x 256]
+  // bf16 | sPart [NT][2] float4; a producer block (FU) reuses it whole
+  constexpr int B_RED = WAVES * (TWO ? 2 : 1) * 4 * 64 * 4;
+  constexpr int B_ST = LR ? MT * 256 * 2 : 16, B_SL = LR ? 16 * 256 * 2 : 16, B_SP = LR ? NT * 32 : 16;
+  constexpr int B_GEMV = B_RED + B_ST + B_SL + B_SP, B_PRO = FU ? WAVES * 16 * 33 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[B_GEMV > B_PRO ? B_GEMV : B_PRO];
+  __shared__ int s_ok;
+  auto red = reinterpret_cast<int (*)[TWO ? 2 : 1][4][64]>(smem);
+  bf16_t* sT = reinterpret_cast<bf16_t*>(smem + B_RED);
+  bf16_t* sL = reinterpret_cast<bf16_t*>(smem + B_RED + B_ST);
+  auto sPart = reinterpret_cast<float4 (*)[2]>(smem + B_RED + B_ST + B_SL);
+  if constexpr (FU) {
+    if ((int)blockIdx.x < f.nprod) {
+      small_producer<WAVES>(f, smem);
+      return;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = (FU ? (int)blockIdx.x - f.nprod : (int)blockIdx.x) * 16;
   const uint8_t* bp = g.B + (size_t)min(n0 + l16, g.N - 1) * g.ldb + 16 * lg;
   const uint8_t* ap0 = g.A + (size_t)min(l16, g.M - 1) * g.lda + 16 * lg;
   const uint8_t* ap1 = g.A + (size_t)min(16 + l16, g.M - 1) * g.lda + 16 * lg;
@@ -81,22 +170,25 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   constexpr int XLN = XL ? gemv_xl_bytes(WAVES) / 16 / NT : 1;
   const int XS = g.Kb + 16, kp = g.Kb >> 4;
   uint4 xst[XLN];
-  if (XL) {
+  auto load_xl = [&]() {
 #pragma unroll
     for (int i = 0; i < XLN; ++i) {
       const int idx = min(tid + NT * i, g.M * kp - 1);
       xst[i] = *reinterpret_cast<const uint4*>(g.A + (size_t)(idx / kp) * g.lda + 16 * (idx % kp));
     }
-  }
+  };
+  if (XL && !FU) load_xl();
 
   // Loads are unconditional, from clamped (always valid) addresses, and
   // masked where used: conditional loads become branches whose register
   // merges force early waits on every load in flight.
   const int kb_last = max(0, min((max(send, sbeg + 1) - 1) * 64, g.Kb - 16 - 16 * lg));
   uint4 bv[U], av0[U], av1[U];
-  auto load_batch = [&](int s0) {
+  auto load_w = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) bv[u] = *reinterpret_cast<const uint4*>(bp + min((s0 + u) * 64, kb_last));
+  };
+  auto load_x = [&](int s0) {
     if (XL) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -104,6 +196,10 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
       av0[u] = *reinterpret_cast<const uint4*>(ap0 + kb);
       if (TWO) av1[u] = *reinterpret_cast<const uint4*>(ap1 + kb);
     }
+  };
+  auto load_batch = [&](int s0) {
+    load_w(s0);
+    load_x(s0);
   };
   const uint8_t* xl0 = xl_lds + min(l16, g.M - 1) * XS + 16 * lg;
   const uint8_t* xl1 = xl_lds + min(16 + l16, g.M - 1) * XS + 16 * lg;
@@ -143,10 +239,13 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   // asymmetric activations (codes u - 8): per row z + 8 s_x, per channel
   // s_w colsum(C_w) (CoQuant Eq. 1 with a zero-point)
   float zzv[4] = {0.f, 0.f, 0.f, 0.f}, wzv = 0.0f;
-  if (LR || QL) {
-    swv = g.sw[min(n0 + l16, g.N - 1)];
+  auto load_sx = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
+  };
+  if (LR || QL) {
+    swv = g.sw[min(n0 + l16, g.N - 1)];
+    if (!FU) load_sx();
     if (LR && g.zx) {
       wzv = swv * (float)g.csw[min(n0 + l16, g.N - 1)];
 #pragma unroll
@@ -175,16 +274,53 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 #pragma unroll
     for (int i = 0; i < 4; ++i) qs[i] = g.st[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)] * (1.0f / 16);
   }
-  load_batch(sbeg);
+  uint4 lv;
+  bool ok = true;  // FU: the producers' results arrived (else the block writes NaN)
+  if constexpr (FU) {
+    // the weights of the first batch and the rows of L2^T depend on nothing
+    load_w(sbeg);
+    if (LR && rp > 0) {
+      const int el = min(tid, 16 * rq - 1);
+      lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
+    }
+    if (wave == 0) {
+      const unsigned* sy = f.sync;
+      const bool clean = ld_agent(sy + kWFlag) == 0;
+      bool done = false;
+      for (unsigned it = 0;; ++it) {
+        if ((int)ld_agent(sy + kFDone + kFStride * (blockIdx.x % kFCopies)) >= f.nprod) {
+          done = true;
+          break;
+        }
+        if (it >= f.spin) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!done && lane == 0)
+        __hip_atomic_store(const_cast<unsigned*>(sy + kWFlag), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) s_ok = (done && clean) ? 1 : 0;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): s_ok written
+    }
+    // a barrier that does not wait for the weight loads in flight
+    asm volatile("s_barrier" ::: "memory");
+    ok = s_ok != 0;
+    if (LR || QL) load_sx();
+    if (XL)
+      load_xl();
+    else
+      load_x(sbeg);
+  } else {
+    load_batch(sbeg);
+  }
   // Low-rank operands, with clamped (always valid) indices, masked where used,
   // so that none of them needs a wait before the integer product: piece
   // tid of L2^T (16 x rp), and for thread (piece p, group q), q < G, of T
   // the chunks q and q + G of the prologue's fp32 partials.
-  uint4 lv;
   float4 pv[2][2];
   if (LR && rp > 0) {
-    const int el = min(tid, 16 * rq - 1);
-    lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
+    if (!FU) {
+      const int el = min(tid, 16 * rq - 1);
+      lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
+    }
     if (tid < NP * G) {
       const int pc = tid % NP, grp = tid / NP;
       const int rowt = pc / rq, qt = pc % rq;
@@ -330,11 +466,31 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * tile + 4 * lg + i;
       if (row >= g.M || col >= g.N) continue;
-      const float y = (float)sacc[i] * (sxv[i] * swv) + lr[i] + zzv[i] * wzv;
+      const float y = ok ? (float)sacc[i] * (sxv[i] * swv) + lr[i] + zzv[i] * wzv : __builtin_nanf("");
       if (g.y_bf16)
         reinterpret_cast<bf16_t*>(g.Y)[(size_t)row * g.ldy + col] = (bf16_t)f32_to_bf16_bits(y);
       else
         reinterpret_cast<float*>(g.Y)[(size_t)row * g.ldy + col] = y;
+    }
+  }
+  if constexpr (FU) {
+    if (wave == 0 && lane == 0) {
+      // the last block overall brings the counters back to zero (every GEMM
+      // block has passed its wait, so no poll of kFDone is still to come)
+      const unsigned ncons = gridDim.x - (unsigned)f.nprod, cb = blockIdx.x - (unsigned)f.nprod;
+      const unsigned gs = max(32u, (ncons + kFGroups - 1) / kFGroups), gi = cb / gs;
+      const unsigned ngr = (ncons + gs - 1) / gs, gsize = min(gs, ncons - gi * gs);
+      unsigned* gc = f.sync + kFGroup + 4 * gi;
+      if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1) {
+        __hip_atomic_fetch_sub(gc, gsize, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__hip_atomic_fetch_add(f.sync + kFFin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngr - 1) {
+          if (!f.silent)
+            for (int i = 0; i < kFCopies; ++i)
+              __hip_atomic_fetch_sub(f.sync + kFDone + kFStride * i, (unsigned)f.nprod, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_sub(f.sync + kFFin, ngr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
   }
 }
@@ -355,16 +511,85 @@ static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
   const bool use_xl = xl <= (size_t)gemv_xl_bytes(g.Kb > 2048 ? 8 : 4) && g.Kb % 16 == 0;
   if (g.Kb > 2048) {
     if (use_xl)
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, true, DBG>), dim3(blocks), dim3(512), xl, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, true, DBG>), dim3(blocks), dim3(512), xl, st, g, SmallFuse{});
     else
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, false, DBG>), dim3(blocks), dim3(512), 0, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 8, TWO, false, DBG>), dim3(blocks), dim3(512), 0, st, g, SmallFuse{});
   } else {
     if (use_xl)
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, true, DBG>), dim3(blocks), dim3(256), xl, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, true, DBG>), dim3(blocks), dim3(256), xl, st, g, SmallFuse{});
     else
-      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, false, DBG>), dim3(blocks), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((k_gemv<BITS, EPI, 4, TWO, false, DBG>), dim3(blocks), dim3(256), 0, st, g, SmallFuse{});
   }
   return hipGetLastError();
+}
+
+// One-launch form (up to 16 tokens): the producers first in the grid, then
+// the GEMM blocks.
+template <bool DBG>
+static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_t st) {
+  const dim3 grid((unsigned)(f.nprod + (g.N + 15) / 16));
+  const size_t xl = (size_t)g.M * (size_t)(g.Kb + 16);
+  const bool use_xl = xl <= (size_t)gemv_xl_bytes(g.Kb > 2048 ? 8 : 4) && g.Kb % 16 == 0;
+  constexpr int E = EPI_LINEAR;
+  if (g.Kb > 2048) {
+    if (use_xl)
+      launch_kernel(k_gemv<4, E, 8, false, true, DBG, true>, grid, dim3(512), (unsigned)xl, st, g, f);
+    else
+      launch_kernel(k_gemv<4, E, 8, false, false, DBG, true>, grid, dim3(512), 0u, st, g, f);
+  } else {
+    if (use_xl)
+      launch_kernel(k_gemv<4, E, 4, false, true, DBG, true>, grid, dim3(256), (unsigned)xl, st, g, f);
+    else
+      launch_kernel(k_gemv<4, E, 4, false, false, DBG, true>, grid, dim3(256), 0u, st, g, f);
+  }
+  return hipGetLastError();
+}
+
+// Whether the one-launch grid is (nearly) resident at once on the current
+// device: at most a quarter more blocks than fit.  The producers come first
+// in the grid, so they never wait for a slot; but GEMM blocks beyond the
+// resident ones start only as others finish, which cuts the weight stream in
+// two.  Measured: 296 blocks on 256 slots (down projection, 8 tokens) still
+// faster than two launches, 1816 on 1024 (gate and up grouped, 16 tokens)
+// slower.
+template <bool DBG>
+static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  const size_t xl = (size_t)M * (size_t)(Kb + 16);
+  const bool use_xl = xl <= (size_t)gemv_xl_bytes(Kb > 2048 ? 8 : 4) && Kb % 16 == 0;
+  constexpr int E = EPI_LINEAR;
+  hipError_t e;
+  if (Kb > 2048)
+    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, true, DBG, true>, 512, xl)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, false, DBG, true>, 512, 0);
+  else
+    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, true, DBG, true>, 256, xl)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, false, DBG, true>, 256, 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return 4 * ((int64_t)nprod + (N + 15) / 16) <= 5 * (int64_t)cus * occ;
+}
+
+bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool dbg) {
+  return dbg ? gemv_fused_fits_t<true>(M, Kb, N, nprod) : gemv_fused_fits_t<false>(M, Kb, N, nprod);
+}
+
+hipError_t launch_gemv_fused(const GemmArgs& g, const SmallFuse& f, hipStream_t st) {
+  const PrologueArgs& a = f.pa;
+  // the producers' shapes: bf16 rows of at most 8 KB (4 waves) or 32 KB
+  // (8 waves) in registers, T partials of 32 columns each, all summed by the
+  // GEMM blocks in one pass
+  if (g.M < 1 || g.M > 16 || a.n != g.M || 2 * g.Kb != a.d || a.d % 32 || a.d > (g.Kb > 2048 ? 16384 : 4096) ||
+      a.nqb != g.M || !f.sync || g.r_pad > 256 || (g.r_pad > 0 && (a.nqg < 1 || a.r_pad % 32 || !g.P)) ||
+      f.nprod != a.nqb + (g.r_pad ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0) || g.nchunk != a.nchunk ||
+      g.nchunk > gemv_max_chunks(g.M, g.Kb, g.ldt))
+    return hipErrorInvalidValue;
+  return g.acc ? gemv_fused_t<true>(g, f, st) : gemv_fused_t<false>(g, f, st);
 }
 
 template <int BITS, int EPI>

@@ -154,6 +154,9 @@ struct ProloguePlan {
 // small: few tokens (T as k-chunk partials for the small-n GEMM, which can sum
 // at most max_chunks of them in one pass).
 ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks);
+// The producers of the one-launch few-token layer (tq_prologue.h, SmallFuse):
+// d % 32 == 0, d <= 16384, r_pad a multiple of 32 (or 0).
+ProloguePlan plan_prologue_fused(int n, int d, int r_pad, int max_chunks);
 // Most k-chunk partials of T the small-n GEMM sums in one pass for M tokens.
 int gemv_max_chunks(int M, int Kb, int r_pad);
 hipError_t launch_prologue(const void* X, bool bf16, int n, int d, const void* L1t, int r_pad, const ProloguePlan& p,

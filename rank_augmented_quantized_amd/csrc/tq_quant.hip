@@ -10,7 +10,7 @@
 // weights (CoQuant experimental protocol).  Low-rank stage: TwinQuant notes
 // section 02.A (X U V) and section 04.C (two-stage low-rank product).
 
-#include "tq_kernels.h"
+#include "tq_prologue.h"
 
 namespace tq {
 
@@ -299,101 +299,6 @@ __global__ __launch_bounds__(256) void k_quant_rows_wave(const T* __restrict__ X
                                     cb ? cb + row * ldb : nullptr, sb ? sb + row : nullptr);
 }
 
-// ---------------------------------------------------------------------------
-// One row quantised at 4 bits by a whole block, each thread holding CHB
-// chunks of 8 values (chunk tid + blockDim.x i) in registers, so X is read
-// once and the row's arithmetic is spread over all the block's waves (the
-// few-token case, where one wave per row would leave the GPU idle).  Every
-// thread of the block must call it (it contains a barrier).
-// ---------------------------------------------------------------------------
-template <typename T, int CHB>
-__device__ __forceinline__ void quant_row_block_reg(const T* __restrict__ x, int d, uint8_t* __restrict__ c,
-                                                    float* __restrict__ s, float* red) {
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, w = tid >> 6, nw = nthr >> 6;
-  const int nch = d >> 3;
-  Row8<T> r[CHB];
-#pragma unroll
-  for (int i = 0; i < CHB; ++i) {
-    const int ch = tid + nthr * i;
-    if (ch < nch) r[i].load(x + 8 * ch);
-  }
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < CHB; ++i) {
-    if (tid + nthr * i < nch) {
-      float v[8];
-      r[i].get(v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-    }
-  }
-  m = wave_max(m);
-  if (lane == 0) red[w] = m;
-  __syncthreads();
-  m = 0.0f;
-  for (int i = 0; i < nw; ++i) m = fmaxf(m, red[i]);
-  const RowScale rs = row_scale<4>(m);
-  if (tid == 0) *s = rs.s;
-  if (__builtin_amdgcn_readfirstlane(rs.fast ? 1 : 0)) {
-#pragma unroll
-    for (int i = 0; i < CHB; ++i) {
-      const int ch = tid + nthr * i;
-      if (ch < nch) {
-        float v[8];
-        int q[8];
-        r[i].get(v);
-        quant8_fast<4>(v, rs, q);
-        *reinterpret_cast<uint32_t*>(c + (size_t)ch * 4) = pack_nibbles(q);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < CHB; ++i) {
-      const int ch = tid + nthr * i;
-      if (ch < nch) {
-        float v[8];
-        int q[8];
-        r[i].get(v);
-        quant8_exact<4>(v, rs.s, q);
-        *reinterpret_cast<uint32_t*>(c + (size_t)ch * 4) = pack_nibbles(q);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Prologue of tq_linear: one launch, two kinds of blocks.
-//  * blocks [0, nqb): 4-bit codes and s_x of WAVES rows, one per wave, or,
-//    for few tokens (row_blocks), of one row per block (skipped, nqb = 0,
-//    when the row does not fit in registers); X8: codes as int8 in the order
-//    of the int8 tile GEMM (d bytes per row), else nibble-packed;
-//  * blocks [nqb, nqb + ntb): the first low-rank stage T = X L1 on
-//    v_mfma_f32_16x16x32_bf16.  Block (rt, c, qg) takes rows 16 rt..16 rt+15,
-//    the k-range [c kc, (c+1) kc) and the QS 16-column slices of group qg;
-//    its waves take the 32-k steps round-robin, U steps per wave in flight,
-//    and their partials are summed through LDS in wave order.
-//    - partial mode (few tokens): the block writes its fp32 partial to
-//      P[c]; the small-n GEMM sums the chunks;
-//    - one k-chunk: the block writes T directly;
-//    - otherwise the block writes its fp32 partial to P and the last block of
-//      the (rt, qg) group to finish (agent-scope counter) sums the partials
-//      in chunk order into T and resets the counter.
-// MFMA operand layout: lane l supplies row (or T column) l % 16 and the 8
-// consecutive k at 32 step + 8 (l / 16), for X and L1^T alike.
-// ---------------------------------------------------------------------------
-struct PrologueArgs {
-  const void* X;
-  int n, d;
-  const bf16_t* L1t;
-  int r_pad, kc, nchunk, qs, nqg, nqb, partial, row_blocks;
-  int sum_to_p0;  // the last block also leaves the fp32 sum of the chunks in chunk 0 of P
-  uint8_t* xc;
-  float* sx;
-  float* P;
-  bf16_t* T;
-  unsigned* counters;
-};
-
 template <typename T, int CH, int QS, int WAVES, int U, bool X8>
 __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
   constexpr int COLS = 16 * QS;
@@ -415,48 +320,10 @@ __global__ __launch_bounds__(WAVES * 64) void k_prologue(PrologueArgs a) {
                                       a.xc + (size_t)row * (X8 ? a.d : (a.d >> 1)), a.sx + row, nullptr, nullptr);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int tb = b - a.nqb;
-  const int per_rt = a.nchunk * a.nqg;
-  const int rt = tb / per_rt, c = (tb % per_rt) / a.nqg, qg = tb % a.nqg;
-  const int d = a.d, n = a.n;
-  // k-chunk c covers the 32-k steps [c * kc / 32, (c + 1) * kc / 32); wave w takes every WAVES-th
-  const int s0 = c * (a.kc >> 5), s1 = min(d >> 5, s0 + (a.kc >> 5));
-  const T* xr = X + (size_t)min(16 * rt + lr, n - 1) * d;
-  const bf16_t* lp = a.L1t + (size_t)(16 * qg * QS + lr) * d;
-
-  f32x4 acc[QS];
-#pragma unroll
-  for (int q = 0; q < QS; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sb = s0 + w; sb < s1; sb += WAVES * U) {  // batches of U steps, all loads in flight
-    uint4 xa[U];
-    uint4 lb[U][QS];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = sb + WAVES * u;
-      const int k = 32 * s + 8 * lg;
-      if (s < s1) {
-        float v[8];
-        Load8<T>::load(xr + k, v, xa[u]);
-#pragma unroll
-        for (int q = 0; q < QS; ++q) lb[u][q] = *reinterpret_cast<const uint4*>(lp + (size_t)16 * q * d + k);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (sb + WAVES * u < s1) {
-#pragma unroll
-        for (int q = 0; q < QS; ++q)
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(lb[u][q]), acc[q], 0, 0, 0);
-      }
-    }
-  }
-  // 16x16 result layout: lane l, element i -> row 4 (l / 16) + i, column l % 16.
-#pragma unroll
-  for (int q = 0; q < QS; ++q)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sP[w][4 * lg + i][16 * q + lr] = acc[q][i];
+  const int tid = threadIdx.x;
+  const TBlock tbk = t_block_products<T, QS, WAVES, U>(a, b - a.nqb, sP);
+  const int rt = tbk.rt, c = tbk.c, qg = tbk.qg;
+  const int n = a.n;
   __syncthreads();
   const int rows = min(16, n - 16 * rt);
   const int col0 = 16 * qg * QS;
@@ -873,6 +740,34 @@ static hipError_t launch_prologue_fused(const void* X, bool bf16, int n, int d, 
 constexpr int kFusedMinRows = 1024;
 // Most k-chunks of T the few-token prologue sums itself.
 constexpr int kMaxPrologueChunks = 64;
+
+// The producers of the one-launch few-token layer: a block per token row,
+// then T blocks of 32 columns each (QS = 2) over k-chunks of at least 16
+// steps, at most max_chunks of them (the GEMM blocks sum them in one pass).
+ProloguePlan plan_prologue_fused(int n, int d, int r_pad, int max_chunks) {
+  ProloguePlan p{};
+  const int steps = d / 32;
+  p.waves = d > 4096 ? 8 : 4;
+  p.qs = 2;
+  p.quant_in_prologue = true;
+  p.row_blocks = true;
+  p.partial = true;
+  p.nqb = n;
+  if (r_pad == 0) {
+    p.nqg = 0;
+    p.nchunk = 1;
+    p.kc = d;
+    p.ntb = 0;
+    return p;
+  }
+  p.nqg = r_pad / 32;
+  const int nch = std::max(1, std::min((steps + 15) / 16, max_chunks));
+  const int chunk_steps = (steps + nch - 1) / nch;
+  p.kc = 32 * chunk_steps;
+  p.nchunk = (steps + chunk_steps - 1) / chunk_steps;
+  p.ntb = ((n + 15) / 16) * p.nchunk * p.nqg;
+  return p;
+}
 
 ProloguePlan plan_prologue(int n, int d, int r_pad, bool small, int max_chunks) {
   ProloguePlan p{};

@@ -368,28 +368,36 @@ def test_linear_r0_is_pure_w4a4_and_deterministic():
 
 
 def _sync_words(ws, n, d, m, r):
-    """The hand-off words (4 KiB): word 0 the one-launch path's call counter, word 16 a counter that is zero between
-    calls, word 32 the wait-limit flag."""
+    """The hand-off words (4 KiB): word 0 the decode kernel's call counter, word 32 the wait-limit flag, every other
+    word a counter that is zero between calls."""
     off = tq.tq_linear_workspace_offsets(n, d, m, r)["sync"]
     return ws[off: off + 4096].view(torch.int32).cpu().numpy()
 
 
 def _one_launch(n, d, r):
-    """Shapes of the one-launch few-token path (include/tq.h): one or two tokens, d a multiple of 32 up to 16384,
-    n d <= 16384, and at most 128 blocks computing partials of T (chunks of 512 k times r_pad / 16 column groups)."""
+    """Shapes of the decode kernel (include/tq.h): one or two tokens, d a multiple of 32 up to 16384, n d <= 16384,
+    and at most 128 blocks computing partials of T (chunks of 512 k times r_pad / 16 column groups)."""
     nt = -(-d // 512) * (_r_pad(r) // 16)
     return n <= 2 and n * d <= 16384 and d <= 16384 and d % 32 == 0 and nt <= 128
+
+
+def _fused_small(n, d, m, r):
+    """Shapes of the one-launch few-token GEMM (bf16 X): up to 16 tokens, d up to 16384, not the decode kernel's, and
+    a grid resident at once (the shapes here have at most a few hundred blocks, or more than a GPU of 256 compute
+    units holds: 2048 blocks of at least 4 waves)."""
+    return n <= 16 and d <= 16384 and not _one_launch(n, d, r) and m // 16 < 2048
 
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 2048, 200, 64), (1, 4064, 64, 32), (2, 512, 40, 0),
                                      (2, 1024, 48, 256), (1, 14336, 64, 32), (1, 16384, 40, 32), (1, 16384, 40, 256), (2, 8192, 72, 32),
                                      (1, 96, 16, 32), (5, 2048, 200, 64), (3, 96, 16, 32), (16, 4096, 300, 64),
-                                     (8, 14336, 72, 64), (11, 4064, 130, 256), (16, 8192, 64, 32), (9, 16384, 40, 32),
+                                     (8, 14336, 72, 64), (11, 4064, 130, 256), (16, 8192, 64, 32), (9, 16384, 40, 32), (3, 16416, 40, 32),
+                                     (8, 1024, 40000, 32),
                                      (24, 2048, 200, 64)])
 def test_small_n_single_launch_handoff(n, d, m, r):
-    """One or two tokens run in one launch whose blocks wait for the partials of T that other blocks compute: every
-    call advances the call counter by one and leaves the other words at zero (no wait gave up), and calls repeated on
-    one workspace give identical outputs (n = 5 takes the two-launch path and leaves the words untouched)."""
+    """Up to 16 tokens run in one launch whose blocks wait for the codes and the partials of T that other blocks
+    compute (17 .. 32 tokens, and rows longer than 16384, take two launches).  The decode kernel (one or two tokens) advances its call counter by one per call; both kernels leave
+    the other words at zero (no wait gave up), and calls repeated on one workspace give identical outputs."""
     print(f"case n={n} d={d} m={m} r={r}", flush=True)
     c = draw_custom(n, d, m, max(r, 1), seed=90 + n)
     wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
@@ -398,8 +406,17 @@ def test_small_n_single_launch_handoff(n, d, m, r):
     x = _x_tensor(c["X"], "bf16")
     ys = []
     for call in range(4):
+        if call == 0:  # which launches the call makes, by the library's own launch records
+            tq.tq_profile_reset()
+            tq.tq_profile_enable(True)
         ys.append(tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws))
         torch.cuda.synchronize()
+        if call == 0:
+            tq.tq_profile_enable(False)
+            names = set(tq.tq_profile_read())
+            tq.tq_profile_reset()
+            assert names == ({"decode"} if _one_launch(n, d, r) else {"small_fused"} if _fused_small(n, d, m, r)
+                             else {"prologue", "gemm_small_n"}), names
         w = _sync_words(ws, n, d, m, r)
         assert w[0] == (call + 1 if _one_launch(n, d, r) else 0)
         assert not w[1:].any()
@@ -409,12 +426,14 @@ def test_small_n_single_launch_handoff(n, d, m, r):
     _assert_y(ys[0], ref["Y"], f"n{n}")
 
 
-@pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 8192, 40, 32)])
+@pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 8192, 40, 32), (16, 4096, 300, 64), (8, 14336, 72, 64),
+                                     (12, 2048, 40, 32)])
 def test_handoff_gives_up_loudly(n, d, m, r):
-    """The one-launch path's failure mode, forced from the host: the blocks computing T tag their partials with the
-    previous call's tag and the waits are limited to a few polls, so every wait gives up (every kernel still exits).
-    Y is then NaN everywhere and the flag word is set; later calls on that workspace keep writing NaN (the flag is
-    sticky), and once the workspace is zero-filled a call gives the correct Y again."""
+    """The one-launch paths' failure mode, forced from the host: the producer blocks never deliver (the decode
+    kernel's tag its partials with the previous call's tag, the few-token GEMM's never signal) and the waits are
+    limited to a few polls, so every wait gives up (every kernel still exits).  Y is then NaN everywhere and the
+    flag word is set; later calls on that workspace keep writing NaN (the flag is sticky), and once the workspace is
+    zero-filled a call gives the correct Y again."""
     print(f"case n={n} d={d} m={m} r={r}", flush=True)
     c = draw_custom(n, d, m, r, seed=70 + n)
     wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
@@ -426,7 +445,7 @@ def test_handoff_gives_up_loudly(n, d, m, r):
     torch.cuda.synchronize()
     assert torch.isnan(y).all()
     w = _sync_words(ws, n, d, m, r)
-    assert w[32] != 0 and w[16] == 0 and w[0] == 1
+    assert w[32] != 0 and not np.delete(w, [0, 32]).any() and w[0] == (1 if _one_launch(n, d, r) else 0)
     y2 = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws)
     torch.cuda.synchronize()
     assert torch.isnan(y2).all()

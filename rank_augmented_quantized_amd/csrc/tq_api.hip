@@ -109,6 +109,9 @@ hipError_t timed(const char* name, hipStream_t st, F&& launch) {
     if (_e != hipSuccess) return TQ_ERR_HIP;                     \
   } while (0)
 
+// Fixed counter region after the hand-off words (see linear_ws).
+constexpr size_t kCtrBytes = 4096;
+
 struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;  // columns of T
@@ -127,14 +130,12 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_laun
   w.r_pad = (int)tcols;
   w.decode = !two_launch && n > 0 && tq::decode_ok((int)n, (int)d, w.r_pad);
   size_t psize = 0;
-  int counters = 0;
   if (w.decode) {
     w.dplan = tq::plan_decode((int)n, (int)d, (int)m, (int)(rp < 0 ? tcols : rp), w.r_pad, false);
     psize = tq::decode_partials_bytes(w.dplan, (int)n, w.r_pad);
   } else {
     w.plan = tq::plan_prologue((int)n, (int)d, w.r_pad, w.small,
                                w.small ? tq::gemv_max_chunks((int)n, (int)(d / 2), w.r_pad) : 1);
-    counters = w.plan.counters;
     if (w.plan.ntb > 0 && (w.plan.nchunk > 1 || w.plan.partial))
       psize = (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
     // one launch up to 16 tokens; for 17 .. 32 (two 16-token tiles per
@@ -146,11 +147,15 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_laun
         psize = std::max(psize, (size_t)w.fplan.nchunk * (size_t)n * (size_t)w.r_pad * 4);
     }
   }
+  // The counters sit at fixed offsets, whatever the shape, so that a
+  // workspace zero-filled once serves calls of any shape in turn: the
+  // hand-off words of the one-launch paths, then kCtrBytes holding the
+  // prologue's counters (fewer than 128).
   size_t o = 0;
   w.sync = o;  // hand-off counters of the few-token launch
   o = tq::kSyncBytes;
   w.ctr = o;
-  o = align256(o + (size_t)counters * 4 + 1);
+  o += kCtrBytes;
   w.sx = o;
   o = align256(o + (size_t)n * 4);
   w.xc = o;  // activation codes: int8 (d bytes per row) for the tile GEMM, else packed
@@ -345,6 +350,8 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   const int rp = (int)r_padded(r);
   const LinearWs L = linear_ws(n, d, m, group_tcols(G, r), false, rp);
   if (ws_bytes < L.total) return TQ_ERR_WORKSPACE;
+  // the fixed counter region holds every counter this shape uses
+  if ((size_t)L.plan.counters * 4 > kCtrBytes) return TQ_ERR_SHAPE;
 
   uint8_t* base = (uint8_t*)ws;
   unsigned* ctr = (unsigned*)(base + L.ctr);

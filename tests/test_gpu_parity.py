@@ -327,6 +327,11 @@ LCASES = [
     # 224 tiles of 256 x 256 with rows of 144 code bytes: the last 128-k
     # stage of each row is partial
     ("n4096_d288_full_tiles_ragged_k", 4096, 288, 3584, 32, "normal", "bf16", 2),
+    # 128 x 128 tiles over long rows: 16, 64 and 17 stages of 128 k (the
+    # last one partial, with fp32 Y)
+    ("n100_d2048_tiles128", 100, 2048, 300, 32, "normal", "bf16", 2),
+    ("n200_d8192_tiles128", 200, 8192, 520, 64, "normal", "bf16", 3),
+    ("n70_d2080_ragged_k_f32_out", 70, 2080, 200, 32, "student_t", "bf16", 0),
 ]
 
 
@@ -458,7 +463,7 @@ def test_handoff_gives_up_loudly(n, d, m, r):
 
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 2048, 300, 64), (16, 1024, 200, 32), (40, 512, 96, 32),
-                                     (1030, 512, 80, 32)])
+                                     (1030, 512, 80, 32), (100, 2048, 300, 32)])
 def test_graph_replay_matches_eager(n, d, m, r):
     """tq_linear captured in a HIP graph (as a serving loop would run it): every replay, with eager calls and
     synchronisations in between, gives the eager output bit for bit and leaves the hand-off words at zero."""
@@ -490,6 +495,27 @@ def test_graph_replay_matches_eager(n, d, m, r):
         y_again = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws_e)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y_again, y_e)
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace, zero-filled once, serves calls of different shapes in turn (the prologue's cross-block
+    counters, the one-launch few-token GEMM, the decode kernel): every call equals the same call on a fresh
+    workspace bit for bit, since every counter sits at a fixed offset and is zero again after each call."""
+    shapes = [(300, 1024, 512, 32), (40, 4096, 256, 32), (200, 1024, 384, 64), (12, 4096, 200, 64), (1, 4096, 300, 64),
+              (100, 2048, 300, 32), (70, 2080, 200, 32)]
+    big = max(tq.tq_linear_workspace_bytes(*sh) for sh in shapes)
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        for i, (n, d, m, r) in enumerate(shapes):
+            print(f"pass {rep} case n={n} d={d} m={m} r={r}", flush=True)
+            c = draw_custom(n, d, m, r, seed=40 + i)
+            wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+            lowrank = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+            x = _x_tensor(c["X"], "bf16")
+            y_fresh = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=tq.linear_workspace(n, d, m, r, DEV))
+            y = tq.tq_linear(x, wc, sw, lowrank, m, r, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_fresh), (rep, i)
 
 
 def test_small_n_and_tile_paths_agree():

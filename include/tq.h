@@ -192,7 +192,7 @@ size_t tq_linear_workspace_bytes(int64_t n, int64_t d, int64_t m, int64_t r);
  * For n <= 32 the call runs a memory-bound path (weight codes streamed once).
  * It is one launch for n <= 2, d <= 16384 and n d <= 16384 (and at most 128
  * partial blocks of T: ceil(d / 512) r_pad / 16 <= 128: the decode kernel),
- * and for any other n <= 16 with bf16 X and d <= 16384 whose grid is at most a
+ * and for any other n <= 16 with d <= 16384 whose grid is at most a
  * quarter larger than what the GPU holds at once (the few-token GEMM, whose
  * first blocks quantise X and compute partials of T; on MI355X 1024 blocks of
  * 16 output channels for d <= 4096, 256 above); otherwise two launches.  In a one-launch path, weight-streaming blocks read what other
@@ -529,8 +529,8 @@ tq_status tq_linear_qlr_debug(const void* X, tq_dtype x_dt, int64_t n, int64_t d
  * delivering (the decode kernel's tag their partials of T with the previous
  * call's tag, the few-token GEMM's never signal), so that every wait gives up
  * and the failure path runs (Y all NaN, the flag word set).  Every kernel
- * still exits.  TQ_ERR_SHAPE when the shape and X's type do not take a
- * one-launch path, or r == 0.
+ * still exits.  TQ_ERR_SHAPE when the shape does not take a one-launch path,
+ * or r == 0.
  */
 tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m, int64_t r,
                                   const void* w_codes, const float* s_w, const void* lowrank, void* Y, tq_dtype y_dt,

@@ -116,7 +116,7 @@ struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;  // columns of T
   bool small, decode;
-  bool fused;  // bf16 X takes the one-launch few-token layer (fplan)
+  bool fused;  // the one-launch few-token layer (fplan), when its grid fits
   tq::ProloguePlan plan, fplan;
   tq::DecodePlan dplan;
 };
@@ -424,7 +424,7 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
   g.y_bf16 = y_dt == TQ_BF16;
   g.acc = acc;
 
-  if (L.fused && xb && tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, acc != nullptr)) {
+  if (L.fused && tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, xb, acc != nullptr)) {
     // one launch: the quantiser and the partials of T run in the GEMM's grid
     const tq::ProloguePlan& fp = L.fplan;
     tq::SmallFuse f{};
@@ -437,7 +437,7 @@ tq_status linear_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t
     g.P = L.r_pad ? P : nullptr;
     g.nchunk = fp.nchunk;
     g.Tout = L.r_pad ? T : nullptr;
-    TQ_RUN("small_fused", stream, tq::launch_gemv_fused(g, f, stream));
+    TQ_RUN("small_fused", stream, tq::launch_gemv_fused(g, f, xb, stream));
     return TQ_OK;
   }
   TQ_RUN("prologue", stream,
@@ -574,8 +574,8 @@ tq_status tq_debug_linear_handoff(const void* X, tq_dtype x_dt, int64_t n, int64
   const tq_status st = linear_check(X, x_dt, n, d, m, r, w_codes, s_w, lowrank, Y, y_dt, ws);
   if (st != TQ_OK || n == 0) return st;
   const LinearWs L = linear_ws(n, d, m, r_padded(r));
-  const bool fused = L.fused && x_dt == TQ_BF16 &&
-                     tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, false);
+  const bool fused =
+      L.fused && tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, x_dt == TQ_BF16, false);
   if (r == 0 || !(L.decode || fused)) return TQ_ERR_SHAPE;  // no hand-off on this path
   const int64_t ms[1] = {m};
   const HandoffDebug dbg{spin, silent};

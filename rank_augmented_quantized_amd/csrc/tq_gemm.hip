@@ -36,7 +36,7 @@ namespace tq {
 //   is one 16x16 bf16 MFMA chain whose result layout matches the integer
 //   accumulator's (lane l, element i -> token 4 (l / 16) + i, channel l % 16).
 //
-// FU, the one-launch form (bf16 X, up to 16 tokens): the prologue's work runs in the same grid
+// FU, the one-launch form (up to 16 tokens): the prologue's work runs in the same grid
 // (TwinQuant notes, section 04.C: the activations are quantised while the
 // residual GEMM runs, and both components meet in one epilogue).  Blocks
 // [0, nqb) quantise one token row each (codes and s_x), blocks [nqb, nprod)
@@ -89,20 +89,20 @@ __device__ __forceinline__ uint32_t ld_agent(const unsigned* p) {
   return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A producer block of the one-launch form (bf16 X): one row's codes and s_x,
-// or one fp32 partial of T (QS = 2: 32 columns), then the release and the
-// signal.  smem: the block's LDS.
-template <int WAVES>
+// A producer block of the one-launch form (X of type XT): one row's codes and s_x,
+// or one fp32 partial of T (QS = 2: 32 columns), then the signal once its
+// stores have completed.  smem: the block's LDS.
+template <int WAVES, typename XT>
 __device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem) {
   const PrologueArgs& a = f.pa;
   const int b = blockIdx.x;
   if (b < a.nqb) {
     constexpr int CHB = WAVES == 4 ? 2 : 4;  // 8-value chunks per thread: rows up to 8 KB (4 waves), 32 KB (8 waves)
-    quant_row_block_reg<bf16_t, CHB, true>((const bf16_t*)a.X + (size_t)b * a.d, a.d, a.xc + (size_t)b * (a.d >> 1),
-                                           a.sx + b, reinterpret_cast<float*>(smem));
+    quant_row_block_reg<XT, CHB, true>((const XT*)a.X + (size_t)b * a.d, a.d, a.xc + (size_t)b * (a.d >> 1), a.sx + b,
+                                       reinterpret_cast<float*>(smem));
   } else {
     auto sP = reinterpret_cast<float (*)[16][33]>(smem);
-    const TBlock t = t_block_products<bf16_t, 2, WAVES, 8>(a, b - a.nqb, sP);
+    const TBlock t = t_block_products<XT, 2, WAVES, 8>(a, b - a.nqb, sP);
     __syncthreads();
     const int rows = min(16, a.n - 16 * t.rt), col0 = 32 * t.qg;
     for (int e = threadIdx.x; e < rows * 32; e += WAVES * 64) {
@@ -120,7 +120,8 @@ __device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem
     __hip_atomic_fetch_add(f.sync + kFDone + kFStride * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false, bool FU = false>
+// FU: 0, or the one-launch form with bf16 (1) or fp32 (2) X.
+template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false, int FU = 0>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g, SmallFuse f) {
   constexpr int U = (WAVES == 4 && TWO && !XL) ? 4 : ((WAVES == 4 || TWO) ? 8 : 16);  // 64-byte steps per wave per batch
   constexpr int NT = WAVES * 64;
@@ -131,22 +132,22 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   // bf16 | sPart [NT][2] float4; a producer block (FU) reuses it whole
   constexpr int B_RED = WAVES * (TWO ? 2 : 1) * 4 * 64 * 4;
   constexpr int B_ST = LR ? MT * 256 * 2 : 16, B_SL = LR ? 16 * 256 * 2 : 16, B_SP = LR ? NT * 32 : 16;
-  constexpr int B_GEMV = B_RED + B_ST + B_SL + B_SP, B_PRO = FU ? WAVES * 16 * 33 * 4 : 0;
+  constexpr int B_GEMV = B_RED + B_ST + B_SL + B_SP, B_PRO = FU != 0 ? WAVES * 16 * 33 * 4 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[B_GEMV > B_PRO ? B_GEMV : B_PRO];
   __shared__ int s_ok;
   auto red = reinterpret_cast<int (*)[TWO ? 2 : 1][4][64]>(smem);
   bf16_t* sT = reinterpret_cast<bf16_t*>(smem + B_RED);
   bf16_t* sL = reinterpret_cast<bf16_t*>(smem + B_RED + B_ST);
   auto sPart = reinterpret_cast<float4 (*)[2]>(smem + B_RED + B_ST + B_SL);
-  if constexpr (FU) {
+  if constexpr (FU != 0) {
     if ((int)blockIdx.x < f.nprod) {
-      small_producer<WAVES>(f, smem);
+      small_producer<WAVES, std::conditional_t<FU == 1, bf16_t, float>>(f, smem);
       return;
     }
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = (FU ? (int)blockIdx.x - f.nprod : (int)blockIdx.x) * 16;
+  const int n0 = (FU != 0 ? (int)blockIdx.x - f.nprod : (int)blockIdx.x) * 16;
   const uint8_t* bp = g.B + (size_t)min(n0 + l16, g.N - 1) * g.ldb + 16 * lg;
   const uint8_t* ap0 = g.A + (size_t)min(l16, g.M - 1) * g.lda + 16 * lg;
   const uint8_t* ap1 = g.A + (size_t)min(16 + l16, g.M - 1) * g.lda + 16 * lg;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
       xst[i] = *reinterpret_cast<const uint4*>(g.A + (size_t)(idx / kp) * g.lda + 16 * (idx % kp));
     }
   };
-  if (XL && !FU) load_xl();
+  if (XL && FU == 0) load_xl();
 
   // Loads are unconditional, from clamped (always valid) addresses, and
   // masked where used: conditional loads become branches whose register
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   };
   if (LR || QL) {
     swv = g.sw[min(n0 + l16, g.N - 1)];
-    if (!FU) load_sx();
+    if (FU == 0) load_sx();
     if (LR && g.zx) {
       wzv = swv * (float)g.csw[min(n0 + l16, g.N - 1)];
 #pragma unroll
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   }
   uint4 lv;
   bool ok = true;  // FU: the producers' results arrived (else the block writes NaN)
-  if constexpr (FU) {
+  if constexpr (FU != 0) {
     // the weights of the first batch and the rows of L2^T depend on nothing
     load_w(sbeg);
     if (LR && rp > 0) {
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   // the chunks q and q + G of the prologue's fp32 partials.
   float4 pv[2][2];
   if (LR && rp > 0) {
-    if (!FU) {
+    if (FU == 0) {
       const int el = min(tid, 16 * rq - 1);
       lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
     }
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
         reinterpret_cast<float*>(g.Y)[(size_t)row * g.ldy + col] = y;
     }
   }
-  if constexpr (FU) {
+  if constexpr (FU != 0) {
     if (wave == 0 && lane == 0) {
       // the last block overall brings the counters back to zero (every GEMM
       // block has passed its wait, so no poll of kFDone is still to come)
@@ -525,7 +526,7 @@ static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
 
 // One-launch form (up to 16 tokens): the producers first in the grid, then
 // the GEMM blocks.
-template <bool DBG>
+template <bool DBG, int FU>
 static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_t st) {
   const dim3 grid((unsigned)(f.nprod + (g.N + 15) / 16));
   const size_t xl = (size_t)g.M * (size_t)(g.Kb + 16);
@@ -533,14 +534,14 @@ static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_
   constexpr int E = EPI_LINEAR;
   if (g.Kb > 2048) {
     if (use_xl)
-      launch_kernel(k_gemv<4, E, 8, false, true, DBG, true>, grid, dim3(512), (unsigned)xl, st, g, f);
+      launch_kernel(k_gemv<4, E, 8, false, true, DBG, FU>, grid, dim3(512), (unsigned)xl, st, g, f);
     else
-      launch_kernel(k_gemv<4, E, 8, false, false, DBG, true>, grid, dim3(512), 0u, st, g, f);
+      launch_kernel(k_gemv<4, E, 8, false, false, DBG, FU>, grid, dim3(512), 0u, st, g, f);
   } else {
     if (use_xl)
-      launch_kernel(k_gemv<4, E, 4, false, true, DBG, true>, grid, dim3(256), (unsigned)xl, st, g, f);
+      launch_kernel(k_gemv<4, E, 4, false, true, DBG, FU>, grid, dim3(256), (unsigned)xl, st, g, f);
     else
-      launch_kernel(k_gemv<4, E, 4, false, false, DBG, true>, grid, dim3(256), 0u, st, g, f);
+      launch_kernel(k_gemv<4, E, 4, false, false, DBG, FU>, grid, dim3(256), 0u, st, g, f);
   }
   return hipGetLastError();
 }
@@ -552,7 +553,7 @@ static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_
 // two.  Measured: 296 blocks on 256 slots (down projection, 8 tokens) still
 // faster than two launches, 1816 on 1024 (gate and up grouped, 16 tokens)
 // slower.
-template <bool DBG>
+template <bool DBG, int FU>
 static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
   int dev = 0, cus = 0, occ = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -563,11 +564,11 @@ static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
   constexpr int E = EPI_LINEAR;
   hipError_t e;
   if (Kb > 2048)
-    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, true, DBG, true>, 512, xl)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, false, DBG, true>, 512, 0);
+    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, true, DBG, FU>, 512, xl)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, false, DBG, FU>, 512, 0);
   else
-    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, true, DBG, true>, 256, xl)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, false, DBG, true>, 256, 0);
+    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, true, DBG, FU>, 256, xl)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, false, DBG, FU>, 256, 0);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return false;
@@ -575,21 +576,23 @@ static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
   return 4 * ((int64_t)nprod + (N + 15) / 16) <= 5 * (int64_t)cus * occ;
 }
 
-bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool dbg) {
-  return dbg ? gemv_fused_fits_t<true>(M, Kb, N, nprod) : gemv_fused_fits_t<false>(M, Kb, N, nprod);
+bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool x_bf16, bool dbg) {
+  if (x_bf16) return dbg ? gemv_fused_fits_t<true, 1>(M, Kb, N, nprod) : gemv_fused_fits_t<false, 1>(M, Kb, N, nprod);
+  return dbg ? gemv_fused_fits_t<true, 2>(M, Kb, N, nprod) : gemv_fused_fits_t<false, 2>(M, Kb, N, nprod);
 }
 
-hipError_t launch_gemv_fused(const GemmArgs& g, const SmallFuse& f, hipStream_t st) {
+hipError_t launch_gemv_fused(const GemmArgs& g, const SmallFuse& f, bool x_bf16, hipStream_t st) {
   const PrologueArgs& a = f.pa;
-  // the producers' shapes: bf16 rows of at most 8 KB (4 waves) or 32 KB
-  // (8 waves) in registers, T partials of 32 columns each, all summed by the
+  // the producers' shapes: rows of at most 4096 (4 waves) or 16384 (8 waves)
+  // values in registers, T partials of 32 columns each, all summed by the
   // GEMM blocks in one pass
   if (g.M < 1 || g.M > 16 || a.n != g.M || 2 * g.Kb != a.d || a.d % 32 || a.d > (g.Kb > 2048 ? 16384 : 4096) ||
       a.nqb != g.M || !f.sync || g.r_pad > 256 || (g.r_pad > 0 && (a.nqg < 1 || a.r_pad % 32 || !g.P)) ||
       f.nprod != a.nqb + (g.r_pad ? ((a.n + 15) / 16) * a.nchunk * a.nqg : 0) || g.nchunk != a.nchunk ||
       g.nchunk > gemv_max_chunks(g.M, g.Kb, g.ldt))
     return hipErrorInvalidValue;
-  return g.acc ? gemv_fused_t<true>(g, f, st) : gemv_fused_t<false>(g, f, st);
+  if (x_bf16) return g.acc ? gemv_fused_t<true, 1>(g, f, st) : gemv_fused_t<false, 1>(g, f, st);
+  return g.acc ? gemv_fused_t<true, 2>(g, f, st) : gemv_fused_t<false, 2>(g, f, st);
 }
 
 template <int BITS, int EPI>

@@ -120,8 +120,8 @@ struct PrologueArgs {
 };
 
 
-// The one-launch few-token layer (tq_gemm.hip): the producers' work (bf16 X;
-// pa in partial mode: pa.nqb = n row blocks, then the T blocks with QS = 2,
+// The one-launch few-token layer (tq_gemm.hip): the producers' work (pa in
+// partial mode: pa.nqb = n row blocks, then the T blocks with QS = 2,
 // pa.nqg = r_pad / 32), nprod = their number, the hand-off words, the polls
 // before a wait gives up, and a test hook (silent: the producers never
 // signal, so every wait gives up).
@@ -132,11 +132,11 @@ struct SmallFuse {
   unsigned spin;
   int silent;
 };
-hipError_t launch_gemv_fused(const GemmArgs& g, const SmallFuse& f, hipStream_t st);
+hipError_t launch_gemv_fused(const GemmArgs& g, const SmallFuse& f, bool x_bf16, hipStream_t st);
 // Whether that launch's grid (nprod producers, N / 16 GEMM blocks) is at most
-// a quarter larger than what is resident at once on the current device; dbg:
-// the accumulator-export instance.
-bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool dbg);
+// a quarter larger than what is resident at once on the current device, for
+// X of that type; dbg: the accumulator-export instance.
+bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool x_bf16, bool dbg);
 
 // The products of T block tb = (rt, c, qg) -- rows 16 rt .. 16 rt + 15, the
 // k-chunk c, the QS 16-column slices of group qg -- left per wave in

@@ -387,7 +387,7 @@ def _one_launch(n, d, r):
 
 
 def _fused_small(n, d, m, r):
-    """Shapes of the one-launch few-token GEMM (bf16 X): up to 16 tokens, d up to 16384, not the decode kernel's, and
+    """Shapes of the one-launch few-token GEMM: up to 16 tokens, d up to 16384, not the decode kernel's, and
     a grid resident at once (the shapes here have at most a few hundred blocks, or more than a GPU of 256 compute
     units holds: 2048 blocks of at least 4 waves)."""
     return n <= 16 and d <= 16384 and not _one_launch(n, d, r) and m // 16 < 2048
@@ -429,6 +429,33 @@ def test_small_n_single_launch_handoff(n, d, m, r):
         assert torch.equal(y, ys[0])
     ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"] if r else None, c["L2"] if r else None)
     _assert_y(ys[0], ref["Y"], f"n{n}")
+
+
+@pytest.mark.parametrize("n,d,m,r", [(16, 512, 512, 16), (5, 14336, 80, 64)])
+def test_one_launch_with_fp32_x(n, d, m, r):
+    """fp32 X takes the one-launch few-token GEMM too (its producers read fp32 rows): one launch per call, codes,
+    scales and every accumulator bit-exact, Y within the tolerance."""
+    print(f"case n={n} d={d} m={m} r={r}", flush=True)
+    c = draw_custom(n, d, m, r, seed=60 + n, x_dtype="f32")
+    y, ws, wc, sw, acc_k = _run_linear(c["X"], "f32", c["R"], c["L1"], c["L2"], torch.bfloat16, want_acc=True)
+    lowrank = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+    xt = _x_tensor(c["X"], "f32")
+    tq.tq_profile_reset()
+    tq.tq_profile_enable(True)
+    y2 = tq.tq_linear(xt, wc, sw, lowrank, m, r, ws=tq.linear_workspace(n, d, m, r, DEV))
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    names = set(tq.tq_profile_read())
+    tq.tq_profile_reset()
+    assert names == {"small_fused"}, names
+    assert torch.equal(y2, y)
+    ref = tqo.tq_linear_ref(c["X"], c["R"], c["L1"], c["L2"])
+    sx, codes = _ws_codes(ws, n, d, m, r)
+    assert np.array_equal(sx, ref["s_x"])
+    assert np.array_equal(codes, ref["codes_x"])
+    assert np.array_equal(acc_k, ref["acc"])
+    _assert_t(ws, c["X"], c["L1"], n, d, m, r)
+    _assert_y(y, ref["Y"], f"fp32 X n={n}")
 
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 8192, 40, 32), (16, 4096, 300, 64), (8, 14336, 72, 64),

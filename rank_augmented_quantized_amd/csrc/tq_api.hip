@@ -116,7 +116,8 @@ struct LinearWs {
   size_t sync, ctr, sx, xc, t, p, total;
   int r_pad;  // columns of T
   bool small, decode;
-  bool fused;  // the one-launch few-token layer (fplan), when its grid fits
+  bool fused;     // tq_linear: the one-launch few-token layer (fplan), when its grid fits
+  bool fusable;   // the shape has a one-launch plan (fplan; the asymmetric layer too)
   tq::ProloguePlan plan, fplan;
   tq::DecodePlan dplan;
 };
@@ -140,8 +141,9 @@ LinearWs linear_ws(int64_t n, int64_t d, int64_t m, int64_t tcols, bool two_laun
       psize = (size_t)w.plan.nchunk * (size_t)n * (size_t)w.r_pad * 4;
     // one launch up to 16 tokens; for 17 .. 32 (two 16-token tiles per
     // block, twice the producers) the two launches measured faster
-    w.fused = !two_launch && n > 0 && n <= 16 && d <= 16384 && w.r_pad % 32 == 0;
-    if (w.fused) {
+    w.fusable = n > 0 && n <= 16 && d <= 16384 && w.r_pad % 32 == 0;
+    w.fused = !two_launch && w.fusable;
+    if (w.fusable) {
       w.fplan = tq::plan_prologue_fused((int)n, (int)d, w.r_pad, tq::gemv_max_chunks((int)n, (int)(d / 2), w.r_pad));
       if (w.fplan.ntb > 0)
         psize = std::max(psize, (size_t)w.fplan.nchunk * (size_t)n * (size_t)w.r_pad * 4);
@@ -974,9 +976,6 @@ tq_status asym_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m
   tq::bf16_t* T = (tq::bf16_t*)(base + L.t);
   const tq::bf16_t* L1t = (const tq::bf16_t*)lowrank;
   float* P = (float*)(base + L.p);
-  TQ_RUN("prologue_asym", stream,
-         tq::launch_prologue_asym(X, x_dt == TQ_BF16, (int)n, (int)d, L1t, rp, L.plan, xc, sx, zx, P,
-                                  rp ? T : nullptr, (unsigned*)(base + L.ctr), stream));
   GemmArgs g{};
   g.A = xc;
   g.lda = L.small ? d / 2 : d;  // codes u - 8: nibble-packed for the small-n GEMM, else int8
@@ -999,6 +998,26 @@ tq_status asym_run(const void* X, tq_dtype x_dt, int64_t n, int64_t d, int64_t m
   g.ldy = m;
   g.y_bf16 = y_dt == TQ_BF16;
   g.acc = acc;
+  const bool xb = x_dt == TQ_BF16;
+  if (L.fusable && tq::gemv_fused_fits((int)n, (int)(d / 2), (int)m, L.fplan.nqb + L.fplan.ntb, xb, acc != nullptr)) {
+    // one launch, as tq_linear's few-token layer, with the asymmetric quantiser in the producers
+    const tq::ProloguePlan& fp = L.fplan;
+    tq::SmallFuse f{};
+    f.pa = tq::PrologueArgs{X, (int)n, (int)d, L1t, rp, fp.kc, fp.nchunk, fp.qs, fp.nqg, fp.nqb, 1, 1, 0, xc, sx, P,
+                            rp ? T : nullptr, (unsigned*)(base + L.ctr)};
+    f.zx = zx;
+    f.nprod = fp.nqb + fp.ntb;
+    f.sync = (unsigned*)(base + L.sync);
+    f.spin = kDecodeSpin;
+    g.P = rp ? P : nullptr;
+    g.nchunk = fp.nchunk;
+    g.Tout = rp ? T : nullptr;
+    TQ_RUN("small_fused_asym", stream, tq::launch_gemv_fused(g, f, xb, stream));
+    return TQ_OK;
+  }
+  TQ_RUN("prologue_asym", stream,
+         tq::launch_prologue_asym(X, xb, (int)n, (int)d, L1t, rp, L.plan, xc, sx, zx, P, rp ? T : nullptr,
+                                  (unsigned*)(base + L.ctr), stream));
   if (L.small) {
     if (rp && (L.plan.partial || L.plan.sum_to_p0)) {
       g.P = P;

@@ -98,8 +98,12 @@ __device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem
   const int b = blockIdx.x;
   if (b < a.nqb) {
     constexpr int CHB = WAVES == 4 ? 2 : 4;  // 8-value chunks per thread: rows up to 8 KB (4 waves), 32 KB (8 waves)
-    quant_row_block_reg<XT, CHB, true>((const XT*)a.X + (size_t)b * a.d, a.d, a.xc + (size_t)b * (a.d >> 1), a.sx + b,
-                                       reinterpret_cast<float*>(smem));
+    const XT* row = (const XT*)a.X + (size_t)b * a.d;
+    uint8_t* codes = a.xc + (size_t)b * (a.d >> 1);
+    if (f.zx)
+      quant_row_block_asym<XT, CHB>(row, a.d, codes, a.sx + b, f.zx + b, reinterpret_cast<float*>(smem));
+    else
+      quant_row_block_reg<XT, CHB, true>(row, a.d, codes, a.sx + b, reinterpret_cast<float*>(smem));
   } else {
     auto sP = reinterpret_cast<float (*)[16][33]>(smem);
     const TBlock t = t_block_products<XT, 2, WAVES, 8>(a, b - a.nqb, sP);
@@ -244,16 +248,19 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 #pragma unroll
     for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
   };
+  auto load_zz = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = min(16 * (wave & 1) + 4 * lg + i, g.M - 1);
+      zzv[i] = g.zx[rr] + 8.0f * g.sx[rr];
+    }
+  };
   if (LR || QL) {
     swv = g.sw[min(n0 + l16, g.N - 1)];
     if (FU == 0) load_sx();
     if (LR && g.zx) {
       wzv = swv * (float)g.csw[min(n0 + l16, g.N - 1)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = min(16 * (wave & 1) + 4 * lg + i, g.M - 1);
-        zzv[i] = g.zx[rr] + 8.0f * g.sx[rr];
-      }
+      if (FU == 0) load_zz();
     }
   }
   // QL: the first 64 ranks of the second stage's operands and its scales
@@ -305,6 +312,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     asm volatile("s_barrier" ::: "memory");
     ok = s_ok != 0;
     if (LR || QL) load_sx();
+    if (LR && g.zx) load_zz();
     if (XL)
       load_xl();
     else

@@ -86,6 +86,69 @@ __device__ __forceinline__ void quant_row_block_reg(const T* __restrict__ x, int
   }
 }
 
+// The same row quantised at 4 bits with a per-token zero-point (CoQuant
+// notes, "CoQuant: Joint Weight-Activation Subspace Projection for
+// Mixed-Precision LLMs", Eq. 1 with a zero-point): z = min, s = fl32(fl32(max
+// - min) / 15), codes u - 8 nibble-packed (even k in the low nibble), with
+// the block-wide min and max (exact in any order).  Codes, s and z stored at
+// agent scope, for readers in other blocks of the same launch.
+template <typename T, int CHB>
+__device__ __forceinline__ void quant_row_block_asym(const T* __restrict__ x, int d, uint8_t* __restrict__ c,
+                                                     float* __restrict__ s, float* __restrict__ z, float* red) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, w = tid >> 6, nw = nthr >> 6;
+  const int nch = d >> 3;
+  Row8<T> r[CHB];
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    const int ch = tid + nthr * i;
+    if (ch < nch) r[i].load(x + 8 * ch);
+  }
+  float mx = -INFINITY, nm = -INFINITY;  // max and -min (threads without values keep -inf)
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    if (tid + nthr * i < nch) {
+      float v[8];
+      r[i].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mx = fmaxf(mx, v[e]);
+        nm = fmaxf(nm, -v[e]);
+      }
+    }
+  }
+  mx = wave_fmax(mx);
+  nm = wave_fmax(nm);
+  if (lane == 0) {
+    red[w] = mx;
+    red[nw + w] = nm;
+  }
+  __syncthreads();
+  mx = -INFINITY;
+  nm = -INFINITY;
+  for (int i = 0; i < nw; ++i) {
+    mx = fmaxf(mx, red[i]);
+    nm = fmaxf(nm, red[nw + i]);
+  }
+  const AsymScale a = asym_scale<4>(-nm, mx);
+  if (tid == 0) {
+    __hip_atomic_store(s, a.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(z, a.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < CHB; ++i) {
+    const int ch = tid + nthr * i;
+    if (ch < nch) {
+      float v[8];
+      int q[8];
+      r[i].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = code_asym<4>(v[e] - a.z, a);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(c + (size_t)ch * 4), pack_nibbles(q), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prologue of tq_linear: one launch, two kinds of blocks.
 //  * blocks [0, nqb): 4-bit codes and s_x of WAVES rows, one per wave, or,
@@ -121,12 +184,13 @@ struct PrologueArgs {
 
 
 // The one-launch few-token layer (tq_gemm.hip): the producers' work (pa in
-// partial mode: pa.nqb = n row blocks, then the T blocks with QS = 2,
+// partial mode; zx: per-token zero-points of asymmetric activations, or null: pa.nqb = n row blocks, then the T blocks with QS = 2,
 // pa.nqg = r_pad / 32), nprod = their number, the hand-off words, the polls
 // before a wait gives up, and a test hook (silent: the producers never
 // signal, so every wait gives up).
 struct SmallFuse {
   PrologueArgs pa;
+  float* zx;
   int nprod;
   unsigned* sync;
   unsigned spin;

@@ -176,3 +176,34 @@ def test_linear_asym_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, eager)
+
+
+@pytest.mark.parametrize("n,d,m,rk,launches", [(16, 4096, 300, 64, {"small_fused_asym"}),
+                                               (5, 14336, 80, 64, {"small_fused_asym"}),
+                                               (24, 2048, 200, 32, {"prologue_asym", "gemm_small_n_asym"})])
+def test_linear_asym_few_token_launches(n, d, m, rk, launches):
+    """Up to 16 tokens the asymmetric layer runs in one launch (the producer blocks quantise with a zero-point),
+    17 .. 32 in two; both give codes, scales, zero-points and accumulators bit-exact and Y within the tolerance,
+    and the hand-off words are zero again after each call."""
+    print(f"case n={n} d={d} m={m} r={rk}", flush=True)
+    c = draw_custom(n, d, m, rk, seed=7100 + n, outlier_count=2, outlier_scale=30.0)
+    wc, sw = tq.tq_pack_weight(_t(c["R"]), 4)
+    cs = tq.tq_weight_colsum(wc, d, 4)
+    lr = tq.tq_pack_lowrank(_t(c["L1"], torch.bfloat16), _t(c["L2"], torch.bfloat16))
+    ws = torch.zeros(tq.load().tq_linear_asym_workspace_bytes(n, d, m, rk), dtype=torch.uint8, device=DEV)
+    xt = _t(c["X"], torch.bfloat16)
+    tq.tq_profile_reset()
+    tq.tq_profile_enable(True)
+    y = tq.tq_linear_asym(xt, wc, sw, cs, lr, m, rk, ws=ws)
+    torch.cuda.synchronize()
+    tq.tq_profile_enable(False)
+    names = set(tq.tq_profile_read())
+    tq.tq_profile_reset()
+    assert names == launches, names
+    assert not ws[:4096].view(torch.int32).cpu().numpy().any()
+    y_again = tq.tq_linear_asym(xt, wc, sw, cs, lr, m, rk, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_again, y)
+    y_run, ws_run, cs_run = _run(c["X"], "bf16", c["R"], c["L1"], c["L2"])
+    assert torch.equal(y_run, y)
+    _check(c["X"], c["R"], c["L1"], c["L2"], y_run, ws_run, cs_run)

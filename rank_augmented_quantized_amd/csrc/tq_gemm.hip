@@ -124,22 +124,28 @@ __device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem
     __hip_atomic_fetch_add(f.sync + kFDone + kFStride * threadIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// FU: 0, or the one-launch form with bf16 (1) or fp32 (2) X.
-template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false, int FU = 0>
+// FU: 0, or the one-launch form with bf16 (1) or fp32 (2) X.  GB: groups of
+// 16 output channels per block (GB > 1: one 16-token tile, the rank-augmented
+// epilogue); every wave streams its k-range of all GB groups' weights and
+// uses each activation fragment GB times, and wave w finishes group w, so a
+// block fetches the codes and the partials of T once for 16 GB channels.
+template <int BITS, int EPI, int WAVES, bool TWO, bool XL, bool DBG = false, int FU = 0, int GB = 1>
 __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmArgs g, SmallFuse f) {
+  static_assert(GB == 1 || (EPI == EPI_LINEAR && !TWO && GB <= WAVES), "channel groups: one token tile");
   constexpr int U = (WAVES == 4 && TWO && !XL) ? 4 : ((WAVES == 4 || TWO) ? 8 : 16);  // 64-byte steps per wave per batch
   constexpr int NT = WAVES * 64;
   constexpr int MT = TWO ? 32 : 16;  // token rows held for the low-rank stage
   constexpr bool LR = EPI == EPI_LINEAR;
   constexpr bool QL = EPI == EPI_QLR;  // quantised low-rank branch: second stage on the int8 MFMA
-  // LDS: red [WAVES][TWO ? 2 : 1][4][64] int | sT [MT x 256] bf16 | sL [16 x 256]
+  // LDS: red [WAVES][RT][4][64] int | sT [MT x 256] bf16 | sL [16 GB x 256]
   // bf16 | sPart [NT][2] float4; a producer block (FU) reuses it whole
-  constexpr int B_RED = WAVES * (TWO ? 2 : 1) * 4 * 64 * 4;
-  constexpr int B_ST = LR ? MT * 256 * 2 : 16, B_SL = LR ? 16 * 256 * 2 : 16, B_SP = LR ? NT * 32 : 16;
+  constexpr int RT = TWO ? 2 : GB;  // finished tiles: token tiles, or channel groups
+  constexpr int B_RED = WAVES * RT * 4 * 64 * 4;
+  constexpr int B_ST = LR ? MT * 256 * 2 : 16, B_SL = LR ? 16 * GB * 256 * 2 : 16, B_SP = LR ? NT * 32 : 16;
   constexpr int B_GEMV = B_RED + B_ST + B_SL + B_SP, B_PRO = FU != 0 ? WAVES * 16 * 33 * 4 : 0;
   __shared__ __attribute__((aligned(16))) uint8_t smem[B_GEMV > B_PRO ? B_GEMV : B_PRO];
   __shared__ int s_ok;
-  auto red = reinterpret_cast<int (*)[TWO ? 2 : 1][4][64]>(smem);
+  auto red = reinterpret_cast<int (*)[RT][4][64]>(smem);
   bf16_t* sT = reinterpret_cast<bf16_t*>(smem + B_RED);
   bf16_t* sL = reinterpret_cast<bf16_t*>(smem + B_RED + B_ST);
   auto sPart = reinterpret_cast<float4 (*)[2]>(smem + B_RED + B_ST + B_SL);
@@ -151,8 +157,11 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = (FU != 0 ? (int)blockIdx.x - f.nprod : (int)blockIdx.x) * 16;
-  const uint8_t* bp = g.B + (size_t)min(n0 + l16, g.N - 1) * g.ldb + 16 * lg;
+  const int n0 = (FU != 0 ? (int)blockIdx.x - f.nprod : (int)blockIdx.x) * 16 * GB;
+  const int wg = GB > 1 ? min(wave, GB - 1) : 0;  // the group this wave finishes (GB > 1)
+  const uint8_t* bp[GB];
+#pragma unroll
+  for (int gb = 0; gb < GB; ++gb) bp[gb] = g.B + (size_t)min(n0 + 16 * gb + l16, g.N - 1) * g.ldb + 16 * lg;
   const uint8_t* ap0 = g.A + (size_t)min(l16, g.M - 1) * g.lda + 16 * lg;
   const uint8_t* ap1 = g.A + (size_t)min(16 + l16, g.M - 1) * g.lda + 16 * lg;
   const int KS = (g.Kb + 63) / 64;
@@ -188,10 +197,13 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   // masked where used: conditional loads become branches whose register
   // merges force early waits on every load in flight.
   const int kb_last = max(0, min((max(send, sbeg + 1) - 1) * 64, g.Kb - 16 - 16 * lg));
-  uint4 bv[U], av0[U], av1[U];
+  uint4 bv[GB][U], av0[U], av1[U];
   auto load_w = [&](int s0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) bv[u] = *reinterpret_cast<const uint4*>(bp + min((s0 + u) * 64, kb_last));
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gb = 0; gb < GB; ++gb)
+        bv[gb][u] = *reinterpret_cast<const uint4*>(bp[gb] + min((s0 + u) * 64, kb_last));
   };
   auto load_x = [&](int s0) {
     if (XL) return;
@@ -208,7 +220,9 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   };
   const uint8_t* xl0 = xl_lds + min(l16, g.M - 1) * XS + 16 * lg;
   const uint8_t* xl1 = xl_lds + min(16 + l16, g.M - 1) * XS + 16 * lg;
-  i32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  i32x4 acc0[GB], acc1 = {0, 0, 0, 0};
+#pragma unroll
+  for (int gb = 0; gb < GB; ++gb) acc0[gb] = i32x4{0, 0, 0, 0};
   auto mma_batch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -219,21 +233,26 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
         if (TWO) av1[u] = *reinterpret_cast<const uint4*>(xl1 + kb);
       }
       if ((s0 + u) * 64 + 16 * lg >= g.Kb) {  // this lane group's 16 bytes lie past the row: zero codes
-        bv[u] = uint4{0, 0, 0, 0};
+#pragma unroll
+        for (int gb = 0; gb < GB; ++gb) bv[gb][u] = uint4{0, 0, 0, 0};
         av0[u] = uint4{0, 0, 0, 0};
         av1[u] = uint4{0, 0, 0, 0};
       }
       if (BITS == 4) {
-        const i32x4 b0 = unpack16(bv[u].x, bv[u].y), b1 = unpack16(bv[u].z, bv[u].w);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].x, av0[u].y), b0, acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av0[u].z, av0[u].w), b1, acc0, 0, 0, 0);
-        if (TWO) {
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].x, av1[u].y), b0, acc1, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].z, av1[u].w), b1, acc1, 0, 0, 0);
+        const i32x4 a0 = unpack16(av0[u].x, av0[u].y), a1 = unpack16(av0[u].z, av0[u].w);
+#pragma unroll
+        for (int gb = 0; gb < GB; ++gb) {
+          const i32x4 b0 = unpack16(bv[gb][u].x, bv[gb][u].y), b1 = unpack16(bv[gb][u].z, bv[gb][u].w);
+          acc0[gb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc0[gb], 0, 0, 0);
+          acc0[gb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc0[gb], 0, 0, 0);
+          if (TWO) {
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].x, av1[u].y), b0, acc1, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(av1[u].z, av1[u].w), b1, acc1, 0, 0, 0);
+          }
         }
       } else {
-        const i32x4 b0 = __builtin_bit_cast(i32x4, bv[u]);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0[u]), b0, acc0, 0, 0, 0);
+        const i32x4 b0 = __builtin_bit_cast(i32x4, bv[0][u]);
+        acc0[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av0[u]), b0, acc0[0], 0, 0, 0);
         if (TWO) acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, av1[u]), b0, acc1, 0, 0, 0);
       }
     }
@@ -244,22 +263,23 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   // asymmetric activations (codes u - 8): per row z + 8 s_x, per channel
   // s_w colsum(C_w) (CoQuant Eq. 1 with a zero-point)
   float zzv[4] = {0.f, 0.f, 0.f, 0.f}, wzv = 0.0f;
+  const int trow = TWO ? 16 * (wave & 1) : 0;  // first token row of the tile this wave may finish
   auto load_sx = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(16 * (wave & 1) + 4 * lg + i, g.M - 1)];
+    for (int i = 0; i < 4; ++i) sxv[i] = g.sx[min(trow + 4 * lg + i, g.M - 1)];
   };
   auto load_zz = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = min(16 * (wave & 1) + 4 * lg + i, g.M - 1);
+      const int rr = min(trow + 4 * lg + i, g.M - 1);
       zzv[i] = g.zx[rr] + 8.0f * g.sx[rr];
     }
   };
   if (LR || QL) {
-    swv = g.sw[min(n0 + l16, g.N - 1)];
+    swv = g.sw[min(n0 + 16 * wg + l16, g.N - 1)];
     if (FU == 0) load_sx();
     if (LR && g.zx) {
-      wzv = swv * (float)g.csw[min(n0 + l16, g.N - 1)];
+      wzv = swv * (float)g.csw[min(n0 + 16 * wg + l16, g.N - 1)];
       if (FU == 0) load_zz();
     }
   }
@@ -288,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     // the weights of the first batch and the rows of L2^T depend on nothing
     load_w(sbeg);
     if (LR && rp > 0) {
-      const int el = min(tid, 16 * rq - 1);
+      const int el = min(tid, 16 * GB * rq - 1);
       lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
     }
     if (wave == 0) {
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
   float4 pv[2][2];
   if (LR && rp > 0) {
     if (FU == 0) {
-      const int el = min(tid, 16 * rq - 1);
+      const int el = min(tid, 16 * GB * rq - 1);
       lv = *reinterpret_cast<const uint4*>(g.L2t + (size_t)min(n0 + el / rq, g.N - 1) * rp + 8 * (el % rq));
     }
     if (tid < NP * G) {
@@ -361,8 +381,8 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 
   // ---- low-rank operands into LDS (T rows >= M are zero) ----
   if (LR && rp > 0) {
-    if (tid < 16 * rq) *reinterpret_cast<uint4*>(sL + tid * 8) = (n0 + tid / rq < g.N) ? lv : uint4{0, 0, 0, 0};
-    for (int e = tid + NT; e < 16 * rq; e += NT) {
+    if (tid < 16 * GB * rq) *reinterpret_cast<uint4*>(sL + tid * 8) = (n0 + tid / rq < g.N) ? lv : uint4{0, 0, 0, 0};
+    for (int e = tid + NT; e < 16 * GB * rq; e += NT) {
       const int c = e / rq, q = e % rq;
       uint4 v = uint4{0, 0, 0, 0};
       if (n0 + c < g.N) v = *reinterpret_cast<const uint4*>(g.L2t + (size_t)(n0 + c) * rp + 8 * q);
@@ -411,23 +431,24 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    red[wave][0][i][lane] = acc0[i];
+#pragma unroll
+    for (int gb = 0; gb < GB; ++gb) red[wave][gb][i][lane] = acc0[gb][i];
     if (TWO) red[wave][TWO ? 1 : 0][i][lane] = acc1[i];
   }
   __syncthreads();
-  // wave t (t < number of 16-token tiles) finishes tile t
-  constexpr int TILES = TWO ? 2 : 1;
-  if (wave >= TILES) return;
-  const int tile = wave;
+  // wave t (t < number of 16-token tiles, or of channel groups) finishes
+  // tile t, or group t
+  if (wave >= RT) return;
+  const int tile = TWO ? wave : 0;
   int sacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int v = 0;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][tile][i][lane];
+    for (int w = 0; w < WAVES; ++w) v += red[w][wave][i][lane];
     sacc[i] = (BITS == 4) ? (v >> 8) : v;
   }
-  const int col = n0 + l16;
+  const int col = n0 + 16 * wg + l16;
   if constexpr (DBG && EPI != EPI_ACC) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -468,7 +489,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4) ? 4 : 2) void k_gemv(GemmA
     for (int t0 = 0; t0 < rp; t0 += 32) {
       // A: T rows (tokens), B: L2^T rows (channels); 8 consecutive t per lane
       const uint4 a8 = *reinterpret_cast<const uint4*>(sT + (16 * tile + l16) * rp + t0 + 8 * lg);
-      const uint4 b8 = *reinterpret_cast<const uint4*>(sL + l16 * rp + t0 + 8 * lg);
+      const uint4 b8 = *reinterpret_cast<const uint4*>(sL + (16 * wg + l16) * rp + t0 + 8 * lg);
       lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a8), as_bf16x8(b8), lr, 0, 0, 0);
     }
 #pragma unroll
@@ -532,11 +553,19 @@ static hipError_t gemv_cols_t(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Groups of 16 channels per block of the one-launch form: 4 when rows are
+// short (4-wave blocks) and more than two 16-channel blocks per compute unit
+// would exist (gate/up of Llama-3-8B: 224 blocks of 64 channels instead of 896
+// of 16, so the codes and the partials of T are fetched a quarter as often),
+// else 1.
+static int fused_gb(int N, int Kb) { return (Kb <= 2048 && (N + 15) / 16 > 512) ? 4 : 1; }
+
 // One-launch form (up to 16 tokens): the producers first in the grid, then
 // the GEMM blocks.
 template <bool DBG, int FU>
 static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_t st) {
-  const dim3 grid((unsigned)(f.nprod + (g.N + 15) / 16));
+  const int gb = fused_gb(g.N, g.Kb);
+  const dim3 grid((unsigned)(f.nprod + (g.N + 16 * gb - 1) / (16 * gb)));
   const size_t xl = (size_t)g.M * (size_t)(g.Kb + 16);
   const bool use_xl = xl <= (size_t)gemv_xl_bytes(g.Kb > 2048 ? 8 : 4) && g.Kb % 16 == 0;
   constexpr int E = EPI_LINEAR;
@@ -545,6 +574,11 @@ static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_
       launch_kernel(k_gemv<4, E, 8, false, true, DBG, FU>, grid, dim3(512), (unsigned)xl, st, g, f);
     else
       launch_kernel(k_gemv<4, E, 8, false, false, DBG, FU>, grid, dim3(512), 0u, st, g, f);
+  } else if (gb == 4) {
+    if (use_xl)
+      launch_kernel(k_gemv<4, E, 4, false, true, DBG, FU, 4>, grid, dim3(256), (unsigned)xl, st, g, f);
+    else
+      launch_kernel(k_gemv<4, E, 4, false, false, DBG, FU, 4>, grid, dim3(256), 0u, st, g, f);
   } else {
     if (use_xl)
       launch_kernel(k_gemv<4, E, 4, false, true, DBG, FU>, grid, dim3(256), (unsigned)xl, st, g, f);
@@ -569,11 +603,15 @@ static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
     return false;
   const size_t xl = (size_t)M * (size_t)(Kb + 16);
   const bool use_xl = xl <= (size_t)gemv_xl_bytes(Kb > 2048 ? 8 : 4) && Kb % 16 == 0;
+  const int gb = fused_gb(N, Kb);
   constexpr int E = EPI_LINEAR;
   hipError_t e;
   if (Kb > 2048)
     e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, true, DBG, FU>, 512, xl)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 8, false, false, DBG, FU>, 512, 0);
+  else if (gb == 4)
+    e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, true, DBG, FU, 4>, 256, xl)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, false, DBG, FU, 4>, 256, 0);
   else
     e = use_xl ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, true, DBG, FU>, 256, xl)
                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_gemv<4, E, 4, false, false, DBG, FU>, 256, 0);
@@ -581,7 +619,7 @@ static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
     (void)hipGetLastError();
     return false;
   }
-  return 4 * ((int64_t)nprod + (N + 15) / 16) <= 5 * (int64_t)cus * occ;
+  return 4 * ((int64_t)nprod + (N + 16 * gb - 1) / (16 * gb)) <= 5 * (int64_t)cus * occ;
 }
 
 bool gemv_fused_fits(int M, int Kb, int N, int nprod, bool x_bf16, bool dbg) {

@@ -98,6 +98,9 @@ GCASES = [
     ("g2_n1030_one_pass_prologue", 1030, 512, (256, 256), 64, "normal", "bf16", 2),
     ("g4_n70_r0", 70, 512, (256, 256, 256, 64), 0, "normal", "bf16", 0),
     ("g8_n33", 33, 256, (256,) * 7 + (48,), 16, "normal", "bf16", 0),
+    # one launch with blocks of 64 channels (more than 512 blocks of 16), the
+    # second layer ragged
+    ("g2_n12_one_launch_64ch", 12, 1024, (4096, 4112), 32, "normal", "bf16", 2),
 ]
 
 

@@ -332,6 +332,9 @@ LCASES = [
     ("n100_d2048_tiles128", 100, 2048, 300, 32, "normal", "bf16", 2),
     ("n200_d8192_tiles128", 200, 8192, 520, 64, "normal", "bf16", 3),
     ("n70_d2080_ragged_k_f32_out", 70, 2080, 200, 32, "student_t", "bf16", 0),
+    # one launch with blocks of 4 groups of 16 channels (more than 512 groups),
+    # the last block with one group inside the layer
+    ("n12_m8272_one_launch_64ch", 12, 2048, 8272, 32, "normal", "bf16", 2),
 ]
 
 
@@ -387,17 +390,18 @@ def _one_launch(n, d, r):
 
 
 def _fused_small(n, d, m, r):
-    """Shapes of the one-launch few-token GEMM: up to 16 tokens, d up to 16384, not the decode kernel's, and
-    a grid resident at once (the shapes here have at most a few hundred blocks, or more than a GPU of 256 compute
-    units holds: 2048 blocks of at least 4 waves)."""
-    return n <= 16 and d <= 16384 and not _one_launch(n, d, r) and m // 16 < 2048
+    """Shapes of the one-launch few-token GEMM: up to 16 tokens, d up to 16384, not the decode kernel's, and a grid
+    about resident at once: blocks of 16 channels up to 512 of them, else (d <= 4096) of 64 channels (the shapes
+    here have at most a few hundred blocks, or far more than a GPU of 256 compute units holds)."""
+    return (n <= 16 and d <= 16384 and not _one_launch(n, d, r)
+            and (m // 16 <= 512 or (d <= 4096 and m // 64 < 600)))
 
 
 @pytest.mark.parametrize("n,d,m,r", [(1, 4096, 300, 64), (2, 2048, 200, 64), (1, 4064, 64, 32), (2, 512, 40, 0),
                                      (2, 1024, 48, 256), (1, 14336, 64, 32), (1, 16384, 40, 32), (1, 16384, 40, 256), (2, 8192, 72, 32),
                                      (1, 96, 16, 32), (5, 2048, 200, 64), (3, 96, 16, 32), (16, 4096, 300, 64),
                                      (8, 14336, 72, 64), (11, 4064, 130, 256), (16, 8192, 64, 32), (9, 16384, 40, 32), (3, 16416, 40, 32),
-                                     (8, 1024, 40000, 32),
+                                     (8, 1024, 60000, 32), (16, 1024, 8256, 32), (5, 4096, 10000, 64),
                                      (24, 2048, 200, 64)])
 def test_small_n_single_launch_handoff(n, d, m, r):
     """Up to 16 tokens run in one launch whose blocks wait for the codes and the partials of T that other blocks

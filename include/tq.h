@@ -365,10 +365,14 @@ tq_status tq_linear_mp_asym_workspace_offsets(int64_t n, int64_t d, int64_t d_hi
  * tq_linear_asym -- tq_linear with per-token asymmetric 4-bit activations
  * (same z, s and codes as tq_linear_mp_asym's 4-bit subspace):
  *   Y = s_x s_w (.) (U C_w^T) + z_x (s_w (.) colsum(C_w)) + (X L1) L2,
- * colsum = tq_weight_colsum(w_codes, m, d, 4) (m int32).  d <= 16384.  Two
- * launches: the quantiser with T = X L1, then the GEMM (the tile GEMM, or for
- * n <= 32 the weight-streaming small-n GEMM) whose epilogue adds the
- * zero-point term.  ws:
+ * colsum = tq_weight_colsum(w_codes, m, d, 4) (m int32).  d <= 16384.  Up to
+ * 16 tokens one launch, as tq_linear's few-token GEMM (its first blocks
+ * quantise with the zero-point and compute partials of T, under the same
+ * grid-size rule); otherwise two launches: the quantiser with T = X L1, then
+ * the GEMM (the tile GEMM, or for n <= 32 the weight-streaming small-n GEMM).
+ * The GEMM's epilogue adds the zero-point term.  The one-launch form's waits
+ * are bounded as tq_linear's (word 32 of the hand-off words at the start of
+ * the workspace, NaN outputs).  ws:
  * tq_linear_asym_workspace_bytes(n, d, m, r) bytes, zero-filled once before
  * its first use (as tq_linear's).  Errors as tq_linear, plus TQ_ERR_SHAPE for
  * d > 16384.

@@ -36,12 +36,13 @@ namespace tq {
 //   is one 16x16 bf16 MFMA chain whose result layout matches the integer
 //   accumulator's (lane l, element i -> token 4 (l / 16) + i, channel l % 16).
 //
-// FU, the one-launch form (up to 16 tokens): the prologue's work runs in the same grid
-// (TwinQuant notes, section 04.C: the activations are quantised while the
-// residual GEMM runs, and both components meet in one epilogue).  Blocks
-// [0, nqb) quantise one token row each (codes and s_x), blocks [nqb, nprod)
-// compute one fp32 partial of T each (rows 16 rt.., k-chunk c, 32 columns),
-// and the GEMM blocks follow.  A GEMM block issues its first batch of weight
+// FU, the one-launch form (up to 16 tokens): the prologue's work runs in the
+// same grid (TwinQuant notes, section 04.C: the activations are quantised
+// while the residual GEMM runs, and both components meet in one epilogue).
+// Blocks [0, nqb) quantise one token row each (codes, s_x, and z_x for
+// asymmetric activations), blocks [nqb, nprod) compute one fp32 partial of T
+// each (rows 16 rt.., k-chunk c, 32 columns), and the GEMM blocks follow,
+// each with GB groups of 16 output channels.  A GEMM block issues its first batch of weight
 // loads, which depend on nothing, and only then waits for the producers:
 //  * a producer stores its results at agent scope (written through to the
 //    device's point of coherence, past the XCDs' separate L2s), waits until
@@ -60,14 +61,13 @@ namespace tq {
 // group's counter (groups of at least 32 consecutive blocks, at most
 // kFGroups groups), the last of a group resets it and adds one to kFFin, and
 // the last group's last block subtracts nprod from every copy of the done
-// counter and the number of
-// groups from kFFin, so every counter is zero again when the kernel ends,
-// whatever the order in which the blocks ran.  One counter for all the
-// blocks would serialise hundreds of returning atomics on one address at
-// the end of the kernel.  The wait is
-// bounded: a block whose wait gives up sets the sticky flag word kWFlag and
-// writes NaN to its outputs, and GEMM blocks that find the flag set when
-// they start write NaN too, until the workspace is zero-filled again.
+// counter and the number of groups from kFFin, so every counter is zero
+// again when the kernel ends, whatever the order in which the blocks ran.
+// One counter for all the blocks would serialise hundreds of returning
+// atomics on one address at the end of the kernel.  The wait is bounded: a
+// block whose wait gives up sets the sticky flag word kWFlag and writes NaN
+// to its outputs, and GEMM blocks that find the flag set when they start
+// write NaN too, until the workspace is zero-filled again.
 // ---------------------------------------------------------------------------
 // Most bytes of activation codes the small-n GEMM stages in LDS: what
 // leaves the blocks per CU of its launch bounds (2 of 8 waves, 4 of 4 waves)
@@ -97,7 +97,7 @@ __device__ __forceinline__ void small_producer(const SmallFuse& f, uint8_t* smem
   const PrologueArgs& a = f.pa;
   const int b = blockIdx.x;
   if (b < a.nqb) {
-    constexpr int CHB = WAVES == 4 ? 2 : 4;  // 8-value chunks per thread: rows up to 8 KB (4 waves), 32 KB (8 waves)
+    constexpr int CHB = WAVES == 4 ? 2 : 4;  // 8-value chunks per thread: rows up to 4096 (4 waves), 16384 (8 waves)
     const XT* row = (const XT*)a.X + (size_t)b * a.d;
     uint8_t* codes = a.xc + (size_t)b * (a.d >> 1);
     if (f.zx)
@@ -592,9 +592,9 @@ static hipError_t gemv_fused_t(const GemmArgs& g, const SmallFuse& f, hipStream_
 // device: at most a quarter more blocks than fit.  The producers come first
 // in the grid, so they never wait for a slot; but GEMM blocks beyond the
 // resident ones start only as others finish, which cuts the weight stream in
-// two.  Measured: 296 blocks on 256 slots (down projection, 8 tokens) still
-// faster than two launches, 1816 on 1024 (gate and up grouped, 16 tokens)
-// slower.
+// two.  Measured with blocks of 16 channels: 296 blocks on 256 slots (down
+// projection, 8 tokens) still faster than two launches, 1816 on 1024 (gate
+// and up grouped, 16 tokens) slower.
 template <bool DBG, int FU>
 static bool gemv_fused_fits_t(int M, int Kb, int N, int nprod) {
   int dev = 0, cus = 0, occ = 0;

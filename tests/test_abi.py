@@ -320,6 +320,20 @@ def test_workspace_regions_fit_and_do_not_overlap(lib, n, d, m, r):
            (off["z_xl"], 4 * n), (off["z_xh"], 4 * n)])
 
 
+def test_counter_block_is_at_fixed_offsets(lib):
+    """The hand-off words and counters that must be zero before a call sit in the first 8 KiB of the workspace
+    whatever the shape, and no other region of tq_linear or tq_linear_asym reaches into them: one workspace,
+    zero-filled once, can serve calls of any shape in turn (and the no-alloc scratch clears 64 KiB once)."""
+    shapes = [(1, 512, 256, 32), (5, 2048, 200, 64), (16, 4096, 14336, 64), (8, 14336, 4096, 64), (33, 256, 130, 0),
+              (200, 1024, 384, 64), (256, 4096, 14336, 64), (1030, 544, 96, 128), (4096, 4096, 4096, 32)]
+    for n, d, m, r in shapes:
+        off = tqb.tq_linear_workspace_offsets(n, d, m, r)
+        assert off["sync"] == 0
+        assert min(off["s_x"], off["x_codes"], off["T"]) >= 8192, (n, d, m, r, off)
+        aoff = tqb.tq_linear_asym_workspace_offsets(n, d, m, r)
+        assert min(aoff.values()) >= 8192, (n, d, m, r, aoff)
+
+
 def test_boundary_departures_are_enforced(lib):
     """Each documented difference from the survey's boundary, checked where it is decided (before any HIP call)."""
     n, m, r = 8, 256, 16

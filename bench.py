@@ -632,7 +632,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": wl.title, "n": n, "d": d, "m": m, "r": r, "x_dtype": wl.x_dtype, "y_dtype": "bf16",
-                   "pct_int8_mfma_peak": round(100 * value / PEAK_INT8_TOPS, 2)},
+                   "pct_int8_mfma_peak": round(100 * value / PEAK_INT8_TOPS, 2),
+                   "why_this_workload": "the metric's prefill half (TOPS and % of int8 MFMA peak) is quoted on the "
+                                        "4096-token attention projection, a whole single-GPU layer; the small case, "
+                                        "the MLP sweep and the decode rows (GB/s and % of HBM) are the sweep lines"},
         "roofline": roofline, "cpu_baseline": cpu, "sweep": sweep, "stream_ceiling": ceiling, "mfma_ceiling": mceiling,
         "kernel_source_hash": khash,
     }
